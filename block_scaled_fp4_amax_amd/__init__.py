@@ -1,0 +1,287 @@
+"""block_scaled_fp4_amax_amd -- Python binding of libfp4q.so, the gfx950
+block-scaled FP4 quantisation library.
+
+The functions carry the C-ABI names (fp4_quantize, fp4_dequantize, fp4_qdq,
+fp4_cast_transpose, fp4_cast_transpose_grouped and the fp4q_* helpers).  They
+only marshal arguments: torch supplies device memory and the current HIP
+stream, every step of the computation runs in the library's HIP kernels.  If
+the library is not built, importing the binding raises; there is no fallback.
+
+Layouts, numerics and error rules are those documented in include/fp4q.h.
+"""
+import ctypes as ct
+import os
+
+__all__ = [
+    "Fp4Error", "Cfg", "Sizes", "make_cfg", "lib", "fp4q_abi_version", "fp4q_status_str", "fp4q_buffer_sizes",
+    "fp4q_workspace_bytes", "fp4_quantize", "fp4_dequantize", "fp4_qdq", "fp4_cast_transpose",
+    "fp4_cast_transpose_grouped", "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp4q.so")
+
+OK, ERR_NULL, ERR_DTYPE, ERR_SHAPE, ERR_MODE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP, ERR_ABI = range(10)
+ABI_VERSION = 1
+
+FORMATS = {"nvfp4": 0, "amdfp4": 1, "mxfp4": 2}
+SCALE_FORMATS = {None: 0, "default": 0, "e4m3": 1, "ue5m3": 2, "ue8m0": 3}
+TWO_LEVEL = {"none": 0, "tensorwise": 1, "outer_block": 2}
+ROUNDING = {"rne": 0, "stochastic": 1}
+DTYPES = {"bf16": 0, "fp16": 1, "fp32": 2}
+
+
+class Fp4Error(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (where, fp4q_status_str(status), status))
+
+
+class Cfg(ct.Structure):
+    _fields_ = [("abi_version", ct.c_uint32), ("format", ct.c_int32), ("scale_format", ct.c_int32),
+                ("two_level", ct.c_int32), ("outer_block_size", ct.c_int32), ("outer_2d", ct.c_int32),
+                ("rounding", ct.c_int32), ("outer_mode", ct.c_int32), ("input_dtype", ct.c_int32),
+                ("reserved", ct.c_int32), ("seed", ct.c_uint64), ("step", ct.c_uint64),
+                ("index_base", ct.c_uint64)]
+
+
+class Sizes(ct.Structure):
+    _fields_ = [(n, ct.c_size_t) for n in ("row_codes", "row_scales", "row_outer", "col_codes", "col_scales",
+                                           "col_outer", "y", "residual", "workspace")]
+
+
+def make_cfg(format="nvfp4", scale_format=None, two_level="none", outer_block_size=0, outer_2d=False,
+             rounding="rne", outer_mode=0, seed=0, step=0, index_base=0, input_dtype="bf16"):
+    """Build an fp4q_cfg (string names or the raw integers of include/fp4q.h)."""
+    def pick(table, v):
+        return v if isinstance(v, int) and not isinstance(v, bool) else table[v]
+    return Cfg(ABI_VERSION, pick(FORMATS, format), pick(SCALE_FORMATS, scale_format), pick(TWO_LEVEL, two_level),
+               int(outer_block_size), int(bool(outer_2d)), pick(ROUNDING, rounding), int(outer_mode),
+               pick(DTYPES, input_dtype), 0, int(seed), int(step), int(index_base))
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libfp4q.so (ctypes), with argument types declared."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libfp4q.so is not built (run __graft_entry__.build() or "
+                              "python block_scaled_fp4_amax_amd/build.py)")
+        L = ct.CDLL(LIB_PATH)
+        P, I64, SZ = ct.c_void_p, ct.c_int64, ct.c_size_t
+        C = ct.POINTER(Cfg)
+        L.fp4q_abi_version.restype = ct.c_uint32
+        L.fp4q_abi_version.argtypes = []
+        L.fp4q_status_str.restype = ct.c_char_p
+        L.fp4q_status_str.argtypes = [ct.c_int]
+        L.fp4q_buffer_sizes.restype = ct.c_int
+        L.fp4q_buffer_sizes.argtypes = [C, I64, I64, ct.POINTER(Sizes)]
+        L.fp4q_workspace_bytes.restype = SZ
+        L.fp4q_workspace_bytes.argtypes = [C, I64, I64]
+        L.fp4_quantize.restype = ct.c_int
+        L.fp4_quantize.argtypes = [C, P, I64, I64, I64, P, P, P, P, P, SZ, P]
+        L.fp4_dequantize.restype = ct.c_int
+        L.fp4_dequantize.argtypes = [C, P, P, P, I64, I64, ct.c_int32, P, P]
+        L.fp4_qdq.restype = ct.c_int
+        L.fp4_qdq.argtypes = [C, P, I64, I64, I64, P, P, P, P, P, P, SZ, P]
+        L.fp4_cast_transpose.restype = ct.c_int
+        L.fp4_cast_transpose.argtypes = [C, P, I64, I64, I64, P, P, P, P, P, P, P, P, SZ, P]
+        L.fp4_cast_transpose_grouped.restype = ct.c_int
+        L.fp4_cast_transpose_grouped.argtypes = [C, ct.c_int32, P, I64, P, I64, P, P, P, P, P, P, P, P, SZ, P]
+        if L.fp4q_abi_version() != ABI_VERSION:
+            raise ImportError("libfp4q.so ABI %d, binding expects %d" % (L.fp4q_abi_version(), ABI_VERSION))
+        _lib = L
+    return _lib
+
+
+def fp4q_abi_version():
+    return lib().fp4q_abi_version()
+
+
+def fp4q_status_str(status):
+    return lib().fp4q_status_str(int(status)).decode()
+
+
+def fp4q_buffer_sizes(cfg, rows, cols):
+    s = Sizes()
+    st = lib().fp4q_buffer_sizes(ct.byref(cfg), int(rows), int(cols), ct.byref(s))
+    if st:
+        raise Fp4Error(st, "fp4q_buffer_sizes")
+    return {n: getattr(s, n) for n, _ in Sizes._fields_}
+
+
+def fp4q_workspace_bytes(cfg, rows, cols):
+    return lib().fp4q_workspace_bytes(ct.byref(cfg), int(rows), int(cols))
+
+
+# ------------------------------------------------------------------ marshalling helpers
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ct.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        return ct.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ct.c_void_p(stream)
+    return ct.c_void_p(stream.cuda_stream)
+
+
+def _check(st, where):
+    if st:
+        raise Fp4Error(st, where)
+
+
+def _src(x):
+    """(tensor, rows, cols, ld) for a 2-D bf16 (or 16-bit integer) source."""
+    torch = _torch()
+    if x.dim() != 2:
+        raise ValueError("expected a 2-D tensor")
+    if x.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise Fp4Error(ERR_DTYPE, "source dtype %s" % x.dtype)
+    if x.shape[1] > 1 and x.stride(1) != 1:
+        raise ValueError("source rows must be contiguous (stride(1) == 1)")
+    ld = x.stride(0) if x.shape[0] > 1 else x.shape[1]
+    return x, x.shape[0], x.shape[1], ld
+
+
+def _empty(n, dtype, device):
+    torch = _torch()
+    return torch.empty(int(n), dtype=dtype, device=device)
+
+
+def _inner(cfg):
+    return 32 if cfg.format == FORMATS["mxfp4"] else 16
+
+
+def _workspace(cfg, rows, cols, device, workspace):
+    nb = fp4q_workspace_bytes(cfg, rows, cols)
+    if nb == 0:
+        return None, 0
+    if workspace is None:
+        workspace = _empty(nb, _torch().uint8, device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+# ------------------------------------------------------------------ entry points
+def fp4_quantize(x, cfg, *, residual=None, outer=None, workspace=None, stream=None, out=None):
+    """Rowwise quantisation.  Returns {"codes", "scales", "outer"} (outer None
+    without a two-level mode).  `outer` is read when cfg.outer_mode == 1.
+    `out` may supply preallocated "codes" / "scales" tensors."""
+    torch = _torch()
+    x, R, C, ld = _src(x)
+    dev = x.device
+    sizes = fp4q_buffer_sizes(cfg, R, C)
+    out = out or {}
+    codes = out.get("codes")
+    if codes is None:
+        codes = _empty(sizes["row_codes"], torch.uint8, dev).view(R, C // 2)
+    scales = out.get("scales")
+    if scales is None:
+        scales = _empty(sizes["row_scales"], torch.uint8, dev).view(R, C // _inner(cfg))
+    if outer is None and sizes["row_outer"]:
+        outer = _empty(sizes["row_outer"] // 4, torch.float32, dev)
+    ws, wsb = _workspace(cfg, R, C, dev, workspace)
+    _check(lib().fp4_quantize(ct.byref(cfg), _ptr(x), R, C, ld, _ptr(codes), _ptr(scales), _ptr(outer),
+                              _ptr(residual), _ptr(ws), wsb, _stream(stream)), "fp4_quantize")
+    return {"codes": codes, "scales": scales, "outer": outer}
+
+
+def fp4_qdq(x, cfg, *, residual=None, outer=None, with_codes=False, workspace=None, stream=None, y=None):
+    """Quantise-dequantise rowwise.  Returns {"y", "codes", "scales", "outer"}."""
+    torch = _torch()
+    x, R, C, ld = _src(x)
+    dev = x.device
+    sizes = fp4q_buffer_sizes(cfg, R, C)
+    if y is None:
+        y = torch.empty((R, C), dtype=torch.bfloat16, device=dev)
+    codes = scales = None
+    if with_codes:
+        codes = _empty(sizes["row_codes"], torch.uint8, dev).view(R, C // 2)
+        scales = _empty(sizes["row_scales"], torch.uint8, dev).view(R, C // _inner(cfg))
+    if outer is None and sizes["row_outer"] and (with_codes or cfg.outer_mode == 0):
+        outer = _empty(sizes["row_outer"] // 4, torch.float32, dev)
+    ws, wsb = _workspace(cfg, R, C, dev, workspace)
+    _check(lib().fp4_qdq(ct.byref(cfg), _ptr(x), R, C, ld, _ptr(y), _ptr(codes), _ptr(scales), _ptr(outer),
+                         _ptr(residual), _ptr(ws), wsb, _stream(stream)), "fp4_qdq")
+    return {"y": y, "codes": codes, "scales": scales, "outer": outer}
+
+
+def fp4_dequantize(codes, scales, outer, rows, cols, cfg, *, outer_transposed=False, stream=None, y=None):
+    """bf16 [rows, cols] from stored codes, scales and outer scales."""
+    torch = _torch()
+    if y is None:
+        y = torch.empty((rows, cols), dtype=torch.bfloat16, device=codes.device)
+    _check(lib().fp4_dequantize(ct.byref(cfg), _ptr(codes), _ptr(scales), _ptr(outer), int(rows), int(cols),
+                                int(bool(outer_transposed)), _ptr(y), _stream(stream)), "fp4_dequantize")
+    return y
+
+
+def fp4_cast_transpose(x, cfg, *, residual=None, row_outer=None, col_outer=None, workspace=None, stream=None,
+                       out=None):
+    """Rowwise and columnwise buffers from one read of x.  Returns
+    {"row_codes", "row_scales", "row_outer", "col_codes", "col_scales", "col_outer"}.
+    `out` may supply any of the four code / scale tensors preallocated."""
+    torch = _torch()
+    x, R, C, ld = _src(x)
+    dev = x.device
+    sizes = fp4q_buffer_sizes(cfg, R, C)
+    given = out or {}
+    out = {
+        "row_codes": given.get("row_codes"), "row_scales": given.get("row_scales"),
+        "col_codes": given.get("col_codes"), "col_scales": given.get("col_scales"),
+    }
+    shapes = {"row_codes": (R, C // 2), "row_scales": (R, C // 16), "col_codes": (C, R // 2),
+              "col_scales": (C, R // 16)}
+    for k, shp in shapes.items():
+        if out[k] is None:
+            out[k] = _empty(shp[0] * shp[1], torch.uint8, dev).view(*shp)
+    if row_outer is None and sizes["row_outer"]:
+        row_outer = _empty(sizes["row_outer"] // 4, torch.float32, dev)
+    if col_outer is None and sizes["col_outer"]:
+        col_outer = _empty(sizes["col_outer"] // 4, torch.float32, dev)
+    out["row_outer"], out["col_outer"] = row_outer, col_outer
+    ws, wsb = _workspace(cfg, R, C, dev, workspace)
+    _check(lib().fp4_cast_transpose(ct.byref(cfg), _ptr(x), R, C, ld, _ptr(out["row_codes"]), _ptr(out["row_scales"]),
+                                    _ptr(row_outer), _ptr(out["col_codes"]), _ptr(out["col_scales"]), _ptr(col_outer),
+                                    _ptr(residual), _ptr(ws), wsb, _stream(stream)), "fp4_cast_transpose")
+    return out
+
+
+def fp4_cast_transpose_grouped(x, rows_per_group, cfg, *, residual=None, stream=None, out=None):
+    """Per-group cast-transpose of groups stacked along rows (one launch per 64
+    groups).  Returns flat stacked buffers (see include/fp4q.h)."""
+    torch = _torch()
+    x, total, C, ld = _src(x)
+    dev = x.device
+    rows = [int(r) for r in rows_per_group]
+    if sum(rows) != total:
+        raise ValueError("rows_per_group does not sum to x.shape[0]")
+    n_ro = n_co = 0
+    for R in rows:
+        s = fp4q_buffer_sizes(cfg, R, C)
+        n_ro += s["row_outer"] // 4
+        n_co += s["col_outer"] // 4
+    if out is None:
+        out = {
+            "row_codes": _empty(total * C // 2, torch.uint8, dev).view(total, C // 2),
+            "row_scales": _empty(total * C // 16, torch.uint8, dev).view(total, C // 16),
+            "col_codes": _empty(total * C // 2, torch.uint8, dev),
+            "col_scales": _empty(total * C // 16, torch.uint8, dev),
+            "row_outer": _empty(n_ro, torch.float32, dev) if n_ro else None,
+            "col_outer": _empty(n_co, torch.float32, dev) if n_co else None,
+        }
+    arr = (ct.c_int64 * max(len(rows), 1))(*rows)
+    _check(lib().fp4_cast_transpose_grouped(ct.byref(cfg), len(rows), arr, C, _ptr(x), ld, _ptr(out["row_codes"]),
+                                            _ptr(out["row_scales"]), _ptr(out["row_outer"]), _ptr(out["col_codes"]),
+                                            _ptr(out["col_scales"]), _ptr(out["col_outer"]), _ptr(residual), None, 0,
+                                            _stream(stream)), "fp4_cast_transpose_grouped")
+    return out

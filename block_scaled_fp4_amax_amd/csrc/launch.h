@@ -1,0 +1,76 @@
+// launch.h -- internal launchers between the C-ABI layer (fp4q_api.cpp) and
+// the kernels.  Every launcher assumes its arguments were validated on the
+// host (shapes, alignment, modes) and only enqueues work on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4q {
+
+constexpr int kMaxGroupsPerLaunch = 64;
+
+// Rowwise NVFP4 / AMDFP4 parameters (modes none, tensorwise, 1D outer).
+struct RowArgs {
+    const uint16_t* x;
+    int64_t rows, cols, ld;
+    uint8_t* codes;          // may be null (qdq without codes)
+    uint8_t* scales;         // may be null
+    float* outer;            // 1D: [rows, cols/obs]; tensorwise: [1]
+    float* residual;         // may be null
+    uint16_t* y;             // may be null
+    const float* tensor_scale;  // tensorwise: device scalar holding s_g
+    uint64_t seed, step, index_base;
+    int32_t obs16;           // 1D outer: obs / 16 (1, 2, 4, 8)
+    int32_t outer_given;     // 1: read outer instead of computing it
+};
+
+// Tile (64 x 64) parameters: cast-transpose, grouped cast-transpose, and the
+// rowwise-only 2D outer mode.
+struct TileArgs {
+    const uint16_t* x;
+    int64_t ld, cols;
+    uint8_t* row_codes;
+    uint8_t* row_scales;
+    float* row_outer;
+    uint8_t* col_codes;      // null: rowwise only
+    uint8_t* col_scales;
+    float* col_outer;        // 1D only
+    float* residual;
+    uint16_t* y;             // rowwise dequantised output (qdq), may be null
+    const float* tensor_scale;
+    uint64_t seed, step, index_base;
+    int32_t obs16;           // 1D: obs / 16 (1, 2, 4); 2D: 4
+    int32_t outer_given;
+    int32_t ngroups;
+    int32_t tiles_c;         // ceil(cols / 64)
+    int32_t total_tiles;
+    int32_t per_xcd;         // tiles handled per XCD slice (grid = 8 * per_xcd)
+    int32_t row0[kMaxGroupsPerLaunch + 1];   // prefix rows of the groups
+    int32_t tile0[kMaxGroupsPerLaunch + 1];  // prefix tile counts of the groups
+};
+
+enum OuterKind { kOuterNone = 0, kOuterTensor = 1, kOuter1D = 2, kOuter2D = 3 };
+
+hipError_t launch_mx_qdq(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, uint16_t* y,
+                         uint8_t* codes, uint8_t* scales, hipStream_t s);
+
+hipError_t launch_amax(int scale_bias, const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                       const float* residual, float* partials, int npartials, float* scale_out,
+                       float* user_outer, hipStream_t s);
+
+hipError_t launch_rows(int scale_bias, int outer_kind, bool stochastic, const RowArgs& a, hipStream_t s);
+
+hipError_t launch_tiles(int scale_bias, int outer_kind, bool stochastic, const TileArgs& a, hipStream_t s);
+
+hipError_t launch_dequant_nv(int scale_bias, int outer_kind, int outer_transposed, int obs,
+                             const uint8_t* codes, const uint8_t* scales, const float* outer,
+                             int64_t rows, int64_t cols, uint16_t* y, hipStream_t s);
+
+hipError_t launch_dequant_mx(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                             uint16_t* y, hipStream_t s);
+
+// partial maxima used by the tensorwise amax pass
+constexpr int kAmaxPartials = 512;
+
+}  // namespace fp4q

@@ -1,0 +1,139 @@
+"""Seeded synthetic inputs for the five reference workloads.
+
+This module draws inputs only; it holds none of the quantiser's arithmetic.
+Samples are float32 from numpy's PCG64 generator, scaled in float32 and
+rounded to bf16 by torch's cast (round to nearest even); tensors are returned
+as uint16 bf16 bit patterns.  Both the HIP path and the CPU oracle are fed the
+same arrays.
+
+Shapes and value distributions follow the pages' workloads: hidden size 2880
+and 32 MoE experts of 2880 x 2880 ("NVFP4 / AMD-FP4 outer-block (two-level)
+scaling for FP4 training"), heavy-tailed outlier channels / tokens and
+lognormal "massive activations" (same page, Background and Op-level tests),
+an 8192 x 8192 bf16 weight ("MXFP4 weight QAT recipes", Implementations), and
+its edge domains (+-0, 2^-127 / 2^-128 / 2^-133 subnormals, values near
+6*2^125, inf and NaN poisoning, RTNE midpoints, scale-threshold triples;
+same page, Correctness).  No model weights or datasets are used.
+"""
+import numpy as np
+import torch
+
+
+def to_bf16(f):
+    """float32 array -> uint16 bf16 bits (torch cast, RNE)."""
+    t = torch.from_numpy(np.ascontiguousarray(f, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def from_bf16(b):
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+# ------------------------------------------------------------------ C1
+def c1_tensor(seed=0, rows=256, cols=256):
+    """NVFP4 tensorwise QDQ input: N(0, 1)."""
+    rng = np.random.default_rng(seed)
+    return to_bf16(rng.standard_normal((rows, cols), dtype=np.float32))
+
+
+# ------------------------------------------------------------------ C2
+def c2_weight(seed=2, rows=4096, cols=4096, outlier_frac=0.005, factor=1000.0):
+    """Weight N(0, 0.02) with round(0.5% of cols) seeded columns scaled x1000."""
+    rng = np.random.default_rng(seed)
+    w = rng.standard_normal((rows, cols), dtype=np.float32) * np.float32(0.02)
+    n_out = int(round(outlier_frac * cols))
+    cols_out = rng.choice(cols, n_out, replace=False)
+    w[:, cols_out] *= np.float32(factor)
+    return to_bf16(w)
+
+
+# ------------------------------------------------------------------ C3
+TINY_BF16 = np.array([0x0000, 0x0040, 0x0020, 0x0001, 0x0060, 0x0080, 0x0100], np.uint16)
+CAP_BF16 = np.array([0x7F3F, 0x7F40, 0x7F41], np.uint16)
+MID_VALUES = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], np.float32)
+
+
+def c3_weight(seed=3, rows=8192, cols=8192, std=0.02):
+    """MXFP4 fake-quant input: N(0, 0.02) with, in every group of 1024
+    consecutive 1x32 blocks, ten seeded blocks rewritten: one single +-inf, one
+    single NaN, one block of tiny values (+-0, 2^-127, 2^-128, 2^-133,
+    3*2^-128, 2^-126, 2^-125), one cap block (first element 0x7F3F / 0x7F40 /
+    0x7F41, i.e. around 6*2^125, rest N(0,1)*2^120), one block of E2M1
+    midpoints and grid points scaled by 2^e with amax 6*2^e (e in [-20, 20]),
+    one scale-threshold block whose amax is 6*2^k or one bf16 ulp either side,
+    and four ordinary blocks sprinkled with +-0 and subnormals."""
+    assert cols % 32 == 0 and (rows * cols // 32) % 1024 == 0
+    rng = np.random.default_rng(seed)
+    x = to_bf16(rng.standard_normal((rows, cols), dtype=np.float32) * np.float32(std))
+    blocks = x.reshape(-1, 32)
+    G = blocks.shape[0] // 1024
+    pick = np.argsort(rng.random((G, 1024), dtype=np.float32), axis=1)[:, :10].astype(np.int64)
+    pick += (np.arange(G, dtype=np.int64) * 1024)[:, None]
+    inf_b, nan_b, tiny_b, cap_b, mid_b, thr_b = (pick[:, k] for k in range(6))
+    sprinkle = pick[:, 6:10].ravel()
+    gi = np.arange(G)
+    sgn = lambda shape: (rng.integers(0, 2, shape).astype(np.uint16) << 15)  # noqa: E731
+
+    blocks[inf_b, rng.integers(0, 32, G)] = np.uint16(0x7F80) | sgn(G)
+    blocks[nan_b, rng.integers(0, 32, G)] = 0x7FC0
+    blocks[tiny_b] = rng.choice(TINY_BF16, (G, 32)) | sgn((G, 32))
+    cap_rest = to_bf16(rng.standard_normal((G, 32), dtype=np.float32) * np.float32(2.0 ** 120))
+    cap_rest[:, 0] = CAP_BF16[gi % 3] | sgn(G)
+    blocks[cap_b] = cap_rest
+    e = rng.integers(-20, 21, G)
+    mids = rng.choice(MID_VALUES, (G, 32)) * np.exp2(e)[:, None].astype(np.float32)
+    mids *= np.where(rng.integers(0, 2, (G, 32)) == 1, -1.0, 1.0).astype(np.float32)
+    mids[:, 0] = np.float32(6.0) * np.exp2(e).astype(np.float32)
+    blocks[mid_b] = to_bf16(mids)
+    k = rng.integers(-20, 21, G)
+    thr = to_bf16(np.clip(rng.standard_normal((G, 32), dtype=np.float32), -4, 4) * np.exp2(k).astype(np.float32))
+    six = to_bf16((np.float32(6.0) * np.exp2(k)).astype(np.float32)).astype(np.int64)
+    thr[gi, rng.integers(0, 32, G)] = (six + rng.integers(-1, 2, G)).astype(np.uint16)
+    blocks[thr_b] = thr
+    spr_pos = rng.integers(0, 32, (sprinkle.size, 3))
+    spr_val = rng.choice(np.array([0x0000, 0x0001, 0x0040, 0x0020], np.uint16), (sprinkle.size, 3))
+    blocks[sprinkle[:, None], spr_pos] = spr_val | sgn((sprinkle.size, 3))
+    return x
+
+
+# ------------------------------------------------------------------ C4
+def c4_activations(seed=4, rows=16384, cols=2880, sigma=2.0, chan_frac=0.001, chan_factor=500.0):
+    """Activations: N(0, 1) x per-token lognormal(0, 2) x500 on round(0.1% of
+    cols) seeded channels."""
+    rng = np.random.default_rng(seed)
+    a = rng.standard_normal((rows, cols), dtype=np.float32)
+    a *= rng.lognormal(0.0, sigma, (rows, 1)).astype(np.float32)
+    chans = rng.choice(cols, int(round(chan_frac * cols)), replace=False)
+    a[:, chans] *= np.float32(chan_factor)
+    return to_bf16(a)
+
+
+# ------------------------------------------------------------------ C5
+def c5_experts(seed=5, experts=32, rows=2880, cols=2880, std=0.02, outlier_rows=2, factor=200.0):
+    """Stacked MoE expert weights [experts * rows, cols]: N(0, 0.02), two seeded
+    rows per expert x200."""
+    rng = np.random.default_rng(seed)
+    w = rng.standard_normal((experts, rows, cols), dtype=np.float32) * np.float32(std)
+    for e in range(experts):
+        w[e, rng.choice(rows, outlier_rows, replace=False), :] *= np.float32(factor)
+    return to_bf16(w.reshape(experts * rows, cols))
+
+
+def c5_update(t, shape, std=1e-4):
+    """Weight update of step t: N(0, 1e-4) float32, seeded 500 + t."""
+    rng = np.random.default_rng(500 + t)
+    return rng.standard_normal(shape, dtype=np.float32) * np.float32(std)
+
+
+def c5_apply_update(w_bits, dw):
+    """W_{t+1} = bf16(f32(W_t) + dW_t); independent of the quantiser output."""
+    return to_bf16(from_bf16(w_bits) + dw)
+
+
+CONFIGS = {
+    "C1": dict(name="nvfp4_tensorwise_qdq_256x256", rows=256, cols=256),
+    "C2": dict(name="nvfp4_outer2d64_cast_transpose_4096x4096", rows=4096, cols=4096),
+    "C3": dict(name="mxfp4_fake_quant_8192x8192", rows=8192, cols=8192),
+    "C4": dict(name="amdfp4_outer1d64_sr_cast_transpose_16384x2880", rows=16384, cols=2880),
+    "C5": dict(name="nvfp4_grouped32_outer2d64_sr_ef_2880x2880", rows=32 * 2880, cols=2880),
+}

@@ -1,0 +1,246 @@
+/*
+ * fp4q.h -- C ABI of the MI355X (gfx950) block-scaled FP4 quantisation library
+ * (libfp4q.so).
+ *
+ * The library quantises bf16 tensors to 4-bit E2M1 codes packed two per byte,
+ * with one of three inner block scales and an optional FP32 level above them:
+ *
+ *   NVFP4   per-16 E4M3 scale of block_absmax/6 ("fp4-train" README, Method);
+ *           may run on the UE5M3 grid ("NVFP4 / AMD-FP4 outer-block (two-level)
+ *           scaling for FP4 training", Implementation: scale_format="ue5m3").
+ *   AMDFP4  per-16 UE5M3 scale, grid max 114688 (same page, Background).
+ *   MXFP4   per-32 (1x32) UE8M0 power-of-two scale, floor 2^-126, cap 2^125,
+ *           E2M1 RTNE ("MXFP4 weight QAT recipes on MXFP8 and FP8 block-scaling
+ *           hosts", Overview and Design).
+ *
+ *   two-level scaling (NVFP4 / AMDFP4 only; ALTO page, Technical design):
+ *     NONE        inner scales only;
+ *     TENSORWISE  one FP32 scale amax/(scale_max*6) for the whole tensor;
+ *     OUTER_BLOCK one FP32 scale amax/(scale_max*6) per 1 x obs row segment
+ *                 (and obs x 1 column segment for the columnwise buffer), or
+ *                 per obs x obs tile shared by both directions (outer_2d).
+ *   rounding: RNE, or stochastic rounding keyed on (seed, step, global index)
+ *   with an optional in-place FP32 error-feedback residual ("fp4-train"
+ *   README, API and Method).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers (hipMalloc / torch CUDA tensors)
+ *     except where an argument says "host".  `stream` is a hipStream_t (NULL =
+ *     the null stream).  Calls are asynchronous: FP4Q_OK means "enqueued".
+ *   - x and y are bf16 tensors passed as their 16-bit patterns, row-major.
+ *     x has leading dimension ld_x >= cols (elements); every other tensor is
+ *     contiguous.
+ *   - Packed codes: uint8 [rows, cols/2], element (i, j) in byte j/2, the low
+ *     nibble holding the even column; a code is sign<<3 | m with m indexing
+ *     the E2M1 grid {0, .5, 1, 1.5, 2, 3, 4, 6}.
+ *   - Inner scale bytes: uint8 [rows, cols/16] (E4M3 / UE5M3 code) or
+ *     [rows, cols/32] (UE8M0 code), row-major, unswizzled.
+ *   - Outer FP32 scales: TENSORWISE [1]; OUTER_BLOCK 2D [rows/obs, cols/obs];
+ *     OUTER_BLOCK 1D rowwise [rows, cols/obs], columnwise [cols, rows/obs].
+ *   - Columnwise buffers are the rowwise layout of X^T: codes [cols, rows/2],
+ *     scales [cols, rows/16] ("Block-Scaled FP8 and FP4 Weight Quantization",
+ *     sections 1-3).
+ *   - The caller owns and allocates every buffer; the library never allocates
+ *     device memory.  Inputs must not alias outputs, except `residual`, which
+ *     is read and rewritten in place.
+ *   - All validation happens on the host before anything is enqueued; on an
+ *     error status nothing is launched and no output byte is written.
+ *   - x, y, codes, residual and workspace must be 16-byte aligned, outer
+ *     arrays 4-byte aligned (scale bytes have no requirement); ld_x must be a
+ *     multiple of 8.
+ *   - An empty tensor (rows == 0 or cols == 0) is valid: the configuration is
+ *     validated, nothing is launched, and pointers may be NULL.
+ *   - No global mutable state: calls are thread-safe.
+ */
+#ifndef FP4Q_H
+#define FP4Q_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP4Q_ABI_VERSION 1
+
+/* Status codes. */
+enum {
+    FP4Q_OK = 0,
+    FP4Q_ERR_NULL = 1,        /* a required pointer is NULL                               */
+    FP4Q_ERR_DTYPE = 2,       /* input dtype other than bf16 (fp16 is rejected: its range
+                                 is smaller than the FP4 grid times the scales, "MXFP4
+                                 weight QAT recipes", Guards)                              */
+    FP4Q_ERR_SHAPE = 3,       /* cols % 16 (32 for MXFP4), rows % 16 for columnwise,
+                                 outer_block_size not a multiple of 16 or not dividing a
+                                 reduction dimension (ALTO page, Technical design),
+                                 ld_x < cols, negative sizes                              */
+    FP4Q_ERR_MODE = 4,        /* illegal combination: tensorwise with outer knobs, outer
+                                 knobs outside outer-block mode, MXFP4 with a two-level
+                                 mode, scale format not allowed for the format, a
+                                 precomputed outer scale without a two-level mode        */
+    FP4Q_ERR_UNSUPPORTED = 5, /* valid on the pages but not built here (see the function) */
+    FP4Q_ERR_ALIGN = 6,       /* a pointer not 16-byte aligned, ld_x % 8 != 0             */
+    FP4Q_ERR_WORKSPACE = 7,   /* workspace smaller than fp4q_workspace_bytes()            */
+    FP4Q_ERR_HIP = 8,         /* the HIP runtime reported a launch error                  */
+    FP4Q_ERR_ABI = 9          /* cfg->abi_version != FP4Q_ABI_VERSION                     */
+};
+
+typedef enum { FP4Q_NVFP4 = 0, FP4Q_AMDFP4 = 1, FP4Q_MXFP4 = 2 } fp4q_format;
+/* DEFAULT resolves to E4M3 (NVFP4), UE5M3 (AMDFP4), UE8M0 (MXFP4). */
+typedef enum { FP4Q_SCALE_DEFAULT = 0, FP4Q_SCALE_E4M3 = 1, FP4Q_SCALE_UE5M3 = 2, FP4Q_SCALE_UE8M0 = 3 } fp4q_scale_format;
+typedef enum { FP4Q_TWO_LEVEL_NONE = 0, FP4Q_TENSORWISE = 1, FP4Q_OUTER_BLOCK = 2 } fp4q_two_level;
+typedef enum { FP4Q_RNE = 0, FP4Q_STOCHASTIC = 1 } fp4q_rounding;
+typedef enum { FP4Q_DTYPE_BF16 = 0, FP4Q_DTYPE_FP16 = 1, FP4Q_DTYPE_FP32 = 2 } fp4q_dtype;
+
+/* Per-call configuration (plain data, passed by host pointer). */
+typedef struct {
+    uint32_t abi_version;      /* must equal FP4Q_ABI_VERSION                                  */
+    int32_t format;            /* fp4q_format                                                 */
+    int32_t scale_format;      /* fp4q_scale_format                                           */
+    int32_t two_level;         /* fp4q_two_level                                              */
+    int32_t outer_block_size;  /* obs, OUTER_BLOCK only (0 otherwise); multiple of 16          */
+    int32_t outer_2d;          /* OUTER_BLOCK only: 1 = obs x obs tiles, 0 = 1 x obs segments */
+    int32_t rounding;          /* fp4q_rounding                                               */
+    int32_t outer_mode;        /* 0: compute and write the outer scales; 1: read them from the
+                                  outer buffers (a precomputed scale, ALTO page,
+                                  Implementation: precomputed_outer_scale)                     */
+    int32_t input_dtype;       /* fp4q_dtype of x; only FP4Q_DTYPE_BF16 is accepted            */
+    int32_t reserved;          /* must be 0                                                    */
+    uint64_t seed;             /* SR key                                                       */
+    uint64_t step;             /* SR step (counter high word)                                  */
+    uint64_t index_base;       /* SR global index of element (0, 0): element (i, j) draws with
+                                  index index_base + i*cols + j (shards, experts)              */
+} fp4q_cfg;
+
+/* Byte sizes of every buffer an entry point may touch, for (cfg, rows, cols).
+ * A size of 0 means the buffer is not used by that configuration. */
+typedef struct {
+    size_t row_codes, row_scales, row_outer;
+    size_t col_codes, col_scales, col_outer;   /* col_outer == 0 when it is shared */
+    size_t y;                                  /* bf16 dequantised output            */
+    size_t residual;                           /* FP32 error-feedback residual       */
+    size_t workspace;                          /* scratch the caller must provide    */
+} fp4q_sizes;
+
+/* ABI version compiled into the library. */
+uint32_t fp4q_abi_version(void);
+
+/* Static English text for a status code (never NULL). */
+const char* fp4q_status_str(int status);
+
+/* Fills *out for an [rows, cols] source quantised by cfg.  Columnwise sizes are
+ * those of fp4_cast_transpose.  Returns a status (validation as for the
+ * entry points, without pointer checks). */
+int fp4q_buffer_sizes(const fp4q_cfg* cfg, int64_t rows, int64_t cols, fp4q_sizes* out);
+
+/* Workspace bytes the entry points need for cfg and shape (0 unless
+ * TENSORWISE computes its scale: then a small array of partial maxima). */
+size_t fp4q_workspace_bytes(const fp4q_cfg* cfg, int64_t rows, int64_t cols);
+
+/*
+ * fp4_quantize -- rowwise quantisation ("fp4-train" README, API: quantize(x,
+ * stochastic, residual, seed, step)).
+ *   x         bf16 [rows, ld_x] device, read.
+ *   codes     uint8 [rows, cols/2] device, written.
+ *   scales    uint8 [rows, cols/16] (cols/32 for MXFP4) device, written.
+ *   outer     FP32 outer scales (layout above) device; written when
+ *             cfg->outer_mode == 0, read when 1; NULL only for mode NONE/MXFP4.
+ *   residual  FP32 [rows, cols] device or NULL.  When given, the value quantised
+ *             is RN(x + residual) and residual is rewritten in place with
+ *             RN(value - dequantised value) (error feedback, "fp4-train"
+ *             README, Method).  NVFP4/AMDFP4 only.
+ *   workspace device scratch of >= fp4q_workspace_bytes() bytes (NULL if 0).
+ * OUTER_BLOCK 2D needs rows % obs == 0 and supports obs == 64; 1D supports
+ * obs in {16, 32, 64, 128} (others: FP4Q_ERR_UNSUPPORTED).  MXFP4 supports RNE
+ * only and no residual.
+ */
+int fp4_quantize(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                 uint8_t* codes, uint8_t* scales, float* outer, float* residual,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fp4_dequantize -- bf16 from stored codes and scales ("fp4-train" README,
+ * API: dequantize(packed, scale, M, K); ALTO page, Implementation:
+ * convert_from).  y = bf16(RN(+-G[m] * dec(s_i) [* s_o])); an MXFP4 scale byte
+ * 0xFF (NaN) gives the quiet NaN 0x7FC0.
+ *   codes, scales, outer  as written by the entry points for a logical
+ *                         [rows, cols] buffer (device, read).
+ *   outer_transposed      1 when a 2D outer array belongs to the transpose of
+ *                         this buffer, i.e. is [cols/obs, rows/obs] -- the case
+ *                         of a columnwise buffer sharing its source's 2D outer
+ *                         scale; 0 otherwise.
+ *   y                     bf16 [rows, cols] device, written.
+ * rounding, seed, step and index_base are ignored.
+ */
+int fp4_dequantize(const fp4q_cfg* cfg, const uint8_t* codes, const uint8_t* scales, const float* outer,
+                   int64_t rows, int64_t cols, int32_t outer_transposed, uint16_t* y, void* stream);
+
+/*
+ * fp4_qdq -- quantise then dequantise, rowwise ("fp4-train" README, API: qdq;
+ * "MXFP4 weight QAT recipes", Design: the fused bf16 -> mxfp4 -> bf16
+ * projection is fp4_qdq with format MXFP4).
+ *   y         bf16 [rows, cols] device, written.
+ *   codes, scales, outer  optional outputs as in fp4_quantize (NULL to skip;
+ *             outer is required when outer_mode == 1).
+ *   residual, workspace   as in fp4_quantize.
+ */
+int fp4_qdq(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+            uint16_t* y, uint8_t* codes, uint8_t* scales, float* outer, float* residual,
+            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fp4_cast_transpose -- one read of x writes the rowwise buffers and the
+ * columnwise buffers (the rowwise layout of X^T) ("Block-Scaled FP8 and FP4
+ * Weight Quantization", sections 2-3: fused cast-transpose; ALTO page,
+ * Implementation: an axis-invariant 2D outer scale computed once and used by
+ * both directions).  NVFP4 / AMDFP4 only.
+ *   row_codes [rows, cols/2], row_scales [rows, cols/16], row_outer (layout
+ *   above) -- device, written (row_outer read when outer_mode == 1).
+ *   col_codes [cols, rows/2], col_scales [cols, rows/16] -- device, written.
+ *   col_outer  1D: [cols, rows/obs] (written, or read when outer_mode == 1).
+ *              2D and TENSORWISE: the scale is shared, col_outer must be NULL or
+ *              equal row_outer.
+ *   residual   FP32 [rows, cols] or NULL; updated from the ROWWISE dequantised
+ *              value; the columnwise direction reads the same value but does not
+ *              update it.
+ * Needs rows % 16 == 0.  OUTER_BLOCK supports obs == 64 (1D and 2D); 1D also
+ * obs in {16, 32}.  Element (i, j) draws its SR variate once and uses it in
+ * both directions.
+ */
+int fp4_cast_transpose(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                       uint8_t* row_codes, uint8_t* row_scales, float* row_outer,
+                       uint8_t* col_codes, uint8_t* col_scales, float* col_outer,
+                       float* residual, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fp4_cast_transpose_grouped -- fp4_cast_transpose of G independent groups
+ * (experts) stacked along rows, in one launch (ALTO page, Implementation:
+ * grouped MoE GEMM with a per-expert outer scale).
+ *   groups          G >= 0.
+ *   rows_per_group  HOST array of G row counts (each a multiple of 16, and of
+ *                   obs in OUTER_BLOCK mode).
+ *   x               bf16 [sum(rows), ld_x] device.
+ *   row_codes/row_scales/residual  stacked along rows exactly as for one tensor
+ *                   of sum(rows) rows.
+ *   col_codes, col_scales  group g's [cols, rows_g/2] and [cols, rows_g/16]
+ *                   buffers, stored one after another in group order.
+ *   row_outer, col_outer   group g's outer arrays one after another (2D
+ *                   [rows_g/obs, cols/obs]; 1D rowwise [rows_g, cols/obs] -- which
+ *                   is again plain row stacking -- and columnwise
+ *                   [cols, rows_g/obs]; TENSORWISE one value per group).
+ * Group g draws SR variates with index_base + (rows before g) * cols + i*cols + j,
+ * the global row-major index in the stacked tensor, so the result equals G
+ * single calls.  TENSORWISE is not supported here (FP4Q_ERR_UNSUPPORTED).
+ */
+int fp4_cast_transpose_grouped(const fp4q_cfg* cfg, int32_t groups, const int64_t* rows_per_group,
+                               int64_t cols, const uint16_t* x, int64_t ld_x,
+                               uint8_t* row_codes, uint8_t* row_scales, float* row_outer,
+                               uint8_t* col_codes, uint8_t* col_scales, float* col_outer,
+                               float* residual, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP4Q_H */

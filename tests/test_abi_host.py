@@ -1,0 +1,161 @@
+"""Host-side tests of the C ABI (no GPU): the library loads, exports every
+function include/fp4q.h declares, and rejects every invalid configuration
+with its documented status before anything is enqueued (no compute call is
+made: every call here either fails validation or has an empty tensor)."""
+import ctypes as ct
+import os
+import re
+
+import pytest
+
+import block_scaled_fp4_amax_amd as fq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp4q.h")
+
+FAKE = 0x10000       # 16-byte aligned, never dereferenced: validation fails first
+FAKE_MIS = 0x10004   # 4-byte aligned only
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp4q?_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert {"fp4_quantize", "fp4_dequantize", "fp4_qdq", "fp4_cast_transpose", "fp4_cast_transpose_grouped",
+            "fp4q_abi_version", "fp4q_status_str", "fp4q_buffer_sizes", "fp4q_workspace_bytes"} <= set(names)
+    L = ct.CDLL(fq.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+    assert fq.fp4q_abi_version() == fq.ABI_VERSION
+
+
+def test_status_strings():
+    for st in range(10):
+        assert fq.fp4q_status_str(st)
+    assert fq.fp4q_status_str(123) == "unknown status"
+
+
+def q(cfg, rows=64, cols=64, ld=None, x=FAKE, codes=FAKE, scales=FAKE, outer=FAKE, residual=None, ws=None, wsb=0):
+    return fq.lib().fp4_quantize(ct.byref(cfg), x, rows, cols, cols if ld is None else ld, codes, scales, outer,
+                                 residual, ws, wsb, None)
+
+
+def ct_(cfg, rows=64, cols=64, ld=None, x=FAKE, row_outer=FAKE, col_outer=None, residual=None, ws=None, wsb=0,
+        col_codes=FAKE):
+    return fq.lib().fp4_cast_transpose(ct.byref(cfg), x, rows, cols, cols if ld is None else ld, FAKE, FAKE,
+                                       row_outer, col_codes, FAKE, col_outer, residual, ws, wsb, None)
+
+
+def test_mode_rules():
+    C = fq.make_cfg
+    # two_level_scaling is one of none / tensorwise / outer_block; outer knobs only in outer-block mode
+    assert q(C(two_level="tensorwise", outer_block_size=64)) == fq.ERR_MODE
+    assert q(C(two_level="none", outer_2d=True)) == fq.ERR_MODE
+    assert q(C(two_level=7)) == fq.ERR_MODE
+    # outer_block_size: a multiple of 16 that divides the reduction dims
+    assert q(C(two_level="outer_block", outer_block_size=24)) == fq.ERR_SHAPE
+    assert q(C(two_level="outer_block", outer_block_size=0)) == fq.ERR_SHAPE
+    assert q(C(two_level="outer_block", outer_block_size=64), cols=2880 - 2880 % 64 + 32, ld=None) == fq.ERR_SHAPE
+    assert q(C(two_level="outer_block", outer_block_size=128), cols=2880) == fq.ERR_SHAPE   # 2880 % 128 != 0
+    # scale-format pins: AMD-FP4 is UE5M3; MXFP4 is UE8M0; NVFP4 may use E4M3 or UE5M3
+    assert q(C(format="amdfp4", scale_format="e4m3")) == fq.ERR_MODE
+    assert q(C(format="mxfp4", scale_format="e4m3")) == fq.ERR_MODE
+    assert q(C(format="nvfp4", scale_format="ue8m0")) == fq.ERR_MODE
+    assert q(C(format="mxfp4", two_level="tensorwise")) == fq.ERR_MODE
+    assert q(C(format="mxfp4", rounding="stochastic")) == fq.ERR_UNSUPPORTED
+    assert q(C(format=9)) == fq.ERR_MODE
+    # precomputed outer without a two-level mode
+    assert q(C(outer_mode=1)) == fq.ERR_MODE
+    # dtype guard: fp16 rejected, fp32 valid on the pages but not built
+    assert q(C(input_dtype="fp16")) == fq.ERR_DTYPE
+    assert q(C(input_dtype="fp32")) == fq.ERR_UNSUPPORTED
+    bad = C()
+    bad.abi_version = 99
+    assert q(bad) == fq.ERR_ABI
+    assert fq.lib().fp4_quantize(None, FAKE, 1, 16, 16, FAKE, FAKE, None, None, None, 0, None) == fq.ERR_NULL
+
+
+def test_shape_and_pointer_rules():
+    C = fq.make_cfg
+    assert q(C(), cols=40) == fq.ERR_SHAPE                      # cols % 16
+    assert q(C(format="mxfp4"), cols=48) == fq.ERR_SHAPE        # cols % 32
+    assert q(C(), rows=-1) == fq.ERR_SHAPE
+    assert q(C(), cols=64, ld=32) == fq.ERR_SHAPE               # ld < cols
+    assert q(C(), cols=64, ld=68) == fq.ERR_ALIGN               # ld % 8
+    assert q(C(), x=None) == fq.ERR_NULL
+    assert q(C(), codes=None) == fq.ERR_NULL
+    assert q(C(two_level="tensorwise"), outer=None) == fq.ERR_NULL
+    assert q(C(), x=FAKE_MIS) == fq.ERR_ALIGN
+    assert q(C(format="mxfp4"), residual=FAKE) == fq.ERR_UNSUPPORTED
+    # 2D outer needs rows % obs; only obs 64 is built for 2D
+    assert q(C(two_level="outer_block", outer_block_size=64, outer_2d=True), rows=80) == fq.ERR_SHAPE
+    assert q(C(two_level="outer_block", outer_block_size=32, outer_2d=True)) == fq.ERR_UNSUPPORTED
+    # tensorwise needs a workspace of fp4q_workspace_bytes()
+    cfg = C(two_level="tensorwise")
+    need = fq.fp4q_workspace_bytes(cfg, 64, 64)
+    assert need > 0
+    assert q(cfg, ws=None, wsb=0) == fq.ERR_NULL
+    assert q(cfg, ws=FAKE, wsb=need - 4) == fq.ERR_WORKSPACE
+
+
+def test_cast_transpose_rules():
+    C = fq.make_cfg
+    assert ct_(C(), rows=40) == fq.ERR_SHAPE                    # rows % 16 for the columnwise buffer
+    assert ct_(C(format="mxfp4")) == fq.ERR_UNSUPPORTED
+    o1 = C(two_level="outer_block", outer_block_size=64)
+    assert ct_(o1, col_outer=None) == fq.ERR_NULL               # 1D needs its columnwise outer array
+    assert ct_(o1, rows=96, col_outer=FAKE) == fq.ERR_SHAPE     # rows % obs in 1D columnwise
+    o2 = C(two_level="outer_block", outer_block_size=64, outer_2d=True)
+    assert ct_(o2, col_outer=FAKE + 4096) == fq.ERR_MODE        # 2D outer is shared
+    assert ct_(o2, col_codes=None) == fq.ERR_NULL
+    assert ct_(C(two_level="outer_block", outer_block_size=128), rows=128, cols=128, col_outer=FAKE) == fq.ERR_UNSUPPORTED
+
+
+def test_grouped_rules():
+    C = fq.make_cfg
+    cfg = C(two_level="outer_block", outer_block_size=64, outer_2d=True)
+    L = fq.lib()
+    rows = (ct.c_int64 * 2)(64, 80)
+    args = (64, FAKE, 64, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, 0, None)
+    assert L.fp4_cast_transpose_grouped(ct.byref(cfg), 2, rows, *args) == fq.ERR_SHAPE
+    assert L.fp4_cast_transpose_grouped(ct.byref(cfg), -1, rows, *args) == fq.ERR_SHAPE
+    assert L.fp4_cast_transpose_grouped(ct.byref(cfg), 2, None, *args) == fq.ERR_NULL
+    assert L.fp4_cast_transpose_grouped(ct.byref(C(two_level="tensorwise")), 1, rows, *args) == fq.ERR_UNSUPPORTED
+    # zero groups is an empty call
+    assert L.fp4_cast_transpose_grouped(ct.byref(cfg), 0, None, *args) == fq.OK
+
+
+def test_empty_tensors_are_accepted_without_launch():
+    C = fq.make_cfg
+    for cfg in (C(), C(format="mxfp4"), C(two_level="outer_block", outer_block_size=64, outer_2d=True)):
+        assert q(cfg, rows=0, x=None, codes=None, scales=None, outer=None) == fq.OK
+    assert fq.lib().fp4_dequantize(ct.byref(C()), None, None, None, 0, 16, 0, None, None) == fq.OK
+
+
+def test_dequantize_rules():
+    C = fq.make_cfg
+    L = fq.lib()
+    assert L.fp4_dequantize(ct.byref(C()), FAKE, FAKE, None, 16, 40, 0, FAKE, None) == fq.ERR_SHAPE
+    assert L.fp4_dequantize(ct.byref(C()), FAKE, FAKE, None, 16, 32, 1, FAKE, None) == fq.ERR_MODE
+    o2 = C(two_level="outer_block", outer_block_size=64, outer_2d=True)
+    assert L.fp4_dequantize(ct.byref(o2), FAKE, FAKE, None, 64, 64, 0, FAKE, None) == fq.ERR_NULL
+    assert L.fp4_dequantize(ct.byref(o2), FAKE, FAKE, FAKE, 48, 64, 0, FAKE, None) == fq.ERR_SHAPE
+
+
+def test_buffer_sizes():
+    C = fq.make_cfg
+    s = fq.fp4q_buffer_sizes(C(two_level="outer_block", outer_block_size=64), 16384, 2880)
+    assert s["row_codes"] == 16384 * 1440 and s["row_scales"] == 16384 * 180
+    assert s["row_outer"] == 16384 * 45 * 4 and s["col_outer"] == 2880 * 256 * 4
+    assert s["col_codes"] == 2880 * 8192 and s["col_scales"] == 2880 * 1024
+    s2 = fq.fp4q_buffer_sizes(C(two_level="outer_block", outer_block_size=64, outer_2d=True), 4096, 4096)
+    assert s2["row_outer"] == 64 * 64 * 4 and s2["col_outer"] == 0
+    s3 = fq.fp4q_buffer_sizes(C(format="mxfp4"), 8192, 8192)
+    assert s3["row_scales"] == 8192 * 256 and s3["col_codes"] == 0 and s3["residual"] == 0
+    assert fq.fp4q_buffer_sizes(C(two_level="tensorwise"), 256, 256)["workspace"] > 0
+    with pytest.raises(fq.Fp4Error):
+        fq.fp4q_buffer_sizes(C(), 16, 40)
