@@ -1,0 +1,341 @@
+#!/usr/bin/env python3
+"""Throughput of the block-scaled FP4 quantisation hot path on one MI355X.
+
+Metric: quantize GB/s -- algorithmic HBM bytes (source read + every output
+written) per second -- and its fraction of MI355X's 8 TB/s HBM peak.
+
+The headline workload is the fused outer-block cast-transpose: NVFP4 with a
+shared 2D 64x64 FP32 outer scale, per-16 E4M3 inner scales, RTNE, rowwise and
+columnwise packed codes from a 4096x4096 bf16 weight N(0, 0.02) with 0.5% of
+its columns x1000.  One step = one launch of fp4_cast_transpose over one copy
+of that weight; copies rotate over enough buffer sets (>= 1 GiB in total) that
+no step reads its source from the 256 MB last-level cache.  Steps are replayed
+from a HIP graph so back-to-back launches are not host-bound.
+
+Also reported (not part of `value`): the other reference workloads (MXFP4
+fake-quant 8192^2, AMD-FP4 1D-outer SR cast-transpose 16384x2880, grouped
+NVFP4 SR+EF over 32 experts of 2880^2, NVFP4 tensorwise QDQ 256^2), and the
+CPU oracle timed on the host cores on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra]
+                       [--no-cpu-baseline] [--copy-probe]
+"""
+import argparse
+import ctypes as ct
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "quantize GB/s (HBM bytes read+written) and fraction of MI355X HBM peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU oracle time for the baseline")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 256 MiB device copy (counter calibration) and exit")
+    ap.add_argument("--only", default=None, help="time a single workload (C1..C5) and exit")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------- helpers
+def kernel_sources_hash():
+    files = sorted(glob.glob(os.path.join(ROOT, "block_scaled_fp4_amax_amd", "csrc", "*")))
+    h = hashlib.sha256()
+    for f in files:
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_key):
+    """HBM bytes per launch from the committed counter summary, or None when the
+    kernels changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    entry = data.get(kernel_key)
+    if not entry or entry.get("sources_sha") != kernel_sources_hash():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+class Timed:
+    """A workload: rotating buffer sets and a launch closure per set."""
+
+    def __init__(self, name, desc, bytes_per_step, sets, launch, kernel):
+        self.name, self.desc, self.bytes, self.sets, self.launch, self.kernel = name, desc, bytes_per_step, sets, launch, kernel
+
+
+def run_timed(torch, w, steps, warmup, graph=True):
+    """Warm up, then time exactly `steps` launches bracketed by synchronisation;
+    events are recorded on the stream the launches use (torch's current stream)."""
+    n = len(w.sets)
+    for i in range(warmup):
+        w.launch(w.sets[i % n])
+    torch.cuda.synchronize()
+    reps, rem = divmod(steps, n)
+    g = None
+    if graph and reps > 0:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for s in w.sets:
+                w.launch(s)
+        g.replay()
+        torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    if g is not None:
+        for _ in range(reps):
+            g.replay()
+        for i in range(rem):
+            w.launch(w.sets[i])
+    else:
+        for i in range(steps):
+            w.launch(w.sets[i % n])
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end)
+    return ms
+
+
+def n_sets_for(bytes_per_set, min_total=1 << 30, cap=64):
+    return max(2, min(cap, -(-min_total // max(bytes_per_set, 1))))
+
+
+# ---------------------------------------------------------------------- workloads
+def make_c2(torch, fq, W):
+    R = C = 4096
+    x = W.c2_weight()
+    cfg = fq.make_cfg(format="nvfp4", two_level="outer_block", outer_block_size=64, outer_2d=True)
+    alg = R * C * 2 + 2 * (R * C // 2) + 2 * (R * C // 16) + (R // 64) * (C // 64) * 4
+    nset = n_sets_for(alg)
+    src = torch.from_numpy(x.view("int16")).cuda()
+    sets = []
+    for _ in range(nset):
+        s = dict(x=src.clone(), rc=torch.empty(R * C // 2, dtype=torch.uint8, device="cuda"),
+                 rs=torch.empty(R * C // 16, dtype=torch.uint8, device="cuda"),
+                 cc=torch.empty(R * C // 2, dtype=torch.uint8, device="cuda"),
+                 cs=torch.empty(R * C // 16, dtype=torch.uint8, device="cuda"),
+                 ro=torch.empty((R // 64) * (C // 64), dtype=torch.float32, device="cuda"))
+        sets.append(s)
+    L = fq.lib()
+
+    def launch(s):
+        st = L.fp4_cast_transpose(ct.byref(cfg), s["x"].data_ptr(), R, C, C, s["rc"].data_ptr(), s["rs"].data_ptr(),
+                                  s["ro"].data_ptr(), s["cc"].data_ptr(), s["cs"].data_ptr(), None, None, None, 0,
+                                  torch.cuda.current_stream().cuda_stream)
+        if st:
+            raise fq.Fp4Error(st, "fp4_cast_transpose")
+    return Timed("C2", "NVFP4 2D 64x64 outer, E4M3/16, RTNE, fused cast-transpose 4096x4096 bf16", alg, sets, launch,
+                 "k_tile<7, 3, false, true>")
+
+
+def make_c3(torch, fq, W):
+    R = C = 8192
+    x = W.c3_weight()
+    cfg = fq.make_cfg(format="mxfp4")
+    alg = R * C * 2 * 2
+    nset = n_sets_for(alg, cap=8)
+    src = torch.from_numpy(x.view("int16")).cuda()
+    sets = [dict(x=src.clone(), y=torch.empty(R * C, dtype=torch.int16, device="cuda")) for _ in range(nset)]
+    L = fq.lib()
+
+    def launch(s):
+        st = L.fp4_qdq(ct.byref(cfg), s["x"].data_ptr(), R, C, C, s["y"].data_ptr(), None, None, None, None, None, 0,
+                       torch.cuda.current_stream().cuda_stream)
+        if st:
+            raise fq.Fp4Error(st, "fp4_qdq")
+    return Timed("C3", "MXFP4 1x32 fake-quant 8192x8192 bf16 -> bf16", alg, sets, launch, "k_mx_qdq<true, true, false>")
+
+
+def make_c4(torch, fq, W):
+    R, C = 16384, 2880
+    x = W.c4_activations()
+    cfg = fq.make_cfg(format="amdfp4", two_level="outer_block", outer_block_size=64, rounding="stochastic", seed=7,
+                      step=3)
+    alg = R * C * 2 + 2 * (R * C // 2) + 2 * (R * C // 16) + (R * (C // 64) + C * (R // 64)) * 4
+    nset = n_sets_for(alg, cap=16)
+    src = torch.from_numpy(x.view("int16")).cuda()
+    sets = []
+    for _ in range(nset):
+        sets.append(dict(x=src.clone(), rc=torch.empty(R * C // 2, dtype=torch.uint8, device="cuda"),
+                         rs=torch.empty(R * C // 16, dtype=torch.uint8, device="cuda"),
+                         cc=torch.empty(R * C // 2, dtype=torch.uint8, device="cuda"),
+                         cs=torch.empty(R * C // 16, dtype=torch.uint8, device="cuda"),
+                         ro=torch.empty(R * (C // 64), dtype=torch.float32, device="cuda"),
+                         co=torch.empty(C * (R // 64), dtype=torch.float32, device="cuda")))
+    L = fq.lib()
+
+    def launch(s):
+        st = L.fp4_cast_transpose(ct.byref(cfg), s["x"].data_ptr(), R, C, C, s["rc"].data_ptr(), s["rs"].data_ptr(),
+                                  s["ro"].data_ptr(), s["cc"].data_ptr(), s["cs"].data_ptr(), s["co"].data_ptr(), None,
+                                  None, 0, torch.cuda.current_stream().cuda_stream)
+        if st:
+            raise fq.Fp4Error(st, "fp4_cast_transpose")
+    return Timed("C4", "AMD-FP4 1D 1x64 outer, UE5M3/16, SR, cast-transpose 16384x2880 bf16", alg, sets, launch,
+                 "k_tile<15, 2, true, true>")
+
+
+def make_c5(torch, fq, W):
+    E, R, C = 32, 2880, 2880
+    w = W.c5_experts()
+    cfg = fq.make_cfg(format="nvfp4", two_level="outer_block", outer_block_size=64, outer_2d=True,
+                      rounding="stochastic", seed=5, step=0)
+    n = E * R * C
+    alg = n * 2 + n * 4 * 2 + 2 * (n // 2) + 2 * (n // 16) + E * (R // 64) * (C // 64) * 4
+    s = dict(x=torch.from_numpy(w.view("int16")).cuda(), z=torch.zeros(n, dtype=torch.float32, device="cuda"),
+             rc=torch.empty(n // 2, dtype=torch.uint8, device="cuda"), rs=torch.empty(n // 16, dtype=torch.uint8, device="cuda"),
+             cc=torch.empty(n // 2, dtype=torch.uint8, device="cuda"), cs=torch.empty(n // 16, dtype=torch.uint8, device="cuda"),
+             ro=torch.empty(E * (R // 64) * (C // 64), dtype=torch.float32, device="cuda"))
+    rows = (ct.c_int64 * E)(*([R] * E))
+    L = fq.lib()
+
+    def launch(s):
+        st = L.fp4_cast_transpose_grouped(ct.byref(cfg), E, rows, C, s["x"].data_ptr(), C, s["rc"].data_ptr(),
+                                          s["rs"].data_ptr(), s["ro"].data_ptr(), s["cc"].data_ptr(), s["cs"].data_ptr(),
+                                          None, s["z"].data_ptr(), None, 0, torch.cuda.current_stream().cuda_stream)
+        if st:
+            raise fq.Fp4Error(st, "fp4_cast_transpose_grouped")
+    # the working set (~3 GB per step) is far beyond the last-level cache: one set
+    return Timed("C5", "grouped NVFP4 2D 64x64 outer, E4M3/16, SR + in-place EF residual, 32 x 2880x2880", alg, [s],
+                 launch, "k_tile<7, 3, true, true>")
+
+
+def make_c1(torch, fq, W):
+    R = C = 256
+    x = W.c1_tensor()
+    cfg = fq.make_cfg(format="nvfp4", two_level="tensorwise")
+    alg = R * C * 2 + R * C // 2 + R * C // 16 + 4 + R * C * 2
+    ws = torch.empty(fq.fp4q_workspace_bytes(cfg, R, C), dtype=torch.uint8, device="cuda")
+    s = dict(x=torch.from_numpy(x.view("int16")).cuda(), y=torch.empty(R * C, dtype=torch.int16, device="cuda"),
+             c=torch.empty(R * C // 2, dtype=torch.uint8, device="cuda"),
+             sc=torch.empty(R * C // 16, dtype=torch.uint8, device="cuda"),
+             o=torch.empty(1, dtype=torch.float32, device="cuda"))
+    L = fq.lib()
+
+    def launch(s):
+        st = L.fp4_qdq(ct.byref(cfg), s["x"].data_ptr(), R, C, C, s["y"].data_ptr(), s["c"].data_ptr(),
+                       s["sc"].data_ptr(), s["o"].data_ptr(), None, ws.data_ptr(), ws.numel(),
+                       torch.cuda.current_stream().cuda_stream)
+        if st:
+            raise fq.Fp4Error(st, "fp4_qdq")
+    return Timed("C1", "NVFP4 tensorwise QDQ 256x256 (3 launches: amax, scale, quantise)", alg, [s], launch,
+                 "k_nv_rows<7, 1, false>")
+
+
+# ---------------------------------------------------------------------- CPU baseline
+def cpu_baseline(W, min_seconds):
+    """The oracle, untuned, on the host cores: the full headline tensor,
+    repeated until at least `min_seconds` have elapsed."""
+    from oracle import ref
+    x = W.c2_weight()
+    R = C = 4096
+    alg = R * C * 2 + 2 * (R * C // 2) + 2 * (R * C // 16) + (R // 64) * (C // 64) * 4
+    ref.nv_quantize(x[:256], two_level="outer", obs=64, outer_2d=True, cols=True, want_y=False)  # warm
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        ref.nv_quantize(x, two_level="outer", obs=64, outer_2d=True, cols=True, want_y=False)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    return {"value": round(alg * reps / el / 1e9, 4), "unit": "GB/s", "cores": ref.threads(), "kind": "oracle",
+            "sample": "the full 4096x4096 headline tensor (both directions), %d repetition(s), %.1f s" % (reps, el)}
+
+
+# ---------------------------------------------------------------------- main
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the quantisation path has no cross-GPU step in this build "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import block_scaled_fp4_amax_amd as fq
+    from block_scaled_fp4_amax_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+
+    if args.copy_probe:
+        n = 256 << 20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(20):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": 20}))
+        return
+
+    if args.only:
+        mk = {"C1": make_c1, "C2": make_c2, "C3": make_c3, "C4": make_c4, "C5": make_c5}[args.only]
+        w = mk(torch, fq, W)
+        ms = run_timed(torch, w, args.steps, args.warmup)
+        per = ms / args.steps
+        print(json.dumps({"workload": w.name, "desc": w.desc, "ms_per_launch": per,
+                          "GB/s": w.bytes / (per * 1e-3) / 1e9, "frac": w.bytes / (per * 1e-3) / 1e9 / HBM_PEAK_GBS}))
+        return
+
+    w = make_c2(torch, fq, W)
+    print("# headline %s: %d buffer sets, %d warmup + %d timed launches" % (w.name, len(w.sets), args.warmup, args.steps),
+          file=sys.stderr, flush=True)
+    ms = run_timed(torch, w, args.steps, args.warmup)
+    per_ms = ms / args.steps
+    gbs = w.bytes * args.steps / (ms * 1e-3) / 1e9
+    traffic = measured_traffic("C2")
+    line = {
+        "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(per_ms, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "C2: " + w.desc, "rows": 4096, "cols": 4096, "format": "nvfp4",
+                   "two_level": "outer_block 2D 64x64", "inner": "E4M3/16", "rounding": "rtne",
+                   "outputs": "rowwise+columnwise codes and scales, shared outer", "source": "bf16 N(0,0.02), 0.5% cols x1000",
+                   "algorithmic_bytes_per_step": w.bytes, "buffer_sets": len(w.sets)},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": w.kernel},
+    }
+    del w
+    torch.cuda.empty_cache()
+    if not args.no_extra:
+        extra = {}
+        for mk, steps in ((make_c3, 400), (make_c4, 400), (make_c5, 20), (make_c1, 400)):
+            e = mk(torch, fq, W)
+            print("# extra %s" % e.name, file=sys.stderr, flush=True)
+            ems = run_timed(torch, e, steps, min(20, steps))
+            per = ems / steps
+            eg = e.bytes / (per * 1e-3) / 1e9
+            extra[e.name] = {"desc": e.desc, "us_per_step": round(per * 1e3, 3), "GB/s": round(eg, 2),
+                             "frac": round(eg / HBM_PEAK_GBS, 4), "algorithmic_bytes": e.bytes, "kernel": e.kernel}
+            del e
+            torch.cuda.empty_cache()
+        line["extra"] = extra
+    if not args.no_cpu_baseline:
+        print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(W, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -86,7 +86,7 @@ def c3_weight(seed=3, rows=8192, cols=8192, std=0.02):
     mids[:, 0] = np.float32(6.0) * np.exp2(e).astype(np.float32)
     blocks[mid_b] = to_bf16(mids)
     k = rng.integers(-20, 21, G)
-    thr = to_bf16(np.clip(rng.standard_normal((G, 32), dtype=np.float32), -4, 4) * np.exp2(k).astype(np.float32))
+    thr = to_bf16(np.clip(rng.standard_normal((G, 32), dtype=np.float32), -4, 4) * np.exp2(k)[:, None].astype(np.float32))
     six = to_bf16((np.float32(6.0) * np.exp2(k)).astype(np.float32)).astype(np.int64)
     thr[gi, rng.integers(0, 32, G)] = (six + rng.integers(-1, 2, G)).astype(np.uint16)
     blocks[thr_b] = thr

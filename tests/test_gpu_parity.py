@@ -32,6 +32,8 @@ def dev(a):
 
 def host(t, dtype):
     torch.cuda.synchronize()
+    if t.dtype == torch.bfloat16:
+        t = t.view(torch.int16)
     return t.detach().cpu().contiguous().numpy().view(dtype)
 
 
