@@ -47,6 +47,7 @@ def parse():
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 256 MiB device copy (counter calibration) and exit")
     ap.add_argument("--only", default=None, help="time a single workload (C1..C5) and exit")
+    ap.add_argument("--eager", action="store_true", help="launch every step from the host (no graph replay)")
     return ap.parse_args()
 
 
@@ -292,7 +293,7 @@ def main():
     if args.only:
         mk = {"C1": make_c1, "C2": make_c2, "C3": make_c3, "C4": make_c4, "C5": make_c5}[args.only]
         w = mk(torch, fq, W)
-        ms = run_timed(torch, w, args.steps, args.warmup)
+        ms = run_timed(torch, w, args.steps, args.warmup, graph=not args.eager)
         per = ms / args.steps
         print(json.dumps({"workload": w.name, "desc": w.desc, "ms_per_launch": per,
                           "GB/s": w.bytes / (per * 1e-3) / 1e9, "frac": w.bytes / (per * 1e-3) / 1e9 / HBM_PEAK_GBS}))
@@ -301,7 +302,7 @@ def main():
     w = make_c2(torch, fq, W)
     print("# headline %s: %d buffer sets, %d warmup + %d timed launches" % (w.name, len(w.sets), args.warmup, args.steps),
           file=sys.stderr, flush=True)
-    ms = run_timed(torch, w, args.steps, args.warmup)
+    ms = run_timed(torch, w, args.steps, args.warmup, graph=not args.eager)
     per_ms = ms / args.steps
     gbs = w.bytes * args.steps / (ms * 1e-3) / 1e9
     traffic = measured_traffic("C2")

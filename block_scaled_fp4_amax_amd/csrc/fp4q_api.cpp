@@ -132,7 +132,7 @@ TileArgs tile_args_single(const uint16_t* x, int64_t rows, int64_t cols, int64_t
     a.tile0[0] = 0;
     a.tile0[1] = (int32_t)(((rows + 63) / 64) * a.tiles_c);
     a.total_tiles = a.tile0[1];
-    a.per_xcd = (a.total_tiles + 7) / 8;
+    set_tile_grid(a.total_tiles, a.per_xcd, a.wgs_per_xcd);
     return a;
 }
 
@@ -437,7 +437,7 @@ int fp4_cast_transpose_grouped(const fp4q_cfg* cfg, int32_t groups, const int64_
         a.row0[ng] = (int32_t)rr;
         a.tile0[ng] = tt;
         a.total_tiles = tt;
-        a.per_xcd = (tt + 7) / 8;
+        set_tile_grid(tt, a.per_xcd, a.wgs_per_xcd);
         row_before = rr;
         if (tt == 0) continue;
         st = hip_status(launch_tiles(r.bias, r.outer_kind, r.sr, a, s));

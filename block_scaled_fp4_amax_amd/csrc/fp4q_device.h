@@ -46,17 +46,65 @@ __device__ __forceinline__ float e2m1_value(uint32_t m)
 // Stochastic rounding of t >= 0 onto the grid: between neighbours lo < hi the
 // result is hi with probability (t - lo) / (hi - lo), realised as
 // u16 < frac * 2^16 with u16 uniform in [0, 2^16) ("fp4-train" README,
-// Method).  Grid points and t >= 6 are deterministic.
-__device__ __forceinline__ uint32_t e2m1_sr(float t, uint32_t u16)
+// Method).  Grid points and t >= 6 are deterministic.  uf is u16 as a float.
+//
+// With k = max(exponent(t), 0) the grid spacing around t is 2^(k-1), so
+// s = t * 2^(1-k) lies in [0, 4), floor(s) + 2k is the code of the lower
+// neighbour and s - floor(s) the fraction; all three steps are exact.  t is
+// first clamped to 6 (code 7, fraction 0).
+__device__ __forceinline__ uint32_t e2m1_sr(float t, float uf)
 {
-    if (t >= 6.0f) return 7u;
-    uint32_t lo = (uint32_t)(t >= 0.5f) + (uint32_t)(t >= 1.0f) + (uint32_t)(t >= 1.5f) + (uint32_t)(t >= 2.0f) +
-                  (uint32_t)(t >= 3.0f) + (uint32_t)(t >= 4.0f);
-    float g = e2m1_value(lo);
-    // gap to the next grid point: 0.5 below 2, 1 in [2, 4), 2 in [4, 6)
-    float inv_gap = lo < 4u ? 2.0f : (lo < 6u ? 1.0f : 0.5f);
-    float frac = (t - g) * inv_gap;            // exact (Sterbenz / power-of-two scaling)
-    return lo + (uint32_t)((float)u16 < frac * 65536.0f);
+    const float tc = fminf(t, 6.0f);
+    const int e = (int)(__float_as_uint(tc) >> 23) - 127;
+    const int k = e < 0 ? 0 : e;
+    const float s = ldexpf(tc, 1 - k);
+    const float f = __builtin_floorf(s);
+    const uint32_t up = uf < (s - f) * 65536.0f;
+    return (uint32_t)f + 2u * (uint32_t)k + up;
+}
+
+// Two E2M1 codes (RNE, ties to the even code, saturating at 6, sign kept,
+// signed zero kept) of a and b, written into byte SEL of `old` (a in the low
+// nibble).  This is gfx950's v_cvt_scalef32_pk_fp4_f32 with scale 1; its
+// rounding equals e2m1_rne() above on every non-negative binary32 (checked
+// exhaustively on the device, together with the sign of every negative).
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2_rne(uint32_t old, float a, float b)
+{
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
+}
+
+// Same with a power-of-two scale 2^k: codes of a / 2^k and b / 2^k, exact for
+// every finite bf16 a, b and k in [-126, 125] (checked on the device).
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2_rne_scaled(uint32_t old, float a, float b, float pow2)
+{
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, pow2, SEL);
+}
+
+// ---------------------------------------------------------------- exact division
+// RN32(a / s) computed as RN32(a * RN64(1 / s)).  For binary32 a and s the
+// exact quotient is never a binary32 rounding midpoint (a midpoint has an odd
+// 25-bit significand, which a * (odd part of s)^-1 cannot produce), and its
+// distance to the nearest midpoint is at least 2^-49 of its magnitude, while
+// a * RN64(1/s) rounded to binary64 is within 2^-52 of a / s.  So the binary32
+// rounding of the binary64 product equals the correctly rounded quotient
+// whenever that quotient is a normal binary32; callers route the few
+// subnormal-range quotients through the IEEE division instead.  Signs and
+// signed zeros carry through exactly.
+__device__ __forceinline__ float div_inv64(float a, double inv)
+{
+    return (float)((double)a * inv);
+}
+
+// True when q is a subnormal binary32 (one v_cmp_class).  div_inv64 is exact
+// for normal-range quotients; below that only an exact rounding tie of the
+// quotient can round differently, and then the binary64 route lands on a
+// subnormal neighbour (or on zero where zero is the correct result), so
+// flagging subnormal results is enough to catch every such case.
+__device__ __forceinline__ bool is_subnormal(float q)
+{
+    return __builtin_amdgcn_class(q, 0x090);   // -denormal | +denormal
 }
 
 // ---------------------------------------------------------------- inner scale grids
@@ -108,9 +156,9 @@ __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1
         uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
         uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
         u32x4 n;
-        n.x = (uint32_t)(p1 >> 32) ^ c.y ^ k0;
+        n.x = (c.y ^ k0) ^ (uint32_t)(p1 >> 32);
         n.y = (uint32_t)p1;
-        n.z = (uint32_t)(p0 >> 32) ^ c.w ^ k1;
+        n.z = (c.w ^ k1) ^ (uint32_t)(p0 >> 32);
         n.w = (uint32_t)p0;
         c = n;
         k0 += 0x9E3779B9u;
@@ -134,6 +182,72 @@ __device__ __forceinline__ uint32_t sr_lane(const u32x4& w, int l)
     return (l & 1) ? (word >> 16) : (word & 0xFFFFu);
 }
 
+// The 16 SR variates of elements idx0 .. idx0+15 (idx0 = global index of the
+// block's first element).  idx0 % 8 equals index_base % 8 for every block of a
+// launch (blocks start at multiples of 16), so the branch is uniform; the
+// aligned case takes exactly two Philox blocks with static lane indexing.
+__device__ __forceinline__ void sr_draws16(uint64_t seed, uint64_t step, uint64_t idx0, uint32_t (&u)[16])
+{
+    const uint64_t b0 = idx0 >> 3;
+    const int off = (int)(idx0 & 7u);
+    const u32x4 w0 = sr_words(seed, step, b0);
+    const u32x4 w1 = sr_words(seed, step, b0 + 1);
+    if (off == 0) {
+        const uint32_t ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            u[2 * j] = ws[j] & 0xFFFFu;
+            u[2 * j + 1] = ws[j] >> 16;
+        }
+    } else {
+        const u32x4 w2 = sr_words(seed, step, b0 + 2);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int e = off + k;
+            const int blk = e >> 3;
+            u32x4 w;
+            w.x = blk == 0 ? w0.x : (blk == 1 ? w1.x : w2.x);
+            w.y = blk == 0 ? w0.y : (blk == 1 ? w1.y : w2.y);
+            w.z = blk == 0 ? w0.z : (blk == 1 ? w1.z : w2.z);
+            w.w = blk == 0 ? w0.w : (blk == 1 ? w1.w : w2.w);
+            u[k] = sr_lane(w, e & 7);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- LDS-only barrier
+// Workgroup barrier whose fences cover LDS only: it orders the workgroup's LDS
+// writes before the barrier against LDS reads after it, but does not wait for
+// this wave's outstanding global loads and stores, so prefetched loads stay in
+// flight across it.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// ---------------------------------------------------------------- packed 16-bit max
+typedef unsigned short fp4q_u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(fp4q_u16x2, a),
+                                                                  __builtin_bit_cast(fp4q_u16x2, b)));
+}
+
+// Largest |x| bit pattern among 2*N packed bf16 (an order-preserving key for
+// the magnitudes; any value >= 0x7F80 means an inf or NaN is present).
+template <int N>
+__device__ __forceinline__ uint32_t bf16_absmax_bits(const uint32_t (&w)[N])
+{
+    uint32_t m = w[0] & 0x7FFF7FFFu;
+#pragma unroll
+    for (int k = 1; k < N; ++k) m = pk_max_u16(m, w[k] & 0x7FFF7FFFu);
+    const uint32_t lo = m & 0xFFFFu, hi = m >> 16;
+    return lo > hi ? lo : hi;
+}
+
 // ---------------------------------------------------------------- sanitisation
 // NaN -> +0, +-inf -> +-largest finite bf16 (0x7F7F), applied to the value
 // being quantised (NVFP4 / AMDFP4 paths).
@@ -146,7 +260,49 @@ __device__ __forceinline__ float sanitize(float v)
     return v;
 }
 
-// ---------------------------------------------------------------- cross-lane max
+// ---------------------------------------------------------------- cross-lane max (DPP)
+// Unsigned max with a DPP-permuted copy; lanes outside the row/bank mask see 0,
+// which is neutral for the non-negative values reduced here (magnitudes, or
+// float bit patterns of magnitudes, which order like the floats).
+template <int CTRL, int ROWMASK = 0xF>
+__device__ __forceinline__ uint32_t max_dpp(uint32_t v)
+{
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWMASK, 0xF, false);
+    return v > o ? v : o;
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+constexpr int kDppBcast15 = 0x142;
+constexpr int kDppBcast31 = 0x143;
+
+// Max over aligned groups of 2 or 4 consecutive lanes (width 1, 2 or 4).
+__device__ __forceinline__ uint32_t quad_max_u32(uint32_t v, int width)
+{
+    if (width > 1) v = max_dpp<kDppXor1>(v);
+    if (width > 2) v = max_dpp<kDppXor2>(v);
+    return v;
+}
+
+// Max over the whole wave64, returned uniformly.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    v = max_dpp<kDppXor1>(v);
+    v = max_dpp<kDppXor2>(v);
+    v = max_dpp<kDppHalfMirror>(v);
+    v = max_dpp<kDppMirror>(v);             // every lane holds its row-of-16 max
+    v = max_dpp<kDppBcast15, 0xA>(v);      // rows 1, 3 take in rows 0, 2
+    v = max_dpp<kDppBcast31, 0xC>(v);      // rows 2, 3 take in rows 0-1
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+__device__ __forceinline__ float quad_max(float v, int width)
+{
+    return __uint_as_float(quad_max_u32(__float_as_uint(v), width));
+}
+
+// ---------------------------------------------------------------- legacy cross-lane max
 // Max over aligned groups of W consecutive lanes (W a power of two <= 64).
 template <int W>
 __device__ __forceinline__ float group_max(float v)

@@ -9,7 +9,11 @@
 //
 // Work decomposition: one lane owns 8 consecutive bf16 (one 16-byte load),
 // four neighbouring lanes own one 32-element block and combine their maxima
-// with two cross-lane steps.  Each workgroup streams kUnroll * 256 chunks with
+// (packed 16-bit integer max of |x| bit patterns) with two DPP steps.  The
+// E2M1 encode of x / 2^k and the decode of +-G[m] * 2^k are gfx950's scaled
+// FP4 conversions, which match the RTNE / satfinite / signed-zero rules
+// exactly for every bf16 input and every k in [-126, 125] (checked
+// exhaustively on the device).  Each workgroup streams kUnroll * 256 chunks with
 // all loads issued before any arithmetic, so a wave keeps kUnroll 16-byte
 // requests in flight.  The kernel is HBM-bound; no LDS, no MFMA.
 #include "fp4q_device.h"
@@ -34,19 +38,17 @@ __device__ __forceinline__ int mx_exponent(uint32_t abits)
     return k > 125 ? 125 : k;
 }
 
-// Quantise two bf16 halves of one 32-bit word; returns two bf16 results and
-// two codes (low nibble = low half).
-__device__ __forceinline__ void mx_pair(uint32_t w, float inv_scale, float scale, uint32_t& yw, uint32_t& cw)
+// bf16 pair (hi halves of two floats): bytes 2-3 of each
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
-    float f0 = bf16_lo(w), f1 = bf16_hi(w);
-    uint32_t m0 = e2m1_rne(__builtin_fabsf(f0) * inv_scale);
-    uint32_t m1 = e2m1_rne(__builtin_fabsf(f1) * inv_scale);
-    uint32_t s0 = (w >> 15) & 1u, s1 = w >> 31;
-    // G[m] * 2^k is exact in binary32 (<= 2 significant bits, >= 2^-127)
-    uint32_t q0 = __float_as_uint(e2m1_value(m0) * scale) >> 16;
-    uint32_t q1 = __float_as_uint(e2m1_value(m1) * scale) >> 16;
-    yw = (q0 | (s0 << 15)) | ((q1 | (s1 << 15)) << 16);
-    cw = (m0 | (s0 << 3)) | ((m1 | (s1 << 3)) << 4);
+    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+template <int Q>
+__device__ __forceinline__ uint32_t decode_pair_bf16(uint32_t codes, float scale)
+{
+    auto f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, scale, Q);   // exact +-G[m] * 2^k
+    return pack_bf16x2(f[0], f[1]);
 }
 
 template <bool CONTIG, bool WY, bool WC>
@@ -75,32 +77,30 @@ __global__ __launch_bounds__(kThreads) void k_mx_qdq(const uint16_t* __restrict_
         // the four lanes of a block are consecutive and nchunks % 4 == 0, so
         // they are all inside or all outside the tensor
         if (c >= nchunks) continue;
-        const uint4 w = in[u];
-        uint32_t a = 0;
-        a = max(a, w.x & 0x7FFFu); a = max(a, (w.x >> 16) & 0x7FFFu);
-        a = max(a, w.y & 0x7FFFu); a = max(a, (w.y >> 16) & 0x7FFFu);
-        a = max(a, w.z & 0x7FFFu); a = max(a, (w.z >> 16) & 0x7FFFu);
-        a = max(a, w.w & 0x7FFFu); a = max(a, (w.w >> 16) & 0x7FFFu);
-        a = group_max_u32<4>(a);
-        const bool poisoned = a >= 0x7F80u;   // any inf or NaN in the block
+        const uint32_t w[4] = {in[u].x, in[u].y, in[u].z, in[u].w};
+        const uint32_t a = quad_max_u32(bf16_absmax_bits(w), 4);   // block amax, as bf16 bits
+        const bool poisoned = a >= 0x7F80u;                          // any inf or NaN in the block
         const int k = mx_exponent(a);
-        const float inv_scale = __uint_as_float((uint32_t)(127 - k) << 23);
-        const float scale = __uint_as_float((uint32_t)(127 + k) << 23);
-        uint4 yo;
-        uint32_t c0, c1, c2, c3;
-        mx_pair(w.x, inv_scale, scale, yo.x, c0);
-        mx_pair(w.y, inv_scale, scale, yo.y, c1);
-        mx_pair(w.z, inv_scale, scale, yo.z, c2);
-        mx_pair(w.w, inv_scale, scale, yo.w, c3);
-        uint32_t cw = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
-        if (poisoned) {
-            yo = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
-            cw = 0;
-        }
+        const float scale = __uint_as_float((uint32_t)(127 + k) << 23);   // 2^k
+        // codes of x / 2^k: hardware RNE onto E2M1, sign kept
+        uint32_t cw = 0;
+        cw = fp4x2_rne_scaled<0>(cw, bf16_lo(w[0]), bf16_hi(w[0]), scale);
+        cw = fp4x2_rne_scaled<1>(cw, bf16_lo(w[1]), bf16_hi(w[1]), scale);
+        cw = fp4x2_rne_scaled<2>(cw, bf16_lo(w[2]), bf16_hi(w[2]), scale);
+        cw = fp4x2_rne_scaled<3>(cw, bf16_lo(w[3]), bf16_hi(w[3]), scale);
+        if (poisoned) cw = 0;
         size_t yoff;
         if (CONTIG) yoff = (size_t)c * 8;
         else { uint32_t r = c / cpr; yoff = (size_t)r * cols + (size_t)(c - r * cpr) * 8; }
-        if (WY) *(uint4*)(y + yoff) = yo;
+        if (WY) {
+            uint4 yo;
+            yo.x = decode_pair_bf16<0>(cw, scale);
+            yo.y = decode_pair_bf16<1>(cw, scale);
+            yo.z = decode_pair_bf16<2>(cw, scale);
+            yo.w = decode_pair_bf16<3>(cw, scale);
+            if (poisoned) yo = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
+            *(uint4*)(y + yoff) = yo;
+        }
         if (WC) {
             *(uint32_t*)(codes + yoff / 2) = cw;
             if ((c & 3u) == 0) scales[yoff / 32] = poisoned ? 0xFFu : (uint8_t)(k + 127);
@@ -108,7 +108,8 @@ __global__ __launch_bounds__(kThreads) void k_mx_qdq(const uint16_t* __restrict_
     }
 }
 
-// Dequantise: y = +-G[m] * 2^(s-127); scale byte 0xFF (NaN) -> 0x7FC0.
+// Dequantise: y = +-G[m] * 2^(s-127) (2^-127 for s == 0 kept); scale byte
+// 0xFF (NaN) -> 0x7FC0.
 __global__ __launch_bounds__(kThreads) void k_mx_dequant(const uint8_t* __restrict__ codes,
                                                          const uint8_t* __restrict__ scales, uint32_t nchunks,
                                                          uint16_t* __restrict__ y)
@@ -117,17 +118,14 @@ __global__ __launch_bounds__(kThreads) void k_mx_dequant(const uint8_t* __restri
     if (c >= nchunks) return;
     const uint32_t cw = *(const uint32_t*)(codes + (size_t)c * 4);
     const uint32_t sb = scales[c >> 2];
-    const float scale = sb == 0 ? __uint_as_float(0x00400000u) : __uint_as_float(sb << 23);  // 2^-127 kept
-    uint32_t out[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        uint32_t n0 = (cw >> (8 * p)) & 0xFu, n1 = (cw >> (8 * p + 4)) & 0xFu;
-        uint32_t q0 = __float_as_uint(e2m1_value(n0 & 7u) * scale) >> 16;
-        uint32_t q1 = __float_as_uint(e2m1_value(n1 & 7u) * scale) >> 16;
-        out[p] = (q0 | ((n0 >> 3) << 15)) | ((q1 | ((n1 >> 3) << 15)) << 16);
-        if (sb == 0xFFu) out[p] = 0x7FC07FC0u;
-    }
-    *(uint4*)(y + (size_t)c * 8) = make_uint4(out[0], out[1], out[2], out[3]);
+    const float scale = sb == 0 ? __uint_as_float(0x00400000u) : __uint_as_float(sb << 23);
+    uint4 yo;
+    yo.x = decode_pair_bf16<0>(cw, scale);
+    yo.y = decode_pair_bf16<1>(cw, scale);
+    yo.z = decode_pair_bf16<2>(cw, scale);
+    yo.w = decode_pair_bf16<3>(cw, scale);
+    if (sb == 0xFFu) yo = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
+    *(uint4*)(y + (size_t)c * 8) = yo;
 }
 
 }  // namespace

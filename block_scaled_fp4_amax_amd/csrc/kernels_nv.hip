@@ -17,8 +17,8 @@
 // Work decomposition: one lane owns one 16-element inner block (two 16-byte
 // loads); the obs/16 lanes of a 1D outer group are neighbours and combine
 // their maxima with cross-lane steps.
-#include "fp4q_device.h"
 #include "launch.h"
+#include "nv_block.h"
 
 namespace fp4q {
 
@@ -26,23 +26,6 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// 16 SR variates for elements idx0 .. idx0+15 (idx0 = global index of the
-// block's first element); draws 2 Philox blocks, or 3 when idx0 % 8 != 0.
-__device__ __forceinline__ void sr_draws16(uint64_t seed, uint64_t step, uint64_t idx0, uint32_t (&u)[16])
-{
-    const uint64_t b0 = idx0 >> 3;
-    const int off = (int)(idx0 & 7u);
-    const u32x4 w0 = sr_words(seed, step, b0);
-    const u32x4 w1 = sr_words(seed, step, b0 + 1);
-    u32x4 w2 = w1;
-    if (off != 0) w2 = sr_words(seed, step, b0 + 2);
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        const int e = off + k;
-        const u32x4& w = (e >> 3) == 0 ? w0 : ((e >> 3) == 1 ? w1 : w2);
-        u[k] = sr_lane(w, e & 7);
-    }
-}
 
 __device__ __forceinline__ void load16_bf16(const uint16_t* p, float (&v)[16])
 {
@@ -68,47 +51,12 @@ __device__ __forceinline__ void store16_f32(float* p, const float (&z)[16])
     for (int q = 0; q < 4; ++q) *(float4*)(p + 4 * q) = make_float4(z[4 * q], z[4 * q + 1], z[4 * q + 2], z[4 * q + 3]);
 }
 
-// Quantise one 16-element block of normalised values; returns the scale code,
-// writes the packed codes and (optionally) the signed inner-dequantised values
-// p = +-G[m] * d.
-template <int BIAS, bool SR>
-__device__ __forceinline__ uint32_t quant_block16(const float (&vn)[16], const uint32_t (&u)[16], uint2& packed,
-                                                  float (&p)[16])
-{
-    float b = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) b = fmaxf(b, __builtin_fabsf(vn[k]));
-    const float ys = b / 6.0f;
-    const uint32_t cs = scale_encode<BIAS>(ys);
-    const float d = scale_decode<BIAS>(cs);
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        const float t = d == 0.0f ? 0.0f : __builtin_fabsf(vn[k]) / d;
-        const uint32_t m = SR ? e2m1_sr(t, u[k]) : e2m1_rne(t);
-        const uint32_t sgn = __float_as_uint(vn[k]) >> 31;
-        const uint32_t code = m | (sgn << 3);
-        if (k < 8) lo |= code << (4 * k);
-        else hi |= code << (4 * (k - 8));
-        const float pm = e2m1_value(m) * d;   // exact
-        p[k] = sgn ? -pm : pm;
-    }
-    packed = make_uint2(lo, hi);
-    return cs;
-}
-
-template <int W>
-__device__ __forceinline__ float runtime_group_max(float v, int width)
-{
-#pragma unroll
-    for (int m = 1; m < W; m <<= 1)
-        if (m < width) v = fmaxf(v, __shfl_xor(v, m, 64));
-    return v;
-}
-
-template <int BIAS, int OUTER, bool SR>
+template <int BIAS, int OUTER, bool SR, bool EF>
 __global__ __launch_bounds__(kThreads) void k_nv_rows(RowArgs a, uint32_t nblocks, uint32_t bpr)
 {
+    __shared__ double rtab[16];
+    fill_recip_table(rtab, (int)threadIdx.x);
+    __syncthreads();
     const uint32_t b = blockIdx.x * kThreads + threadIdx.x;   // inner block id
     // lanes of one 1D outer group are consecutive and bpr % obs16 == 0, so a
     // group is entirely inside or outside the tensor
@@ -119,18 +67,43 @@ __global__ __launch_bounds__(kThreads) void k_nv_rows(RowArgs a, uint32_t nblock
     const int64_t e0 = (int64_t)i * a.cols + j0;   // element offset in contiguous outputs
 
     float v[16];
-    load16_bf16(a.x + (int64_t)i * a.ld + j0, v);
     float z[16];
-    if (a.residual) {
-        load16_f32(a.residual + e0, z);
+    uint32_t am_bits = 0;
+    {
+        const uint16_t* px = a.x + (int64_t)i * a.ld + j0;
+        const uint4 w0 = *(const uint4*)px;
+        const uint4 w1 = *(const uint4*)(px + 8);
+        const uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
-        for (int k = 0; k < 16; ++k) v[k] = v[k] + z[k];
+        for (int k = 0; k < 8; ++k) { v[2 * k] = bf16_lo(w[k]); v[2 * k + 1] = bf16_hi(w[k]); }
+        if (EF) {
+            load16_f32(a.residual + e0, z);
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                v[k] = v[k] + z[k];
+                const uint32_t bb = __float_as_uint(v[k]) & 0x7FFFFFFFu;
+                am_bits = am_bits > bb ? am_bits : bb;
+            }
+        } else {
+            am_bits = bf16_absmax_bits(w) << 16;
+        }
+        if (__builtin_expect(am_bits >= 0x7F800000u, 0)) {
+            am_bits = 0;
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                v[k] = sanitize(v[k]);
+                const uint32_t bb = __float_as_uint(v[k]) & 0x7FFFFFFFu;
+                am_bits = am_bits > bb ? am_bits : bb;
+            }
+        }
     }
-#pragma unroll
-    for (int k = 0; k < 16; ++k) v[k] = sanitize(v[k]);
 
     uint32_t u[16];
     if (SR) sr_draws16(a.seed, a.step, a.index_base + (uint64_t)e0, u);
+    else {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) u[k] = 0;
+    }
 
     float s_o = 1.0f;
     if (OUTER == kOuterTensor) {
@@ -140,29 +113,32 @@ __global__ __launch_bounds__(kThreads) void k_nv_rows(RowArgs a, uint32_t nblock
         if (a.outer_given) {
             s_o = a.outer[og];
         } else {
-            float am = 0.0f;
-#pragma unroll
-            for (int k = 0; k < 16; ++k) am = fmaxf(am, __builtin_fabsf(v[k]));
-            am = runtime_group_max<8>(am, a.obs16);
-            s_o = am / ScaleFmt<BIAS>::outer_den();
+            uint32_t m = am_bits;
+            if (a.obs16 > 1) m = max_dpp<kDppXor1>(m);
+            if (a.obs16 > 2) m = max_dpp<kDppXor2>(m);
+            if (a.obs16 > 4) m = max_dpp<kDppHalfMirror>(m);
+            s_o = __uint_as_float(m) / ScaleFmt<BIAS>::outer_den();
             if (a.outer && jb % (uint32_t)a.obs16 == 0) a.outer[og] = s_o;
         }
     }
     float vn[16];
+    if (OUTER == kOuterNone) {
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        if (OUTER == kOuterNone) vn[k] = v[k];
-        else vn[k] = s_o == 0.0f ? __builtin_copysignf(0.0f, v[k]) : v[k] / s_o;
+        for (int k = 0; k < 16; ++k) vn[k] = v[k];
+    } else {
+        normalize16(v, s_o, outer_inv(s_o), vn);
     }
-    uint2 packed;
-    float p[16];
-    const uint32_t cs = quant_block16<BIAS, SR>(vn, u, packed, p);
+    const BlockScale<BIAS> sc = block_scale<BIAS>(max_abs16(vn), rtab);
+    const uint2 packed = SR ? codes16_sr<BIAS>(vn, u, sc) : codes16_rne(vn, sc.rd);
     if (a.codes) *(uint2*)(a.codes + e0 / 2) = packed;
-    if (a.scales) a.scales[(int64_t)i * bpr + jb] = (uint8_t)cs;
-    if (a.y || a.residual) {
+    if (a.scales) a.scales[(int64_t)i * bpr + jb] = (uint8_t)sc.code;
+    if (a.y || EF) {
         float w[16];
+        decode16(packed, sc.d, w);
+        if (OUTER != kOuterNone) {
 #pragma unroll
-        for (int k = 0; k < 16; ++k) w[k] = (OUTER == kOuterNone) ? p[k] : p[k] * s_o;
+            for (int k = 0; k < 16; ++k) w[k] = w[k] * s_o;
+        }
         if (a.y) {
             uint32_t o[8];
 #pragma unroll
@@ -170,7 +146,7 @@ __global__ __launch_bounds__(kThreads) void k_nv_rows(RowArgs a, uint32_t nblock
             *(uint4*)(a.y + e0) = make_uint4(o[0], o[1], o[2], o[3]);
             *(uint4*)(a.y + e0 + 8) = make_uint4(o[4], o[5], o[6], o[7]);
         }
-        if (a.residual) {
+        if (EF) {
 #pragma unroll
             for (int k = 0; k < 16; ++k) z[k] = v[k] - w[k];
             store16_f32(a.residual + e0, z);
@@ -271,16 +247,24 @@ hipError_t launch_rows(int bias, int outer_kind, bool sr, const RowArgs& a, hipS
     const uint32_t bpr = (uint32_t)(a.cols / 16);
     const uint32_t nblocks = (uint32_t)(a.rows * bpr);
     const uint32_t grid = (nblocks + kThreads - 1) / kThreads;
-#define FP4Q_ROWS(B, O, S) hipLaunchKernelGGL((k_nv_rows<B, O, S>), dim3(grid), dim3(kThreads), 0, s, a, nblocks, bpr)
-#define FP4Q_ROWS_O(B, S)                                           \
-    do {                                                            \
-        if (outer_kind == kOuterNone) FP4Q_ROWS(B, kOuterNone, S);   \
-        else if (outer_kind == kOuterTensor) FP4Q_ROWS(B, kOuterTensor, S); \
-        else FP4Q_ROWS(B, kOuter1D, S);                             \
+    const bool ef = a.residual != nullptr;
+#define FP4Q_ROWS(B, O, S, E) \
+    hipLaunchKernelGGL((k_nv_rows<B, O, S, E>), dim3(grid), dim3(kThreads), 0, s, a, nblocks, bpr)
+#define FP4Q_ROWS_E(B, O, S)                     \
+    do {                                         \
+        if (ef) FP4Q_ROWS(B, O, S, true);        \
+        else FP4Q_ROWS(B, O, S, false);          \
+    } while (0)
+#define FP4Q_ROWS_O(B, S)                                                 \
+    do {                                                                  \
+        if (outer_kind == kOuterNone) FP4Q_ROWS_E(B, kOuterNone, S);       \
+        else if (outer_kind == kOuterTensor) FP4Q_ROWS_E(B, kOuterTensor, S); \
+        else FP4Q_ROWS_E(B, kOuter1D, S);                                 \
     } while (0)
     if (bias == 7) { if (sr) FP4Q_ROWS_O(7, true); else FP4Q_ROWS_O(7, false); }
     else { if (sr) FP4Q_ROWS_O(15, true); else FP4Q_ROWS_O(15, false); }
 #undef FP4Q_ROWS_O
+#undef FP4Q_ROWS_E
 #undef FP4Q_ROWS
     return hipGetLastError();
 }

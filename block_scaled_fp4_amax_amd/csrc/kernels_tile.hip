@@ -29,8 +29,12 @@
 // Tiles are taken in row-major order, split into 8 contiguous slices, one per
 // XCD (workgroup ids are dealt round-robin to the XCDs), so the partial cache
 // lines that neighbouring tiles write meet in the same L2.
-#include "fp4q_device.h"
+#include <cstdlib>
+#include <mutex>
+#include <vector>
+
 #include "launch.h"
+#include "nv_block.h"
 
 namespace fp4q {
 
@@ -39,253 +43,352 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kTile = 64;
 
-__device__ __forceinline__ void sr_draws16_t(uint64_t seed, uint64_t step, uint64_t idx0, uint32_t (&u)[16])
-{
-    const uint64_t b0 = idx0 >> 3;
-    const int off = (int)(idx0 & 7u);
-    const u32x4 w0 = sr_words(seed, step, b0);
-    const u32x4 w1 = sr_words(seed, step, b0 + 1);
-    u32x4 w2 = w1;
-    if (off != 0) w2 = sr_words(seed, step, b0 + 2);
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        const int e = off + k;
-        const u32x4& w = (e >> 3) == 0 ? w0 : ((e >> 3) == 1 ? w1 : w2);
-        u[k] = sr_lane(w, e & 7);
-    }
-}
 
 template <int BIAS, bool SR>
-__device__ __forceinline__ uint32_t quant16(const float (&vn)[16], const uint32_t (&u)[16], uint2& packed,
-                                            float (&p)[16])
+__device__ __forceinline__ uint2 quant16(const float (&vn)[16], const uint32_t (&u)[16], const double* tab,
+                                         BlockScale<BIAS>& sc)
 {
-    float b = 0.0f;
+    sc = block_scale<BIAS>(max_abs16(vn), tab);
+    if (SR) return codes16_sr<BIAS>(vn, u, sc);
+    return codes16_rne(vn, sc.rd);
+}
+
+// Where one tile sits: group, tile row / column, valid extent, and this
+// lane's row block.
+struct TileCoord {
+    int g, ti, tj, rows_valid, cols_valid;
+    int64_t Rg, lrow0, i_g, c0, e0;
+    bool act;
+};
+
+__device__ __forceinline__ TileCoord tile_coord(const TileArgs& a, int tile, int r, int sg)
+{
+    TileCoord c;
+    int g = 0;
+    while (g + 1 < a.ngroups && a.tile0[g + 1] <= tile) ++g;
+    const int lt = tile - a.tile0[g];
+    c.g = g;
+    c.ti = lt / a.tiles_c;
+    c.tj = lt - c.ti * a.tiles_c;
+    c.Rg = (int64_t)(a.row0[g + 1] - a.row0[g]);
+    c.lrow0 = (int64_t)c.ti * kTile;
+    c.c0 = (int64_t)c.tj * kTile;
+    c.rows_valid = (int)min((int64_t)kTile, c.Rg - c.lrow0);
+    c.cols_valid = (int)min((int64_t)kTile, a.cols - c.c0);
+    c.act = (r < c.rows_valid) && (16 * sg < c.cols_valid);
+    c.i_g = (int64_t)a.row0[g] + c.lrow0 + r;
+    c.e0 = c.i_g * a.cols + c.c0 + 16 * sg;
+    return c;
+}
+
+// The lane's raw inputs for one tile: 16 bf16 (two 16-byte loads) and, with
+// error feedback, the 16 FP32 residuals.
+template <bool EF>
+struct TileInput {
+    uint4 w0, w1;
+    float4 z[EF ? 4 : 1];
+};
+
+template <bool EF>
+__device__ __forceinline__ void load_tile_input(const TileArgs& a, const TileCoord& c, TileInput<EF>& in)
+{
+    if (c.act) {
+        const uint16_t* px = a.x + c.i_g * a.ld + c.c0 + 16 * (threadIdx.x & 3);
+        in.w0 = *(const uint4*)px;
+        in.w1 = *(const uint4*)(px + 8);
+        if (EF) {
 #pragma unroll
-    for (int k = 0; k < 16; ++k) b = fmaxf(b, __builtin_fabsf(vn[k]));
-    const uint32_t cs = scale_encode<BIAS>(b / 6.0f);
-    const float d = scale_decode<BIAS>(cs);
-    uint32_t lo = 0, hi = 0;
+            for (int q = 0; q < 4; ++q) in.z[q] = *(const float4*)(a.residual + c.e0 + 4 * q);
+        }
+    } else {
+        in.w0 = make_uint4(0, 0, 0, 0);
+        in.w1 = make_uint4(0, 0, 0, 0);
+        if (EF) {
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        const float t = d == 0.0f ? 0.0f : __builtin_fabsf(vn[k]) / d;
-        const uint32_t m = SR ? e2m1_sr(t, u[k]) : e2m1_rne(t);
-        const uint32_t sgn = __float_as_uint(vn[k]) >> 31;
-        const uint32_t code = m | (sgn << 3);
-        if (k < 8) lo |= code << (4 * k);
-        else hi |= code << (4 * (k - 8));
-        const float pm = e2m1_value(m) * d;
-        p[k] = sgn ? -pm : pm;
+            for (int q = 0; q < 4; ++q) in.z[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
     }
-    packed = make_uint2(lo, hi);
-    return cs;
 }
 
-__device__ __forceinline__ float lanes_max(float v, int width)
+// Persistent workgroups: workgroup (xcd = id % 8, slot = id / 8) walks the
+// tiles xcd * per_xcd + slot + j * wgs_per_xcd of its XCD's contiguous slice,
+// loading tile j+1's inputs before it computes tile j.
+// Register budget per lane: 64 VGPRs (8 waves per SIMD) for the plain RTNE
+// kernels, 72 (7 waves) for 1D outer groups, 128 (4 waves) with stochastic
+// rounding or a residual.
+template <int BIAS, int OUTER, bool SR, bool COLS, bool EF>
+constexpr int tile_waves_per_simd()
 {
-    // max over aligned groups of `width` (1, 2 or 4) consecutive lanes
-    if (width > 1) v = fmaxf(v, __shfl_xor(v, 1, 64));
-    if (width > 2) v = fmaxf(v, __shfl_xor(v, 2, 64));
-    return v;
+    return (SR || EF) ? 4 : (OUTER == kOuter1D ? 7 : 8);
 }
 
-template <int BIAS, int OUTER, bool SR, bool COLS>
-__global__ __launch_bounds__(kThreads) void k_tile(TileArgs a)
+template <int BIAS, int OUTER, bool SR, bool COLS, bool EF, bool GIVEN>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(tile_waves_per_simd<BIAS, OUTER, SR, COLS, EF>())))
+void k_tile(TileArgs a)
 {
     __shared__ float lds_v[kTile][kTile + 1];
     __shared__ uint16_t lds_u[SR ? kTile : 1][SR ? kTile + 2 : 1];
     __shared__ float red[kThreads / 64];
-
-    const int bid = (int)blockIdx.x;
-    const int tile = (bid & 7) * a.per_xcd + (bid >> 3);
-    if (tile >= a.total_tiles) return;   // uniform per workgroup
-    int g = 0;
-    while (g + 1 < a.ngroups && a.tile0[g + 1] <= tile) ++g;
-    const int lt = tile - a.tile0[g];
-    const int ti = lt / a.tiles_c, tj = lt - ti * a.tiles_c;
-    const int64_t cols = a.cols;
-    const int64_t Rg = (int64_t)(a.row0[g + 1] - a.row0[g]);
-    const int64_t lrow0 = (int64_t)ti * kTile;          // first tile row inside the group
-    const int64_t grow0 = (int64_t)a.row0[g] + lrow0;  // ... in the stacked tensor
-    const int64_t c0 = (int64_t)tj * kTile;
-    const int rows_valid = (int)min((int64_t)kTile, Rg - lrow0);
-    const int cols_valid = (int)min((int64_t)kTile, cols - c0);
-    const float den = ScaleFmt<BIAS>::outer_den();
+    __shared__ double rtab[16];
 
     const int tid = (int)threadIdx.x;
     const int r = tid >> 2, sg = tid & 3;
-    const bool act = (r < rows_valid) && (16 * sg < cols_valid);
-    const int64_t i_g = grow0 + r;
-    const int64_t e0 = i_g * cols + c0 + 16 * sg;   // element offset in the stacked row-major tensor
+    const int xcd = (int)(blockIdx.x & 7u), slot = (int)(blockIdx.x >> 3);
+    const int slice0 = xcd * a.per_xcd;
+    const int slice_end = min(slice0 + a.per_xcd, a.total_tiles);
+    int tile = slice0 + slot;
+    if (tile >= slice_end) return;   // uniform per workgroup
+    fill_recip_table(rtab, tid);
+    const float den = ScaleFmt<BIAS>::outer_den();
+    const int64_t cols = a.cols;
 
-    // ---------------- row phase
-    float v[16];
-    float z[16];
+    TileInput<EF> in;
+    load_tile_input<EF>(a, tile_coord(a, tile, r, sg), in);
+
+    for (;;) {
+        const TileCoord cur = tile_coord(a, tile, r, sg);
+        // ---- prefetch the next tile's inputs
+        const int next = tile + a.wgs_per_xcd;
+        const bool has_next = next < slice_end;
+        TileInput<EF> nin = in;
+        if (has_next) load_tile_input<EF>(a, tile_coord(a, next, r, sg), nin);
+
+        // ---------------- row phase
+        float v[16];
+        uint32_t am_bits = 0;    // bit pattern of max |v| over the lane's 16 values
+        {
+            const uint32_t w[8] = {in.w0.x, in.w0.y, in.w0.z, in.w0.w, in.w1.x, in.w1.y, in.w1.z, in.w1.w};
 #pragma unroll
-    for (int k = 0; k < 16; ++k) { v[k] = 0.0f; z[k] = 0.0f; }
-    if (act) {
-        const uint16_t* px = a.x + i_g * a.ld + c0 + 16 * sg;
-        const uint4 w0 = *(const uint4*)px;
-        const uint4 w1 = *(const uint4*)(px + 8);
-        const uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+            for (int k = 0; k < 8; ++k) { v[2 * k] = bf16_lo(w[k]); v[2 * k + 1] = bf16_hi(w[k]); }
+            if (EF) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) { v[2 * k] = bf16_lo(w[k]); v[2 * k + 1] = bf16_hi(w[k]); }
-        if (a.residual) {
+                for (int q = 0; q < 4; ++q) {
+                    v[4 * q] = v[4 * q] + in.z[q].x;
+                    v[4 * q + 1] = v[4 * q + 1] + in.z[q].y;
+                    v[4 * q + 2] = v[4 * q + 2] + in.z[q].z;
+                    v[4 * q + 3] = v[4 * q + 3] + in.z[q].w;
+                }
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float4 f = *(const float4*)(a.residual + e0 + 4 * q);
-                z[4 * q] = f.x; z[4 * q + 1] = f.y; z[4 * q + 2] = f.z; z[4 * q + 3] = f.w;
+                for (int k = 0; k < 16; ++k) {
+                    const uint32_t b = __float_as_uint(v[k]) & 0x7FFFFFFFu;
+                    am_bits = am_bits > b ? am_bits : b;
+                }
+            } else {
+                am_bits = bf16_absmax_bits(w) << 16;
             }
+            // NaN / inf anywhere in the lane's 16 values (rare): sanitise them
+            if (__builtin_expect(am_bits >= 0x7F800000u, 0)) {
+                am_bits = 0;
 #pragma unroll
-            for (int k = 0; k < 16; ++k) v[k] = v[k] + z[k];
-        }
-#pragma unroll
-        for (int k = 0; k < 16; ++k) v[k] = sanitize(v[k]);
-    }
-    uint32_t u[16];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) u[k] = 0;
-    if (SR && act) sr_draws16_t(a.seed, a.step, a.index_base + (uint64_t)e0, u);
-
-    float am = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) am = fmaxf(am, __builtin_fabsf(v[k]));
-
-    float s_row = 1.0f;
-    if (OUTER == kOuterTensor) {
-        s_row = *a.tensor_scale;
-    } else if (OUTER == kOuter2D) {
-        const int64_t oidx = ((int64_t)a.row0[g] / kTile) * (cols / kTile) + (int64_t)ti * (cols / kTile) + tj;
-        if (a.outer_given) {
-            s_row = a.row_outer[oidx];
-        } else {
-            float m = group_max<64>(am);
-            if ((tid & 63) == 0) red[tid >> 6] = m;
-            __syncthreads();
-            m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-            s_row = m / den;
-            if (tid == 0 && a.row_outer) a.row_outer[oidx] = s_row;
-        }
-    } else if (OUTER == kOuter1D) {
-        const int64_t ogr = i_g * (cols / (16 * a.obs16)) + (c0 + 16 * sg) / (16 * a.obs16);
-        if (a.outer_given) {
-            s_row = act ? a.row_outer[ogr] : 1.0f;
-        } else {
-            s_row = lanes_max(am, a.obs16) / den;
-            if (act && a.row_outer && (sg % a.obs16) == 0) a.row_outer[ogr] = s_row;
-        }
-    }
-
-    float vn[16];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        if (OUTER == kOuterNone) vn[k] = v[k];
-        else vn[k] = s_row == 0.0f ? __builtin_copysignf(0.0f, v[k]) : v[k] / s_row;
-    }
-    if (act) {
-        uint2 packed;
-        float p[16];
-        const uint32_t cs = quant16<BIAS, SR>(vn, u, packed, p);
-        if (a.row_codes) *(uint2*)(a.row_codes + e0 / 2) = packed;
-        if (a.row_scales) a.row_scales[e0 / 16] = (uint8_t)cs;
-        if (a.y || a.residual) {
-            float w[16];
-#pragma unroll
-            for (int k = 0; k < 16; ++k) w[k] = (OUTER == kOuterNone) ? p[k] : p[k] * s_row;
-            if (a.y) {
-                uint32_t o[8];
-#pragma unroll
-                for (int k = 0; k < 8; ++k) o[k] = f32_to_bf16(w[2 * k]) | (f32_to_bf16(w[2 * k + 1]) << 16);
-                *(uint4*)(a.y + e0) = make_uint4(o[0], o[1], o[2], o[3]);
-                *(uint4*)(a.y + e0 + 8) = make_uint4(o[4], o[5], o[6], o[7]);
-            }
-            if (a.residual) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    *(float4*)(a.residual + e0 + 4 * q) =
-                        make_float4(v[4 * q] - w[4 * q], v[4 * q + 1] - w[4 * q + 1], v[4 * q + 2] - w[4 * q + 2],
-                                    v[4 * q + 3] - w[4 * q + 3]);
+                for (int k = 0; k < 16; ++k) {
+                    v[k] = sanitize(v[k]);
+                    const uint32_t b = __float_as_uint(v[k]) & 0x7FFFFFFFu;
+                    am_bits = am_bits > b ? am_bits : b;
+                }
             }
         }
-    }
-    if (!COLS) return;
+        uint32_t u[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) u[k] = 0;
+        if (SR && cur.act) sr_draws16(a.seed, a.step, a.index_base + (uint64_t)cur.e0, u);
 
-    // ---------------- stage through LDS
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        lds_v[r][16 * sg + k] = (OUTER == kOuter1D) ? v[k] : vn[k];
-        if (SR) lds_u[r][16 * sg + k] = (uint16_t)u[k];
-    }
-    __syncthreads();
-
-    // ---------------- column phase
-    const int cc = tid >> 2, rs = tid & 3;
-    const bool actc = (cc < cols_valid) && (16 * rs < rows_valid);
-    float cv[16];
-    uint32_t cu[16];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        cv[k] = lds_v[16 * rs + k][cc];
-        cu[k] = SR ? (uint32_t)lds_u[16 * rs + k][cc] : 0u;
-    }
-    if (OUTER == kOuter1D) {
-        const int64_t colbase = (int64_t)a.row0[g] * cols / (16 * a.obs16);   // this group's col outer array
-        const int64_t ogc = colbase + (c0 + cc) * (Rg / (16 * a.obs16)) + (lrow0 + 16 * rs) / (16 * a.obs16);
-        float s_col;
-        if (a.outer_given) {
-            s_col = actc ? a.col_outer[ogc] : 1.0f;
-        } else {
-            float m = 0.0f;
-#pragma unroll
-            for (int k = 0; k < 16; ++k) m = fmaxf(m, __builtin_fabsf(cv[k]));
-            s_col = lanes_max(m, a.obs16) / den;
-            if (actc && a.col_outer && (rs % a.obs16) == 0) a.col_outer[ogc] = s_col;
+        float s_row = 1.0f;
+        if (OUTER == kOuterTensor) {
+            s_row = *a.tensor_scale;
+        } else if (OUTER == kOuter2D) {
+            const int64_t oidx =
+                ((int64_t)a.row0[cur.g] / kTile) * (cols / kTile) + (int64_t)cur.ti * (cols / kTile) + cur.tj;
+            if (GIVEN) {
+                s_row = a.row_outer[oidx];
+            } else {
+                const uint32_t m = wave_max_u32(am_bits);
+                if ((tid & 63) == 0) red[tid >> 6] = __uint_as_float(m);
+                lds_barrier();
+                s_row = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])) / den;
+                if (tid == 0 && a.row_outer) a.row_outer[oidx] = s_row;
+            }
+        } else if (OUTER == kOuter1D) {
+            const int64_t ogr = cur.i_g * (cols / (16 * a.obs16)) + (cur.c0 + 16 * sg) / (16 * a.obs16);
+            if (GIVEN) {
+                s_row = cur.act ? a.row_outer[ogr] : 1.0f;
+            } else {
+                s_row = __uint_as_float(quad_max_u32(am_bits, a.obs16)) / den;
+                if (cur.act && a.row_outer && (sg % a.obs16) == 0) a.row_outer[ogr] = s_row;
+            }
         }
+        lds_barrier();   // reciprocal table filled; previous tile's column reads done
+
+        float vn[16];
+        if (OUTER == kOuterNone) {
 #pragma unroll
-        for (int k = 0; k < 16; ++k) cv[k] = s_col == 0.0f ? __builtin_copysignf(0.0f, cv[k]) : cv[k] / s_col;
+            for (int k = 0; k < 16; ++k) vn[k] = v[k];
+        } else {
+            normalize16(v, s_row, outer_inv(s_row), vn);
+        }
+        if (cur.act) {
+            BlockScale<BIAS> sc;
+            const uint2 packed = quant16<BIAS, SR>(vn, u, rtab, sc);
+            if (a.row_codes) *(uint2*)(a.row_codes + cur.e0 / 2) = packed;
+            if (a.row_scales) a.row_scales[cur.e0 / 16] = (uint8_t)sc.code;
+            if (EF || a.y) {
+                float w[16];
+                decode16(packed, sc.d, w);
+                if (OUTER != kOuterNone) {
+#pragma unroll
+                    for (int k = 0; k < 16; ++k) w[k] = w[k] * s_row;
+                }
+                if (a.y) {
+                    uint32_t o[8];
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) o[k] = f32_to_bf16(w[2 * k]) | (f32_to_bf16(w[2 * k + 1]) << 16);
+                    *(uint4*)(a.y + cur.e0) = make_uint4(o[0], o[1], o[2], o[3]);
+                    *(uint4*)(a.y + cur.e0 + 8) = make_uint4(o[4], o[5], o[6], o[7]);
+                }
+                if (EF) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        *(float4*)(a.residual + cur.e0 + 4 * q) =
+                            make_float4(v[4 * q] - w[4 * q], v[4 * q + 1] - w[4 * q + 1],
+                                        v[4 * q + 2] - w[4 * q + 2], v[4 * q + 3] - w[4 * q + 3]);
+                }
+            }
+        }
+        if (COLS) {
+            // ---------------- stage through LDS
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                lds_v[r][16 * sg + k] = (OUTER == kOuter1D) ? v[k] : vn[k];
+                if (SR) lds_u[r][16 * sg + k] = (uint16_t)u[k];
+            }
+            lds_barrier();
+
+            // ---------------- column phase
+            const int cc = tid >> 2, rs = tid & 3;
+            const bool actc = (cc < cur.cols_valid) && (16 * rs < cur.rows_valid);
+            float cv[16];
+            uint32_t cu[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                cv[k] = lds_v[16 * rs + k][cc];
+                cu[k] = SR ? (uint32_t)lds_u[16 * rs + k][cc] : 0u;
+            }
+            if (OUTER == kOuter1D) {
+                const int64_t colbase = (int64_t)a.row0[cur.g] * cols / (16 * a.obs16);
+                const int64_t ogc = colbase + (cur.c0 + cc) * (cur.Rg / (16 * a.obs16)) +
+                                    (cur.lrow0 + 16 * rs) / (16 * a.obs16);
+                float s_col;
+                if (GIVEN) {
+                    s_col = actc ? a.col_outer[ogc] : 1.0f;
+                } else {
+                    s_col = quad_max(max_abs16(cv), a.obs16) / den;
+                    if (actc && a.col_outer && (rs % a.obs16) == 0) a.col_outer[ogc] = s_col;
+                }
+                float cn[16];
+                normalize16(cv, s_col, outer_inv(s_col), cn);
+#pragma unroll
+                for (int k = 0; k < 16; ++k) cv[k] = cn[k];
+            }
+            if (actc) {
+                BlockScale<BIAS> sc;
+                const uint2 packed = quant16<BIAS, SR>(cv, cu, rtab, sc);
+                const int64_t colrow = cur.c0 + cc;                   // row of the columnwise buffer
+                const int64_t gbase = (int64_t)a.row0[cur.g] * cols;  // elements before this group
+                const int64_t ce0 = gbase + colrow * cur.Rg + cur.lrow0 + 16 * rs;
+                *(uint2*)(a.col_codes + ce0 / 2) = packed;
+                a.col_scales[ce0 / 16] = (uint8_t)sc.code;
+            }
+        }
+        if (!has_next) break;
+        tile = next;
+        in = nin;
     }
-    if (actc) {
-        uint2 packed;
-        float p[16];
-        const uint32_t cs = quant16<BIAS, SR>(cv, cu, packed, p);
-        const int64_t colrow = c0 + cc;                       // row of the columnwise buffer
-        const int64_t gbase = (int64_t)a.row0[g] * cols;      // elements before this group
-        const int64_t ce0 = gbase + colrow * Rg + lrow0 + 16 * rs;
-        *(uint2*)(a.col_codes + ce0 / 2) = packed;
-        a.col_scales[ce0 / 16] = (uint8_t)cs;
-    }
+}
+
+// Workgroups of `fn` resident per CU, and the CU count, of the current
+// device (queried once per device and kernel).
+struct Residency {
+    int wgs_per_cu;
+    int cus;
+};
+
+Residency residency(const void* fn)
+{
+    struct Entry {
+        int dev;
+        const void* fn;
+        Residency r;
+    };
+    static std::mutex mu;
+    static std::vector<Entry> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return {1, 8};
+    std::lock_guard<std::mutex> lock(mu);
+    for (const Entry& e : cache)
+        if (e.dev == dev && e.fn == fn) return e.r;
+    Residency r{1, 8};
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kThreads, 0) == hipSuccess && n > 0) r.wgs_per_cu = n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n >= 8) r.cus = n;
+    cache.push_back({dev, fn, r});
+    return r;
+}
+
+// Launch one persistent grid: as many workgroups per XCD as fit at once,
+// spread so that every workgroup of a slice takes the same number of tiles
+// (to within one).
+hipError_t launch_persistent(void (*fn)(TileArgs), TileArgs a, hipStream_t s)
+{
+    const Residency r = residency(reinterpret_cast<const void*>(fn));
+    const int cap = r.wgs_per_cu * (r.cus / 8);
+    int w = a.wgs_per_xcd < cap ? a.wgs_per_xcd : cap;
+    if (w < 1) w = 1;
+    const int rounds = (a.per_xcd + w - 1) / w;
+    if (rounds > 1) w = (a.per_xcd + rounds - 1) / rounds;
+    a.wgs_per_xcd = w;
+    hipLaunchKernelGGL(fn, dim3(8 * w), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_tiles(int bias, int outer_kind, bool sr, const TileArgs& a, hipStream_t s)
 {
-    const dim3 grid(8 * a.per_xcd);
     const bool cols = (a.col_codes != nullptr);
-#define FP4Q_T(B, O, S, C) hipLaunchKernelGGL((k_tile<B, O, S, C>), grid, dim3(kThreads), 0, s, a)
-#define FP4Q_T_C(B, O, S)                      \
-    do {                                       \
-        if (cols) FP4Q_T(B, O, S, true);       \
-        else FP4Q_T(B, O, S, false);           \
+    const bool ef = (a.residual != nullptr);
+    const bool given = a.outer_given != 0;
+#define FP4Q_T(B, O, S, C, E, G) return launch_persistent(k_tile<B, O, S, C, E, G>, a, s)
+#define FP4Q_T_G(B, O, S, C, E)                 \
+    do {                                        \
+        if (given) FP4Q_T(B, O, S, C, E, true); \
+        else FP4Q_T(B, O, S, C, E, false);      \
     } while (0)
-#define FP4Q_T_S(B, O)                         \
-    do {                                       \
-        if (sr) FP4Q_T_C(B, O, true);          \
-        else FP4Q_T_C(B, O, false);            \
+#define FP4Q_T_E(B, O, S, C, G)                 \
+    do {                                        \
+        if (ef) G(B, O, S, C, true);            \
+        else G(B, O, S, C, false);              \
     } while (0)
-#define FP4Q_T_O(B)                                            \
-    do {                                                       \
-        if (outer_kind == kOuterNone) FP4Q_T_S(B, kOuterNone); \
-        else if (outer_kind == kOuterTensor) FP4Q_T_S(B, kOuterTensor); \
-        else if (outer_kind == kOuter1D) FP4Q_T_S(B, kOuter1D); \
-        else FP4Q_T_S(B, kOuter2D);                            \
+#define FP4Q_T_NG(B, O, S, C, E) FP4Q_T(B, O, S, C, E, false)
+#define FP4Q_T_S(B, O, C, G)                    \
+    do {                                        \
+        if (sr) FP4Q_T_E(B, O, true, C, G);     \
+        else FP4Q_T_E(B, O, false, C, G);       \
+    } while (0)
+#define FP4Q_T_O(B)                                                               \
+    do {                                                                          \
+        if (!cols) FP4Q_T_S(B, kOuter2D, false, FP4Q_T_G);                        \
+        else if (outer_kind == kOuterNone) FP4Q_T_S(B, kOuterNone, true, FP4Q_T_NG); \
+        else if (outer_kind == kOuterTensor) FP4Q_T_S(B, kOuterTensor, true, FP4Q_T_NG); \
+        else if (outer_kind == kOuter1D) FP4Q_T_S(B, kOuter1D, true, FP4Q_T_G);  \
+        else FP4Q_T_S(B, kOuter2D, true, FP4Q_T_G);                               \
     } while (0)
     if (bias == 7) FP4Q_T_O(7);
-    else FP4Q_T_O(15);
+    FP4Q_T_O(15);
 #undef FP4Q_T_O
 #undef FP4Q_T_S
-#undef FP4Q_T_C
+#undef FP4Q_T_NG
+#undef FP4Q_T_E
+#undef FP4Q_T_G
 #undef FP4Q_T
-    return hipGetLastError();
 }
 
 }  // namespace fp4q

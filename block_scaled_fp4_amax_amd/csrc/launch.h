@@ -9,6 +9,15 @@
 namespace fp4q {
 
 constexpr int kMaxGroupsPerLaunch = 64;
+// Persistent tile workgroups resident per XCD (32 CUs x 8 workgroups of 4 waves).
+constexpr int kTileWgsPerXcd = 256;
+
+inline void set_tile_grid(int32_t total_tiles, int32_t& per_xcd, int32_t& wgs_per_xcd)
+{
+    per_xcd = (total_tiles + 7) / 8;
+    wgs_per_xcd = per_xcd < kTileWgsPerXcd ? per_xcd : kTileWgsPerXcd;
+    if (wgs_per_xcd < 1) wgs_per_xcd = 1;
+}
 
 // Rowwise NVFP4 / AMDFP4 parameters (modes none, tensorwise, 1D outer).
 struct RowArgs {
@@ -45,7 +54,8 @@ struct TileArgs {
     int32_t ngroups;
     int32_t tiles_c;         // ceil(cols / 64)
     int32_t total_tiles;
-    int32_t per_xcd;         // tiles handled per XCD slice (grid = 8 * per_xcd)
+    int32_t per_xcd;         // tiles in each XCD's contiguous slice
+    int32_t wgs_per_xcd;     // persistent workgroups per XCD (grid = 8 * wgs_per_xcd)
     int32_t row0[kMaxGroupsPerLaunch + 1];   // prefix rows of the groups
     int32_t tile0[kMaxGroupsPerLaunch + 1];  // prefix tile counts of the groups
 };

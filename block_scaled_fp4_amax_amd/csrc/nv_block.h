@@ -1,0 +1,160 @@
+// nv_block.h -- per-16-element NVFP4 / AMD-FP4 inner quantisation shared by the
+// rowwise and tile kernels (device only).
+//
+// "fp4-train" README, Method: a block's scale is block_absmax / 6 encoded on
+// the inner grid (E4M3, or UE5M3 for AMD-FP4 -- "NVFP4 / AMD-FP4 outer-block
+// (two-level) scaling", Background); every element is divided by the decoded
+// scale and rounded onto the E2M1 grid, to nearest-even or stochastically.
+#pragma once
+
+#include "fp4q_device.h"
+
+namespace fp4q {
+
+// RN64(1 / d) for every decoded inner scale d, from a 16-entry table of the
+// reciprocals of the 3-bit significands: d = (1 + m/8) * 2^(e - BIAS) for
+// e >= 1 and d = (m / 8) * 2^(1 - BIAS) for e == 0; entry 8 (d == 0) is 0, so
+// a zero scale yields quotients of (signed) zero.  Exact power-of-two scaling
+// of a binary64 value commutes with its rounding, so the result is RN64(1/d).
+struct RecipTable {
+    double r[16];
+};
+
+__device__ __forceinline__ void fill_recip_table(double* t, int lane)
+{
+    if (lane < 8) t[lane] = 1.0 / (1.0 + lane * 0.125);
+    else if (lane < 16) t[lane] = lane == 8 ? 0.0 : 8.0 / (double)(lane - 8);
+}
+
+template <int BIAS>
+__device__ __forceinline__ double inner_recip(uint32_t code, const double* tab)
+{
+    const uint32_t e = code >> 3, m = code & 7u;
+    const uint32_t idx = m | (e == 0u ? 8u : 0u);
+    const int sh = BIAS - (int)(e == 0u ? 1u : e);
+    return ldexp(tab[idx], sh);
+}
+
+// Scale of one block from its max |v_n|: code, decoded value, RN64(1/d).
+template <int BIAS>
+struct BlockScale {
+    uint32_t code;
+    float d;
+    double rd;
+};
+
+template <int BIAS>
+__device__ __forceinline__ BlockScale<BIAS> block_scale(float bmax, const double* tab)
+{
+    BlockScale<BIAS> s;
+    // RN32(bmax / 6): any quotient below the normal range encodes to code 0
+    // either way (the smallest nonzero inner scale is far above it).
+    const float ys = div_inv64(bmax, 1.0 / 6.0);
+    s.code = scale_encode<BIAS>(ys);
+    s.d = scale_decode<BIAS>(s.code);
+    s.rd = inner_recip<BIAS>(s.code, tab);
+    return s;
+}
+
+__device__ __forceinline__ float max_abs16(const float (&v)[16])
+{
+    float m = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) m = fmaxf(m, __builtin_fabsf(v[k]));
+    return m;
+}
+
+// RNE codes of 16 normalised values (t = RN32(v_n / d), hardware E2M1 pack).
+// A quotient too small for div_inv64's guarantee still lands below 0.25 and
+// keeps its sign, so its code (+-0) is exact.
+__device__ __forceinline__ uint2 codes16_rne(const float (&vn)[16], double rd)
+{
+    float t[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) t[k] = div_inv64(vn[k], rd);
+    uint32_t lo = 0, hi = 0;
+    lo = fp4x2_rne<0>(lo, t[0], t[1]);
+    lo = fp4x2_rne<1>(lo, t[2], t[3]);
+    lo = fp4x2_rne<2>(lo, t[4], t[5]);
+    lo = fp4x2_rne<3>(lo, t[6], t[7]);
+    hi = fp4x2_rne<0>(hi, t[8], t[9]);
+    hi = fp4x2_rne<1>(hi, t[10], t[11]);
+    hi = fp4x2_rne<2>(hi, t[12], t[13]);
+    hi = fp4x2_rne<3>(hi, t[14], t[15]);
+    return make_uint2(lo, hi);
+}
+
+// Stochastic-rounding codes of 16 normalised values.  Here the exact value of
+// a tiny quotient matters (zero never rounds up, any positive t can), so
+// quotients that may leave the normal range are recomputed by IEEE division.
+template <int BIAS>
+__device__ __forceinline__ uint2 codes16_sr(const float (&vn)[16], const uint32_t (&u)[16], const BlockScale<BIAS>& s)
+{
+    float t[16];
+    bool slow = false;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        t[k] = div_inv64(__builtin_fabsf(vn[k]), s.rd);
+        slow |= is_subnormal(t[k]);
+    }
+    if (__builtin_expect(slow, 0)) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+            if (is_subnormal(t[k])) t[k] = __builtin_fabsf(vn[k]) / s.d;
+    }
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const uint32_t code = e2m1_sr(t[k], (float)u[k]) | ((__float_as_uint(vn[k]) >> 31) << 3);
+        if (k < 8) lo |= code << (4 * k);
+        else hi |= code << (4 * (k - 8));
+    }
+    return make_uint2(lo, hi);
+}
+
+// Signed inner-dequantised values p = +-G[m] * d from 16 packed codes (the
+// hardware E2M1 decode at scale 1, then an exact product with d).
+template <int Q>
+__device__ __forceinline__ void decode_byte(uint32_t w, float d, float& a, float& b)
+{
+    auto f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, Q);
+    a = f[0] * d;
+    b = f[1] * d;
+}
+
+__device__ __forceinline__ void decode16(uint2 packed, float d, float (&p)[16])
+{
+    decode_byte<0>(packed.x, d, p[0], p[1]);
+    decode_byte<1>(packed.x, d, p[2], p[3]);
+    decode_byte<2>(packed.x, d, p[4], p[5]);
+    decode_byte<3>(packed.x, d, p[6], p[7]);
+    decode_byte<0>(packed.y, d, p[8], p[9]);
+    decode_byte<1>(packed.y, d, p[10], p[11]);
+    decode_byte<2>(packed.y, d, p[12], p[13]);
+    decode_byte<3>(packed.y, d, p[14], p[15]);
+}
+
+// Normalise by an outer scale: v_n = RN32(v / s_o), v_n = +-0 when s_o == 0.
+// inv = RN64(1 / s_o) (0 when s_o == 0); subnormal results are recomputed by
+// IEEE division.
+__device__ __forceinline__ void normalize16(const float (&v)[16], float s_o, double inv, float (&vn)[16])
+{
+    bool slow = false;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        vn[k] = div_inv64(v[k], inv);
+        slow |= is_subnormal(vn[k]);
+    }
+    if (__builtin_expect(slow, 0)) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+            if (is_subnormal(vn[k])) vn[k] = v[k] / s_o;
+    }
+}
+
+__device__ __forceinline__ double outer_inv(float s_o)
+{
+    return s_o == 0.0f ? 0.0 : 1.0 / (double)s_o;
+}
+
+}  // namespace fp4q
