@@ -48,10 +48,72 @@ def parse():
                     help="only run a plain 256 MiB device copy (counter calibration) and exit")
     ap.add_argument("--only", default=None, help="time a single workload (C1..C5) and exit")
     ap.add_argument("--eager", action="store_true", help="launch every step from the host (no graph replay)")
+    ap.add_argument("--pmc-summary", nargs=5, metavar=("KEY", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    default=None,
+                    help="write profiles/traffic_counters.json[KEY] from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE "
+                         "output directories of `--only KEY --eager` and of `--copy-probe`, then exit (no GPU)")
     return ap.parse_args()
 
 
 # ---------------------------------------------------------------------- helpers
+KERNEL_NAME_PREFIX = {"C1": "fp4q::(anonymous namespace)::k_nv_rows", "C2": "fp4q::(anonymous namespace)::k_tile",
+                      "C3": "fp4q::(anonymous namespace)::k_mx_qdq", "C4": "fp4q::(anonymous namespace)::k_tile",
+                      "C5": "fp4q::(anonymous namespace)::k_tile"}
+COPY_PROBE_BYTES = 256 << 20
+
+
+def _pmc_rows(directory, counter):
+    """(kernel name, value) of every dispatch in a rocprofv3 --pmc csv directory."""
+    import csv
+    out = []
+    for f in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    out.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return out
+
+
+def pmc_summary(key, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
+    """HBM bytes per launch of the workload's kernel, each counter scaled by
+    what it reads for a plain copy of known size (the copy probe moves
+    COPY_PROBE_BYTES each way per launch)."""
+    def per_dispatch(directory, counter, match):
+        vals = [v for n, v in _pmc_rows(directory, counter) if match(n)]
+        if not vals:
+            raise SystemExit("no %s rows for the kernel in %s" % (counter, directory))
+        return sum(vals) / len(vals), len(vals)
+    def copy_kernel(directory, counter):
+        # the copy itself is the kernel with 20 dispatches (the fill before it runs once)
+        names = {}
+        for n, _ in _pmc_rows(directory, counter):
+            names[n] = names.get(n, 0) + 1
+        best = max(names, key=lambda n: names[n])
+        return per_dispatch(directory, counter, lambda n: n == best)[0]
+    cf = copy_kernel(copy_fetch_dir, "FETCH_SIZE")
+    cw = copy_kernel(copy_write_dir, "WRITE_SIZE")
+    fetch_scale = COPY_PROBE_BYTES / (cf * 1024.0)
+    write_scale = COPY_PROBE_BYTES / (cw * 1024.0)
+    pre = KERNEL_NAME_PREFIX[key]
+    ours = lambda n: pre in n
+    kf, nf = per_dispatch(fetch_dir, "FETCH_SIZE", ours)
+    kw, nw = per_dispatch(write_dir, "WRITE_SIZE", ours)
+    read_b = kf * 1024.0 * fetch_scale
+    write_b = kw * 1024.0 * write_scale
+    path = os.path.join(ROOT, "profiles", "traffic_counters.json")
+    data = {}
+    if os.path.exists(path):
+        with open(path) as fh:
+            data = json.load(fh)
+    data[key] = {"bytes_per_launch": int(round(read_b + write_b)), "read_bytes": int(round(read_b)),
+                 "write_bytes": int(round(write_b)), "fetch_kib_per_dispatch": kf, "write_kib_per_dispatch": kw,
+                 "dispatches": [nf, nw], "fetch_scale": fetch_scale, "write_scale": write_scale,
+                 "sources_sha": kernel_sources_hash()}
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as fh:
+        json.dump(data, fh, indent=1, sort_keys=True)
+    print(json.dumps({key: data[key]}))
+
 def kernel_sources_hash():
     files = sorted(glob.glob(os.path.join(ROOT, "block_scaled_fp4_amax_amd", "csrc", "*")))
     h = hashlib.sha256()
@@ -266,6 +328,9 @@ def cpu_baseline(W, min_seconds):
 # ---------------------------------------------------------------------- main
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the quantisation path has no cross-GPU step in this build "
@@ -281,7 +346,7 @@ def main():
     torch.cuda.set_device(0)
 
     if args.copy_probe:
-        n = 256 << 20
+        n = COPY_PROBE_BYTES
         a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
         b = torch.empty_like(a)
         for _ in range(20):

@@ -95,8 +95,10 @@ int check_shape(const Resolved& r, int64_t rows, int64_t cols, int64_t ld, bool 
         if (cols % r.obs) return FP4Q_ERR_SHAPE;
         if ((r.outer_kind == kOuter2D || columnwise) && rows % r.obs) return FP4Q_ERR_SHAPE;
     }
-    // 32-bit block indexing inside the kernels
+    // 32-bit block indexing inside the kernels, and 32-bit byte offsets within
+    // a 64-row tile (x rows of ld_x bf16, residual rows of cols FP32)
     if (rows * (cols / 8) >= (int64_t)1 << 31) return FP4Q_ERR_UNSUPPORTED;
+    if (ld > ((int64_t)1 << 24) || cols > ((int64_t)1 << 23)) return FP4Q_ERR_UNSUPPORTED;
     return FP4Q_OK;
 }
 

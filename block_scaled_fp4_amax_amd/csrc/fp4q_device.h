@@ -215,6 +215,66 @@ __device__ __forceinline__ void sr_draws16(uint64_t seed, uint64_t step, uint64_
     }
 }
 
+// ---------------------------------------------------------------- buffer resources
+// Raw buffer descriptors: a lane whose byte offset is at or beyond the
+// descriptor's record count reads zeros and its stores are dropped by the
+// hardware, so masked lanes need no branch.  Kernels keep every global access
+// inside a loop on buffer instructions with such offsets: with no branches
+// around memory instructions the compiler's wait counts stay exact, and a
+// wait for the next tile's loads does not also wait for the stores issued
+// after them.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+constexpr uint32_t kRecords = 0x7FFFFFFFu;   // every in-range offset is below 2^31
+constexpr uint32_t kOff = 0x80000000u;       // offset of a masked lane
+
+// Descriptor over [p, p + 2^31): NULL gives an empty one (every access dropped).
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, p ? kRecords : 0u, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t off)
+{
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ float buf_load_f32(rsrc_t r, uint32_t off)
+{
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+__device__ __forceinline__ void buf_store16(rsrc_t r, uint32_t off, uint4 v)
+{
+    const u32x4_t w = {v.x, v.y, v.z, v.w};
+    __builtin_amdgcn_raw_buffer_store_b128(w, r, off, 0, 0);
+}
+
+__device__ __forceinline__ void buf_store8(rsrc_t r, uint32_t off, uint2 v)
+{
+    const u32x2_t w = {v.x, v.y};
+    __builtin_amdgcn_raw_buffer_store_b64(w, r, off, 0, 0);
+}
+
+__device__ __forceinline__ void buf_store_u32(rsrc_t r, uint32_t off, uint32_t v)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);
+}
+
+__device__ __forceinline__ void buf_store_u8(rsrc_t r, uint32_t off, uint32_t v)
+{
+    __builtin_amdgcn_raw_buffer_store_b8((unsigned char)v, r, off, 0, 0);
+}
+
+// Wait until every outstanding vector memory operation of this wave has
+// completed (s_waitcnt vmcnt(0); expcnt and lgkmcnt left alone).
+__device__ __forceinline__ void wait_vmem_all()
+{
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
 // ---------------------------------------------------------------- LDS-only barrier
 // Workgroup barrier whose fences cover LDS only: it orders the workgroup's LDS
 // writes before the barrier against LDS reads after it, but does not wait for

@@ -126,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void k_nv_rows(RowArgs a, uint32_t nblock
 #pragma unroll
         for (int k = 0; k < 16; ++k) vn[k] = v[k];
     } else {
-        normalize16(v, s_o, outer_inv(s_o), vn);
+        normalize16(v, s_o, outer_inv(s_o), vn, true);
     }
     const BlockScale<BIAS> sc = block_scale<BIAS>(max_abs16(vn), rtab);
     const uint2 packed = SR ? codes16_sr<BIAS>(vn, u, sc) : codes16_rne(vn, sc.rd);

@@ -13,23 +13,31 @@
 // (1 x obs along rows, obs x 1 along columns); grouped MoE quantisation keeps
 // one outer grid per expert.
 //
-// Per workgroup (256 lanes, 4 waves) one 64 x 64 source tile:
+// Per workgroup (256 lanes, 4 waves) one 64 x 64 source tile at a time:
 //   row phase  lane (r = t/4, s = t%4) owns the 16-element row block
 //              [r, 16s .. 16s+15]: two 16-byte loads, (residual add),
-//              outer scale (2D: block-wide max; 1D: max over the obs/16 lanes
-//              of the row group), normalise, quantise, store 8 bytes of codes
-//              and one scale byte; (qdq output, residual update).
+//              outer scale (2D: tile-wide max through a DPP wave max and LDS;
+//              1D: max over the obs/16 lanes of the row group), normalise,
+//              quantise, store 8 bytes of codes and one scale byte; (qdq
+//              output, residual update).
 //   LDS        the tile's values (normalised for 2D / tensorwise / none, raw
 //              for 1D) and SR draws, so each element keeps one draw in both
-//              directions.
+//              directions.  16-byte chunks are XOR-swizzled by row so that the
+//              row phase's 128-bit writes and the column phase's 32-bit reads
+//              are both free of bank conflicts.
 //   col phase  lane (c = t/4, q = t%4) owns the column block [16q .. 16q+15, c]:
 //              (1D: column outer scale over obs/16 lanes), quantise, store
 //              8 bytes of columnwise codes; the 4 lanes of a column write its
 //              32 contiguous bytes.
+// Two workgroup barriers per tile: one before the tile's LDS writes (the
+// previous tile's column reads are done; for 2D it also publishes the wave
+// maxima) and one after them.
+//
 // Tiles are taken in row-major order, split into 8 contiguous slices, one per
 // XCD (workgroup ids are dealt round-robin to the XCDs), so the partial cache
-// lines that neighbouring tiles write meet in the same L2.
-#include <cstdlib>
+// lines that neighbouring tiles write meet in the same L2.  Workgroups are
+// persistent within their slice and load tile j+1's inputs before computing
+// tile j.
 #include <mutex>
 #include <vector>
 
@@ -43,6 +51,15 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kTile = 64;
 
+// Physical 16-byte chunk (4 floats) of logical chunk ch = col / 4 in tile row
+// `row`.  A bijection on ch for every row.  It spreads a ds_write_b128 group
+// of 8 lanes {rows r, r+1} x {segments 0..3} over 8 distinct 4-bank groups,
+// and the 32 lanes of each half-wave of the column phase (8 columns x 4 row
+// quarters, one row each) over 32 distinct banks.
+__device__ __forceinline__ int swz_chunk(int row, int ch)
+{
+    return ch ^ (((row >> 4) & 3) << 1) ^ (row & 1) ^ (((ch >> 3) & 1) << 1);
+}
 
 template <int BIAS, bool SR>
 __device__ __forceinline__ uint2 quant16(const float (&vn)[16], const uint32_t (&u)[16], const double* tab,
@@ -53,105 +70,173 @@ __device__ __forceinline__ uint2 quant16(const float (&vn)[16], const uint32_t (
     return codes16_rne(vn, sc.rd);
 }
 
-// Where one tile sits: group, tile row / column, valid extent, and this
-// lane's row block.
-struct TileCoord {
-    int g, ti, tj, rows_valid, cols_valid;
-    int64_t Rg, lrow0, i_g, c0, e0;
-    bool act;
+// Walks a workgroup's tiles t = first, first + W, ... in the row-major order
+// of (group, tile row, tile column) without dividing per step: the column
+// advances by W % tiles_c and the row by W / tiles_c.  The current group's
+// row range is kept in registers; crossing into another group (rare)
+// re-derives the position from the prefix tables.
+struct TileWalk {
+    int t, g, ti, tj, di, dj;
+    int r0, Rg, tile_end;   // group's first row, row count, end of its tiles
 };
 
-__device__ __forceinline__ TileCoord tile_coord(const TileArgs& a, int tile, int r, int sg)
+__device__ __forceinline__ void walk_locate(const TileArgs& a, TileWalk& w)
 {
-    TileCoord c;
-    int g = 0;
-    while (g + 1 < a.ngroups && a.tile0[g + 1] <= tile) ++g;
-    const int lt = tile - a.tile0[g];
-    c.g = g;
-    c.ti = lt / a.tiles_c;
-    c.tj = lt - c.ti * a.tiles_c;
-    c.Rg = (int64_t)(a.row0[g + 1] - a.row0[g]);
-    c.lrow0 = (int64_t)c.ti * kTile;
-    c.c0 = (int64_t)c.tj * kTile;
-    c.rows_valid = (int)min((int64_t)kTile, c.Rg - c.lrow0);
-    c.cols_valid = (int)min((int64_t)kTile, a.cols - c.c0);
-    c.act = (r < c.rows_valid) && (16 * sg < c.cols_valid);
-    c.i_g = (int64_t)a.row0[g] + c.lrow0 + r;
-    c.e0 = c.i_g * a.cols + c.c0 + 16 * sg;
-    return c;
+    while (w.g + 1 < a.ngroups && a.tile0[w.g + 1] <= w.t) ++w.g;
+    const int lt = w.t - a.tile0[w.g];
+    w.ti = lt / a.tiles_c;
+    w.tj = lt - w.ti * a.tiles_c;
+    w.r0 = a.row0[w.g];
+    w.Rg = a.row0[w.g + 1] - w.r0;
+    w.tile_end = a.tile0[w.g + 1];
 }
 
-// The lane's raw inputs for one tile: 16 bf16 (two 16-byte loads) and, with
-// error feedback, the 16 FP32 residuals.
-template <bool EF>
-struct TileInput {
-    uint4 w0, w1;
-    float4 z[EF ? 4 : 1];
-};
-
-template <bool EF>
-__device__ __forceinline__ void load_tile_input(const TileArgs& a, const TileCoord& c, TileInput<EF>& in)
+__device__ __forceinline__ void walk_next(const TileArgs& a, TileWalk& w, int step)
 {
-    if (c.act) {
-        const uint16_t* px = a.x + c.i_g * a.ld + c.c0 + 16 * (threadIdx.x & 3);
-        in.w0 = *(const uint4*)px;
-        in.w1 = *(const uint4*)(px + 8);
-        if (EF) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) in.z[q] = *(const float4*)(a.residual + c.e0 + 4 * q);
-        }
-    } else {
-        in.w0 = make_uint4(0, 0, 0, 0);
-        in.w1 = make_uint4(0, 0, 0, 0);
-        if (EF) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) in.z[q] = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
+    w.t += step;
+    if (w.t >= w.tile_end) {
+        walk_locate(a, w);
+        return;
+    }
+    w.ti += w.di;
+    w.tj += w.dj;
+    if (w.tj >= a.tiles_c) {
+        w.tj -= a.tiles_c;
+        ++w.ti;
     }
 }
 
-// Persistent workgroups: workgroup (xcd = id % 8, slot = id / 8) walks the
-// tiles xcd * per_xcd + slot + j * wgs_per_xcd of its XCD's contiguous slice,
-// loading tile j+1's inputs before it computes tile j.
-// Register budget per lane: 64 VGPRs (8 waves per SIMD) for the plain RTNE
-// kernels, 72 (7 waves) for 1D outer groups, 128 (4 waves) with stochastic
-// rounding or a residual.
+// One tile's place, uniform across the workgroup: group g (first row r0, Rg
+// rows), tile row ti within the group, tile column tj, the valid extent
+// (edge tiles are partial), and the element indices of its (0, 0) element in
+// the row-major source and in the columnwise buffers.
+struct Tile {
+    int g, r0, ti, tj, rows_valid, cols_valid, Rg, grow0, c0, lrow0;
+    int64_t e_base;    // (grow0) * cols + c0
+    int64_t ce_base;   // r0 * cols + c0 * Rg + lrow0
+};
+
+__device__ __forceinline__ Tile make_tile(const TileArgs& a, const TileWalk& w)
+{
+    Tile t;
+    t.g = w.g;
+    t.r0 = w.r0;
+    t.ti = w.ti;
+    t.tj = w.tj;
+    t.Rg = w.Rg;
+    t.lrow0 = w.ti * kTile;
+    t.grow0 = w.r0 + t.lrow0;
+    t.c0 = w.tj * kTile;
+    t.rows_valid = min(kTile, t.Rg - t.lrow0);
+    t.cols_valid = min(kTile, (int)a.cols - t.c0);
+    t.e_base = (int64_t)t.grow0 * a.cols + t.c0;
+    t.ce_base = (int64_t)w.r0 * a.cols + (int64_t)t.c0 * t.Rg + t.lrow0;
+    return t;
+}
+
+// The lane's raw inputs for one tile: 16 bf16 (two 16-byte loads) and, with
+// error feedback, the 16 FP32 residuals.  Lanes outside the tensor (and every
+// lane when `valid` is false) read zeros.
+template <bool EF>
+struct TileInput {
+    uint4 w0, w1;
+    uint4 z[EF ? 4 : 1];
+};
+
+template <bool EF>
+__device__ __forceinline__ void load_tile_input(const TileArgs& a, const Tile& t, bool valid, int r, int sg,
+                                                TileInput<EF>& in)
+{
+    const bool act = valid && r < t.rows_valid && 16 * sg < t.cols_valid;
+    const rsrc_t rx = make_rsrc(a.x + (int64_t)t.grow0 * a.ld + t.c0);
+    const uint32_t ox = act ? (uint32_t)(r * (int)a.ld + 16 * sg) * 2u : kOff;
+    in.w0 = buf_load16(rx, ox);
+    in.w1 = buf_load16(rx, ox + 16u);
+    if (EF) {
+        const rsrc_t rz = make_rsrc(a.residual + t.e_base);
+        const uint32_t oz = act ? (uint32_t)(r * (int)a.cols + 16 * sg) * 4u : kOff;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) in.z[q] = buf_load16(rz, oz + 16u * q);
+    }
+}
+
+// Register budget per lane: 72 VGPRs (7 waves per SIMD) for the RTNE kernels,
+// 128 (4 waves) with stochastic rounding or a residual, 168 (3 waves) with
+// both.  Tighter budgets make the compiler spill to scratch inside the tile
+// loop.
 template <int BIAS, int OUTER, bool SR, bool COLS, bool EF>
 constexpr int tile_waves_per_simd()
 {
-    return (SR || EF) ? 4 : (OUTER == kOuter1D ? 7 : 8);
+    return (SR && EF) ? 3 : ((SR || EF) ? 4 : 7);
 }
 
-template <int BIAS, int OUTER, bool SR, bool COLS, bool EF, bool GIVEN>
+// Smallest binary32 outer scale for which v / s_o can be subnormal for some
+// nonzero bf16 v: |v| >= 2^-133, so below 2^-7 every nonzero quotient is a
+// normal binary32 and the reciprocal-product division needs no re-check.
+constexpr float kNoSubnormalScale = 0x1p-7f;
+
+// Every global access in the tile loop is a buffer instruction whose masked
+// lanes carry an out-of-range offset, and there is no branch around any of
+// them, so the wait for the next tile's loads never waits for this tile's
+// stores.
+template <int BIAS, int OUTER, bool SR, bool COLS, bool EF, bool GIVEN, bool Y>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(tile_waves_per_simd<BIAS, OUTER, SR, COLS, EF>())))
 void k_tile(TileArgs a)
 {
-    __shared__ float lds_v[kTile][kTile + 1];
-    __shared__ uint16_t lds_u[SR ? kTile : 1][SR ? kTile + 2 : 1];
-    __shared__ float red[kThreads / 64];
-    __shared__ double rtab[16];
+    __shared__ float4 lds_v[COLS ? kTile * kTile / 4 : 1];
+    __shared__ uint16_t lds_u[(COLS && SR) ? kTile : 1][(COLS && SR) ? kTile + 2 : 1];
+    __shared__ uint32_t red[2][kThreads / 64];
+    __shared__ double rtab[kRecipTableSize];
 
     const int tid = (int)threadIdx.x;
-    const int r = tid >> 2, sg = tid & 3;
+    const int r = tid >> 2, sg = tid & 3;       // row phase: row, 16-column segment
+    const int cc = tid >> 2, rs = tid & 3;      // column phase: column, 16-row segment
     const int xcd = (int)(blockIdx.x & 7u), slot = (int)(blockIdx.x >> 3);
     const int slice0 = xcd * a.per_xcd;
     const int slice_end = min(slice0 + a.per_xcd, a.total_tiles);
-    int tile = slice0 + slot;
-    if (tile >= slice_end) return;   // uniform per workgroup
-    fill_recip_table(rtab, tid);
-    const float den = ScaleFmt<BIAS>::outer_den();
-    const int64_t cols = a.cols;
-
+    const int W = a.wgs_per_xcd;
+    TileWalk walk;
+    walk.t = slice0 + slot;
+    if (walk.t >= slice_end) return;   // uniform per workgroup
+    walk.g = 0;
+    walk.di = W / a.tiles_c;
+    walk.dj = W - walk.di * a.tiles_c;
+    walk_locate(a, walk);
+    Tile cur = make_tile(a, walk);
     TileInput<EF> in;
-    load_tile_input<EF>(a, tile_coord(a, tile, r, sg), in);
+    load_tile_input<EF>(a, cur, true, r, sg, in);
+    fill_recip_table(rtab, tid);
+    lds_barrier();
+    const float den = ScaleFmt<BIAS>::outer_den();
+    const int cols = (int)a.cols;
+    const int obs = 16 * a.obs16;
+    // lane offsets that do not depend on the tile
+    const uint32_t erow = (uint32_t)(r * cols + 16 * sg);   // row phase: first element, tile-relative
+    const int lds_row = r * 16;
+    const int lds_col = 4 * swz_chunk(16 * rs, cc >> 2) + (cc & 3);   // + row * kTile, swizzle parity below
 
-    for (;;) {
-        const TileCoord cur = tile_coord(a, tile, r, sg);
-        // ---- prefetch the next tile's inputs
-        const int next = tile + a.wgs_per_xcd;
-        const bool has_next = next < slice_end;
-        TileInput<EF> nin = in;
-        if (has_next) load_tile_input<EF>(a, tile_coord(a, next, r, sg), nin);
+    // tensorwise: one scale for the whole launch
+    float s_tensor = 1.0f;
+    double inv_tensor = 1.0;
+    if (OUTER == kOuterTensor) {
+        s_tensor = *a.tensor_scale;
+        inv_tensor = outer_inv(s_tensor);
+    }
+
+    // Let the first tile's loads land here, so that at the loop head the
+    // current tile's registers are complete on every path; otherwise the wait
+    // placed for the first iteration would, on later ones, also wait for the
+    // previous tile's stores.
+    wait_vmem_all();
+
+    for (int iter = 0;; ++iter) {
+        const bool act = r < cur.rows_valid && 16 * sg < cur.cols_valid;
+        // ---- prefetch the next tile's inputs (zeros when there is none)
+        const bool has_next = walk.t + W < slice_end;
+        if (has_next) walk_next(a, walk, W);
+        const Tile nxt = make_tile(a, walk);
+        TileInput<EF> nin;
+        load_tile_input<EF>(a, nxt, has_next, r, sg, nin);
 
         // ---------------- row phase
         float v[16];
@@ -163,10 +248,10 @@ void k_tile(TileArgs a)
             if (EF) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    v[4 * q] = v[4 * q] + in.z[q].x;
-                    v[4 * q + 1] = v[4 * q + 1] + in.z[q].y;
-                    v[4 * q + 2] = v[4 * q + 2] + in.z[q].z;
-                    v[4 * q + 3] = v[4 * q + 3] + in.z[q].w;
+                    v[4 * q] = v[4 * q] + __uint_as_float(in.z[q].x);
+                    v[4 * q + 1] = v[4 * q + 1] + __uint_as_float(in.z[q].y);
+                    v[4 * q + 2] = v[4 * q + 2] + __uint_as_float(in.z[q].z);
+                    v[4 * q + 3] = v[4 * q + 3] + __uint_as_float(in.z[q].w);
                 }
 #pragma unroll
                 for (int k = 0; k < 16; ++k) {
@@ -190,116 +275,147 @@ void k_tile(TileArgs a)
         uint32_t u[16];
 #pragma unroll
         for (int k = 0; k < 16; ++k) u[k] = 0;
-        if (SR && cur.act) sr_draws16(a.seed, a.step, a.index_base + (uint64_t)cur.e0, u);
+        if (SR && act) sr_draws16(a.seed, a.step, a.index_base + (uint64_t)cur.e_base + erow, u);
 
+        bool barrier_done = false;   // the pre-LDS-write barrier has been passed
         float s_row = 1.0f;
+        double inv_row = 1.0;
         if (OUTER == kOuterTensor) {
-            s_row = *a.tensor_scale;
+            s_row = s_tensor;
+            inv_row = inv_tensor;
         } else if (OUTER == kOuter2D) {
-            const int64_t oidx =
-                ((int64_t)a.row0[cur.g] / kTile) * (cols / kTile) + (int64_t)cur.ti * (cols / kTile) + cur.tj;
+            const int64_t oidx = (int64_t)(cur.grow0 / kTile) * (cols / kTile) + cur.tj;
+            const rsrc_t ro = make_rsrc(a.row_outer ? a.row_outer + oidx : nullptr);
             if (GIVEN) {
-                s_row = a.row_outer[oidx];
+                s_row = buf_load_f32(ro, 0u);
             } else {
                 const uint32_t m = wave_max_u32(am_bits);
-                if ((tid & 63) == 0) red[tid >> 6] = __uint_as_float(m);
+                uint32_t* rb = red[iter & 1];
+                if ((tid & 63) == 0) rb[tid >> 6] = m;
                 lds_barrier();
-                s_row = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])) / den;
-                if (tid == 0 && a.row_outer) a.row_outer[oidx] = s_row;
+                barrier_done = true;
+                const uint32_t mm = max(max(rb[0], rb[1]), max(rb[2], rb[3]));
+                s_row = outer_scale(__uint_as_float(mm), den);
+                buf_store_u32(ro, tid == 0 ? 0u : kOff, __float_as_uint(s_row));
             }
+            inv_row = outer_inv(s_row);
         } else if (OUTER == kOuter1D) {
-            const int64_t ogr = cur.i_g * (cols / (16 * a.obs16)) + (cur.c0 + 16 * sg) / (16 * a.obs16);
+            // rowwise 1D groups: [rows, cols / obs]
+            const int gpr = cols / obs;
+            const rsrc_t ro =
+                make_rsrc(a.row_outer ? a.row_outer + (int64_t)cur.grow0 * gpr + cur.c0 / obs : nullptr);
+            const uint32_t oo = (uint32_t)(r * gpr + (16 * sg) / obs) * 4u;
             if (GIVEN) {
-                s_row = cur.act ? a.row_outer[ogr] : 1.0f;
+                s_row = buf_load_f32(ro, act ? oo : kOff);
+                if (!act) s_row = 1.0f;
             } else {
-                s_row = __uint_as_float(quad_max_u32(am_bits, a.obs16)) / den;
-                if (cur.act && a.row_outer && (sg % a.obs16) == 0) a.row_outer[ogr] = s_row;
+                s_row = outer_scale(__uint_as_float(quad_max_u32(am_bits, a.obs16)), den);
+                buf_store_u32(ro, (act && (sg % a.obs16) == 0) ? oo : kOff, __float_as_uint(s_row));
             }
+            inv_row = outer_inv(s_row);
         }
-        lds_barrier();   // reciprocal table filled; previous tile's column reads done
 
         float vn[16];
         if (OUTER == kOuterNone) {
 #pragma unroll
             for (int k = 0; k < 16; ++k) vn[k] = v[k];
         } else {
-            normalize16(v, s_row, outer_inv(s_row), vn);
+            // without a residual the source is bf16: a small outer scale rules
+            // out subnormal quotients for the whole tile
+            const bool recheck = EF || OUTER == kOuter1D || GIVEN || !(s_row <= kNoSubnormalScale);
+            normalize16(v, s_row, inv_row, vn, recheck);
         }
-        if (cur.act) {
+        {
             BlockScale<BIAS> sc;
             const uint2 packed = quant16<BIAS, SR>(vn, u, rtab, sc);
-            if (a.row_codes) *(uint2*)(a.row_codes + cur.e0 / 2) = packed;
-            if (a.row_scales) a.row_scales[cur.e0 / 16] = (uint8_t)sc.code;
-            if (EF || a.y) {
+            buf_store8(make_rsrc(a.row_codes ? a.row_codes + cur.e_base / 2 : nullptr), act ? erow / 2u : kOff,
+                       packed);
+            buf_store_u8(make_rsrc(a.row_scales ? a.row_scales + cur.e_base / 16 : nullptr),
+                         act ? erow / 16u : kOff, sc.code);
+            if (EF || Y) {
                 float w[16];
                 decode16(packed, sc.d, w);
                 if (OUTER != kOuterNone) {
 #pragma unroll
                     for (int k = 0; k < 16; ++k) w[k] = w[k] * s_row;
                 }
-                if (a.y) {
+                if (Y) {
                     uint32_t o[8];
 #pragma unroll
                     for (int k = 0; k < 8; ++k) o[k] = f32_to_bf16(w[2 * k]) | (f32_to_bf16(w[2 * k + 1]) << 16);
-                    *(uint4*)(a.y + cur.e0) = make_uint4(o[0], o[1], o[2], o[3]);
-                    *(uint4*)(a.y + cur.e0 + 8) = make_uint4(o[4], o[5], o[6], o[7]);
+                    const rsrc_t ry = make_rsrc(a.y + cur.e_base);
+                    const uint32_t oy = act ? erow * 2u : kOff;
+                    buf_store16(ry, oy, make_uint4(o[0], o[1], o[2], o[3]));
+                    buf_store16(ry, oy + 16u, make_uint4(o[4], o[5], o[6], o[7]));
                 }
                 if (EF) {
+                    const rsrc_t rz = make_rsrc(a.residual + cur.e_base);
+                    const uint32_t oz = act ? erow * 4u : kOff;
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
-                        *(float4*)(a.residual + cur.e0 + 4 * q) =
-                            make_float4(v[4 * q] - w[4 * q], v[4 * q + 1] - w[4 * q + 1],
-                                        v[4 * q + 2] - w[4 * q + 2], v[4 * q + 3] - w[4 * q + 3]);
+                        buf_store16(rz, oz + 16u * q,
+                                    make_uint4(__float_as_uint(v[4 * q] - w[4 * q]),
+                                               __float_as_uint(v[4 * q + 1] - w[4 * q + 1]),
+                                               __float_as_uint(v[4 * q + 2] - w[4 * q + 2]),
+                                               __float_as_uint(v[4 * q + 3] - w[4 * q + 3])));
                 }
             }
         }
         if (COLS) {
             // ---------------- stage through LDS
+            if (!barrier_done) lds_barrier();   // previous tile's column reads are done
+            const float* src = (OUTER == kOuter1D) ? v : vn;
 #pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                lds_v[r][16 * sg + k] = (OUTER == kOuter1D) ? v[k] : vn[k];
-                if (SR) lds_u[r][16 * sg + k] = (uint16_t)u[k];
+            for (int j = 0; j < 4; ++j)
+                lds_v[lds_row + swz_chunk(r, 4 * sg + j)] =
+                    make_float4(src[4 * j], src[4 * j + 1], src[4 * j + 2], src[4 * j + 3]);
+            if (SR) {
+#pragma unroll
+                for (int k = 0; k < 16; ++k) lds_u[r][16 * sg + k] = (uint16_t)u[k];
             }
             lds_barrier();
 
             // ---------------- column phase
-            const int cc = tid >> 2, rs = tid & 3;
             const bool actc = (cc < cur.cols_valid) && (16 * rs < cur.rows_valid);
+            const float* lf = reinterpret_cast<const float*>(lds_v);
             float cv[16];
             uint32_t cu[16];
 #pragma unroll
             for (int k = 0; k < 16; ++k) {
-                cv[k] = lds_v[16 * rs + k][cc];
-                cu[k] = SR ? (uint32_t)lds_u[16 * rs + k][cc] : 0u;
+                const int row = 16 * rs + k;
+                // rows of one parity share the swizzled column
+                cv[k] = lf[row * kTile + (lds_col ^ (4 * (k & 1)))];
+                cu[k] = SR ? (uint32_t)lds_u[row][cc] : 0u;
             }
+            const uint32_t ecol = (uint32_t)(cc * cur.Rg + 16 * rs);   // lane's first element, relative
             if (OUTER == kOuter1D) {
-                const int64_t colbase = (int64_t)a.row0[cur.g] * cols / (16 * a.obs16);
-                const int64_t ogc = colbase + (cur.c0 + cc) * (cur.Rg / (16 * a.obs16)) +
-                                    (cur.lrow0 + 16 * rs) / (16 * a.obs16);
+                // columnwise 1D groups: [cols, Rg / obs] per group
+                const int gpc = cur.Rg / obs;
+                const rsrc_t ro =
+                    make_rsrc(a.col_outer ? a.col_outer + (int64_t)cur.r0 * cols / obs +
+                                                (int64_t)cur.c0 * gpc + cur.lrow0 / obs
+                                          : nullptr);
+                const uint32_t oo = (uint32_t)(cc * gpc + (16 * rs) / obs) * 4u;
                 float s_col;
                 if (GIVEN) {
-                    s_col = actc ? a.col_outer[ogc] : 1.0f;
+                    s_col = buf_load_f32(ro, actc ? oo : kOff);
+                    if (!actc) s_col = 1.0f;
                 } else {
-                    s_col = quad_max(max_abs16(cv), a.obs16) / den;
-                    if (actc && a.col_outer && (rs % a.obs16) == 0) a.col_outer[ogc] = s_col;
+                    s_col = outer_scale(quad_max(max_abs16(cv), a.obs16), den);
+                    buf_store_u32(ro, (actc && (rs % a.obs16) == 0) ? oo : kOff, __float_as_uint(s_col));
                 }
                 float cn[16];
-                normalize16(cv, s_col, outer_inv(s_col), cn);
+                normalize16(cv, s_col, outer_inv(s_col), cn, true);
 #pragma unroll
                 for (int k = 0; k < 16; ++k) cv[k] = cn[k];
             }
-            if (actc) {
-                BlockScale<BIAS> sc;
-                const uint2 packed = quant16<BIAS, SR>(cv, cu, rtab, sc);
-                const int64_t colrow = cur.c0 + cc;                   // row of the columnwise buffer
-                const int64_t gbase = (int64_t)a.row0[cur.g] * cols;  // elements before this group
-                const int64_t ce0 = gbase + colrow * cur.Rg + cur.lrow0 + 16 * rs;
-                *(uint2*)(a.col_codes + ce0 / 2) = packed;
-                a.col_scales[ce0 / 16] = (uint8_t)sc.code;
-            }
+            BlockScale<BIAS> sc;
+            const uint2 packed = quant16<BIAS, SR>(cv, cu, rtab, sc);
+            buf_store8(make_rsrc(a.col_codes + cur.ce_base / 2), actc ? ecol / 2u : kOff, packed);
+            buf_store_u8(make_rsrc(a.col_scales + cur.ce_base / 16), actc ? ecol / 16u : kOff, sc.code);
         }
         if (!has_next) break;
-        tile = next;
+        cur = nxt;
         in = nin;
     }
 }
@@ -351,44 +467,54 @@ hipError_t launch_persistent(void (*fn)(TileArgs), TileArgs a, hipStream_t s)
 
 }  // namespace
 
+namespace {
+
+// Kernel selection: the tensorwise and no-outer modes take their scale from
+// tensor_scale (or have none), so they have no precomputed-outer variant; the
+// bf16 dequantised output exists only for the rowwise-only (2D outer) use.
+template <int B, int O, bool S, bool C, bool E>
+hipError_t pick_given_y(const TileArgs& a, hipStream_t s)
+{
+    const bool given = a.outer_given != 0;
+    const bool y = a.y != nullptr;
+    if constexpr (O == kOuterNone || O == kOuterTensor) {
+        return launch_persistent(k_tile<B, O, S, C, E, false, false>, a, s);
+    } else if constexpr (C) {
+        return given ? launch_persistent(k_tile<B, O, S, C, E, true, false>, a, s)
+                     : launch_persistent(k_tile<B, O, S, C, E, false, false>, a, s);
+    } else {
+        if (given) return y ? launch_persistent(k_tile<B, O, S, C, E, true, true>, a, s)
+                            : launch_persistent(k_tile<B, O, S, C, E, true, false>, a, s);
+        return y ? launch_persistent(k_tile<B, O, S, C, E, false, true>, a, s)
+                 : launch_persistent(k_tile<B, O, S, C, E, false, false>, a, s);
+    }
+}
+
+template <int B, int O, bool C>
+hipError_t pick_sr_ef(bool sr, bool ef, const TileArgs& a, hipStream_t s)
+{
+    if (sr) return ef ? pick_given_y<B, O, true, C, true>(a, s) : pick_given_y<B, O, true, C, false>(a, s);
+    return ef ? pick_given_y<B, O, false, C, true>(a, s) : pick_given_y<B, O, false, C, false>(a, s);
+}
+
+template <int B>
+hipError_t pick_outer(int outer_kind, bool sr, const TileArgs& a, hipStream_t s)
+{
+    const bool ef = a.residual != nullptr;
+    if (a.col_codes == nullptr) return pick_sr_ef<B, kOuter2D, false>(sr, ef, a, s);   // rowwise 2D outer
+    switch (outer_kind) {
+    case kOuterNone: return pick_sr_ef<B, kOuterNone, true>(sr, ef, a, s);
+    case kOuterTensor: return pick_sr_ef<B, kOuterTensor, true>(sr, ef, a, s);
+    case kOuter1D: return pick_sr_ef<B, kOuter1D, true>(sr, ef, a, s);
+    default: return pick_sr_ef<B, kOuter2D, true>(sr, ef, a, s);
+    }
+}
+
+}  // namespace
+
 hipError_t launch_tiles(int bias, int outer_kind, bool sr, const TileArgs& a, hipStream_t s)
 {
-    const bool cols = (a.col_codes != nullptr);
-    const bool ef = (a.residual != nullptr);
-    const bool given = a.outer_given != 0;
-#define FP4Q_T(B, O, S, C, E, G) return launch_persistent(k_tile<B, O, S, C, E, G>, a, s)
-#define FP4Q_T_G(B, O, S, C, E)                 \
-    do {                                        \
-        if (given) FP4Q_T(B, O, S, C, E, true); \
-        else FP4Q_T(B, O, S, C, E, false);      \
-    } while (0)
-#define FP4Q_T_E(B, O, S, C, G)                 \
-    do {                                        \
-        if (ef) G(B, O, S, C, true);            \
-        else G(B, O, S, C, false);              \
-    } while (0)
-#define FP4Q_T_NG(B, O, S, C, E) FP4Q_T(B, O, S, C, E, false)
-#define FP4Q_T_S(B, O, C, G)                    \
-    do {                                        \
-        if (sr) FP4Q_T_E(B, O, true, C, G);     \
-        else FP4Q_T_E(B, O, false, C, G);       \
-    } while (0)
-#define FP4Q_T_O(B)                                                               \
-    do {                                                                          \
-        if (!cols) FP4Q_T_S(B, kOuter2D, false, FP4Q_T_G);                        \
-        else if (outer_kind == kOuterNone) FP4Q_T_S(B, kOuterNone, true, FP4Q_T_NG); \
-        else if (outer_kind == kOuterTensor) FP4Q_T_S(B, kOuterTensor, true, FP4Q_T_NG); \
-        else if (outer_kind == kOuter1D) FP4Q_T_S(B, kOuter1D, true, FP4Q_T_G);  \
-        else FP4Q_T_S(B, kOuter2D, true, FP4Q_T_G);                               \
-    } while (0)
-    if (bias == 7) FP4Q_T_O(7);
-    FP4Q_T_O(15);
-#undef FP4Q_T_O
-#undef FP4Q_T_S
-#undef FP4Q_T_NG
-#undef FP4Q_T_E
-#undef FP4Q_T_G
-#undef FP4Q_T
+    return bias == 7 ? pick_outer<7>(outer_kind, sr, a, s) : pick_outer<15>(outer_kind, sr, a, s);
 }
 
 }  // namespace fp4q

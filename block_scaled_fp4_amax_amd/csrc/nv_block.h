@@ -16,14 +16,21 @@ namespace fp4q {
 // e >= 1 and d = (m / 8) * 2^(1 - BIAS) for e == 0; entry 8 (d == 0) is 0, so
 // a zero scale yields quotients of (signed) zero.  Exact power-of-two scaling
 // of a binary64 value commutes with its rounding, so the result is RN64(1/d).
-struct RecipTable {
-    double r[16];
-};
+constexpr int kRecipTableSize = 16;
+
+// Entries m = 0..7: RN64(1 / (1 + m/8)); 8: 0; 9..15: RN64(8 / (m - 8)).
+// Each quotient is a constant expression, evaluated by the compiler as one
+// correctly rounded binary64 division.
+constexpr double kRecipTable[16] = {
+    1.0 / 1.0, 1.0 / 1.125, 1.0 / 1.25, 1.0 / 1.375, 1.0 / 1.5, 1.0 / 1.625, 1.0 / 1.75, 1.0 / 1.875,
+    0.0, 8.0 / 1.0, 8.0 / 2.0, 8.0 / 3.0, 8.0 / 4.0, 8.0 / 5.0, 8.0 / 6.0, 8.0 / 7.0};
 
 __device__ __forceinline__ void fill_recip_table(double* t, int lane)
 {
-    if (lane < 8) t[lane] = 1.0 / (1.0 + lane * 0.125);
-    else if (lane < 16) t[lane] = lane == 8 ? 0.0 : 8.0 / (double)(lane - 8);
+    double v = 0.0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v = lane == i ? kRecipTable[i] : v;
+    if (lane < 16) t[lane] = v;
 }
 
 template <int BIAS>
@@ -49,9 +56,21 @@ __device__ __forceinline__ BlockScale<BIAS> block_scale(float bmax, const double
     BlockScale<BIAS> s;
     // RN32(bmax / 6): any quotient below the normal range encodes to code 0
     // either way (the smallest nonzero inner scale is far above it).
-    const float ys = div_inv64(bmax, 1.0 / 6.0);
-    s.code = scale_encode<BIAS>(ys);
-    s.d = scale_decode<BIAS>(s.code);
+    const float y = div_inv64(bmax, 1.0 / 6.0);
+    constexpr float kMax = BIAS == 7 ? 448.0f : 114688.0f;
+    constexpr uint32_t kMaxCode = BIAS == 7 ? 0x7Eu : 0xFEu;
+    constexpr float kMinNormal = BIAS == 7 ? 0x1p-6f : 0x1p-14f;
+    constexpr float kToSteps = BIAS == 7 ? 0x1p9f : 0x1p17f;      // subnormal grid step 2^-(BIAS+2)
+    constexpr float kFromSteps = BIAS == 7 ? 0x1p-9f : 0x1p-17f;
+    // normal range: round to nearest even at 3 mantissa bits on the bit pattern
+    const uint32_t u = __float_as_uint(y);
+    const uint32_t un = (u + 0x7FFFFu + ((u >> 20) & 1u)) & 0xFFF00000u;
+    // subnormal range: a whole number of grid steps, 0..8 (8 is the smallest normal)
+    const float steps = __builtin_rintf(y * kToSteps);
+    const bool sat = y >= kMax;
+    const bool sub = y < kMinNormal;
+    s.code = sat ? kMaxCode : (sub ? (uint32_t)steps : (un >> 20) - ((127u - (uint32_t)BIAS) << 3));
+    s.d = sat ? kMax : (sub ? steps * kFromSteps : __uint_as_float(un));
     s.rd = inner_recip<BIAS>(s.code, tab);
     return s;
 }
@@ -135,21 +154,32 @@ __device__ __forceinline__ void decode16(uint2 packed, float d, float (&p)[16])
 }
 
 // Normalise by an outer scale: v_n = RN32(v / s_o), v_n = +-0 when s_o == 0.
-// inv = RN64(1 / s_o) (0 when s_o == 0); subnormal results are recomputed by
-// IEEE division.
-__device__ __forceinline__ void normalize16(const float (&v)[16], float s_o, double inv, float (&vn)[16])
+// inv = RN64(1 / s_o) (0 when s_o == 0).  The reciprocal product is exact for
+// normal-range quotients; with `recheck` subnormal results are recomputed by
+// IEEE division (callers pass false only where no quotient can be subnormal).
+__device__ __forceinline__ void normalize16(const float (&v)[16], float s_o, double inv, float (&vn)[16],
+                                            bool recheck)
 {
     bool slow = false;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        vn[k] = div_inv64(v[k], inv);
-        slow |= is_subnormal(vn[k]);
+    for (int k = 0; k < 16; ++k) vn[k] = div_inv64(v[k], inv);
+    if (recheck) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) slow |= is_subnormal(vn[k]);
     }
     if (__builtin_expect(slow, 0)) {
 #pragma unroll
         for (int k = 0; k < 16; ++k)
             if (is_subnormal(vn[k])) vn[k] = v[k] / s_o;
     }
+}
+
+// Outer scale RN32(amax / den) for den = scale_max * 6 (2688 or 688128).
+__device__ __forceinline__ float outer_scale(float amax, float den)
+{
+    float s = div_inv64(amax, 1.0 / (double)den);
+    if (__builtin_expect(is_subnormal(s), 0)) s = amax / den;
+    return s;
 }
 
 __device__ __forceinline__ double outer_inv(float s_o)
