@@ -128,11 +128,11 @@ TileArgs tile_args_single(const uint16_t* x, int64_t rows, int64_t cols, int64_t
     a.ld = ld;
     a.cols = cols;
     a.ngroups = 1;
-    a.tiles_c = (int32_t)((cols + 63) / 64);
+    a.tiles_c = (int32_t)((cols + 127) / 128);
     a.row0[0] = 0;
     a.row0[1] = (int32_t)rows;
     a.tile0[0] = 0;
-    a.tile0[1] = (int32_t)(((rows + 63) / 64) * a.tiles_c);
+    a.tile0[1] = (int32_t)(((rows + 127) / 128) * a.tiles_c);
     a.total_tiles = a.tile0[1];
     set_tile_grid(a.total_tiles, a.per_xcd, a.wgs_per_xcd);
     return a;
@@ -404,7 +404,7 @@ int fp4_cast_transpose_grouped(const fp4q_cfg* cfg, int32_t groups, const int64_
         misaligned(row_outer, 4) || misaligned(col_outer, 4))
         return FP4Q_ERR_ALIGN;
     hipStream_t s = (hipStream_t)stream;
-    const int32_t tiles_c = (int32_t)((cols + 63) / 64);
+    const int32_t tiles_c = (int32_t)((cols + 127) / 128);
     int64_t row_before = 0;
     for (int32_t g0 = 0; g0 < groups; g0 += kMaxGroupsPerLaunch) {
         const int32_t ng = std::min<int32_t>(kMaxGroupsPerLaunch, groups - g0);
@@ -434,7 +434,7 @@ int fp4_cast_transpose_grouped(const fp4q_cfg* cfg, int32_t groups, const int64_
             a.tile0[k] = tt;
             const int64_t R = rows_per_group[g0 + k];
             rr += R;
-            tt += (int32_t)(((R + 63) / 64) * tiles_c);
+            tt += (int32_t)(((R + 127) / 128) * tiles_c);
         }
         a.row0[ng] = (int32_t)rr;
         a.tile0[ng] = tt;

@@ -183,24 +183,23 @@ __device__ __forceinline__ uint32_t sr_lane(const u32x4& w, int l)
 }
 
 // The 16 SR variates of elements idx0 .. idx0+15 (idx0 = global index of the
-// block's first element).  idx0 % 8 equals index_base % 8 for every block of a
-// launch (blocks start at multiples of 16), so the branch is uniform; the
-// aligned case takes exactly two Philox blocks with static lane indexing.
-__device__ __forceinline__ void sr_draws16(uint64_t seed, uint64_t step, uint64_t idx0, uint32_t (&u)[16])
+// block's first element), packed two per word: element k's variate is bits
+// 16*(k&1) .. 16*(k&1)+15 of u[k >> 1].  idx0 % 8 equals index_base % 8 for
+// every block of a launch (blocks start at multiples of 16), so the branch is
+// uniform; in the aligned case the eight Philox output words of the two
+// 8-element counters are the packed variates themselves.
+__device__ __forceinline__ void sr_draws16(uint64_t seed, uint64_t step, uint64_t idx0, uint32_t (&u)[8])
 {
     const uint64_t b0 = idx0 >> 3;
     const int off = (int)(idx0 & 7u);
     const u32x4 w0 = sr_words(seed, step, b0);
     const u32x4 w1 = sr_words(seed, step, b0 + 1);
     if (off == 0) {
-        const uint32_t ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            u[2 * j] = ws[j] & 0xFFFFu;
-            u[2 * j + 1] = ws[j] >> 16;
-        }
+        u[0] = w0.x; u[1] = w0.y; u[2] = w0.z; u[3] = w0.w;
+        u[4] = w1.x; u[5] = w1.y; u[6] = w1.z; u[7] = w1.w;
     } else {
         const u32x4 w2 = sr_words(seed, step, b0 + 2);
+        uint32_t e16[16];
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
             const int e = off + k;
@@ -210,9 +209,17 @@ __device__ __forceinline__ void sr_draws16(uint64_t seed, uint64_t step, uint64_
             w.y = blk == 0 ? w0.y : (blk == 1 ? w1.y : w2.y);
             w.z = blk == 0 ? w0.z : (blk == 1 ? w1.z : w2.z);
             w.w = blk == 0 ? w0.w : (blk == 1 ? w1.w : w2.w);
-            u[k] = sr_lane(w, e & 7);
+            e16[k] = sr_lane(w, e & 7);
         }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) u[j] = e16[2 * j] | (e16[2 * j + 1] << 16);
     }
+}
+
+// Variate k of a packed set, as a float (exact: < 2^16).
+__device__ __forceinline__ float sr_var(const uint32_t (&u)[8], int k)
+{
+    return (float)((u[k >> 1] >> (16 * (k & 1))) & 0xFFFFu);
 }
 
 // ---------------------------------------------------------------- buffer resources

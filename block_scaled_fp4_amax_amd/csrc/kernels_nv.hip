@@ -98,11 +98,11 @@ __global__ __launch_bounds__(kThreads) void k_nv_rows(RowArgs a, uint32_t nblock
         }
     }
 
-    uint32_t u[16];
+    uint32_t u[8];
     if (SR) sr_draws16(a.seed, a.step, a.index_base + (uint64_t)e0, u);
     else {
 #pragma unroll
-        for (int k = 0; k < 16; ++k) u[k] = 0;
+        for (int k = 0; k < 8; ++k) u[k] = 0;
     }
 
     float s_o = 1.0f;

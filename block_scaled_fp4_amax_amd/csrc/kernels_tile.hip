@@ -13,7 +13,8 @@
 // (1 x obs along rows, obs x 1 along columns); grouped MoE quantisation keeps
 // one outer grid per expert.
 //
-// Per workgroup (256 lanes, 4 waves) one 64 x 64 source tile at a time:
+// Per workgroup (256 lanes, 4 waves) one 2 x 2 super-tile of 64 x 64 source
+// tiles at a time, the four tiles one after another:
 //   row phase  lane (r = t/4, s = t%4) owns the 16-element row block
 //              [r, 16s .. 16s+15]: two 16-byte loads, (residual add),
 //              outer scale (2D: tile-wide max through a DPP wave max and LDS;
@@ -31,13 +32,15 @@
 //              32 contiguous bytes.
 // Two workgroup barriers per tile: one before the tile's LDS writes (the
 // previous tile's column reads are done; for 2D it also publishes the wave
-// maxima) and one after them.
+// maxima) and one after them.  Codes, scale bytes and 1D outer scales of the
+// two tiles of a super-tile row (column) are stored together, as runs of 64
+// code bytes and 8 scale bytes per row (column).
 //
-// Tiles are taken in row-major order, split into 8 contiguous slices, one per
-// XCD (workgroup ids are dealt round-robin to the XCDs), so the partial cache
-// lines that neighbouring tiles write meet in the same L2.  Workgroups are
-// persistent within their slice and load tile j+1's inputs before computing
-// tile j.
+// Super-tiles are taken in row-major order, split into 8 contiguous slices,
+// one per XCD (workgroup ids are dealt round-robin to the XCDs), so the
+// partial cache lines that neighbouring super-tiles write meet in the same
+// L2.  Workgroups are persistent within their slice and load each tile's
+// inputs before computing the tile before it.
 #include <mutex>
 #include <vector>
 
@@ -62,7 +65,7 @@ __device__ __forceinline__ int swz_chunk(int row, int ch)
 }
 
 template <int BIAS, bool SR>
-__device__ __forceinline__ uint2 quant16(const float (&vn)[16], const uint32_t (&u)[16], const double* tab,
+__device__ __forceinline__ uint2 quant16(const float (&vn)[16], const uint32_t (&u)[8], const double* tab,
                                          BlockScale<BIAS>& sc)
 {
     sc = block_scale<BIAS>(max_abs16(vn), tab);
@@ -70,22 +73,28 @@ __device__ __forceinline__ uint2 quant16(const float (&vn)[16], const uint32_t (
     return codes16_rne(vn, sc.rd);
 }
 
-// Walks a workgroup's tiles t = first, first + W, ... in the row-major order
-// of (group, tile row, tile column) without dividing per step: the column
-// advances by W % tiles_c and the row by W / tiles_c.  The current group's
-// row range is kept in registers; crossing into another group (rare)
+// Super-tiles: the unit a workgroup walks is a 2 x 2 block of 64 x 64 tiles
+// (128 x 128 elements), so that the outputs of horizontally (vertically)
+// neighbouring tiles can be stored together: 64-byte code runs and 8-byte
+// scale runs per row (column) instead of 32 and 4.
+constexpr int kSuper = 2 * kTile;
+
+// Walks a workgroup's super-tiles t = first, first + W, ... in the row-major
+// order of (group, super-tile row, super-tile column) without dividing per
+// step: the column advances by W % st_c and the row by W / st_c.  The current
+// group's row range is kept in registers; crossing into another group (rare)
 // re-derives the position from the prefix tables.
 struct TileWalk {
-    int t, g, ti, tj, di, dj;
-    int r0, Rg, tile_end;   // group's first row, row count, end of its tiles
+    int t, g, si, sj, di, dj;
+    int r0, Rg, tile_end;   // group's first row, row count, end of its super-tiles
 };
 
 __device__ __forceinline__ void walk_locate(const TileArgs& a, TileWalk& w)
 {
     while (w.g + 1 < a.ngroups && a.tile0[w.g + 1] <= w.t) ++w.g;
     const int lt = w.t - a.tile0[w.g];
-    w.ti = lt / a.tiles_c;
-    w.tj = lt - w.ti * a.tiles_c;
+    w.si = lt / a.tiles_c;
+    w.sj = lt - w.si * a.tiles_c;
     w.r0 = a.row0[w.g];
     w.Rg = a.row0[w.g + 1] - w.r0;
     w.tile_end = a.tile0[w.g + 1];
@@ -98,37 +107,38 @@ __device__ __forceinline__ void walk_next(const TileArgs& a, TileWalk& w, int st
         walk_locate(a, w);
         return;
     }
-    w.ti += w.di;
-    w.tj += w.dj;
-    if (w.tj >= a.tiles_c) {
-        w.tj -= a.tiles_c;
-        ++w.ti;
+    w.si += w.di;
+    w.sj += w.dj;
+    if (w.sj >= a.tiles_c) {
+        w.sj -= a.tiles_c;
+        ++w.si;
     }
 }
 
-// One tile's place, uniform across the workgroup: group g (first row r0, Rg
-// rows), tile row ti within the group, tile column tj, the valid extent
-// (edge tiles are partial), and the element indices of its (0, 0) element in
-// the row-major source and in the columnwise buffers.
+// One 64 x 64 tile's place, uniform across the workgroup: group g (first row
+// r0, Rg rows), tile row ti within the group, tile column tj, the valid extent
+// (0 for a tile of a super-tile that lies outside the tensor), and the element
+// indices of its (0, 0) element in the row-major source and in the columnwise
+// buffers.
 struct Tile {
     int g, r0, ti, tj, rows_valid, cols_valid, Rg, grow0, c0, lrow0;
     int64_t e_base;    // (grow0) * cols + c0
     int64_t ce_base;   // r0 * cols + c0 * Rg + lrow0
 };
 
-__device__ __forceinline__ Tile make_tile(const TileArgs& a, const TileWalk& w)
+__device__ __forceinline__ Tile make_tile(const TileArgs& a, const TileWalk& w, int sub)
 {
     Tile t;
     t.g = w.g;
     t.r0 = w.r0;
-    t.ti = w.ti;
-    t.tj = w.tj;
+    t.ti = 2 * w.si + (sub >> 1);
+    t.tj = 2 * w.sj + (sub & 1);
     t.Rg = w.Rg;
-    t.lrow0 = w.ti * kTile;
+    t.lrow0 = t.ti * kTile;
     t.grow0 = w.r0 + t.lrow0;
-    t.c0 = w.tj * kTile;
-    t.rows_valid = min(kTile, t.Rg - t.lrow0);
-    t.cols_valid = min(kTile, (int)a.cols - t.c0);
+    t.c0 = t.tj * kTile;
+    t.rows_valid = max(0, min(kTile, t.Rg - t.lrow0));
+    t.cols_valid = max(0, min(kTile, (int)a.cols - t.c0));
     t.e_base = (int64_t)t.grow0 * a.cols + t.c0;
     t.ce_base = (int64_t)w.r0 * a.cols + (int64_t)t.c0 * t.Rg + t.lrow0;
     return t;
@@ -160,14 +170,73 @@ __device__ __forceinline__ void load_tile_input(const TileArgs& a, const Tile& t
     }
 }
 
-// Register budget per lane: 72 VGPRs (7 waves per SIMD) for the RTNE kernels,
-// 128 (4 waves) with stochastic rounding or a residual, 168 (3 waves) with
-// both.  Tighter budgets make the compiler spill to scratch inside the tile
-// loop.
+// One direction's per-lane result for one tile: 16 packed codes, the scale
+// byte and (1D) the lane's outer scale.
+struct DirOut {
+    uint2 codes;
+    uint32_t scale;
+    float outer;
+};
+
+// Per-wave staging used to pair two tiles' outputs: each lane deposits its 8
+// code bytes and its scale byte, then reads back 16 contiguous code bytes
+// (and lanes 0-1 four scale bytes) of the 64-byte / 8-byte run of its row
+// (column).  Four lanes of a row share a wave, so no barrier is needed.
+struct alignas(16) PairStage {
+    uint2 codes[kThreads / 4][8];
+    uint8_t scales[kThreads / 4][8];
+};
+
+// Orders this wave's LDS accesses before and after it (the lanes of a line
+// exchange data through LDS within one wave).
+__device__ __forceinline__ void wave_lds_fence()
+{
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
+}
+
+// Stores one row (or column) run made of tile A's and tile B's results for
+// the four lanes (k = lane & 3) of line `line`.  nvalid = valid 16-element
+// blocks in the run (A's first, then B's; B is present only when A is full).
+// Every lane issues the same five store instructions; the hardware drops the
+// masked ones.
+__device__ __forceinline__ void store_pair(PairStage& st, int line, int k, const DirOut& A, const DirOut& B,
+                                           bool line_ok, int nvalid, rsrc_t rc, uint32_t oc, rsrc_t rsc,
+                                           uint32_t osc)
+{
+    wave_lds_fence();   // earlier reads of this line's staging are done
+    st.codes[line][k] = A.codes;
+    st.codes[line][4 + k] = B.codes;
+    st.scales[line][k] = (uint8_t)A.scale;
+    st.scales[line][4 + k] = (uint8_t)B.scale;
+    wave_lds_fence();   // the other lanes' deposits are visible
+    const uint4 c16 = *reinterpret_cast<const uint4*>(&st.codes[line][2 * k]);
+    const uint32_t s4 = *reinterpret_cast<const uint32_t*>(&st.scales[line][4 * (k & 1)]);
+    // 16-byte code chunk k holds blocks 2k and 2k+1
+    const bool full = line_ok && 2 * k + 1 < nvalid;
+    const bool half = line_ok && 2 * k + 1 == nvalid;
+    buf_store16(rc, full ? oc + 16u * k : kOff, c16);
+    buf_store8(rc, half ? oc + 16u * k : kOff, make_uint2(c16.x, c16.y));
+    // scale dword k (k < 2) holds blocks 4k .. 4k+3
+    buf_store_u32(rsc, (line_ok && k < 2 && 4 * k + 3 < nvalid) ? osc + 4u * k : kOff, s4);
+    // the remaining blocks of a partial run, one byte each
+    const int full_words = nvalid >> 2;
+    buf_store_u8(rsc, (line_ok && full_words == 0 && k < nvalid) ? osc + k : kOff, A.scale);
+    buf_store_u8(rsc, (line_ok && full_words == 1 && 4 + k < nvalid) ? osc + 4u + k : kOff, B.scale);
+}
+
+// Register budget per lane: 128 VGPRs (4 waves per SIMD), 168 (3 waves) for
+// the tile loop that holds results across iterations.  Tighter budgets make
+// the compiler spill to scratch inside the loop.
+template <int OUTER, bool SR, bool EF>
+constexpr bool tile_unrolled()
+{
+    return !SR && !EF && OUTER != kOuter1D;
+}
+
 template <int BIAS, int OUTER, bool SR, bool COLS, bool EF>
 constexpr int tile_waves_per_simd()
 {
-    return (SR && EF) ? 3 : ((SR || EF) ? 4 : 7);
+    return (tile_unrolled<OUTER, SR, EF>() || (OUTER == kOuter1D && !SR)) ? 4 : 3;
 }
 
 // Smallest binary32 outer scale for which v / s_o can be subnormal for some
@@ -175,18 +244,19 @@ constexpr int tile_waves_per_simd()
 // normal binary32 and the reciprocal-product division needs no re-check.
 constexpr float kNoSubnormalScale = 0x1p-7f;
 
-// Every global access in the tile loop is a buffer instruction whose masked
-// lanes carry an out-of-range offset, and there is no branch around any of
-// them, so the wait for the next tile's loads never waits for this tile's
-// stores.
+// Every global access is a buffer instruction whose masked lanes carry an
+// out-of-range offset, and every tile iteration issues the same sequence of
+// memory instructions with no branch around any of them, so the compiler's
+// wait for the next tile's loads never waits for earlier stores.
 template <int BIAS, int OUTER, bool SR, bool COLS, bool EF, bool GIVEN, bool Y>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(tile_waves_per_simd<BIAS, OUTER, SR, COLS, EF>())))
 void k_tile(TileArgs a)
 {
     __shared__ float4 lds_v[COLS ? kTile * kTile / 4 : 1];
-    __shared__ uint16_t lds_u[(COLS && SR) ? kTile : 1][(COLS && SR) ? kTile + 2 : 1];
+    __shared__ uint4 lds_u[(COLS && SR) ? kTile * kTile / 8 : 1];   // SR variates, [row][col] u16
     __shared__ uint32_t red[2][kThreads / 64];
     __shared__ double rtab[kRecipTableSize];
+    __shared__ PairStage stage;
 
     const int tid = (int)threadIdx.x;
     const int r = tid >> 2, sg = tid & 3;       // row phase: row, 16-column segment
@@ -202,9 +272,8 @@ void k_tile(TileArgs a)
     walk.di = W / a.tiles_c;
     walk.dj = W - walk.di * a.tiles_c;
     walk_locate(a, walk);
-    Tile cur = make_tile(a, walk);
     TileInput<EF> in;
-    load_tile_input<EF>(a, cur, true, r, sg, in);
+    load_tile_input<EF>(a, make_tile(a, walk, 0), true, r, sg, in);
     fill_recip_table(rtab, tid);
     lds_barrier();
     const float den = ScaleFmt<BIAS>::outer_den();
@@ -224,34 +293,30 @@ void k_tile(TileArgs a)
     }
 
     // Let the first tile's loads land here, so that at the loop head the
-    // current tile's registers are complete on every path; otherwise the wait
-    // placed for the first iteration would, on later ones, also wait for the
-    // previous tile's stores.
+    // current tile's registers are complete on every path.
     wait_vmem_all();
 
-    for (int iter = 0;; ++iter) {
-        const bool act = r < cur.rows_valid && 16 * sg < cur.cols_valid;
-        // ---- prefetch the next tile's inputs (zeros when there is none)
-        const bool has_next = walk.t + W < slice_end;
-        if (has_next) walk_next(a, walk, W);
-        const Tile nxt = make_tile(a, walk);
-        TileInput<EF> nin;
-        load_tile_input<EF>(a, nxt, has_next, r, sg, nin);
+    int iter = 0;   // tiles processed (parity of the reduction slots)
 
+    // One tile: row phase, LDS transpose, column phase.  Writes the dequantised
+    // output, the residual and 2D outer scales itself; returns the codes, scale
+    // bytes and 1D outer scales of both directions for the paired stores.
+    auto tile_body = [&](const Tile& cur, const TileInput<EF>& tin, DirOut& ro, DirOut& co) {
+        const bool act = r < cur.rows_valid && 16 * sg < cur.cols_valid;
         // ---------------- row phase
         float v[16];
         uint32_t am_bits = 0;    // bit pattern of max |v| over the lane's 16 values
         {
-            const uint32_t w[8] = {in.w0.x, in.w0.y, in.w0.z, in.w0.w, in.w1.x, in.w1.y, in.w1.z, in.w1.w};
+            const uint32_t w[8] = {tin.w0.x, tin.w0.y, tin.w0.z, tin.w0.w, tin.w1.x, tin.w1.y, tin.w1.z, tin.w1.w};
 #pragma unroll
             for (int k = 0; k < 8; ++k) { v[2 * k] = bf16_lo(w[k]); v[2 * k + 1] = bf16_hi(w[k]); }
             if (EF) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    v[4 * q] = v[4 * q] + __uint_as_float(in.z[q].x);
-                    v[4 * q + 1] = v[4 * q + 1] + __uint_as_float(in.z[q].y);
-                    v[4 * q + 2] = v[4 * q + 2] + __uint_as_float(in.z[q].z);
-                    v[4 * q + 3] = v[4 * q + 3] + __uint_as_float(in.z[q].w);
+                    v[4 * q] = v[4 * q] + __uint_as_float(tin.z[q].x);
+                    v[4 * q + 1] = v[4 * q + 1] + __uint_as_float(tin.z[q].y);
+                    v[4 * q + 2] = v[4 * q + 2] + __uint_as_float(tin.z[q].z);
+                    v[4 * q + 3] = v[4 * q + 3] + __uint_as_float(tin.z[q].w);
                 }
 #pragma unroll
                 for (int k = 0; k < 16; ++k) {
@@ -272,22 +337,25 @@ void k_tile(TileArgs a)
                 }
             }
         }
-        uint32_t u[16];
+        uint32_t u[8];
 #pragma unroll
-        for (int k = 0; k < 16; ++k) u[k] = 0;
+        for (int k = 0; k < 8; ++k) u[k] = 0;
         if (SR && act) sr_draws16(a.seed, a.step, a.index_base + (uint64_t)cur.e_base + erow, u);
 
         bool barrier_done = false;   // the pre-LDS-write barrier has been passed
         float s_row = 1.0f;
         double inv_row = 1.0;
+        ro.outer = 0.0f;
+        co.outer = 0.0f;
         if (OUTER == kOuterTensor) {
             s_row = s_tensor;
             inv_row = inv_tensor;
         } else if (OUTER == kOuter2D) {
             const int64_t oidx = (int64_t)(cur.grow0 / kTile) * (cols / kTile) + cur.tj;
-            const rsrc_t ro = make_rsrc(a.row_outer ? a.row_outer + oidx : nullptr);
+            const rsrc_t ro2 = make_rsrc(a.row_outer ? a.row_outer + oidx : nullptr);
+            const bool tile_ok = cur.rows_valid > 0 && cur.cols_valid > 0;
             if (GIVEN) {
-                s_row = buf_load_f32(ro, 0u);
+                s_row = buf_load_f32(ro2, tile_ok ? 0u : kOff);
             } else {
                 const uint32_t m = wave_max_u32(am_bits);
                 uint32_t* rb = red[iter & 1];
@@ -296,21 +364,21 @@ void k_tile(TileArgs a)
                 barrier_done = true;
                 const uint32_t mm = max(max(rb[0], rb[1]), max(rb[2], rb[3]));
                 s_row = outer_scale(__uint_as_float(mm), den);
-                buf_store_u32(ro, tid == 0 ? 0u : kOff, __float_as_uint(s_row));
+                buf_store_u32(ro2, (tid == 0 && tile_ok) ? 0u : kOff, __float_as_uint(s_row));
             }
             inv_row = outer_inv(s_row);
         } else if (OUTER == kOuter1D) {
             // rowwise 1D groups: [rows, cols / obs]
             const int gpr = cols / obs;
-            const rsrc_t ro =
+            const rsrc_t ro1 =
                 make_rsrc(a.row_outer ? a.row_outer + (int64_t)cur.grow0 * gpr + cur.c0 / obs : nullptr);
             const uint32_t oo = (uint32_t)(r * gpr + (16 * sg) / obs) * 4u;
             if (GIVEN) {
-                s_row = buf_load_f32(ro, act ? oo : kOff);
+                s_row = buf_load_f32(ro1, act ? oo : kOff);
                 if (!act) s_row = 1.0f;
             } else {
                 s_row = outer_scale(__uint_as_float(quad_max_u32(am_bits, a.obs16)), den);
-                buf_store_u32(ro, (act && (sg % a.obs16) == 0) ? oo : kOff, __float_as_uint(s_row));
+                ro.outer = s_row;
             }
             inv_row = outer_inv(s_row);
         }
@@ -328,10 +396,8 @@ void k_tile(TileArgs a)
         {
             BlockScale<BIAS> sc;
             const uint2 packed = quant16<BIAS, SR>(vn, u, rtab, sc);
-            buf_store8(make_rsrc(a.row_codes ? a.row_codes + cur.e_base / 2 : nullptr), act ? erow / 2u : kOff,
-                       packed);
-            buf_store_u8(make_rsrc(a.row_scales ? a.row_scales + cur.e_base / 16 : nullptr),
-                         act ? erow / 16u : kOff, sc.code);
+            ro.codes = packed;
+            ro.scale = sc.code;
             if (EF || Y) {
                 float w[16];
                 decode16(packed, sc.d, w);
@@ -371,38 +437,43 @@ void k_tile(TileArgs a)
                     make_float4(src[4 * j], src[4 * j + 1], src[4 * j + 2], src[4 * j + 3]);
             if (SR) {
 #pragma unroll
-                for (int k = 0; k < 16; ++k) lds_u[r][16 * sg + k] = (uint16_t)u[k];
+                for (int j = 0; j < 2; ++j)
+                    lds_u[r * 8 + 2 * sg + j] = make_uint4(u[4 * j], u[4 * j + 1], u[4 * j + 2], u[4 * j + 3]);
             }
             lds_barrier();
 
             // ---------------- column phase
-            const bool actc = (cc < cur.cols_valid) && (16 * rs < cur.rows_valid);
             const float* lf = reinterpret_cast<const float*>(lds_v);
             float cv[16];
-            uint32_t cu[16];
+            uint32_t cu[8];
+            const uint16_t* lu = reinterpret_cast<const uint16_t*>(lds_u);
 #pragma unroll
             for (int k = 0; k < 16; ++k) {
                 const int row = 16 * rs + k;
                 // rows of one parity share the swizzled column
                 cv[k] = lf[row * kTile + (lds_col ^ (4 * (k & 1)))];
-                cu[k] = SR ? (uint32_t)lds_u[row][cc] : 0u;
             }
-            const uint32_t ecol = (uint32_t)(cc * cur.Rg + 16 * rs);   // lane's first element, relative
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                cu[j] = SR ? (uint32_t)lu[(16 * rs + 2 * j) * kTile + cc] |
+                                 ((uint32_t)lu[(16 * rs + 2 * j + 1) * kTile + cc] << 16)
+                           : 0u;
             if (OUTER == kOuter1D) {
-                // columnwise 1D groups: [cols, Rg / obs] per group
-                const int gpc = cur.Rg / obs;
-                const rsrc_t ro =
-                    make_rsrc(a.col_outer ? a.col_outer + (int64_t)cur.r0 * cols / obs +
-                                                (int64_t)cur.c0 * gpc + cur.lrow0 / obs
-                                          : nullptr);
-                const uint32_t oo = (uint32_t)(cc * gpc + (16 * rs) / obs) * 4u;
+                const bool actc = (cc < cur.cols_valid) && (16 * rs < cur.rows_valid);
                 float s_col;
                 if (GIVEN) {
-                    s_col = buf_load_f32(ro, actc ? oo : kOff);
+                    // columnwise 1D groups: [cols, Rg / obs] per group
+                    const int gpc = cur.Rg / obs;
+                    const rsrc_t rco =
+                        make_rsrc(a.col_outer ? a.col_outer + (int64_t)cur.r0 * cols / obs +
+                                                    (int64_t)cur.c0 * gpc + cur.lrow0 / obs
+                                              : nullptr);
+                    const uint32_t oo = (uint32_t)(cc * gpc + (16 * rs) / obs) * 4u;
+                    s_col = buf_load_f32(rco, actc ? oo : kOff);
                     if (!actc) s_col = 1.0f;
                 } else {
                     s_col = outer_scale(quad_max(max_abs16(cv), a.obs16), den);
-                    buf_store_u32(ro, (actc && (rs % a.obs16) == 0) ? oo : kOff, __float_as_uint(s_col));
+                    co.outer = s_col;
                 }
                 float cn[16];
                 normalize16(cv, s_col, outer_inv(s_col), cn, true);
@@ -410,13 +481,166 @@ void k_tile(TileArgs a)
                 for (int k = 0; k < 16; ++k) cv[k] = cn[k];
             }
             BlockScale<BIAS> sc;
-            const uint2 packed = quant16<BIAS, SR>(cv, cu, rtab, sc);
-            buf_store8(make_rsrc(a.col_codes + cur.ce_base / 2), actc ? ecol / 2u : kOff, packed);
-            buf_store_u8(make_rsrc(a.col_scales + cur.ce_base / 16), actc ? ecol / 16u : kOff, sc.code);
+            co.codes = quant16<BIAS, SR>(cv, cu, rtab, sc);
+            co.scale = sc.code;
         }
-        if (!has_next) break;
-        cur = nxt;
-        in = nin;
+        ++iter;
+    };
+
+    // 1D outer scales of a tile pair: with 64-element groups one lane per line
+    // holds both tiles' values (stored as one 8-byte run); smaller groups are
+    // stored lane by lane.
+    auto store_outer_pair = [&](rsrc_t rb, uint32_t off_a, uint32_t off_b, bool lead, bool ok_a, bool ok_b,
+                                const DirOut& A, const DirOut& B) {
+        const bool wide = a.obs16 == 4;
+        buf_store8(rb, (wide && lead && ok_a && ok_b) ? off_a : kOff,
+                   make_uint2(__float_as_uint(A.outer), __float_as_uint(B.outer)));
+        buf_store_u32(rb, ((wide && ok_a && !ok_b) || (!wide && ok_a)) && lead ? off_a : kOff,
+                      __float_as_uint(A.outer));
+        buf_store_u32(rb, (!wide && lead && ok_b) ? off_b : kOff, __float_as_uint(B.outer));
+    };
+
+    // Row runs of tiles (sub, sub + 1) of the current super-tile.
+    auto emit_rows = [&](const Tile& ta, const Tile& tb, const DirOut& A, const DirOut& B, bool enable) {
+        const int nvalid = ta.cols_valid / 16 + tb.cols_valid / 16;
+        const bool line_ok = enable && r < ta.rows_valid;
+        const rsrc_t rc = make_rsrc(a.row_codes ? a.row_codes + ta.e_base / 2 : nullptr);
+        const rsrc_t rsc = make_rsrc(a.row_scales ? a.row_scales + ta.e_base / 16 : nullptr);
+        store_pair(stage, r, sg, A, B, line_ok, nvalid, rc, (uint32_t)(r * cols) / 2u, rsc,
+                   (uint32_t)(r * cols) / 16u);
+        if (OUTER == kOuter1D && !GIVEN) {
+            const int gpr = cols / obs;
+            const rsrc_t rb =
+                make_rsrc(a.row_outer ? a.row_outer + (int64_t)ta.grow0 * gpr + ta.c0 / obs : nullptr);
+            const uint32_t off_a = (uint32_t)(r * gpr + (16 * sg) / obs) * 4u;
+            store_outer_pair(rb, off_a, off_a + (uint32_t)(kTile / obs) * 4u, (sg % a.obs16) == 0,
+                             line_ok && 16 * sg < ta.cols_valid, line_ok && 16 * sg < tb.cols_valid, A, B);
+        }
+    };
+
+    // Column runs of tiles (sub, sub + 2) of the current super-tile.
+    auto emit_cols = [&](const Tile& ta, const Tile& tb, const DirOut& A, const DirOut& B, bool enable) {
+        const int nvalid = ta.rows_valid / 16 + tb.rows_valid / 16;
+        const bool line_ok = enable && cc < ta.cols_valid;
+        const uint32_t ecol = (uint32_t)(cc * ta.Rg);   // lane's column, relative to the run start
+        store_pair(stage, cc, rs, A, B, line_ok, nvalid, make_rsrc(a.col_codes + ta.ce_base / 2), ecol / 2u,
+                   make_rsrc(a.col_scales + ta.ce_base / 16), ecol / 16u);
+        if (OUTER == kOuter1D && !GIVEN) {
+            const int gpc = ta.Rg / obs;
+            const rsrc_t rb = make_rsrc(a.col_outer ? a.col_outer + (int64_t)ta.r0 * cols / obs +
+                                                          (int64_t)ta.c0 * gpc + ta.lrow0 / obs
+                                                    : nullptr);
+            const uint32_t off_a = (uint32_t)(cc * gpc + (16 * rs) / obs) * 4u;
+            store_outer_pair(rb, off_a, off_a + (uint32_t)(kTile / obs) * 4u, (rs % a.obs16) == 0,
+                             line_ok && 16 * rs < ta.rows_valid, line_ok && 16 * rs < tb.rows_valid, A, B);
+        }
+    };
+
+    // A tile stored on its own: 8 code bytes and a scale byte per lane in
+    // each direction, and the lane's 1D outer scale.
+    auto emit_single = [&](const Tile& t, const DirOut& ro, const DirOut& co) {
+        const bool act = r < t.rows_valid && 16 * sg < t.cols_valid;
+        const uint32_t erow_t = (uint32_t)(r * cols + 16 * sg);
+        buf_store8(make_rsrc(a.row_codes ? a.row_codes + t.e_base / 2 : nullptr), act ? erow_t / 2u : kOff, ro.codes);
+        buf_store_u8(make_rsrc(a.row_scales ? a.row_scales + t.e_base / 16 : nullptr), act ? erow_t / 16u : kOff,
+                     ro.scale);
+        if (OUTER == kOuter1D && !GIVEN) {
+            const int gpr = cols / obs;
+            const rsrc_t rb =
+                make_rsrc(a.row_outer ? a.row_outer + (int64_t)t.grow0 * gpr + t.c0 / obs : nullptr);
+            const uint32_t oo = (uint32_t)(r * gpr + (16 * sg) / obs) * 4u;
+            buf_store_u32(rb, (act && (sg % a.obs16) == 0) ? oo : kOff, __float_as_uint(ro.outer));
+        }
+        if (COLS) {
+            const bool actc = (cc < t.cols_valid) && (16 * rs < t.rows_valid);
+            const uint32_t ecol = (uint32_t)(cc * t.Rg + 16 * rs);
+            buf_store8(make_rsrc(a.col_codes + t.ce_base / 2), actc ? ecol / 2u : kOff, co.codes);
+            buf_store_u8(make_rsrc(a.col_scales + t.ce_base / 16), actc ? ecol / 16u : kOff, co.scale);
+            if (OUTER == kOuter1D && !GIVEN) {
+                const int gpc = t.Rg / obs;
+                const rsrc_t rb = make_rsrc(a.col_outer ? a.col_outer + (int64_t)t.r0 * cols / obs +
+                                                              (int64_t)t.c0 * gpc + t.lrow0 / obs
+                                                        : nullptr);
+                const uint32_t oo = (uint32_t)(cc * gpc + (16 * rs) / obs) * 4u;
+                buf_store_u32(rb, (actc && (rs % a.obs16) == 0) ? oo : kOff, __float_as_uint(co.outer));
+            }
+        }
+    };
+
+    TileWalk st = walk;
+    if constexpr (tile_unrolled<OUTER, SR, EF>()) {
+        // RTNE: the four tiles of a super-tile as straight-line code; the row
+        // runs of tiles (0, 1) and (2, 3) are stored after tiles 1 and 3, the
+        // column runs of tiles (0, 2) and (1, 3) after tiles 2 and 3.
+        for (;;) {
+            const bool has_next = st.t + W < slice_end;
+            TileWalk nst = st;
+            if (has_next) walk_next(a, nst, W);
+            DirOut r0o, c0o, r1o, c1o, r2o, c2o, r3o, c3o;
+            TileInput<EF> nin;
+
+            load_tile_input<EF>(a, make_tile(a, st, 1), true, r, sg, nin);
+            tile_body(make_tile(a, st, 0), in, r0o, c0o);
+            in = nin;
+            __builtin_amdgcn_sched_barrier(0);
+            load_tile_input<EF>(a, make_tile(a, st, 2), true, r, sg, nin);
+            tile_body(make_tile(a, st, 1), in, r1o, c1o);
+            emit_rows(make_tile(a, st, 0), make_tile(a, st, 1), r0o, r1o, true);
+            in = nin;
+            __builtin_amdgcn_sched_barrier(0);
+            load_tile_input<EF>(a, make_tile(a, st, 3), true, r, sg, nin);
+            tile_body(make_tile(a, st, 2), in, r2o, c2o);
+            if (COLS) emit_cols(make_tile(a, st, 0), make_tile(a, st, 2), c0o, c2o, true);
+            in = nin;
+            __builtin_amdgcn_sched_barrier(0);
+            load_tile_input<EF>(a, make_tile(a, nst, 0), has_next, r, sg, nin);
+            tile_body(make_tile(a, st, 3), in, r3o, c3o);
+            emit_rows(make_tile(a, st, 2), make_tile(a, st, 3), r2o, r3o, true);
+            if (COLS) emit_cols(make_tile(a, st, 1), make_tile(a, st, 3), c1o, c3o, true);
+            if (!has_next) break;
+            st = nst;
+            in = nin;
+        }
+    } else {
+        // Stochastic rounding, a residual or 1D outer groups need about twice
+        // the registers, so the tiles run as a loop, one per iteration; every
+        // iteration issues the same memory instructions (on iterations without
+        // a finished pair the pair stores are issued fully masked).  With 1D
+        // outer groups each tile is stored on its own (no results are held
+        // across iterations).
+        constexpr bool kPair = OUTER != kOuter1D;
+        int sub = 0;
+        DirOut row_a = {}, col_a0 = {}, col_a1 = {};   // results waiting for their partner tile
+        for (;;) {
+            const Tile cur = make_tile(a, st, sub);
+            const bool last_sub = sub == 3;
+            const bool has_next = !last_sub || st.t + W < slice_end;
+            TileWalk nst = st;
+            if (last_sub && has_next) walk_next(a, nst, W);
+            const int nsub = (sub + 1) & 3;
+            TileInput<EF> nin;
+            load_tile_input<EF>(a, make_tile(a, nst, nsub), has_next, r, sg, nin);
+
+            DirOut ro, co;
+            tile_body(cur, in, ro, co);
+            const bool odd = (sub & 1) != 0;
+            if (kPair) {
+                emit_rows(make_tile(a, st, sub & 2), make_tile(a, st, sub | 1), row_a, ro, odd);
+                if (COLS) {
+                    emit_cols(make_tile(a, st, sub & 1), make_tile(a, st, (sub & 1) | 2), odd ? col_a1 : col_a0, co,
+                              sub >= 2);
+                    if (sub == 0) col_a0 = co;
+                    if (sub == 1) col_a1 = co;
+                }
+                if (!odd) row_a = ro;
+            } else {
+                emit_single(cur, ro, co);
+            }
+            if (!has_next) break;
+            st = nst;
+            sub = nsub;
+            in = nin;
+        }
     }
 }
 

@@ -34,7 +34,8 @@ struct RowArgs {
     int32_t outer_given;     // 1: read outer instead of computing it
 };
 
-// Tile (64 x 64) parameters: cast-transpose, grouped cast-transpose, and the
+// Tile parameters (64 x 64 tiles walked as 2 x 2 super-tiles): cast-transpose,
+// grouped cast-transpose, and the
 // rowwise-only 2D outer mode.
 struct TileArgs {
     const uint16_t* x;
@@ -52,12 +53,12 @@ struct TileArgs {
     int32_t obs16;           // 1D: obs / 16 (1, 2, 4); 2D: 4
     int32_t outer_given;
     int32_t ngroups;
-    int32_t tiles_c;         // ceil(cols / 64)
-    int32_t total_tiles;
-    int32_t per_xcd;         // tiles in each XCD's contiguous slice
+    int32_t tiles_c;         // super-tile (128 x 128) columns: ceil(cols / 128)
+    int32_t total_tiles;     // super-tiles in the launch
+    int32_t per_xcd;         // super-tiles in each XCD's contiguous slice
     int32_t wgs_per_xcd;     // persistent workgroups per XCD (grid = 8 * wgs_per_xcd)
     int32_t row0[kMaxGroupsPerLaunch + 1];   // prefix rows of the groups
-    int32_t tile0[kMaxGroupsPerLaunch + 1];  // prefix tile counts of the groups
+    int32_t tile0[kMaxGroupsPerLaunch + 1];  // prefix super-tile counts of the groups
 };
 
 enum OuterKind { kOuterNone = 0, kOuterTensor = 1, kOuter1D = 2, kOuter2D = 3 };

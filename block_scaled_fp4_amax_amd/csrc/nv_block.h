@@ -107,7 +107,7 @@ __device__ __forceinline__ uint2 codes16_rne(const float (&vn)[16], double rd)
 // a tiny quotient matters (zero never rounds up, any positive t can), so
 // quotients that may leave the normal range are recomputed by IEEE division.
 template <int BIAS>
-__device__ __forceinline__ uint2 codes16_sr(const float (&vn)[16], const uint32_t (&u)[16], const BlockScale<BIAS>& s)
+__device__ __forceinline__ uint2 codes16_sr(const float (&vn)[16], const uint32_t (&u)[8], const BlockScale<BIAS>& s)
 {
     float t[16];
     bool slow = false;
@@ -124,7 +124,7 @@ __device__ __forceinline__ uint2 codes16_sr(const float (&vn)[16], const uint32_
     uint32_t lo = 0, hi = 0;
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-        const uint32_t code = e2m1_sr(t[k], (float)u[k]) | ((__float_as_uint(vn[k]) >> 31) << 3);
+        const uint32_t code = e2m1_sr(t[k], sr_var(u, k)) | ((__float_as_uint(vn[k]) >> 31) << 3);
         if (k < 8) lo |= code << (4 * k);
         else hi |= code << (4 * (k - 8));
     }
