@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU oracle time for the baseline")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 256 MiB device copy (counter calibration) and exit")
-    ap.add_argument("--only", default=None, help="time a single workload (C1..C5) and exit")
+    ap.add_argument("--only", default=None, help="time a single workload (nv_tensorwise_qdq_256, nv_2d_cast_transpose_4096, mx_fake_quant_8192, amd_1d_sr_cast_transpose_16384x2880, nv_grouped_sr_ef_32x2880) and exit")
     ap.add_argument("--eager", action="store_true", help="launch every step from the host (no graph replay)")
     ap.add_argument("--pmc-summary", nargs=5, metavar=("KEY", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     default=None,
@@ -56,9 +56,9 @@ def parse():
 
 
 # ---------------------------------------------------------------------- helpers
-KERNEL_NAME_PREFIX = {"C1": "fp4q::(anonymous namespace)::k_nv_rows", "C2": "fp4q::(anonymous namespace)::k_tile",
-                      "C3": "fp4q::(anonymous namespace)::k_mx_qdq", "C4": "fp4q::(anonymous namespace)::k_tile",
-                      "C5": "fp4q::(anonymous namespace)::k_tile"}
+KERNEL_NAME_PREFIX = {"nv_tensorwise_qdq_256": "fp4q::(anonymous namespace)::k_nv_rows", "nv_2d_cast_transpose_4096": "fp4q::(anonymous namespace)::k_tile",
+                      "mx_fake_quant_8192": "fp4q::(anonymous namespace)::k_mx_qdq", "amd_1d_sr_cast_transpose_16384x2880": "fp4q::(anonymous namespace)::k_tile",
+                      "nv_grouped_sr_ef_32x2880": "fp4q::(anonymous namespace)::k_tile"}
 COPY_PROBE_BYTES = 256 << 20
 
 
@@ -184,9 +184,9 @@ def n_sets_for(bytes_per_set, min_total=1 << 30, cap=64):
 
 
 # ---------------------------------------------------------------------- workloads
-def make_c2(torch, fq, W):
+def make_cast_transpose_2d(torch, fq, W):
     R = C = 4096
-    x = W.c2_weight()
+    x = W.weight_4096_outlier_cols()
     cfg = fq.make_cfg(format="nvfp4", two_level="outer_block", outer_block_size=64, outer_2d=True)
     alg = R * C * 2 + 2 * (R * C // 2) + 2 * (R * C // 16) + (R // 64) * (C // 64) * 4
     nset = n_sets_for(alg)
@@ -207,13 +207,13 @@ def make_c2(torch, fq, W):
                                   torch.cuda.current_stream().cuda_stream)
         if st:
             raise fq.Fp4Error(st, "fp4_cast_transpose")
-    return Timed("C2", "NVFP4 2D 64x64 outer, E4M3/16, RTNE, fused cast-transpose 4096x4096 bf16", alg, sets, launch,
-                 "k_tile<7, 3, false, true>")
+    return Timed("nv_2d_cast_transpose_4096", "NVFP4 2D 64x64 outer, E4M3/16, RTNE, fused cast-transpose 4096x4096 bf16", alg, sets, launch,
+                 "k_tile<7, 3, false, true, false, false, false>")
 
 
-def make_c3(torch, fq, W):
+def make_mx_fake_quant(torch, fq, W):
     R = C = 8192
-    x = W.c3_weight()
+    x = W.mx_weight_8192_edges()
     cfg = fq.make_cfg(format="mxfp4")
     alg = R * C * 2 * 2
     nset = n_sets_for(alg, cap=8)
@@ -226,12 +226,12 @@ def make_c3(torch, fq, W):
                        torch.cuda.current_stream().cuda_stream)
         if st:
             raise fq.Fp4Error(st, "fp4_qdq")
-    return Timed("C3", "MXFP4 1x32 fake-quant 8192x8192 bf16 -> bf16", alg, sets, launch, "k_mx_qdq<true, true, false>")
+    return Timed("mx_fake_quant_8192", "MXFP4 1x32 fake-quant 8192x8192 bf16 -> bf16", alg, sets, launch, "k_mx_qdq<true, true, false>")
 
 
-def make_c4(torch, fq, W):
+def make_cast_transpose_1d_sr(torch, fq, W):
     R, C = 16384, 2880
-    x = W.c4_activations()
+    x = W.activations_16384x2880()
     cfg = fq.make_cfg(format="amdfp4", two_level="outer_block", outer_block_size=64, rounding="stochastic", seed=7,
                       step=3)
     alg = R * C * 2 + 2 * (R * C // 2) + 2 * (R * C // 16) + (R * (C // 64) + C * (R // 64)) * 4
@@ -253,13 +253,13 @@ def make_c4(torch, fq, W):
                                   None, 0, torch.cuda.current_stream().cuda_stream)
         if st:
             raise fq.Fp4Error(st, "fp4_cast_transpose")
-    return Timed("C4", "AMD-FP4 1D 1x64 outer, UE5M3/16, SR, cast-transpose 16384x2880 bf16", alg, sets, launch,
-                 "k_tile<15, 2, true, true>")
+    return Timed("amd_1d_sr_cast_transpose_16384x2880", "AMD-FP4 1D 1x64 outer, UE5M3/16, SR, cast-transpose 16384x2880 bf16", alg, sets, launch,
+                 "k_tile<15, 2, true, true, false, false, false>")
 
 
-def make_c5(torch, fq, W):
+def make_grouped_sr_ef(torch, fq, W):
     E, R, C = 32, 2880, 2880
-    w = W.c5_experts()
+    w = W.experts_32x2880()
     cfg = fq.make_cfg(format="nvfp4", two_level="outer_block", outer_block_size=64, outer_2d=True,
                       rounding="stochastic", seed=5, step=0)
     n = E * R * C
@@ -278,13 +278,13 @@ def make_c5(torch, fq, W):
         if st:
             raise fq.Fp4Error(st, "fp4_cast_transpose_grouped")
     # the working set (~3 GB per step) is far beyond the last-level cache: one set
-    return Timed("C5", "grouped NVFP4 2D 64x64 outer, E4M3/16, SR + in-place EF residual, 32 x 2880x2880", alg, [s],
-                 launch, "k_tile<7, 3, true, true>")
+    return Timed("nv_grouped_sr_ef_32x2880", "grouped NVFP4 2D 64x64 outer, E4M3/16, SR + in-place EF residual, 32 x 2880x2880", alg, [s],
+                 launch, "k_tile<7, 3, true, true, true, false, false>")
 
 
-def make_c1(torch, fq, W):
+def make_tensorwise_qdq(torch, fq, W):
     R = C = 256
-    x = W.c1_tensor()
+    x = W.tensorwise_input_256()
     cfg = fq.make_cfg(format="nvfp4", two_level="tensorwise")
     alg = R * C * 2 + R * C // 2 + R * C // 16 + 4 + R * C * 2
     ws = torch.empty(fq.fp4q_workspace_bytes(cfg, R, C), dtype=torch.uint8, device="cuda")
@@ -300,8 +300,8 @@ def make_c1(torch, fq, W):
                        torch.cuda.current_stream().cuda_stream)
         if st:
             raise fq.Fp4Error(st, "fp4_qdq")
-    return Timed("C1", "NVFP4 tensorwise QDQ 256x256 (3 launches: amax, scale, quantise)", alg, [s], launch,
-                 "k_nv_rows<7, 1, false>")
+    return Timed("nv_tensorwise_qdq_256", "NVFP4 tensorwise QDQ 256x256 (3 launches: amax, scale, quantise)", alg, [s], launch,
+                 "k_nv_rows<7, 1, false, false>")
 
 
 # ---------------------------------------------------------------------- CPU baseline
@@ -309,7 +309,7 @@ def cpu_baseline(W, min_seconds):
     """The oracle, untuned, on the host cores: the full headline tensor,
     repeated until at least `min_seconds` have elapsed."""
     from oracle import ref
-    x = W.c2_weight()
+    x = W.weight_4096_outlier_cols()
     R = C = 4096
     alg = R * C * 2 + 2 * (R * C // 2) + 2 * (R * C // 16) + (R // 64) * (C // 64) * 4
     ref.nv_quantize(x[:256], two_level="outer", obs=64, outer_2d=True, cols=True, want_y=False)  # warm
@@ -356,7 +356,7 @@ def main():
         return
 
     if args.only:
-        mk = {"C1": make_c1, "C2": make_c2, "C3": make_c3, "C4": make_c4, "C5": make_c5}[args.only]
+        mk = {"nv_tensorwise_qdq_256": make_tensorwise_qdq, "nv_2d_cast_transpose_4096": make_cast_transpose_2d, "mx_fake_quant_8192": make_mx_fake_quant, "amd_1d_sr_cast_transpose_16384x2880": make_cast_transpose_1d_sr, "nv_grouped_sr_ef_32x2880": make_grouped_sr_ef}[args.only]
         w = mk(torch, fq, W)
         ms = run_timed(torch, w, args.steps, args.warmup, graph=not args.eager)
         per = ms / args.steps
@@ -364,18 +364,18 @@ def main():
                           "GB/s": w.bytes / (per * 1e-3) / 1e9, "frac": w.bytes / (per * 1e-3) / 1e9 / HBM_PEAK_GBS}))
         return
 
-    w = make_c2(torch, fq, W)
+    w = make_cast_transpose_2d(torch, fq, W)
     print("# headline %s: %d buffer sets, %d warmup + %d timed launches" % (w.name, len(w.sets), args.warmup, args.steps),
           file=sys.stderr, flush=True)
     ms = run_timed(torch, w, args.steps, args.warmup, graph=not args.eager)
     per_ms = ms / args.steps
     gbs = w.bytes * args.steps / (ms * 1e-3) / 1e9
-    traffic = measured_traffic("C2")
+    traffic = measured_traffic("nv_2d_cast_transpose_4096")
     line = {
         "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(per_ms, 6), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": "C2: " + w.desc, "rows": 4096, "cols": 4096, "format": "nvfp4",
+        "config": {"workload": w.desc, "rows": 4096, "cols": 4096, "format": "nvfp4",
                    "two_level": "outer_block 2D 64x64", "inner": "E4M3/16", "rounding": "rtne",
                    "outputs": "rowwise+columnwise codes and scales, shared outer", "source": "bf16 N(0,0.02), 0.5% cols x1000",
                    "algorithmic_bytes_per_step": w.bytes, "buffer_sets": len(w.sets)},
@@ -386,7 +386,7 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_extra:
         extra = {}
-        for mk, steps in ((make_c3, 400), (make_c4, 400), (make_c5, 20), (make_c1, 400)):
+        for mk, steps in ((make_mx_fake_quant, 400), (make_cast_transpose_1d_sr, 400), (make_grouped_sr_ef, 20), (make_tensorwise_qdq, 400)):
             e = mk(torch, fq, W)
             print("# extra %s" % e.name, file=sys.stderr, flush=True)
             ems = run_timed(torch, e, steps, min(20, steps))

@@ -29,15 +29,15 @@ def from_bf16(b):
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
-# ------------------------------------------------------------------ C1
-def c1_tensor(seed=0, rows=256, cols=256):
+# ------------------------------------------------------------------ NVFP4 tensorwise QDQ, 256 x 256
+def tensorwise_input_256(seed=0, rows=256, cols=256):
     """NVFP4 tensorwise QDQ input: N(0, 1)."""
     rng = np.random.default_rng(seed)
     return to_bf16(rng.standard_normal((rows, cols), dtype=np.float32))
 
 
-# ------------------------------------------------------------------ C2
-def c2_weight(seed=2, rows=4096, cols=4096, outlier_frac=0.005, factor=1000.0):
+# ------------------------------------------------------------------ NVFP4 2D-outer cast-transpose, 4096 x 4096
+def weight_4096_outlier_cols(seed=2, rows=4096, cols=4096, outlier_frac=0.005, factor=1000.0):
     """Weight N(0, 0.02) with round(0.5% of cols) seeded columns scaled x1000."""
     rng = np.random.default_rng(seed)
     w = rng.standard_normal((rows, cols), dtype=np.float32) * np.float32(0.02)
@@ -47,13 +47,13 @@ def c2_weight(seed=2, rows=4096, cols=4096, outlier_frac=0.005, factor=1000.0):
     return to_bf16(w)
 
 
-# ------------------------------------------------------------------ C3
+# ------------------------------------------------------------------ MXFP4 fake-quant, 8192 x 8192
 TINY_BF16 = np.array([0x0000, 0x0040, 0x0020, 0x0001, 0x0060, 0x0080, 0x0100], np.uint16)
 CAP_BF16 = np.array([0x7F3F, 0x7F40, 0x7F41], np.uint16)
 MID_VALUES = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], np.float32)
 
 
-def c3_weight(seed=3, rows=8192, cols=8192, std=0.02):
+def mx_weight_8192_edges(seed=3, rows=8192, cols=8192, std=0.02):
     """MXFP4 fake-quant input: N(0, 0.02) with, in every group of 1024
     consecutive 1x32 blocks, ten seeded blocks rewritten: one single +-inf, one
     single NaN, one block of tiny values (+-0, 2^-127, 2^-128, 2^-133,
@@ -96,8 +96,8 @@ def c3_weight(seed=3, rows=8192, cols=8192, std=0.02):
     return x
 
 
-# ------------------------------------------------------------------ C4
-def c4_activations(seed=4, rows=16384, cols=2880, sigma=2.0, chan_frac=0.001, chan_factor=500.0):
+# ------------------------------------------------------------------ AMD-FP4 1D-outer SR cast-transpose, 16384 x 2880
+def activations_16384x2880(seed=4, rows=16384, cols=2880, sigma=2.0, chan_frac=0.001, chan_factor=500.0):
     """Activations: N(0, 1) x per-token lognormal(0, 2) x500 on round(0.1% of
     cols) seeded channels."""
     rng = np.random.default_rng(seed)
@@ -108,8 +108,8 @@ def c4_activations(seed=4, rows=16384, cols=2880, sigma=2.0, chan_frac=0.001, ch
     return to_bf16(a)
 
 
-# ------------------------------------------------------------------ C5
-def c5_experts(seed=5, experts=32, rows=2880, cols=2880, std=0.02, outlier_rows=2, factor=200.0):
+# ------------------------------------------------------------------ grouped NVFP4 SR + EF, 32 x 2880 x 2880
+def experts_32x2880(seed=5, experts=32, rows=2880, cols=2880, std=0.02, outlier_rows=2, factor=200.0):
     """Stacked MoE expert weights [experts * rows, cols]: N(0, 0.02), two seeded
     rows per expert x200."""
     rng = np.random.default_rng(seed)
@@ -119,21 +119,21 @@ def c5_experts(seed=5, experts=32, rows=2880, cols=2880, std=0.02, outlier_rows=
     return to_bf16(w.reshape(experts * rows, cols))
 
 
-def c5_update(t, shape, std=1e-4):
+def expert_update(t, shape, std=1e-4):
     """Weight update of step t: N(0, 1e-4) float32, seeded 500 + t."""
     rng = np.random.default_rng(500 + t)
     return rng.standard_normal(shape, dtype=np.float32) * np.float32(std)
 
 
-def c5_apply_update(w_bits, dw):
+def apply_expert_update(w_bits, dw):
     """W_{t+1} = bf16(f32(W_t) + dW_t); independent of the quantiser output."""
     return to_bf16(from_bf16(w_bits) + dw)
 
 
 CONFIGS = {
-    "C1": dict(name="nvfp4_tensorwise_qdq_256x256", rows=256, cols=256),
-    "C2": dict(name="nvfp4_outer2d64_cast_transpose_4096x4096", rows=4096, cols=4096),
-    "C3": dict(name="mxfp4_fake_quant_8192x8192", rows=8192, cols=8192),
-    "C4": dict(name="amdfp4_outer1d64_sr_cast_transpose_16384x2880", rows=16384, cols=2880),
-    "C5": dict(name="nvfp4_grouped32_outer2d64_sr_ef_2880x2880", rows=32 * 2880, cols=2880),
+    "nv_tensorwise_qdq_256": dict(name="nvfp4_tensorwise_qdq_256x256", rows=256, cols=256),
+    "nv_2d_cast_transpose_4096": dict(name="nvfp4_outer2d64_cast_transpose_4096x4096", rows=4096, cols=4096),
+    "mx_fake_quant_8192": dict(name="mxfp4_fake_quant_8192x8192", rows=8192, cols=8192),
+    "amd_1d_sr_cast_transpose_16384x2880": dict(name="amdfp4_outer1d64_sr_cast_transpose_16384x2880", rows=16384, cols=2880),
+    "nv_grouped_sr_ef_32x2880": dict(name="nvfp4_grouped32_outer2d64_sr_ef_2880x2880", rows=32 * 2880, cols=2880),
 }

@@ -114,18 +114,18 @@ def test_mx_shapes_and_strides(shape, ld):
     same(host(q["scales"], np.uint8), s, "quantize scales")
 
 
-def test_mx_c3_full_size():
-    x = W.c3_weight()
+def test_mx_fake_quant_8192_full_size():
+    x = W.mx_weight_8192_edges()
     c, s, y = ref.mx_qdq(x)
     xd = dev(x)
     out = fq.fp4_qdq(xd, fq.make_cfg(format="mxfp4"))
-    same(host(out["y"], np.uint16), y, "C3 y")
+    same(host(out["y"], np.uint16), y, "MXFP4 y")
     out2 = fq.fp4_qdq(xd, fq.make_cfg(format="mxfp4"), with_codes=True)
-    same(host(out2["y"], np.uint16), y, "C3 y (with codes)")
-    same(host(out2["codes"], np.uint8), c, "C3 codes")
-    same(host(out2["scales"], np.uint8), s, "C3 scales")
+    same(host(out2["y"], np.uint16), y, "MXFP4 y (with codes)")
+    same(host(out2["codes"], np.uint8), c, "MXFP4 codes")
+    same(host(out2["scales"], np.uint8), s, "MXFP4 scales")
     yd = fq.fp4_dequantize(out2["codes"], out2["scales"], None, 8192, 8192, fq.make_cfg(format="mxfp4"))
-    same(host(yd, np.uint16), y, "C3 dequantize")
+    same(host(yd, np.uint16), y, "MXFP4 dequantize")
 
 
 # =============================================================== NVFP4 / AMD-FP4 rowwise
@@ -176,15 +176,15 @@ def test_rowwise_quantize_and_qdq(case):
         same(host(zd2, np.float32), zo, "quantize residual")
 
 
-def test_c1_full_size():
-    x = W.c1_tensor()
+def test_tensorwise_qdq_256_full_size():
+    x = W.tensorwise_input_256()
     g, o = cfgs("nvfp4", "tensorwise")
     want = ref.nv_quantize(x, **o)
     out = fq.fp4_qdq(dev(x), g, with_codes=True)
-    same(host(out["y"], np.uint16), want["row_y"], "C1 y")
-    same(host(out["codes"], np.uint8), want["row_codes"], "C1 codes")
-    same(host(out["scales"], np.uint8), want["row_scales"], "C1 scales")
-    same(host(out["outer"], np.float32), want["row_outer"], "C1 global scale")
+    same(host(out["y"], np.uint16), want["row_y"], "tensorwise y")
+    same(host(out["codes"], np.uint8), want["row_codes"], "tensorwise codes")
+    same(host(out["scales"], np.uint8), want["row_scales"], "tensorwise scales")
+    same(host(out["outer"], np.float32), want["row_outer"], "tensorwise global scale")
 
 
 def test_rowwise_2d_outer_qdq():
@@ -333,30 +333,30 @@ def test_dequantize_nv_all_outer_kinds():
 
 
 # =============================================================== full-size workloads
-def test_c2_full_size_cast_transpose():
-    x = W.c2_weight()
+def test_cast_transpose_2d_4096_full_size():
+    x = W.weight_4096_outlier_cols()
     g, o = cfgs("nvfp4", "outer", 64, True)
     want = ref.nv_quantize(x, cols=True, want_y=False, **o)
     out = fq.fp4_cast_transpose(dev(x), g)
     for k in ("row_codes", "row_scales", "col_codes", "col_scales"):
-        same(host(out[k], np.uint8), want[k], "C2 " + k)
-    same(host(out["row_outer"], np.float32), want["row_outer"], "C2 outer")
+        same(host(out[k], np.uint8), want[k], "2D cast-transpose " + k)
+    same(host(out["row_outer"], np.float32), want["row_outer"], "2D cast-transpose outer")
 
 
-def test_c4_full_size_cast_transpose_sr():
-    x = W.c4_activations()
+def test_cast_transpose_1d_sr_16384x2880_full_size():
+    x = W.activations_16384x2880()
     g, o = cfgs("amdfp4", "outer", 64, False, True, seed=7, step=3)
     want = ref.nv_quantize(x, cols=True, want_y=False, **o)
     out = fq.fp4_cast_transpose(dev(x), g)
     for k in ("row_codes", "row_scales", "col_codes", "col_scales"):
-        same(host(out[k], np.uint8), want[k], "C4 " + k)
-    same(host(out["row_outer"], np.float32), want["row_outer"], "C4 row outer")
-    same(host(out["col_outer"], np.float32), want["col_outer"], "C4 col outer")
+        same(host(out[k], np.uint8), want[k], "1D SR cast-transpose " + k)
+    same(host(out["row_outer"], np.float32), want["row_outer"], "1D SR cast-transpose row outer")
+    same(host(out["col_outer"], np.float32), want["col_outer"], "1D SR cast-transpose col outer")
 
 
-def test_c5_grouped_sr_ef_four_steps():
+def test_grouped_sr_ef_32x2880_four_steps():
     E, R, C = 32, 2880, 2880
-    w = W.c5_experts()
+    w = W.experts_32x2880()
     g = fq.make_cfg(format="nvfp4", two_level="outer_block", outer_block_size=64, outer_2d=True, rounding="stochastic",
                     seed=5)
     zd = torch.zeros((E * R, C), dtype=torch.float32, device="cuda")
@@ -374,13 +374,13 @@ def test_c5_grouped_sr_ef_four_steps():
         for e in sample:
             want = ref.nv_quantize(w[e * R:(e + 1) * R], two_level="outer", obs=64, outer_2d=True, stochastic=True,
                                    seed=5, step=t, index_base=e * R * C, residual=z_or[e], cols=True, want_y=False)
-            same(rc[e], want["row_codes"], "C5 step %d expert %d row codes" % (t, e))
-            same(rs[e], want["row_scales"], "C5 step %d expert %d row scales" % (t, e))
-            same(cc[e], want["col_codes"], "C5 step %d expert %d col codes" % (t, e))
-            same(cs[e], want["col_scales"], "C5 step %d expert %d col scales" % (t, e))
-            same(ro[e], want["row_outer"], "C5 step %d expert %d outer" % (t, e))
-            same(zg[e], z_or[e], "C5 step %d expert %d residual" % (t, e))
-        w = W.c5_apply_update(w, W.c5_update(t, w.shape))
+            same(rc[e], want["row_codes"], "grouped step %d expert %d row codes" % (t, e))
+            same(rs[e], want["row_scales"], "grouped step %d expert %d row scales" % (t, e))
+            same(cc[e], want["col_codes"], "grouped step %d expert %d col codes" % (t, e))
+            same(cs[e], want["col_scales"], "grouped step %d expert %d col scales" % (t, e))
+            same(ro[e], want["row_outer"], "grouped step %d expert %d outer" % (t, e))
+            same(zg[e], z_or[e], "grouped step %d expert %d residual" % (t, e))
+        w = W.apply_expert_update(w, W.expert_update(t, w.shape))
 
 
 def test_grouped_uneven_groups_equal_single_calls():
