@@ -13,9 +13,11 @@
 // E2M1 encode of x / 2^k and the decode of +-G[m] * 2^k are gfx950's scaled
 // FP4 conversions, which match the RTNE / satfinite / signed-zero rules
 // exactly for every bf16 input and every k in [-126, 125] (checked
-// exhaustively on the device).  Each workgroup streams kUnroll * 256 chunks with
-// all loads issued before any arithmetic, so a wave keeps kUnroll 16-byte
-// requests in flight.  The kernel is HBM-bound; no LDS, no MFMA.
+// exhaustively on the device).  One 16-byte chunk per lane, with non-temporal
+// loads and stores (one chunk per lane and the non-temporal policy measured
+// fastest on MI355X: 6.3 TB/s at 8192 x 8192 against 5.6 TB/s for four
+// chunks per lane with default caching).  The kernel is HBM-bound; no LDS,
+// no MFMA.
 #include "fp4q_device.h"
 #include "launch.h"
 
@@ -24,7 +26,7 @@ namespace fp4q {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 1;
 
 // Scale exponent k = ceil(log2(amax / 6)) from the bf16 bits of amax
 // (amax = 2^e (1 + f)  ->  k = e - 2 + [f > 1/2]), zero and subnormal amax at
@@ -66,7 +68,7 @@ __global__ __launch_bounds__(kThreads) void k_mx_qdq(const uint16_t* __restrict_
             size_t off;
             if (CONTIG) off = (size_t)c * 8;
             else { uint32_t r = c / cpr; off = (size_t)r * (size_t)ld + (size_t)(c - r * cpr) * 8; }
-            in[u] = *(const uint4*)(x + off);
+            in[u] = ld_nt16(x + off);
         } else {
             in[u] = make_uint4(0, 0, 0, 0);
         }
@@ -99,11 +101,11 @@ __global__ __launch_bounds__(kThreads) void k_mx_qdq(const uint16_t* __restrict_
             yo.z = decode_pair_bf16<2>(cw, scale);
             yo.w = decode_pair_bf16<3>(cw, scale);
             if (poisoned) yo = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
-            *(uint4*)(y + yoff) = yo;
+            st_nt16(y + yoff, yo);
         }
         if (WC) {
-            *(uint32_t*)(codes + yoff / 2) = cw;
-            if ((c & 3u) == 0) scales[yoff / 32] = poisoned ? 0xFFu : (uint8_t)(k + 127);
+            st_nt32(codes + yoff / 2, cw);
+            if ((c & 3u) == 0) st_nt8(scales + yoff / 32, poisoned ? 0xFFu : (uint32_t)(k + 127));
         }
     }
 }
@@ -125,7 +127,7 @@ __global__ __launch_bounds__(kThreads) void k_mx_dequant(const uint8_t* __restri
     yo.z = decode_pair_bf16<2>(cw, scale);
     yo.w = decode_pair_bf16<3>(cw, scale);
     if (sb == 0xFFu) yo = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
-    *(uint4*)(y + (size_t)c * 8) = yo;
+    st_nt16(y + (size_t)c * 8, yo);
 }
 
 }  // namespace

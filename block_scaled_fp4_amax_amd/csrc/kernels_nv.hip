@@ -29,8 +29,8 @@ constexpr int kThreads = 256;
 
 __device__ __forceinline__ void load16_bf16(const uint16_t* p, float (&v)[16])
 {
-    const uint4 a = *(const uint4*)p;
-    const uint4 b = *(const uint4*)(p + 8);
+    const uint4 a = ld_nt16(p);
+    const uint4 b = ld_nt16(p + 8);
     const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
     for (int k = 0; k < 8; ++k) { v[2 * k] = bf16_lo(w[k]); v[2 * k + 1] = bf16_hi(w[k]); }
@@ -40,15 +40,17 @@ __device__ __forceinline__ void load16_f32(const float* p, float (&z)[16])
 {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const float4 f = *(const float4*)(p + 4 * q);
-        z[4 * q] = f.x; z[4 * q + 1] = f.y; z[4 * q + 2] = f.z; z[4 * q + 3] = f.w;
+        const uint4 f = ld_nt16(p + 4 * q);
+        z[4 * q] = __uint_as_float(f.x); z[4 * q + 1] = __uint_as_float(f.y); z[4 * q + 2] = __uint_as_float(f.z); z[4 * q + 3] = __uint_as_float(f.w);
     }
 }
 
 __device__ __forceinline__ void store16_f32(float* p, const float (&z)[16])
 {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) *(float4*)(p + 4 * q) = make_float4(z[4 * q], z[4 * q + 1], z[4 * q + 2], z[4 * q + 3]);
+    for (int q = 0; q < 4; ++q)
+        st_nt16(p + 4 * q, make_uint4(__float_as_uint(z[4 * q]), __float_as_uint(z[4 * q + 1]), __float_as_uint(z[4 * q + 2]),
+                                      __float_as_uint(z[4 * q + 3])));
 }
 
 template <int BIAS, int OUTER, bool SR, bool EF>
@@ -71,8 +73,8 @@ __global__ __launch_bounds__(kThreads) void k_nv_rows(RowArgs a, uint32_t nblock
     uint32_t am_bits = 0;
     {
         const uint16_t* px = a.x + (int64_t)i * a.ld + j0;
-        const uint4 w0 = *(const uint4*)px;
-        const uint4 w1 = *(const uint4*)(px + 8);
+        const uint4 w0 = ld_nt16(px);
+        const uint4 w1 = ld_nt16(px + 8);
         const uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
         for (int k = 0; k < 8; ++k) { v[2 * k] = bf16_lo(w[k]); v[2 * k + 1] = bf16_hi(w[k]); }
@@ -130,8 +132,8 @@ __global__ __launch_bounds__(kThreads) void k_nv_rows(RowArgs a, uint32_t nblock
     }
     const BlockScale<BIAS> sc = block_scale<BIAS>(max_abs16(vn), rtab);
     const uint2 packed = SR ? codes16_sr<BIAS>(vn, u, sc) : codes16_rne(vn, sc.rd);
-    if (a.codes) *(uint2*)(a.codes + e0 / 2) = packed;
-    if (a.scales) a.scales[(int64_t)i * bpr + jb] = (uint8_t)sc.code;
+    if (a.codes) st_nt64(a.codes + e0 / 2, packed);
+    if (a.scales) st_nt8(a.scales + (int64_t)i * bpr + jb, sc.code);
     if (a.y || EF) {
         float w[16];
         decode16(packed, sc.d, w);
@@ -143,8 +145,8 @@ __global__ __launch_bounds__(kThreads) void k_nv_rows(RowArgs a, uint32_t nblock
             uint32_t o[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k) o[k] = f32_to_bf16(w[2 * k]) | (f32_to_bf16(w[2 * k + 1]) << 16);
-            *(uint4*)(a.y + e0) = make_uint4(o[0], o[1], o[2], o[3]);
-            *(uint4*)(a.y + e0 + 8) = make_uint4(o[4], o[5], o[6], o[7]);
+            st_nt16(a.y + e0, make_uint4(o[0], o[1], o[2], o[3]));
+            st_nt16(a.y + e0 + 8, make_uint4(o[4], o[5], o[6], o[7]));
         }
         if (EF) {
 #pragma unroll
@@ -236,8 +238,8 @@ __global__ __launch_bounds__(kThreads) void k_nv_dequant(const uint8_t* __restri
         if (k & 1) o[k >> 1] |= h << 16;
         else o[k >> 1] = h;
     }
-    *(uint4*)(y + e0) = make_uint4(o[0], o[1], o[2], o[3]);
-    *(uint4*)(y + e0 + 8) = make_uint4(o[4], o[5], o[6], o[7]);
+    st_nt16(y + e0, make_uint4(o[0], o[1], o[2], o[3]));
+    st_nt16(y + e0 + 8, make_uint4(o[4], o[5], o[6], o[7]));
 }
 
 }  // namespace

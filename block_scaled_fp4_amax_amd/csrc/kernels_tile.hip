@@ -166,7 +166,7 @@ __device__ __forceinline__ void load_tile_input(const TileArgs& a, const Tile& t
         const rsrc_t rz = make_rsrc(a.residual + t.e_base);
         const uint32_t oz = act ? (uint32_t)(r * (int)a.cols + 16 * sg) * 4u : kOff;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) in.z[q] = buf_load16(rz, oz + 16u * q);
+        for (int q = 0; q < 4; ++q) in.z[q] = buf_load16<0>(rz, oz + 16u * q);
     }
 }
 
@@ -411,8 +411,8 @@ void k_tile(TileArgs a)
                     for (int k = 0; k < 8; ++k) o[k] = f32_to_bf16(w[2 * k]) | (f32_to_bf16(w[2 * k + 1]) << 16);
                     const rsrc_t ry = make_rsrc(a.y + cur.e_base);
                     const uint32_t oy = act ? erow * 2u : kOff;
-                    buf_store16(ry, oy, make_uint4(o[0], o[1], o[2], o[3]));
-                    buf_store16(ry, oy + 16u, make_uint4(o[4], o[5], o[6], o[7]));
+                    buf_store16<kNT>(ry, oy, make_uint4(o[0], o[1], o[2], o[3]));
+                    buf_store16<kNT>(ry, oy + 16u, make_uint4(o[4], o[5], o[6], o[7]));
                 }
                 if (EF) {
                     const rsrc_t rz = make_rsrc(a.residual + cur.e_base);
