@@ -43,24 +43,38 @@ __device__ __forceinline__ float e2m1_value(uint32_t m)
     return m < 2u ? lo : hi;
 }
 
-// Stochastic rounding of t >= 0 onto the grid: between neighbours lo < hi the
+// Stochastic rounding of t = |T| / 2^24 onto the grid: between neighbours lo < hi the
 // result is hi with probability (t - lo) / (hi - lo), realised as
 // u16 < frac * 2^16 with u16 uniform in [0, 2^16) ("fp4-train" README,
-// Method).  Grid points and t >= 6 are deterministic.  uf is u16 as a float.
+// Method).  Grid points and t >= 6 are deterministic.
 //
-// With k = max(exponent(t), 0) the grid spacing around t is 2^(k-1), so
-// s = t * 2^(1-k) lies in [0, 4), floor(s) + 2k is the code of the lower
-// neighbour and s - floor(s) the fraction; all three steps are exact.  t is
-// first clamped to 6 (code 7, fraction 0).
-__device__ __forceinline__ uint32_t e2m1_sr(float t, float uf)
+// Integer form.  Let pos(t) be the position of t on the grid: the code of the
+// lower neighbour plus the fraction (pos = 2t on [0, 2), t + 2 on [2, 4),
+// t/2 + 4 on [4, 6]), and P = pos * 2^23.  For u16 an integer,
+// u16 < frac * 2^16 is 128 u16 < P mod 2^23, i.e. 128 u16 + 1 <= ceil(P) mod
+// 2^23, so the rounded code is floor((ceil(P) + 2^23 - 1 - 128 u16) / 2^23):
+// the carry out of the low 23 bits is the round-up.  With nu = 0xFFFF - u16,
+// 2^23 - 1 - 128 u16 = 128 nu + 127.  The caller passes T = t * 2^24:
+//   t < 2:   P = 2t * 2^23 = T;
+//   t >= 2:  within a binade the bit pattern of t is linear in t with the
+//            grid's own slope, so P = 2 bits(t) - 504 * 2^22
+//            = 2 bits(T) - 600 * 2^22 (bits(T) = bits(t) + 24 * 2^23).
+// t is clamped to 6 first (code 7, no round-up).  T may also be the binary32
+// rounding of t * 2^24 where t itself is below the normal range: then t > 0
+// exactly when T > 2^-126 (no binary32 quotient lies between the two
+// roundings' thresholds), and every positive subnormal t rounds up exactly
+// when u16 == 0.  ceil(T - 2^-126) gives both: 0 for T <= 2^-126, 1 above it
+// (T - 2^-126 is exact there), and ceil(T) from 2^-100 on, where subtracting
+// 2^-126 cannot cross an integer.
+__device__ __forceinline__ uint32_t e2m1_sr_code(float T, uint32_t nu)
 {
-    const float tc = fminf(t, 6.0f);
-    const int e = (int)(__float_as_uint(tc) >> 23) - 127;
-    const int k = e < 0 ? 0 : e;
-    const float s = ldexpf(tc, 1 - k);
-    const float f = __builtin_floorf(s);
-    const uint32_t up = uf < (s - f) * 65536.0f;
-    return (uint32_t)f + 2u * (uint32_t)k + up;
+    // |T| clamped to [0, 6 * 2^24] (t <= 6); the sign of T is ignored
+    const uint32_t b = __float_as_uint(__builtin_amdgcn_fmed3f(__builtin_fabsf(T), 0.0f, 0x1.8p26f));
+    const int32_t m = (int32_t)__builtin_floorf(0x1p-126f - __uint_as_float(b));   // -ceil(T - 2^-126)
+    const uint32_t nf = 127u - (uint32_t)m;                    // 127 + P, t < 2
+    const uint32_t ni = 2u * b + (127u - 600u * (1u << 22));  // 127 + P, t >= 2
+    const uint32_t n = b < 0x4C000000u ? nf : ni;             // bits(2^25): t = 2
+    return (n + (nu << 7)) >> 23;
 }
 
 // Two E2M1 codes (RNE, ties to the even code, saturating at 6, sign kept,
@@ -149,6 +163,13 @@ __device__ __forceinline__ float scale_decode(uint32_t c)
 // style mixing; the key is bumped by the Weyl constants between rounds.
 struct u32x4 { uint32_t x, y, z, w; };
 
+// a ^ b ^ c in one instruction (gfx950's three-input bitwise operation;
+// truth table 0x96 is the three-way exclusive or).
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c)
+{
+    return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
+
 __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1)
 {
 #pragma unroll
@@ -156,9 +177,9 @@ __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1
         uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
         uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
         u32x4 n;
-        n.x = (c.y ^ k0) ^ (uint32_t)(p1 >> 32);
+        n.x = xor3(c.y, k0, (uint32_t)(p1 >> 32));
         n.y = (uint32_t)p1;
-        n.z = (c.w ^ k1) ^ (uint32_t)(p0 >> 32);
+        n.z = xor3(c.w, k1, (uint32_t)(p0 >> 32));
         n.w = (uint32_t)p0;
         c = n;
         k0 += 0x9E3779B9u;
@@ -214,12 +235,6 @@ __device__ __forceinline__ void sr_draws16(uint64_t seed, uint64_t step, uint64_
 #pragma unroll
         for (int j = 0; j < 8; ++j) u[j] = e16[2 * j] | (e16[2 * j + 1] << 16);
     }
-}
-
-// Variate k of a packed set, as a float (exact: < 2^16).
-__device__ __forceinline__ float sr_var(const uint32_t (&u)[8], int k)
-{
-    return (float)((u[k >> 1] >> (16 * (k & 1))) & 0xFFFFu);
 }
 
 // ---------------------------------------------------------------- buffer resources

@@ -62,16 +62,23 @@ __device__ __forceinline__ BlockScale<BIAS> block_scale(float bmax, const double
     constexpr float kMinNormal = BIAS == 7 ? 0x1p-6f : 0x1p-14f;
     constexpr float kToSteps = BIAS == 7 ? 0x1p9f : 0x1p17f;      // subnormal grid step 2^-(BIAS+2)
     constexpr float kFromSteps = BIAS == 7 ? 0x1p-9f : 0x1p-17f;
-    // normal range: round to nearest even at 3 mantissa bits on the bit pattern
+    // normal range (the common case): round to nearest even at 3 mantissa
+    // bits on the bit pattern; RN64(1 / d) is the table entry of the 3-bit
+    // significand times 2^-(exponent of d)
     const uint32_t u = __float_as_uint(y);
     const uint32_t un = (u + 0x7FFFFu + ((u >> 20) & 1u)) & 0xFFF00000u;
-    // subnormal range: a whole number of grid steps, 0..8 (8 is the smallest normal)
-    const float steps = __builtin_rintf(y * kToSteps);
-    const bool sat = y >= kMax;
-    const bool sub = y < kMinNormal;
-    s.code = sat ? kMaxCode : (sub ? (uint32_t)steps : (un >> 20) - ((127u - (uint32_t)BIAS) << 3));
-    s.d = sat ? kMax : (sub ? steps * kFromSteps : __uint_as_float(un));
-    s.rd = inner_recip<BIAS>(s.code, tab);
+    s.code = (un >> 20) - ((127u - (uint32_t)BIAS) << 3);
+    s.d = __uint_as_float(un);
+    s.rd = ldexp(tab[(un >> 20) & 7u], 127 - (int)(un >> 23));
+    if (!(y >= kMinNormal && y < kMax)) {
+        // saturated, or below the normal range: a whole number of subnormal
+        // grid steps, 0..8 (8 is the smallest normal)
+        const float steps = __builtin_rintf(y * kToSteps);
+        const bool sat = y >= kMax;
+        s.code = sat ? kMaxCode : (uint32_t)steps;
+        s.d = sat ? kMax : steps * kFromSteps;
+        s.rd = inner_recip<BIAS>(s.code, tab);
+    }
     return s;
 }
 
@@ -103,31 +110,38 @@ __device__ __forceinline__ uint2 codes16_rne(const float (&vn)[16], double rd)
     return make_uint2(lo, hi);
 }
 
-// Stochastic-rounding codes of 16 normalised values.  Here the exact value of
-// a tiny quotient matters (zero never rounds up, any positive t can), so
-// quotients that may leave the normal range are recomputed by IEEE division.
+// Stochastic-rounding codes of 16 normalised values.  T_k = t_k * 2^24 with
+// t_k = RN32(|v_n,k| / d) comes from the scaled reciprocal RN64(2^24 / d) =
+// 2^24 RN64(1 / d): exact while t_k is a normal binary32 (power-of-two
+// scaling commutes with rounding), and otherwise the rounding of the exact
+// t_k * 2^24, which e2m1_sr_code() takes as it is.  The sign bits come from
+// the hardware pack of v_n / 2^125, which rounds every v_n to a zero of its
+// own sign.
+template <int BIAS>
+__device__ __forceinline__ uint32_t codes8_sr(const float* vn, const uint32_t* u, double rd24)
+{
+    constexpr float kSignOnly = 0x1p125f;
+    uint32_t w = 0;
+    w = fp4x2_rne_scaled<0>(w, vn[0], vn[1], kSignOnly);
+    w = fp4x2_rne_scaled<1>(w, vn[2], vn[3], kSignOnly);
+    w = fp4x2_rne_scaled<2>(w, vn[4], vn[5], kSignOnly);
+    w = fp4x2_rne_scaled<3>(w, vn[6], vn[7], kSignOnly);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const float T = div_inv64(vn[k], rd24);               // +-t * 2^24
+        const uint32_t nw = ~u[k >> 1];                       // element k's variate: half (k & 1)
+        const uint32_t nu = (k & 1) ? (nw >> 16) : (nw & 0xFFFFu);
+        w |= e2m1_sr_code(T, nu) << (4 * k);
+    }
+    return w;
+}
+
 template <int BIAS>
 __device__ __forceinline__ uint2 codes16_sr(const float (&vn)[16], const uint32_t (&u)[8], const BlockScale<BIAS>& s)
 {
-    float t[16];
-    bool slow = false;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        t[k] = div_inv64(__builtin_fabsf(vn[k]), s.rd);
-        slow |= is_subnormal(t[k]);
-    }
-    if (__builtin_expect(slow, 0)) {
-#pragma unroll
-        for (int k = 0; k < 16; ++k)
-            if (is_subnormal(t[k])) t[k] = __builtin_fabsf(vn[k]) / s.d;
-    }
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        const uint32_t code = e2m1_sr(t[k], sr_var(u, k)) | ((__float_as_uint(vn[k]) >> 31) << 3);
-        if (k < 8) lo |= code << (4 * k);
-        else hi |= code << (4 * (k - 8));
-    }
+    const double rd24 = s.rd * 0x1p24;
+    const uint32_t lo = codes8_sr<BIAS>(vn, u, rd24);
+    const uint32_t hi = codes8_sr<BIAS>(vn + 8, u + 4, rd24);
     return make_uint2(lo, hi);
 }
 

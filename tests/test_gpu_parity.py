@@ -263,15 +263,19 @@ def test_cast_transpose_edge_values():
     x = rng.choice(vals, size=(128, 128)).astype(np.uint16)
     x[:64, 64:] = rng.choice(vals[:6], size=(64, 64))      # a tile of zeros / subnormals
     x[64:, :64] = 0                                         # an all-zero tile
+    # stochastic rounding too: blocks holding both 0x7F7F and 0x0001 give quotients below the binary32
+    # normal range, where only "t > 0" and "u16 == 0" decide the code
     for fmt in ("nvfp4", "amdfp4"):
         for tl, obs, o2d in (("none", 0, False), ("tensorwise", 0, False), ("outer", 64, True), ("outer", 64, False),
                              ("outer", 16, False)):
-            g, o = cfgs(fmt, tl, obs, o2d)
-            want = ref.nv_quantize(x, cols=True, want_y=False, **o)
-            out = fq.fp4_cast_transpose(dev(x), g)
-            for k in ("row_codes", "row_scales", "col_codes", "col_scales", "row_outer", "col_outer"):
-                if k in want:
-                    same(host(out[k], np.float32 if "outer" in k else np.uint8), want[k], "%s %s %s" % (fmt, tl, k))
+            for sr in (False, True):
+                g, o = cfgs(fmt, tl, obs, o2d, sr=sr, seed=11, step=2)
+                want = ref.nv_quantize(x, cols=True, want_y=False, **o)
+                out = fq.fp4_cast_transpose(dev(x), g)
+                for k in ("row_codes", "row_scales", "col_codes", "col_scales", "row_outer", "col_outer"):
+                    if k in want:
+                        same(host(out[k], np.float32 if "outer" in k else np.uint8), want[k],
+                             "%s %s sr=%s %s" % (fmt, tl, sr, k))
 
 
 def test_precomputed_outer_equals_recompute():
