@@ -333,7 +333,7 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: the quantisation path has no cross-GPU step in this build "
+        print("bench.py measures one GPU only: the quantisation path has no cross-GPU step "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     import torch

@@ -209,10 +209,10 @@ __device__ __forceinline__ uint32_t sr_lane(const u32x4& w, int l)
 // every block of a launch (blocks start at multiples of 16), so the branch is
 // uniform; in the aligned case the eight Philox output words of the two
 // 8-element counters are the packed variates themselves.
-__device__ __forceinline__ void sr_draws16(uint64_t seed, uint64_t step, uint64_t idx0, uint32_t (&u)[8])
+//
+// The core takes the first 8-element counter b0 = idx0 >> 3 and off = idx0 % 8.
+__device__ __forceinline__ void sr_draws16_at(uint64_t seed, uint64_t step, uint64_t b0, int off, uint32_t (&u)[8])
 {
-    const uint64_t b0 = idx0 >> 3;
-    const int off = (int)(idx0 & 7u);
     const u32x4 w0 = sr_words(seed, step, b0);
     const u32x4 w1 = sr_words(seed, step, b0 + 1);
     if (off == 0) {
@@ -235,6 +235,20 @@ __device__ __forceinline__ void sr_draws16(uint64_t seed, uint64_t step, uint64_
 #pragma unroll
         for (int j = 0; j < 8; ++j) u[j] = e16[2 * j] | (e16[2 * j + 1] << 16);
     }
+}
+
+__device__ __forceinline__ void sr_draws16(uint64_t seed, uint64_t step, uint64_t idx0, uint32_t (&u)[8])
+{
+    sr_draws16_at(seed, step, idx0 >> 3, (int)(idx0 & 7u), u);
+}
+
+// Same for idx0 = base + lane_off with base the same in every lane and
+// lane_off a multiple of 8: the counter is (base >> 3) + (lane_off >> 3), so
+// no per-lane 64-bit index is formed.
+__device__ __forceinline__ void sr_draws16(uint64_t seed, uint64_t step, uint64_t base, uint32_t lane_off,
+                                           uint32_t (&u)[8])
+{
+    sr_draws16_at(seed, step, (base >> 3) + (lane_off >> 3), (int)(base & 7u), u);
 }
 
 // ---------------------------------------------------------------- buffer resources

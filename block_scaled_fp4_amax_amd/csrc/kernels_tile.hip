@@ -224,19 +224,23 @@ __device__ __forceinline__ void store_pair(PairStage& st, int line, int k, const
     buf_store_u8(rsc, (line_ok && full_words == 1 && 4 + k < nvalid) ? osc + 4u + k : kOff, B.scale);
 }
 
-// Register budget per lane: 128 VGPRs (4 waves per SIMD), 168 (3 waves) for
-// the tile loop that holds results across iterations.  Tighter budgets make
-// the compiler spill to scratch inside the loop.
+// The straight-line (RTNE, no residual, not 1D) form of a super-tile.
 template <int OUTER, bool SR, bool EF>
 constexpr bool tile_unrolled()
 {
     return !SR && !EF && OUTER != kOuter1D;
 }
 
+// Register budget per lane: 128 VGPRs (4 waves per SIMD) wherever the kernel
+// fits in them without scratch spills, 168 (3 waves) for the stochastic-
+// rounding variants that do not (2D / tensorwise / no outer scale without a
+// residual, and tensorwise with one): a spill reload inside the tile loop
+// waits for every load in flight, the next tile's prefetch included.
 template <int BIAS, int OUTER, bool SR, bool COLS, bool EF>
 constexpr int tile_waves_per_simd()
 {
-    return (tile_unrolled<OUTER, SR, EF>() || (OUTER == kOuter1D && !SR)) ? 4 : 3;
+    const bool tight = SR && ((!EF && OUTER != kOuter1D) || (EF && OUTER == kOuterTensor));
+    return tight ? 3 : 4;
 }
 
 // Smallest binary32 outer scale for which v / s_o can be subnormal for some
@@ -340,7 +344,7 @@ void k_tile(TileArgs a)
         uint32_t u[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) u[k] = 0;
-        if (SR && act) sr_draws16(a.seed, a.step, a.index_base + (uint64_t)cur.e_base + erow, u);
+        if (SR && act) sr_draws16(a.seed, a.step, a.index_base + (uint64_t)cur.e_base, erow, u);   // erow % 16 == 0
 
         bool barrier_done = false;   // the pre-LDS-write barrier has been passed
         float s_row = 1.0f;
@@ -359,7 +363,7 @@ void k_tile(TileArgs a)
             } else {
                 const uint32_t m = wave_max_u32(am_bits);
                 uint32_t* rb = red[iter & 1];
-                if ((tid & 63) == 0) rb[tid >> 6] = m;
+                if ((tid & 63) == 0) rb[__builtin_amdgcn_readfirstlane(tid >> 6)] = m;   // wave index, uniform
                 lds_barrier();
                 barrier_done = true;
                 const uint32_t mm = max(max(rb[0], rb[1]), max(rb[2], rb[3]));
