@@ -172,6 +172,10 @@ __device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c)
 
 __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1)
 {
+    // The round keys are formed here, two scalar adds per round, rather than
+    // hoisted out of the caller's loop as twenty loop-invariant scalars that
+    // would overflow the scalar register file (and be spilled to vector lanes).
+    asm volatile("" : "+s"(k0), "+s"(k1));
 #pragma unroll
     for (int r = 0; r < 10; ++r) {
         uint64_t p0 = (uint64_t)0xD2511F53u * c.x;

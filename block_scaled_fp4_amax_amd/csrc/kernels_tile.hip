@@ -64,6 +64,15 @@ __device__ __forceinline__ int swz_chunk(int row, int ch)
     return ch ^ (((row >> 4) & 3) << 1) ^ (row & 1) ^ (((ch >> 3) & 1) << 1);
 }
 
+// Physical 16-byte chunk (8 u16 variates) of chunk ch = col / 8 in row `row`
+// of the SR-variate tile: XOR by twice the 16-row band.  The column phase's
+// u16 reads (one column per lane pair, the four bands of a wave at once) then
+// spread over 8 chunks = all 32 banks.
+__device__ __forceinline__ int swz_u_chunk(int row, int ch)
+{
+    return ch ^ (2 * ((row >> 4) & 3));
+}
+
 template <int BIAS, bool SR>
 __device__ __forceinline__ uint2 quant16(const float (&vn)[16], const uint32_t (&u)[8], const double* tab,
                                          BlockScale<BIAS>& sc)
@@ -257,7 +266,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(tile_w
 void k_tile(TileArgs a)
 {
     __shared__ float4 lds_v[COLS ? kTile * kTile / 4 : 1];
-    __shared__ uint4 lds_u[(COLS && SR) ? kTile * kTile / 8 : 1];   // SR variates, [row][col] u16
+    __shared__ uint4 lds_u[(COLS && SR) ? kTile * kTile / 8 : 1];   // SR variates, [row][col] u16, swizzled
     __shared__ uint32_t red[2][kThreads / 64];
     __shared__ double rtab[kRecipTableSize];
     __shared__ PairStage stage;
@@ -442,7 +451,8 @@ void k_tile(TileArgs a)
             if (SR) {
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
-                    lds_u[r * 8 + 2 * sg + j] = make_uint4(u[4 * j], u[4 * j + 1], u[4 * j + 2], u[4 * j + 3]);
+                    lds_u[r * 8 + swz_u_chunk(r, 2 * sg + j)] =
+                        make_uint4(u[4 * j], u[4 * j + 1], u[4 * j + 2], u[4 * j + 3]);
             }
             lds_barrier();
 
@@ -457,10 +467,12 @@ void k_tile(TileArgs a)
                 // rows of one parity share the swizzled column
                 cv[k] = lf[row * kTile + (lds_col ^ (4 * (k & 1)))];
             }
+            // column cc of rows 16 rs .. 16 rs + 15, all in 16-row band rs
+            const int lu_col = 8 * swz_u_chunk(16 * rs, cc >> 3) + (cc & 7);
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                cu[j] = SR ? (uint32_t)lu[(16 * rs + 2 * j) * kTile + cc] |
-                                 ((uint32_t)lu[(16 * rs + 2 * j + 1) * kTile + cc] << 16)
+                cu[j] = SR ? (uint32_t)lu[(16 * rs + 2 * j) * kTile + lu_col] |
+                                 ((uint32_t)lu[(16 * rs + 2 * j + 1) * kTile + lu_col] << 16)
                            : 0u;
             if (OUTER == kOuter1D) {
                 const bool actc = (cc < cur.cols_valid) && (16 * rs < cur.rows_valid);
