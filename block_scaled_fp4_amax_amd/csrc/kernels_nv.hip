@@ -57,7 +57,9 @@ template <int BIAS, int OUTER, bool SR, bool EF>
 __global__ __launch_bounds__(kThreads) void k_nv_rows(RowArgs a, uint32_t nblocks, uint32_t bpr)
 {
     __shared__ double rtab[16];
+    __shared__ float2 ktab[SR ? 1 : kRneTableSize];
     fill_recip_table(rtab, (int)threadIdx.x);
+    if (!SR) fill_rne_table<BIAS>(ktab, (int)threadIdx.x);
     __syncthreads();
     const uint32_t b = blockIdx.x * kThreads + threadIdx.x;   // inner block id
     // lanes of one 1D outer group are consecutive and bpr % obs16 == 0, so a
@@ -131,7 +133,7 @@ __global__ __launch_bounds__(kThreads) void k_nv_rows(RowArgs a, uint32_t nblock
         normalize16(v, s_o, outer_inv(s_o), vn, true);
     }
     const BlockScale<BIAS> sc = block_scale<BIAS>(max_abs16(vn), rtab);
-    const uint2 packed = SR ? codes16_sr<BIAS>(vn, u, sc) : codes16_rne(vn, sc.rd);
+    const uint2 packed = SR ? codes16_sr<BIAS>(vn, u, sc) : codes16_rne(vn, ktab[sc.code]);
     if (a.codes) st_nt64(a.codes + e0 / 2, packed);
     if (a.scales) st_nt8(a.scales + (int64_t)i * bpr + jb, sc.code);
     if (a.y || EF) {

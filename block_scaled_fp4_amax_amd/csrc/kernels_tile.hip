@@ -75,11 +75,11 @@ __device__ __forceinline__ int swz_u_chunk(int row, int ch)
 
 template <int BIAS, bool SR>
 __device__ __forceinline__ uint2 quant16(const float (&vn)[16], const uint32_t (&u)[8], const double* tab,
-                                         BlockScale<BIAS>& sc)
+                                         const float2* ktab, BlockScale<BIAS>& sc)
 {
     sc = block_scale<BIAS>(max_abs16(vn), tab);
     if (SR) return codes16_sr<BIAS>(vn, u, sc);
-    return codes16_rne(vn, sc.rd);
+    return codes16_rne(vn, ktab[sc.code]);
 }
 
 // Super-tiles: the unit a workgroup walks is a 2 x 2 block of 64 x 64 tiles
@@ -269,6 +269,7 @@ void k_tile(TileArgs a)
     __shared__ uint4 lds_u[(COLS && SR) ? kTile * kTile / 8 : 1];   // SR variates, [row][col] u16, swizzled
     __shared__ uint32_t red[2][kThreads / 64];
     __shared__ double rtab[kRecipTableSize];
+    __shared__ float2 ktab[SR ? 1 : kRneTableSize];
     __shared__ PairStage stage;
 
     const int tid = (int)threadIdx.x;
@@ -288,6 +289,7 @@ void k_tile(TileArgs a)
     TileInput<EF> in;
     load_tile_input<EF>(a, make_tile(a, walk, 0), true, r, sg, in);
     fill_recip_table(rtab, tid);
+    if (!SR) fill_rne_table<BIAS>(ktab, tid);
     lds_barrier();
     const float den = ScaleFmt<BIAS>::outer_den();
     const int cols = (int)a.cols;
@@ -408,7 +410,7 @@ void k_tile(TileArgs a)
         }
         {
             BlockScale<BIAS> sc;
-            const uint2 packed = quant16<BIAS, SR>(vn, u, rtab, sc);
+            const uint2 packed = quant16<BIAS, SR>(vn, u, rtab, ktab, sc);
             ro.codes = packed;
             ro.scale = sc.code;
             if (EF || Y) {
@@ -497,7 +499,7 @@ void k_tile(TileArgs a)
                 for (int k = 0; k < 16; ++k) cv[k] = cn[k];
             }
             BlockScale<BIAS> sc;
-            co.codes = quant16<BIAS, SR>(cv, cu, rtab, sc);
+            co.codes = quant16<BIAS, SR>(cv, cu, rtab, ktab, sc);
             co.scale = sc.code;
         }
         ++iter;

@@ -90,14 +90,53 @@ __device__ __forceinline__ float max_abs16(const float (&v)[16])
     return m;
 }
 
-// RNE codes of 16 normalised values (t = RN32(v_n / d), hardware E2M1 pack).
-// A quotient too small for div_inv64's guarantee still lands below 0.25 and
-// keeps its sign, so its code (+-0) is exact.
-__device__ __forceinline__ uint2 codes16_rne(const float (&vn)[16], double rd)
+// ---------------------------------------------------------------- RNE codes without a division
+// The RNE code of t = RN32(v / d) depends only on where v / d lies relative to
+// the binary32 rounding boundaries B next to the E2M1 decision points
+// 0.25, 0.75, 1.25, 1.75, 2.5, 3.5 and 5 (B = point +- half an ulp; ties at B
+// round to the point, whose last significand bit is 0).  Write d = D 2^E with
+// D in 8..15.  In units of 2^(e - 25) (e the decision point's exponent) B is
+// an integer with at most one factor 2, so v / d = B would need a factor 16 in
+// D (D = 8 divides exactly anyway); otherwise v (24 significant bits) is at
+// least one such unit times d away from B d, so |v / d - B| >= 2^-30 |v / d|.
+// With Kh = RD32(1 / D) 2^-E (rounded down) and Kl = RN32(1 / D - RD32(1 / D)) 2^-E
+// (so Kl >= 0 and v Kh and v Kl share the sign of v, which keeps -0 a -0),
+// u = v Kh + RN32(v Kl) is within 2^-46 |v / d| of v / d, on the same side of
+// every B, so RN32(u) (one fused multiply-add) has the same code as t: one
+// multiply and one fma per value instead of a binary64 product.  Zero scale:
+// Kh = Kl = 0 gives signed zeros, as t does.  Results far below 0.25 (code 0,
+// sign kept) are exact either way.  The table holds (Kh, Kl) per scale code.
+constexpr int kRneTableSize = 256;
+
+template <int BIAS>
+__device__ __forceinline__ void fill_rne_table(float2* tab, int code)
+{
+    // RD32(1 / D) and RN32(1 / D - RD32(1 / D)) for D = 8..15
+    constexpr float kh[8] = {0x1p-3f, 0x1.c71c7p-4f, 0x1.999998p-4f, 0x1.745d16p-4f,
+                             0x1.555554p-4f, 0x1.3b13bp-4f, 0x1.249248p-4f, 0x1.11111p-4f};
+    constexpr float kl[8] = {0.0f, 0x1.c71c72p-28f, 0x1.99999ap-28f, 0x1.45d174p-28f,
+                             0x1.555556p-28f, 0x1.3b13b2p-28f, 0x1.24924ap-28f, 0x1.111112p-28f};
+    if (code >= kRneTableSize) return;
+    const float d = code <= (int)ScaleFmt<BIAS>::max_code ? scale_decode<BIAS>((uint32_t)code) : 0.0f;
+    const uint32_t bd = __float_as_uint(d);
+    const int m = (int)((bd >> 20) & 7u);                // D = 8 + m
+    const int e = (int)(bd >> 23) - 127 - 3;              // d = D 2^e
+    float h = 0.0f, l = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        h = m == i ? kh[i] : h;
+        l = m == i ? kl[i] : l;
+    }
+    tab[code] = d == 0.0f ? make_float2(0.0f, 0.0f) : make_float2(ldexpf(h, -e), ldexpf(l, -e));
+}
+
+// RNE codes of 16 normalised values: t = RN32(v_n / d) through the table entry
+// k = (Kh, Kl) of the block's scale code, then the hardware E2M1 pack.
+__device__ __forceinline__ uint2 codes16_rne(const float (&vn)[16], float2 k)
 {
     float t[16];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) t[k] = div_inv64(vn[k], rd);
+    for (int i = 0; i < 16; ++i) t[i] = __builtin_fmaf(vn[i], k.x, vn[i] * k.y);
     uint32_t lo = 0, hi = 0;
     lo = fp4x2_rne<0>(lo, t[0], t[1]);
     lo = fp4x2_rne<1>(lo, t[2], t[3]);
@@ -110,13 +149,6 @@ __device__ __forceinline__ uint2 codes16_rne(const float (&vn)[16], double rd)
     return make_uint2(lo, hi);
 }
 
-// Stochastic-rounding codes of 16 normalised values.  T_k = t_k * 2^24 with
-// t_k = RN32(|v_n,k| / d) comes from the scaled reciprocal RN64(2^24 / d) =
-// 2^24 RN64(1 / d): exact while t_k is a normal binary32 (power-of-two
-// scaling commutes with rounding), and otherwise the rounding of the exact
-// t_k * 2^24, which e2m1_sr_code() takes as it is.  The sign bits come from
-// the hardware pack of v_n / 2^125, which rounds every v_n to a zero of its
-// own sign.
 template <int BIAS>
 __device__ __forceinline__ uint32_t codes8_sr(const float* vn, const uint32_t* u, double rd24)
 {

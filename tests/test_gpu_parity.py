@@ -176,6 +176,51 @@ def test_rowwise_quantize_and_qdq(case):
         same(host(zd2, np.float32), zo, "quantize residual")
 
 
+def _every_bf16_at_every_scale(scale_fmt):
+    """Blocks of 16: element 0 is 6 * d_c for inner scale code c (so the block's scale is c), elements 1..15
+    run through every finite bf16 value of magnitude <= 6 * d_c, both signs; every code c that such an
+    amax can reach."""
+    mags = np.arange(0x0000, 0x7F80, dtype=np.uint32)                      # finite non-negative bf16
+    fmag = (mags << 16).view(np.float32)
+    blocks = []
+    for c in range(1, 255):
+        d = np.float32(ref.scale_decode(scale_fmt, c))
+        if not np.isfinite(d) or d <= 0:
+            continue
+        amax = np.float32(6) * d
+        ab = W.to_bf16(np.array([amax], np.float32))
+        if W.from_bf16(ab)[0] != amax or ref.scale_encode(scale_fmt, float(amax / np.float32(6))) != c:
+            continue
+        v = mags[fmag <= amax].astype(np.uint16)
+        v = np.concatenate([v, v | np.uint16(0x8000)])
+        n = -(-v.size // 15) * 15
+        v = np.concatenate([v, np.zeros(n - v.size, np.uint16)]).reshape(-1, 15)
+        blocks.append(np.concatenate([np.full((v.shape[0], 1), ab[0], np.uint16), v], axis=1))
+    x = np.concatenate(blocks).reshape(-1)
+    cols = 1024
+    x = np.concatenate([x, np.zeros(-x.size % cols, np.uint16)]).reshape(-1, cols)
+    return x
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "nvfp4-ue5m3"])
+def test_rne_every_bf16_at_every_scale_code(fmt):
+    # the RNE inner quantisation (binary32 quotient by the decoded scale, E2M1 round to nearest even) on
+    # every finite bf16 value against every inner scale code it can meet
+    f, sf, osf = FMT[fmt]
+    x = _every_bf16_at_every_scale(osf)
+    g, o = cfgs(fmt, "none")
+    want = ref.nv_quantize(x, **o)
+    R, C = x.shape
+    q = fq.fp4_quantize(dev(x), g, out={"codes": canary((R, C // 2)), "scales": canary((R, C // 16))})
+    same(host(q["scales"], np.uint8), want["row_scales"], "scales")
+    same(host(q["codes"], np.uint8), want["row_codes"], "codes")
+    xt = np.ascontiguousarray(x[: R // 64 * 64])                 # the tile kernel, both directions
+    out = fq.fp4_cast_transpose(dev(xt), g)
+    want2 = ref.nv_quantize(xt, cols=True, want_y=False, **o)
+    for k in ("row_codes", "row_scales", "col_codes", "col_scales"):
+        same(host(out[k], np.uint8), want2[k], "cast-transpose " + k)
+
+
 def test_tensorwise_qdq_256_full_size():
     x = W.tensorwise_input_256()
     g, o = cfgs("nvfp4", "tensorwise")
