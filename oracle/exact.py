@@ -166,7 +166,7 @@ def _bf16max():
 
 
 def nv_quantize(x_bits, *, scale_fmt="e4m3", two_level="none", obs=0, outer_2d=False,
-                stochastic=False, u16=None, residual=None, cols=False):
+                stochastic=False, u16=None, residual=None, cols=False, inner_2d=False):
     """Exact model of the NVFP4 / AMD-FP4 pipeline on a small [R, C] input.
 
     x_bits: uint16 bf16 bits.  residual: float32 array (read, not written; the
@@ -250,9 +250,15 @@ def nv_quantize(x_bits, *, scale_fmt="e4m3", two_level="none", obs=0, outer_2d=F
         q = rn32(v[i][j] / s)
         return q, (q < 0) if q != 0 else vneg[i][j]
 
-    def quant_block(vals):
-        """vals: list of (value, neg, u16) for one 16-block -> (scale code, d, [(code, p)])"""
-        b = max(abs(a) for a, _, _ in vals)
+    def tile_max(i0, j0, so):
+        """largest |normalised value| of the 16 x 16 tile with corner (i0, j0) (2D inner scaling)"""
+        return max(abs(normalised(i, j, so)[0]) for i in range(i0, i0 + 16) for j in range(j0, j0 + 16))
+
+    def quant_block(vals, b=None):
+        """vals: list of (value, neg, u16) for one 16-block -> (scale code, d, [(code, p)]);
+        b: the block amax, when it comes from the enclosing 16 x 16 tile"""
+        if b is None:
+            b = max(abs(a) for a, _, _ in vals)
         y = rn32(b / 6)
         cs = scale_encode(scale_fmt, y)
         d = scale_decode(scale_fmt, cs)
@@ -277,7 +283,7 @@ def nv_quantize(x_bits, *, scale_fmt="e4m3", two_level="none", obs=0, outer_2d=F
             for j in range(j0, j0 + 16):
                 a, neg = normalised(i, j, so_r)
                 vals.append((a, neg, draws(i, j)))
-            cs, d, res = quant_block(vals)
+            cs, d, res = quant_block(vals, tile_max(i - i % 16, j0, so_r) if inner_2d else None)
             row_scales[i, j0 // 16] = cs
             for k, (code, p) in enumerate(res):
                 j = j0 + k
@@ -309,7 +315,7 @@ def nv_quantize(x_bits, *, scale_fmt="e4m3", two_level="none", obs=0, outer_2d=F
                 for i in range(i0, i0 + 16):
                     a, neg = normalised(i, j, so_c)
                     vals.append((a, neg, draws(i, j)))
-                cs, d, res = quant_block(vals)
+                cs, d, res = quant_block(vals, tile_max(i0, j - j % 16, so_c) if inner_2d else None)
                 col_scales[j, i0 // 16] = cs
                 for k, (code, p) in enumerate(res):
                     i = i0 + k

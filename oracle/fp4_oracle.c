@@ -248,6 +248,7 @@ typedef struct {
     int32_t outer_2d;        /* 1: obs x obs tiles shared by both directions         */
     int32_t stochastic;      /* 0 RNE, 1 stochastic rounding                         */
     int32_t use_given_outer; /* 1: row_outer (and col_outer in 1D) are inputs        */
+    int32_t inner_2d;        /* 1: 16 x 16 inner tiles share one scale               */
     uint64_t seed, step, index_base;
 } orc_nv_params;
 
@@ -272,18 +273,23 @@ static float sanitize(float v)
  * Writes packed codes [R, C/2] (low nibble = even column), scale bytes
  * [R, C/16] and the signed inner-dequantised value p = +-G[m]*d (exact). */
 static void quantize_rows(const float* vn, const uint16_t* u, int64_t R, int64_t C,
-                          int sfmt, int stochastic,
+                          int sfmt, int stochastic, const float* tile_max,
                           uint8_t* codes, uint8_t* scales, float* p_out)
 {
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < R; ++i) {
         for (int64_t j0 = 0; j0 < C; j0 += INNER) {
             const float* blk = vn + i * C + j0;
-            /* block amax */
+            /* block amax: of the 1 x 16 block, or (2D inner scaling) of the
+             * 16 x 16 tile holding it */
             float b = 0.0f;
-            for (int k = 0; k < INNER; ++k) {
-                float a = fabsf(blk[k]);
-                if (a > b) b = a;
+            if (tile_max) {
+                b = tile_max[(i / INNER) * (C / INNER) + j0 / INNER];
+            } else {
+                for (int k = 0; k < INNER; ++k) {
+                    float a = fabsf(blk[k]);
+                    if (a > b) b = a;
+                }
             }
             /* block_absmax / 6, encoded onto the scale grid; elements are then
              * divided by the DECODED scale ([FP4T] Method). */
@@ -356,7 +362,31 @@ static int check_params(const orc_nv_params* p, int64_t R, int64_t C, int need_c
         if (C % p->obs) return -3;
         if ((p->outer_2d || need_cols) && (R % p->obs)) return -3;
     }
+    if (p->inner_2d) {
+        /* one quantisation decision per element shared by both directions:
+         * a per-direction (1D) outer scale would make two */
+        if (p->two_level == 2 && !p->outer_2d) return -4;
+        if (R % INNER) return -2;
+    }
     return 0;
+}
+
+/* Largest |vn| of every 16 x 16 tile of an [R, C] matrix ("Block-Scaled FP8
+ * and FP4 Weight Quantization", section 6: a square tile shares one scale,
+ * computed from all of its values). */
+static void tile_maxima(const float* vn, int64_t R, int64_t C, float* tmax)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t ti = 0; ti < R / INNER; ++ti)
+        for (int64_t tj = 0; tj < C / INNER; ++tj) {
+            float b = 0.0f;
+            for (int64_t i = ti * INNER; i < (ti + 1) * INNER; ++i)
+                for (int64_t j = tj * INNER; j < (tj + 1) * INNER; ++j) {
+                    float a = fabsf(vn[i * C + j]);
+                    if (a > b) b = a;
+                }
+            tmax[ti * (C / INNER) + tj] = b;
+        }
 }
 
 /* Full NVFP4 / AMD-FP4 quantisation of X [R, C] (bf16 bits, row-major,
@@ -483,7 +513,12 @@ int orc_nv_quantize(const orc_nv_params* prm, const uint16_t* X, int64_t R, int6
         for (int64_t j = 0; j < C; ++j)
             vn_r[i * C + j] = has_outer ? normalize(v[i * C + j], outer_at(&om_r, R, C, i, j)) : v[i * C + j];
     if (N) memset(rc_codes, 0, (size_t)(N / 2));
-    quantize_rows(vn_r, u, R, C, sfmt, prm->stochastic, rc_codes, rc_scales, p_r);
+    float* tmax = NULL;
+    if (prm->inner_2d) {
+        tmax = (float*)malloc(sizeof(float) * (size_t)((R / INNER) * (C / INNER) + 1));
+        tile_maxima(vn_r, R, C, tmax);
+    }
+    quantize_rows(vn_r, u, R, C, sfmt, prm->stochastic, tmax, rc_codes, rc_scales, p_r);
 
     /* step 5 + 6, rowwise */
 #pragma omp parallel for schedule(static)
@@ -495,8 +530,28 @@ int orc_nv_quantize(const orc_nv_params* prm, const uint16_t* X, int64_t R, int6
             if (residual) residual[i * C + j] = v[i * C + j] - w;
         }
 
+    /* columnwise with 2D inner scaling: the transpose of the rowwise result
+     * ([BSWQ] section 6: the scale moves with the tile, so the columnwise
+     * codes and scales follow by transposition, with no second decision) */
+    if (want_cols && prm->inner_2d) {
+#pragma omp parallel for schedule(static)
+        for (int64_t j = 0; j < C; ++j)
+            for (int64_t i = 0; i < R; ++i) {
+                const uint8_t rb = rc_codes[i * (C / 2) + j / 2];
+                const int code = (j & 1) ? (rb >> 4) : (rb & 0x0F);
+                uint8_t* byte = &col_codes[j * (R / 2) + i / 2];
+                if ((i & 1) == 0) *byte = (uint8_t)((*byte & 0xF0) | code);
+                else *byte = (uint8_t)((*byte & 0x0F) | (code << 4));
+                if (i % INNER == 0) col_scales[j * (R / INNER) + i / INNER] = rc_scales[i * (C / INNER) + j / INNER];
+                if (col_y) {
+                    float so = has_outer ? outer_at(&om_r, R, C, i, j) : 1.0f;
+                    col_y[j * R + i] = orc_f32_to_bf16(dequant_value(p_r[i * C + j], has_outer, so));
+                }
+            }
+    }
+
     /* columnwise: quantise the rows of the transpose, [BSWQ] sections 2-4 */
-    if (want_cols) {
+    if (want_cols && !prm->inner_2d) {
         float* vT = (float*)malloc(sizeof(float) * (size_t)(N ? N : 1));
         uint16_t* uT = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(N ? N : 1));
         float* pT = (float*)malloc(sizeof(float) * (size_t)(N ? N : 1));
@@ -509,7 +564,7 @@ int orc_nv_quantize(const orc_nv_params* prm, const uint16_t* X, int64_t R, int6
                 uT[j * R + i] = u[i * C + j];
             }
         if (N) memset(col_codes, 0, (size_t)(N / 2));
-        quantize_rows(vT, uT, C, R, sfmt, prm->stochastic, col_codes, col_scales, pT);
+        quantize_rows(vT, uT, C, R, sfmt, prm->stochastic, NULL, col_codes, col_scales, pT);
         if (col_y) {
 #pragma omp parallel for schedule(static)
             for (int64_t j = 0; j < C; ++j)
@@ -521,6 +576,7 @@ int orc_nv_quantize(const orc_nv_params* prm, const uint16_t* X, int64_t R, int6
         free(vT); free(uT); free(pT);
     }
 
+    free(tmax);
     if (so_row && so_row != &tensor_scale) free(so_row);
     if (so_col) free(so_col);
     if (!row_codes) free(rc_codes);

@@ -19,6 +19,7 @@ TWO_LEVEL = {"none": 0, "tensorwise": 1, "outer": 2}
 class _NvParams(ct.Structure):
     _fields_ = [("scale_fmt", ct.c_int32), ("two_level", ct.c_int32), ("obs", ct.c_int32),
                 ("outer_2d", ct.c_int32), ("stochastic", ct.c_int32), ("use_given_outer", ct.c_int32),
+                ("inner_2d", ct.c_int32),
                 ("seed", ct.c_uint64), ("step", ct.c_uint64), ("index_base", ct.c_uint64)]
 
 
@@ -164,9 +165,10 @@ def div_f32(a, b):
 
 
 # ---------------------------------------------------------------- algorithms
-def _params(scale_fmt, two_level, obs, outer_2d, stochastic, seed, step, index_base, given):
+def _params(scale_fmt, two_level, obs, outer_2d, stochastic, seed, step, index_base, given, inner_2d=False):
     return _NvParams(SCALE_FMT[scale_fmt], TWO_LEVEL[two_level], int(obs), int(bool(outer_2d)),
-                     int(bool(stochastic)), int(bool(given)), int(seed), int(step), int(index_base))
+                     int(bool(stochastic)), int(bool(given)), int(bool(inner_2d)), int(seed), int(step),
+                     int(index_base))
 
 
 def outer_shapes(two_level, obs, outer_2d, R, C):
@@ -182,11 +184,13 @@ def outer_shapes(two_level, obs, outer_2d, R, C):
 
 def nv_quantize(x, *, scale_fmt="e4m3", two_level="none", obs=0, outer_2d=False,
                 stochastic=False, seed=0, step=0, index_base=0, residual=None,
-                given_outer=None, cols=False, want_y=True):
+                given_outer=None, cols=False, want_y=True, inner_2d=False):
     """Oracle NVFP4 / AMD-FP4 quantisation of x (uint16 bf16 bits, [R, C]).
 
     residual: float32 [R, C] updated in place (error feedback) or None.
     given_outer: (row_outer, col_outer) supplied by the caller instead of computed.
+    inner_2d: 16 x 16 inner tiles share one scale (replicated in each of their 16
+    rows of row_scales; the columnwise buffers are the transposes).
     Returns a dict of numpy arrays.
     """
     x = np.ascontiguousarray(x, dtype=np.uint16)
@@ -211,7 +215,8 @@ def nv_quantize(x, *, scale_fmt="e4m3", two_level="none", obs=0, outer_2d=False,
             out["col_y"] = np.zeros((C, R), np.uint16)
     if residual is not None:
         assert residual.dtype == np.float32 and residual.flags.c_contiguous and residual.shape == (R, C)
-    prm = _params(scale_fmt, two_level, obs, outer_2d, stochastic, seed, step, index_base, given_outer is not None)
+    prm = _params(scale_fmt, two_level, obs, outer_2d, stochastic, seed, step, index_base, given_outer is not None,
+                  inner_2d)
     rc = lib().orc_nv_quantize(ct.byref(prm), _p(x), R, C, _p(residual),
                                _p(out["row_codes"]), _p(out["row_scales"]), _p(out.get("row_outer")),
                                _p(out.get("row_y")), _p(out.get("col_codes")), _p(out.get("col_scales")),
@@ -222,7 +227,7 @@ def nv_quantize(x, *, scale_fmt="e4m3", two_level="none", obs=0, outer_2d=False,
 
 
 def nv_quantize_grouped(x, rows, *, scale_fmt="e4m3", two_level="outer", obs=64, outer_2d=True,
-                        stochastic=False, seed=0, step=0, index_base=0, residual=None):
+                        stochastic=False, seed=0, step=0, index_base=0, residual=None, inner_2d=False):
     """Per-group (expert) quantisation of stacked x [sum(rows), C], both directions."""
     x = np.ascontiguousarray(x, dtype=np.uint16)
     total, C = x.shape
@@ -236,7 +241,7 @@ def nv_quantize_grouped(x, rows, *, scale_fmt="e4m3", two_level="outer", obs=64,
     out = {"row_codes": np.zeros((total, C // 2), np.uint8), "row_scales": np.zeros((total, C // 16), np.uint8),
            "col_codes": np.zeros((total * C // 2,), np.uint8), "col_scales": np.zeros((total * C // 16,), np.uint8),
            "row_outer": np.zeros(max(n_outer_r, 1), np.float32), "col_outer": np.zeros(max(n_outer_c, 1), np.float32)}
-    prm = _params(scale_fmt, two_level, obs, outer_2d, stochastic, seed, step, index_base, False)
+    prm = _params(scale_fmt, two_level, obs, outer_2d, stochastic, seed, step, index_base, False, inner_2d)
     rc = lib().orc_nv_quantize_grouped(ct.byref(prm), len(rows), _p(rows), C, _p(x), _p(residual),
                                        _p(out["row_codes"]), _p(out["row_scales"]), _p(out["row_outer"]),
                                        _p(out["col_codes"]), _p(out["col_scales"]), _p(out["col_outer"]))

@@ -435,3 +435,116 @@ def test_grouped_equals_loop_of_single_calls():
         np.testing.assert_array_equal(zg[r0:r0 + R], zs)
         off += n
         r0 += R
+
+
+# ---------------------------------------------------------------- 2D (16 x 16) inner scaling
+# "Block-Scaled FP8 and FP4 Weight Quantization", section 6: a 16 x 16 tile shares one inner
+# scale computed from all its values; transposing moves the scale with the tile, so the
+# columnwise buffers are the transposes of the rowwise ones (no second decision).
+INNER2D_MODES = [
+    # (scale_fmt, two_level, obs, outer_2d, stochastic, ef, shape)
+    ("e4m3", "none", 0, False, False, False, (32, 48)),
+    ("e4m3", "none", 0, False, True, True, (32, 32)),
+    ("e4m3", "tensorwise", 0, False, False, True, (48, 32)),
+    ("ue5m3", "tensorwise", 0, False, True, False, (32, 32)),
+    ("e4m3", "outer", 16, True, False, False, (32, 48)),
+    ("e4m3", "outer", 32, True, True, True, (64, 32)),
+    ("ue5m3", "outer", 16, True, False, True, (32, 32)),
+]
+
+
+@pytest.mark.parametrize("mode", INNER2D_MODES, ids=lambda m: "-".join(str(v) for v in m[:6]))
+def test_nv_inner_2d_matches_exact_model(mode):
+    # the exact model quantises the columnwise direction on its own (tile maxima over each
+    # column's tiles); the C oracle transposes the rowwise result
+    sfmt, tl, obs, o2d, sr, ef, shape = mode
+    rng = np.random.default_rng(zlib.crc32(repr(mode).encode()))
+    R, C = shape
+    x = (rng.standard_normal(shape) * np.exp(rng.standard_normal((R, 1)))).astype(np.float32)
+    x[rng.integers(0, R), rng.integers(0, C)] *= 500                # one outlier element
+    x.ravel()[rng.integers(0, R * C, 4)] = -0.0
+    xb = bf16(x)
+    resid = (rng.standard_normal(shape) * 0.01).astype(np.float32) if ef else None
+    kw = dict(scale_fmt=sfmt, two_level=tl, obs=obs, outer_2d=o2d, stochastic=sr)
+    res_c = None if resid is None else resid.copy()
+    c_out = ref.nv_quantize(xb, residual=res_c, cols=True, inner_2d=True, seed=9, step=4, index_base=77, **kw)
+    u = ref.sr_u16_array(9, 4, 77, R * C).reshape(R, C) if sr else None
+    e_out = exact.nv_quantize(xb, u16=u, residual=resid, cols=True, inner_2d=True, **kw)
+    _compare(c_out, e_out, KEYS)
+    if ef:
+        np.testing.assert_array_equal(res_c.view(np.uint32), e_out["residual"].view(np.uint32))
+
+
+def test_nv_inner_2d_edge_values_match_exact_model():
+    vals = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x0040, 0x7F7F, 0xFF7F, 0x7F80, 0xFF80, 0x7FC0,
+                     0x3F80, 0xBF80, 0x4013, 0x2000, 0x1000, 0x0100], np.uint16)
+    rng = np.random.default_rng(33)
+    for tl, obs, o2d in [("none", 0, False), ("tensorwise", 0, False), ("outer", 16, True)]:
+        for sfmt in ("e4m3", "ue5m3"):
+            xb = rng.choice(vals, size=(32, 32)).astype(np.uint16)
+            xb[16:, 16:] = rng.choice(vals[:6], size=(16, 16))          # a tile of tiny / zero values
+            c_out = ref.nv_quantize(xb, scale_fmt=sfmt, two_level=tl, obs=obs, outer_2d=o2d, cols=True,
+                                    inner_2d=True)
+            e_out = exact.nv_quantize(xb, scale_fmt=sfmt, two_level=tl, obs=obs, outer_2d=o2d, cols=True,
+                                      inner_2d=True)
+            _compare(c_out, e_out, KEYS)
+
+
+@pytest.mark.parametrize("tl,obs,o2d,sr", [("none", 0, False, False), ("tensorwise", 0, False, True),
+                                           ("outer", 64, True, False), ("outer", 64, True, True)])
+def test_inner_2d_equals_1d_when_every_row_block_holds_the_tile_max(tl, obs, o2d, sr):
+    # if each 1 x 16 row block of a tile already contains the tile's largest magnitude, the
+    # tile scale is every row block's own scale: 2D and 1D inner scaling agree on the rowwise
+    # direction (codes, scales, dequantised values)
+    rng = np.random.default_rng(5)
+    x = _rand_bf16(rng, (64, 128)).astype(np.uint16)
+    xf = f32(x).reshape(4, 16, 8, 16)
+    tmax = np.abs(xf).max(axis=(1, 3), keepdims=True)                 # per 16 x 16 tile
+    sign = np.where(rng.integers(0, 2, (4, 16, 8, 1)) == 1, -1.0, 1.0).astype(np.float32)
+    col = rng.integers(0, 16, (4, 16, 8))
+    for a in range(4):
+        for i in range(16):
+            for b in range(8):
+                xf[a, i, b, col[a, i, b]] = sign[a, i, b, 0] * tmax[a, 0, b, 0]
+    x = bf16(xf.reshape(64, 128))
+    kw = dict(two_level=tl, obs=obs, outer_2d=o2d, stochastic=sr, seed=2, step=1)
+    a = ref.nv_quantize(x, inner_2d=False, **kw)
+    b = ref.nv_quantize(x, inner_2d=True, **kw)
+    for k in ("row_codes", "row_scales", "row_y"):
+        np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+
+
+def test_inner_2d_scales_follow_the_tile_and_columns_are_the_transpose():
+    rng = np.random.default_rng(8)
+    x = _rand_bf16(rng, (64, 96))
+    for kw in (dict(two_level="none"), dict(two_level="tensorwise"), dict(two_level="outer", obs=32, outer_2d=True)):
+        o = ref.nv_quantize(x, cols=True, inner_2d=True, **kw)
+        rs = o["row_scales"].reshape(4, 16, 6)
+        assert (rs == rs[:, :1, :]).all()                              # one scale per 16 x 16 tile
+        np.testing.assert_array_equal(o["col_scales"], o["row_scales"][::16].T.repeat(16, axis=0))
+        lo, hi = o["row_codes"] & 0xF, o["row_codes"] >> 4
+        codes = np.stack([lo, hi], axis=-1).reshape(64, 96)           # nibble per element
+        clo, chi = o["col_codes"] & 0xF, o["col_codes"] >> 4
+        np.testing.assert_array_equal(np.stack([clo, chi], axis=-1).reshape(96, 64), codes.T)
+        np.testing.assert_array_equal(o["col_y"], o["row_y"].T)
+
+
+def test_inner_2d_change_stays_in_its_tile():
+    rng = np.random.default_rng(12)
+    x = _rand_bf16(rng, (48, 64))
+    a = ref.nv_quantize(x, inner_2d=True)
+    x2 = x.copy()
+    x2[20, 37] = bf16([100.0])[0]                                      # tile (1, 2)
+    b = ref.nv_quantize(x2, inner_2d=True)
+    ca = np.stack([a["row_codes"] & 0xF, a["row_codes"] >> 4], -1).reshape(48, 64)
+    cb = np.stack([b["row_codes"] & 0xF, b["row_codes"] >> 4], -1).reshape(48, 64)
+    diff = np.argwhere(ca != cb)
+    assert diff.size and (diff[:, 0] // 16 == 1).all() and (diff[:, 1] // 16 == 2).all()
+    sd = np.argwhere(a["row_scales"] != b["row_scales"])
+    assert sd.size and (sd[:, 0] // 16 == 1).all() and (sd[:, 1] == 2).all()
+
+
+def test_inner_2d_rejected_with_1d_outer_groups():
+    x = _rand_bf16(np.random.default_rng(0), (32, 64))
+    with pytest.raises(ValueError):
+        ref.nv_quantize(x, two_level="outer", obs=32, outer_2d=False, inner_2d=True)
