@@ -14,7 +14,8 @@ from a HIP graph so back-to-back launches are not host-bound.
 
 Also reported (not part of `value`): the other reference workloads (MXFP4
 fake-quant 8192^2, AMD-FP4 1D-outer SR cast-transpose 16384x2880, grouped
-NVFP4 SR+EF over 32 experts of 2880^2, NVFP4 tensorwise QDQ 256^2), and the
+NVFP4 SR+EF over 32 experts of 2880^2, NVFP4 tensorwise QDQ 256^2, and the
+4096^2 weight under 16x16 inner tiles inside the 64x64 outer tiles), and the
 CPU oracle timed on the host cores on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra]
@@ -46,7 +47,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU oracle time for the baseline")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 256 MiB device copy (counter calibration) and exit")
-    ap.add_argument("--only", default=None, help="time a single workload (nv_tensorwise_qdq_256, nv_2d_cast_transpose_4096, mx_fake_quant_8192, amd_1d_sr_cast_transpose_16384x2880, nv_grouped_sr_ef_32x2880) and exit")
+    ap.add_argument("--only", default=None, help="time a single workload (nv_tensorwise_qdq_256, nv_2d_cast_transpose_4096, mx_fake_quant_8192, amd_1d_sr_cast_transpose_16384x2880, nv_grouped_sr_ef_32x2880, nv_2d_inner16_cast_transpose_4096) and exit")
     ap.add_argument("--eager", action="store_true", help="launch every step from the host (no graph replay)")
     ap.add_argument("--pmc-summary", nargs=5, metavar=("KEY", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     default=None,
@@ -58,7 +59,8 @@ def parse():
 # ---------------------------------------------------------------------- helpers
 KERNEL_NAME_PREFIX = {"nv_tensorwise_qdq_256": "fp4q::(anonymous namespace)::k_nv_rows", "nv_2d_cast_transpose_4096": "fp4q::(anonymous namespace)::k_tile",
                       "mx_fake_quant_8192": "fp4q::(anonymous namespace)::k_mx_qdq", "amd_1d_sr_cast_transpose_16384x2880": "fp4q::(anonymous namespace)::k_tile",
-                      "nv_grouped_sr_ef_32x2880": "fp4q::(anonymous namespace)::k_tile"}
+                      "nv_grouped_sr_ef_32x2880": "fp4q::(anonymous namespace)::k_tile",
+                      "nv_2d_inner16_cast_transpose_4096": "fp4q::(anonymous namespace)::k_tile"}
 COPY_PROBE_BYTES = 256 << 20
 
 
@@ -184,10 +186,10 @@ def n_sets_for(bytes_per_set, min_total=1 << 30, cap=64):
 
 
 # ---------------------------------------------------------------------- workloads
-def make_cast_transpose_2d(torch, fq, W):
+def make_cast_transpose_2d(torch, fq, W, inner_2d=False):
     R = C = 4096
     x = W.weight_4096_outlier_cols()
-    cfg = fq.make_cfg(format="nvfp4", two_level="outer_block", outer_block_size=64, outer_2d=True)
+    cfg = fq.make_cfg(format="nvfp4", two_level="outer_block", outer_block_size=64, outer_2d=True, inner_2d=inner_2d)
     alg = R * C * 2 + 2 * (R * C // 2) + 2 * (R * C // 16) + (R // 64) * (C // 64) * 4
     nset = n_sets_for(alg)
     src = torch.from_numpy(x.view("int16")).cuda()
@@ -207,8 +209,16 @@ def make_cast_transpose_2d(torch, fq, W):
                                   torch.cuda.current_stream().cuda_stream)
         if st:
             raise fq.Fp4Error(st, "fp4_cast_transpose")
+    if inner_2d:
+        return Timed("nv_2d_inner16_cast_transpose_4096",
+                     "NVFP4 2D 64x64 outer, E4M3 16x16 inner tiles, RTNE, fused cast-transpose 4096x4096 bf16", alg,
+                     sets, launch, "k_tile<7, 3, false, true, false, false, false, true>")
     return Timed("nv_2d_cast_transpose_4096", "NVFP4 2D 64x64 outer, E4M3/16, RTNE, fused cast-transpose 4096x4096 bf16", alg, sets, launch,
-                 "k_tile<7, 3, false, true, false, false, false>")
+                 "k_tile<7, 3, false, true, false, false, false, false>")
+
+
+def make_cast_transpose_2d_inner16(torch, fq, W):
+    return make_cast_transpose_2d(torch, fq, W, inner_2d=True)
 
 
 def make_mx_fake_quant(torch, fq, W):
@@ -254,7 +264,7 @@ def make_cast_transpose_1d_sr(torch, fq, W):
         if st:
             raise fq.Fp4Error(st, "fp4_cast_transpose")
     return Timed("amd_1d_sr_cast_transpose_16384x2880", "AMD-FP4 1D 1x64 outer, UE5M3/16, SR, cast-transpose 16384x2880 bf16", alg, sets, launch,
-                 "k_tile<15, 2, true, true, false, false, false>")
+                 "k_tile<15, 2, true, true, false, false, false, false>")
 
 
 def make_grouped_sr_ef(torch, fq, W):
@@ -279,7 +289,7 @@ def make_grouped_sr_ef(torch, fq, W):
             raise fq.Fp4Error(st, "fp4_cast_transpose_grouped")
     # the working set (~3 GB per step) is far beyond the last-level cache: one set
     return Timed("nv_grouped_sr_ef_32x2880", "grouped NVFP4 2D 64x64 outer, E4M3/16, SR + in-place EF residual, 32 x 2880x2880", alg, [s],
-                 launch, "k_tile<7, 3, true, true, true, false, false>")
+                 launch, "k_tile<7, 3, true, true, true, false, false, false>")
 
 
 def make_tensorwise_qdq(torch, fq, W):
@@ -356,7 +366,11 @@ def main():
         return
 
     if args.only:
-        mk = {"nv_tensorwise_qdq_256": make_tensorwise_qdq, "nv_2d_cast_transpose_4096": make_cast_transpose_2d, "mx_fake_quant_8192": make_mx_fake_quant, "amd_1d_sr_cast_transpose_16384x2880": make_cast_transpose_1d_sr, "nv_grouped_sr_ef_32x2880": make_grouped_sr_ef}[args.only]
+        mk = {"nv_tensorwise_qdq_256": make_tensorwise_qdq, "nv_2d_cast_transpose_4096": make_cast_transpose_2d,
+              "mx_fake_quant_8192": make_mx_fake_quant,
+              "amd_1d_sr_cast_transpose_16384x2880": make_cast_transpose_1d_sr,
+              "nv_grouped_sr_ef_32x2880": make_grouped_sr_ef,
+              "nv_2d_inner16_cast_transpose_4096": make_cast_transpose_2d_inner16}[args.only]
         w = mk(torch, fq, W)
         ms = run_timed(torch, w, args.steps, args.warmup, graph=not args.eager)
         per = ms / args.steps
@@ -386,7 +400,8 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_extra:
         extra = {}
-        for mk, steps in ((make_mx_fake_quant, 400), (make_cast_transpose_1d_sr, 400), (make_grouped_sr_ef, 20), (make_tensorwise_qdq, 400)):
+        for mk, steps in ((make_mx_fake_quant, 400), (make_cast_transpose_1d_sr, 400), (make_grouped_sr_ef, 20),
+                          (make_tensorwise_qdq, 400), (make_cast_transpose_2d_inner16, 2000)):
             e = mk(torch, fq, W)
             print("# extra %s" % e.name, file=sys.stderr, flush=True)
             ems = run_timed(torch, e, steps, min(20, steps))

@@ -40,7 +40,7 @@ class Cfg(ct.Structure):
     _fields_ = [("abi_version", ct.c_uint32), ("format", ct.c_int32), ("scale_format", ct.c_int32),
                 ("two_level", ct.c_int32), ("outer_block_size", ct.c_int32), ("outer_2d", ct.c_int32),
                 ("rounding", ct.c_int32), ("outer_mode", ct.c_int32), ("input_dtype", ct.c_int32),
-                ("reserved", ct.c_int32), ("seed", ct.c_uint64), ("step", ct.c_uint64),
+                ("inner_2d", ct.c_int32), ("seed", ct.c_uint64), ("step", ct.c_uint64),
                 ("index_base", ct.c_uint64)]
 
 
@@ -50,13 +50,15 @@ class Sizes(ct.Structure):
 
 
 def make_cfg(format="nvfp4", scale_format=None, two_level="none", outer_block_size=0, outer_2d=False,
-             rounding="rne", outer_mode=0, seed=0, step=0, index_base=0, input_dtype="bf16"):
-    """Build an fp4q_cfg (string names or the raw integers of include/fp4q.h)."""
+             rounding="rne", outer_mode=0, seed=0, step=0, index_base=0, input_dtype="bf16", inner_2d=False):
+    """Build an fp4q_cfg (string names or the raw integers of include/fp4q.h).
+
+    inner_2d: one inner scale per 16 x 16 tile instead of per 1 x 16 block."""
     def pick(table, v):
         return v if isinstance(v, int) and not isinstance(v, bool) else table[v]
     return Cfg(ABI_VERSION, pick(FORMATS, format), pick(SCALE_FORMATS, scale_format), pick(TWO_LEVEL, two_level),
                int(outer_block_size), int(bool(outer_2d)), pick(ROUNDING, rounding), int(outer_mode),
-               pick(DTYPES, input_dtype), 0, int(seed), int(step), int(index_base))
+               pick(DTYPES, input_dtype), int(inner_2d), int(seed), int(step), int(index_base))
 
 
 _lib = None

@@ -21,6 +21,7 @@ struct Resolved {
     int obs;
     bool sr;
     bool given;       // outer scales supplied by the caller
+    bool inner2d;     // 16 x 16 inner tiles
 };
 
 bool misaligned(const void* p, uintptr_t a) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) % a) != 0; }
@@ -33,7 +34,7 @@ int resolve(const fp4q_cfg* c, Resolved& r)
 {
     if (!c) return FP4Q_ERR_NULL;
     if (c->abi_version != FP4Q_ABI_VERSION) return FP4Q_ERR_ABI;
-    if (c->reserved != 0) return FP4Q_ERR_MODE;
+    if (c->inner_2d != 0 && c->inner_2d != 1) return FP4Q_ERR_MODE;
     if (c->input_dtype == FP4Q_DTYPE_FP32) return FP4Q_ERR_UNSUPPORTED;
     if (c->input_dtype != FP4Q_DTYPE_BF16) return FP4Q_ERR_DTYPE;
     if (c->rounding != FP4Q_RNE && c->rounding != FP4Q_STOCHASTIC) return FP4Q_ERR_MODE;
@@ -42,6 +43,7 @@ int resolve(const fp4q_cfg* c, Resolved& r)
     r.fmt = c->format;
     r.sr = c->rounding == FP4Q_STOCHASTIC;
     r.given = c->outer_mode == 1;
+    r.inner2d = c->inner_2d == 1;
     r.obs = 0;
     r.bias = 0;
     r.outer_kind = kOuterNone;
@@ -57,7 +59,8 @@ int resolve(const fp4q_cfg* c, Resolved& r)
         break;
     case FP4Q_MXFP4:
         if (c->scale_format != FP4Q_SCALE_DEFAULT && c->scale_format != FP4Q_SCALE_UE8M0) return FP4Q_ERR_MODE;
-        if (c->two_level != FP4Q_TWO_LEVEL_NONE || c->outer_block_size != 0 || c->outer_2d != 0 || r.given)
+        if (c->two_level != FP4Q_TWO_LEVEL_NONE || c->outer_block_size != 0 || c->outer_2d != 0 || r.given ||
+            r.inner2d)
             return FP4Q_ERR_MODE;
         if (r.sr) return FP4Q_ERR_UNSUPPORTED;
         return FP4Q_OK;
@@ -75,6 +78,9 @@ int resolve(const fp4q_cfg* c, Resolved& r)
         if (c->outer_block_size <= 0 || c->outer_block_size % 16 != 0) return FP4Q_ERR_SHAPE;
         r.obs = c->outer_block_size;
         r.outer_kind = c->outer_2d ? kOuter2D : kOuter1D;
+        // 16 x 16 inner tiles make one decision per element for both
+        // directions; 1D outer groups normalise each direction differently
+        if (r.inner2d && r.outer_kind == kOuter1D) return FP4Q_ERR_MODE;
         break;
     default:
         return FP4Q_ERR_MODE;
@@ -90,7 +96,7 @@ int check_shape(const Resolved& r, int64_t rows, int64_t cols, int64_t ld, bool 
     if (cols % inner) return FP4Q_ERR_SHAPE;
     if (rows > 0 && ld < cols) return FP4Q_ERR_SHAPE;
     if (ld % 8) return FP4Q_ERR_ALIGN;
-    if (columnwise && rows % 16) return FP4Q_ERR_SHAPE;
+    if ((columnwise || r.inner2d) && rows % 16) return FP4Q_ERR_SHAPE;
     if (r.outer_kind == kOuter1D || r.outer_kind == kOuter2D) {
         if (cols % r.obs) return FP4Q_ERR_SHAPE;
         if ((r.outer_kind == kOuter2D || columnwise) && rows % r.obs) return FP4Q_ERR_SHAPE;
@@ -175,7 +181,8 @@ int rowwise(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int64_t cols, 
 
     if (r.fmt == FP4Q_MXFP4) return hip_status(launch_mx_qdq(x, rows, cols, ld, y, codes, scales, s));
 
-    if (r.outer_kind == kOuter2D) {
+    if (r.outer_kind == kOuter2D || r.inner2d) {
+        // 64 x 64 tiles: the 2D outer tile, and the 16 x 16 inner tiles
         TileArgs a = tile_args_single(x, rows, cols, ld);
         a.row_codes = codes;
         a.row_scales = scales;
@@ -187,7 +194,18 @@ int rowwise(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int64_t cols, 
         a.index_base = cfg->index_base;
         a.obs16 = 4;
         a.outer_given = r.given;
-        return hip_status(launch_tiles(r.bias, kOuter2D, r.sr, a, s));
+        a.inner_2d = r.inner2d ? 1 : 0;
+        if (r.outer_kind == kOuterTensor) {
+            if (r.given) {
+                a.tensor_scale = outer;
+            } else {
+                float* wsf = (float*)ws;
+                hipError_t e = launch_amax(r.bias, x, rows, cols, ld, residual, wsf + 1, kAmaxPartials, wsf, outer, s);
+                if (e != hipSuccess) return FP4Q_ERR_HIP;
+                a.tensor_scale = wsf;
+            }
+        }
+        return hip_status(launch_tiles(r.bias, r.outer_kind, r.sr, a, s));
     }
     RowArgs a;
     std::memset(&a, 0, sizeof(a));
@@ -357,6 +375,7 @@ int fp4_cast_transpose(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int
     a.index_base = cfg->index_base;
     a.obs16 = r.obs ? r.obs / 16 : 1;
     a.outer_given = r.given;
+    a.inner_2d = r.inner2d ? 1 : 0;
     if (r.outer_kind == kOuterTensor) {
         if (r.given) {
             a.tensor_scale = row_outer;
@@ -425,6 +444,7 @@ int fp4_cast_transpose_grouped(const fp4q_cfg* cfg, int32_t groups, const int64_
         a.index_base = cfg->index_base;
         a.obs16 = r.obs ? r.obs / 16 : 1;
         a.outer_given = r.given;
+        a.inner_2d = r.inner2d ? 1 : 0;
         a.ngroups = ng;
         a.tiles_c = tiles_c;
         int64_t rr = row_before;

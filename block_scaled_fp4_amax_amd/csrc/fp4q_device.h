@@ -416,6 +416,8 @@ constexpr int kDppHalfMirror = 0x141;
 constexpr int kDppMirror = 0x140;
 constexpr int kDppBcast15 = 0x142;
 constexpr int kDppBcast31 = 0x143;
+constexpr int kDppRowRor4 = 0x124;    // rotate right by 4 within each row of 16 lanes
+constexpr int kDppRowRor8 = 0x128;    // rotate right by 8 within each row of 16 lanes
 
 // Max over aligned groups of 2 or 4 consecutive lanes (width 1, 2 or 4).
 __device__ __forceinline__ uint32_t quad_max_u32(uint32_t v, int width)

@@ -36,6 +36,15 @@
 // two tiles of a super-tile row (column) are stored together, as runs of 64
 // code bytes and 8 scale bytes per row (column).
 //
+// With 16 x 16 inner tiles ("Block-Scaled FP8 and FP4 Weight Quantization",
+// section 6) the row phase takes each inner scale from the largest normalised
+// magnitude of the 16 lanes holding one 16 x 16 tile (the lanes of equal
+// column segment in one wave), publishes the 16 scale codes of the 64 x 64
+// tile in LDS, and the column phase encodes its column block with the scale
+// of the tile it lies in: the same quotient and the same SR variate as the
+// row phase, so the columnwise codes and scales are the transposes of the
+// rowwise ones.
+//
 // Super-tiles are taken in row-major order, split into 8 contiguous slices,
 // one per XCD (workgroup ids are dealt round-robin to the XCDs), so the
 // partial cache lines that neighbouring super-tiles write meet in the same
@@ -73,13 +82,40 @@ __device__ __forceinline__ int swz_u_chunk(int row, int ch)
     return ch ^ (2 * ((row >> 4) & 3));
 }
 
+// Largest value of m over the 16 lanes of a wave whose lane index is congruent
+// to this lane's modulo 4 (m >= 0): the lanes of one 16 x 16 inner tile in the
+// row phase.  Two rotations within each 16-lane row, then two exchanges across
+// rows.
+__device__ __forceinline__ float tile16_max(float m)
+{
+    uint32_t v = __float_as_uint(m);
+    v = max_dpp<kDppRowRor4>(v);
+    v = max_dpp<kDppRowRor8>(v);
+    uint32_t o = (uint32_t)__shfl_xor((int)v, 16, 64);
+    v = v > o ? v : o;
+    o = (uint32_t)__shfl_xor((int)v, 32, 64);
+    v = v > o ? v : o;
+    return __uint_as_float(v);
+}
+
+// Codes of 16 normalised values with a given inner scale.
 template <int BIAS, bool SR>
+__device__ __forceinline__ uint2 encode16(const float (&vn)[16], const uint32_t (&u)[8], const float2* ktab,
+                                          const BlockScale<BIAS>& sc)
+{
+    if (SR) return codes16_sr<BIAS>(vn, u, sc);
+    return codes16_rne(vn, ktab[sc.code]);
+}
+
+// One block's scale and codes; with I2D the scale comes from the 16 x 16 tile
+// (tile16_max) instead of the lane's own 16 values.
+template <int BIAS, bool SR, bool I2D>
 __device__ __forceinline__ uint2 quant16(const float (&vn)[16], const uint32_t (&u)[8], const double* tab,
                                          const float2* ktab, BlockScale<BIAS>& sc)
 {
-    sc = block_scale<BIAS>(max_abs16(vn), tab);
-    if (SR) return codes16_sr<BIAS>(vn, u, sc);
-    return codes16_rne(vn, ktab[sc.code]);
+    const float b = max_abs16(vn);
+    sc = block_scale<BIAS>(I2D ? tile16_max(b) : b, tab);
+    return encode16<BIAS, SR>(vn, u, ktab, sc);
 }
 
 // Super-tiles: the unit a workgroup walks is a 2 x 2 block of 64 x 64 tiles
@@ -261,12 +297,13 @@ constexpr float kNoSubnormalScale = 0x1p-7f;
 // out-of-range offset, and every tile iteration issues the same sequence of
 // memory instructions with no branch around any of them, so the compiler's
 // wait for the next tile's loads never waits for earlier stores.
-template <int BIAS, int OUTER, bool SR, bool COLS, bool EF, bool GIVEN, bool Y>
+template <int BIAS, int OUTER, bool SR, bool COLS, bool EF, bool GIVEN, bool Y, bool I2D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(tile_waves_per_simd<BIAS, OUTER, SR, COLS, EF>())))
 void k_tile(TileArgs a)
 {
     __shared__ float4 lds_v[COLS ? kTile * kTile / 4 : 1];
     __shared__ uint4 lds_u[(COLS && SR) ? kTile * kTile / 8 : 1];   // SR variates, [row][col] u16, swizzled
+    __shared__ uint32_t lds_tsc[(COLS && I2D) ? 16 : 1];   // 16 x 16 inner scale codes, [tile row][tile col]
     __shared__ uint32_t red[2][kThreads / 64];
     __shared__ double rtab[kRecipTableSize];
     __shared__ float2 ktab[SR ? 1 : kRneTableSize];
@@ -410,7 +447,7 @@ void k_tile(TileArgs a)
         }
         {
             BlockScale<BIAS> sc;
-            const uint2 packed = quant16<BIAS, SR>(vn, u, rtab, ktab, sc);
+            const uint2 packed = quant16<BIAS, SR, I2D>(vn, u, rtab, ktab, sc);
             ro.codes = packed;
             ro.scale = sc.code;
             if (EF || Y) {
@@ -456,6 +493,7 @@ void k_tile(TileArgs a)
                     lds_u[r * 8 + swz_u_chunk(r, 2 * sg + j)] =
                         make_uint4(u[4 * j], u[4 * j + 1], u[4 * j + 2], u[4 * j + 3]);
             }
+            if (I2D && (r & 15) == 0) lds_tsc[(r >> 4) * 4 + sg] = ro.scale;
             lds_barrier();
 
             // ---------------- column phase
@@ -498,9 +536,19 @@ void k_tile(TileArgs a)
 #pragma unroll
                 for (int k = 0; k < 16; ++k) cv[k] = cn[k];
             }
-            BlockScale<BIAS> sc;
-            co.codes = quant16<BIAS, SR>(cv, cu, rtab, ktab, sc);
-            co.scale = sc.code;
+            if (I2D) {
+                // the scale of the 16 x 16 tile holding this column block
+                BlockScale<BIAS> sc;
+                sc.code = lds_tsc[rs * 4 + (cc >> 4)];
+                sc.d = 0.0f;   // not needed for encoding
+                sc.rd = inner_recip<BIAS>(sc.code, rtab);
+                co.codes = encode16<BIAS, SR>(cv, cu, ktab, sc);
+                co.scale = sc.code;
+            } else {
+                BlockScale<BIAS> sc;
+                co.codes = quant16<BIAS, SR, false>(cv, cu, rtab, ktab, sc);
+                co.scale = sc.code;
+            }
         }
         ++iter;
     };
@@ -713,42 +761,63 @@ namespace {
 
 // Kernel selection: the tensorwise and no-outer modes take their scale from
 // tensor_scale (or have none), so they have no precomputed-outer variant; the
-// bf16 dequantised output exists only for the rowwise-only (2D outer) use.
-template <int B, int O, bool S, bool C, bool E>
+// bf16 dequantised output exists only for the rowwise-only uses (2D outer, and
+// 16 x 16 inner tiles under any of none / tensorwise / 2D outer).
+template <int B, int O, bool S, bool C, bool E, bool I>
 hipError_t pick_given_y(const TileArgs& a, hipStream_t s)
 {
     const bool given = a.outer_given != 0;
     const bool y = a.y != nullptr;
-    if constexpr (O == kOuterNone || O == kOuterTensor) {
-        return launch_persistent(k_tile<B, O, S, C, E, false, false>, a, s);
-    } else if constexpr (C) {
-        return given ? launch_persistent(k_tile<B, O, S, C, E, true, false>, a, s)
-                     : launch_persistent(k_tile<B, O, S, C, E, false, false>, a, s);
+    if constexpr (C) {
+        if constexpr (O == kOuterNone || O == kOuterTensor) {
+            return launch_persistent(k_tile<B, O, S, C, E, false, false, I>, a, s);
+        } else {
+            return given ? launch_persistent(k_tile<B, O, S, C, E, true, false, I>, a, s)
+                         : launch_persistent(k_tile<B, O, S, C, E, false, false, I>, a, s);
+        }
+    } else if constexpr (O == kOuterNone || O == kOuterTensor) {
+        return y ? launch_persistent(k_tile<B, O, S, C, E, false, true, I>, a, s)
+                 : launch_persistent(k_tile<B, O, S, C, E, false, false, I>, a, s);
     } else {
-        if (given) return y ? launch_persistent(k_tile<B, O, S, C, E, true, true>, a, s)
-                            : launch_persistent(k_tile<B, O, S, C, E, true, false>, a, s);
-        return y ? launch_persistent(k_tile<B, O, S, C, E, false, true>, a, s)
-                 : launch_persistent(k_tile<B, O, S, C, E, false, false>, a, s);
+        if (given) return y ? launch_persistent(k_tile<B, O, S, C, E, true, true, I>, a, s)
+                            : launch_persistent(k_tile<B, O, S, C, E, true, false, I>, a, s);
+        return y ? launch_persistent(k_tile<B, O, S, C, E, false, true, I>, a, s)
+                 : launch_persistent(k_tile<B, O, S, C, E, false, false, I>, a, s);
     }
 }
 
-template <int B, int O, bool C>
+template <int B, int O, bool C, bool I>
 hipError_t pick_sr_ef(bool sr, bool ef, const TileArgs& a, hipStream_t s)
 {
-    if (sr) return ef ? pick_given_y<B, O, true, C, true>(a, s) : pick_given_y<B, O, true, C, false>(a, s);
-    return ef ? pick_given_y<B, O, false, C, true>(a, s) : pick_given_y<B, O, false, C, false>(a, s);
+    if (sr) return ef ? pick_given_y<B, O, true, C, true, I>(a, s) : pick_given_y<B, O, true, C, false, I>(a, s);
+    return ef ? pick_given_y<B, O, false, C, true, I>(a, s) : pick_given_y<B, O, false, C, false, I>(a, s);
 }
 
 template <int B>
 hipError_t pick_outer(int outer_kind, bool sr, const TileArgs& a, hipStream_t s)
 {
     const bool ef = a.residual != nullptr;
-    if (a.col_codes == nullptr) return pick_sr_ef<B, kOuter2D, false>(sr, ef, a, s);   // rowwise 2D outer
+    const bool i2d = a.inner_2d != 0;
+    if (a.col_codes == nullptr) {
+        // rowwise only: the 2D outer mode, or 16 x 16 inner tiles
+        if (!i2d) return pick_sr_ef<B, kOuter2D, false, false>(sr, ef, a, s);
+        switch (outer_kind) {
+        case kOuterNone: return pick_sr_ef<B, kOuterNone, false, true>(sr, ef, a, s);
+        case kOuterTensor: return pick_sr_ef<B, kOuterTensor, false, true>(sr, ef, a, s);
+        default: return pick_sr_ef<B, kOuter2D, false, true>(sr, ef, a, s);
+        }
+    }
     switch (outer_kind) {
-    case kOuterNone: return pick_sr_ef<B, kOuterNone, true>(sr, ef, a, s);
-    case kOuterTensor: return pick_sr_ef<B, kOuterTensor, true>(sr, ef, a, s);
-    case kOuter1D: return pick_sr_ef<B, kOuter1D, true>(sr, ef, a, s);
-    default: return pick_sr_ef<B, kOuter2D, true>(sr, ef, a, s);
+    case kOuterNone:
+        return i2d ? pick_sr_ef<B, kOuterNone, true, true>(sr, ef, a, s)
+                   : pick_sr_ef<B, kOuterNone, true, false>(sr, ef, a, s);
+    case kOuterTensor:
+        return i2d ? pick_sr_ef<B, kOuterTensor, true, true>(sr, ef, a, s)
+                   : pick_sr_ef<B, kOuterTensor, true, false>(sr, ef, a, s);
+    case kOuter1D: return pick_sr_ef<B, kOuter1D, true, false>(sr, ef, a, s);   // no 16 x 16 inner tiles
+    default:
+        return i2d ? pick_sr_ef<B, kOuter2D, true, true>(sr, ef, a, s)
+                   : pick_sr_ef<B, kOuter2D, true, false>(sr, ef, a, s);
     }
 }
 

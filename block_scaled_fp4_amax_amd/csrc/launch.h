@@ -35,8 +35,8 @@ struct RowArgs {
 };
 
 // Tile parameters (64 x 64 tiles walked as 2 x 2 super-tiles): cast-transpose,
-// grouped cast-transpose, and the
-// rowwise-only 2D outer mode.
+// grouped cast-transpose, and the rowwise-only 2D outer and 16 x 16 inner
+// modes.
 struct TileArgs {
     const uint16_t* x;
     int64_t ld, cols;
@@ -52,6 +52,7 @@ struct TileArgs {
     uint64_t seed, step, index_base;
     int32_t obs16;           // 1D: obs / 16 (1, 2, 4); 2D: 4
     int32_t outer_given;
+    int32_t inner_2d;        // 1: one inner scale per 16 x 16 tile (none, tensorwise, 2D outer)
     int32_t ngroups;
     int32_t tiles_c;         // super-tile (128 x 128) columns: ceil(cols / 128)
     int32_t total_tiles;     // super-tiles in the launch

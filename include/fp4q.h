@@ -13,6 +13,10 @@
  *           E2M1 RTNE ("MXFP4 weight QAT recipes on MXFP8 and FP8 block-scaling
  *           hosts", Overview and Design).
  *
+ *   inner geometry (NVFP4 / AMDFP4): 1 x 16 blocks along the quantisation axis,
+ *           or 16 x 16 tiles sharing one scale ("Block-Scaled FP8 and FP4 Weight
+ *           Quantization", section 6: the transpose-consistent weight recipe).
+ *
  *   two-level scaling (NVFP4 / AMDFP4 only; ALTO page, Technical design):
  *     NONE        inner scales only;
  *     TENSORWISE  one FP32 scale amax/(scale_max*6) for the whole tensor;
@@ -78,7 +82,8 @@ enum {
     FP4Q_ERR_MODE = 4,        /* illegal combination: tensorwise with outer knobs, outer
                                  knobs outside outer-block mode, MXFP4 with a two-level
                                  mode, scale format not allowed for the format, a
-                                 precomputed outer scale without a two-level mode        */
+                                 precomputed outer scale without a two-level mode,
+                                 16 x 16 inner tiles with MXFP4 or 1D outer blocks        */
     FP4Q_ERR_UNSUPPORTED = 5, /* valid on the pages but not built here (see the function) */
     FP4Q_ERR_ALIGN = 6,       /* a pointer not 16-byte aligned, ld_x % 8 != 0             */
     FP4Q_ERR_WORKSPACE = 7,   /* workspace smaller than fp4q_workspace_bytes()            */
@@ -106,7 +111,17 @@ typedef struct {
                                   outer buffers (a precomputed scale, ALTO page,
                                   Implementation: precomputed_outer_scale)                     */
     int32_t input_dtype;       /* fp4q_dtype of x; only FP4Q_DTYPE_BF16 is accepted            */
-    int32_t reserved;          /* must be 0                                                    */
+    int32_t inner_2d;          /* NVFP4 / AMDFP4 inner scale geometry: 0 = one scale per 1 x 16
+                                  block along the quantisation axis; 1 = one scale per 16 x 16
+                                  tile of the source, from the largest normalised magnitude of
+                                  all its 256 values ("Block-Scaled FP8 and FP4 Weight
+                                  Quantization", section 6).  The scale byte is replicated for
+                                  each of the tile's 16 rows in row_scales (the 1 x 16 microblock
+                                  layout, same section), and the columnwise codes and scales are
+                                  the transposes of the rowwise ones: one quantisation decision
+                                  per element serves both directions.  Needs rows % 16 == 0;
+                                  not with MXFP4 or 1D outer blocks (their scales differ per
+                                  direction): FP4Q_ERR_MODE.                                   */
     uint64_t seed;             /* SR key                                                       */
     uint64_t step;             /* SR step (counter high word)                                  */
     uint64_t index_base;       /* SR global index of element (0, 0): element (i, j) draws with
@@ -153,7 +168,8 @@ size_t fp4q_workspace_bytes(const fp4q_cfg* cfg, int64_t rows, int64_t cols);
  *   workspace device scratch of >= fp4q_workspace_bytes() bytes (NULL if 0).
  * OUTER_BLOCK 2D needs rows % obs == 0 and supports obs == 64; 1D supports
  * obs in {16, 32, 64, 128} (others: FP4Q_ERR_UNSUPPORTED).  MXFP4 supports RNE
- * only and no residual.
+ * only and no residual.  With cfg->inner_2d, rows % 16 == 0 (FP4Q_ERR_SHAPE
+ * otherwise) and scales hold each 16 x 16 tile's byte in every one of its rows.
  */
 int fp4_quantize(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                  uint8_t* codes, uint8_t* scales, float* outer, float* residual,
@@ -171,7 +187,8 @@ int fp4_quantize(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int64_t c
  *                         of a columnwise buffer sharing its source's 2D outer
  *                         scale; 0 otherwise.
  *   y                     bf16 [rows, cols] device, written.
- * rounding, seed, step and index_base are ignored.
+ * rounding, seed, step and index_base are ignored; so is inner_2d, whose
+ * replicated scale layout dequantises exactly like 1 x 16 blocks.
  */
 int fp4_dequantize(const fp4q_cfg* cfg, const uint8_t* codes, const uint8_t* scales, const float* outer,
                    int64_t rows, int64_t cols, int32_t outer_transposed, uint16_t* y, void* stream);
@@ -206,7 +223,8 @@ int fp4_qdq(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int64_t cols, 
  *              update it.
  * Needs rows % 16 == 0.  OUTER_BLOCK supports obs == 64 (1D and 2D); 1D also
  * obs in {16, 32}.  Element (i, j) draws its SR variate once and uses it in
- * both directions.
+ * both directions.  With cfg->inner_2d the columnwise codes and scales are
+ * exactly the transposes of the rowwise ones.
  */
 int fp4_cast_transpose(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                        uint8_t* row_codes, uint8_t* row_scales, float* row_outer,
@@ -231,7 +249,8 @@ int fp4_cast_transpose(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int
  *                   [cols, rows_g/obs]; TENSORWISE one value per group).
  * Group g draws SR variates with index_base + (rows before g) * cols + i*cols + j,
  * the global row-major index in the stacked tensor, so the result equals G
- * single calls.  TENSORWISE is not supported here (FP4Q_ERR_UNSUPPORTED).
+ * single calls (also with cfg->inner_2d).  TENSORWISE is not supported here
+ * (FP4Q_ERR_UNSUPPORTED).
  */
 int fp4_cast_transpose_grouped(const fp4q_cfg* cfg, int32_t groups, const int64_t* rows_per_group,
                                int64_t cols, const uint16_t* x, int64_t ld_x,

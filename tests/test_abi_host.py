@@ -129,6 +129,35 @@ def test_grouped_rules():
     assert L.fp4_cast_transpose_grouped(ct.byref(cfg), 0, None, *args) == fq.OK
 
 
+def test_inner_2d_rules():
+    """16 x 16 inner tiles ("Block-Scaled FP8 and FP4 Weight Quantization",
+    section 6): NVFP4 / AMD-FP4 only, not with 1D outer groups (each direction
+    would be normalised differently), whole 16-row bands."""
+    C = fq.make_cfg
+    L = fq.lib()
+    assert q(C(format="mxfp4", inner_2d=True)) == fq.ERR_MODE
+    assert q(C(two_level="outer_block", outer_block_size=64, inner_2d=True)) == fq.ERR_MODE
+    assert ct_(C(two_level="outer_block", outer_block_size=64, inner_2d=True), col_outer=FAKE) == fq.ERR_MODE
+    bad = C()
+    bad.inner_2d = 2
+    assert q(bad) == fq.ERR_MODE
+    assert q(C(inner_2d=True), rows=40) == fq.ERR_SHAPE          # rows % 16, also rowwise
+    assert q(C(inner_2d=True), rows=40, cols=64) == fq.ERR_SHAPE
+    y = fq.lib().fp4_qdq(ct.byref(C(inner_2d=True)), FAKE, 24, 64, 64, FAKE, None, None, None, None, None, 0, None)
+    assert y == fq.ERR_SHAPE
+    cfg = C(two_level="outer_block", outer_block_size=64, outer_2d=True, inner_2d=True)
+    rows = (ct.c_int64 * 2)(64, 72)
+    args = (64, FAKE, 64, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, 0, None)
+    assert L.fp4_cast_transpose_grouped(ct.byref(cfg), 2, rows, *args) == fq.ERR_SHAPE
+    # the sizes of a 16 x 16 layout are those of the 1 x 16 one (scales replicated per row)
+    s = fq.fp4q_buffer_sizes(C(inner_2d=True, two_level="tensorwise"), 256, 512)
+    assert s["row_scales"] == 256 * 32 and s["col_scales"] == 512 * 16
+    with pytest.raises(fq.Fp4Error):
+        fq.fp4q_buffer_sizes(C(inner_2d=True), 40, 64)
+    # empty tensors validate the configuration only
+    assert q(C(inner_2d=True), rows=0, x=None, codes=None, scales=None, outer=None) == fq.OK
+
+
 def test_empty_tensors_are_accepted_without_launch():
     C = fq.make_cfg
     for cfg in (C(), C(format="mxfp4"), C(two_level="outer_block", outer_block_size=64, outer_2d=True)):
