@@ -43,40 +43,6 @@ __device__ __forceinline__ float e2m1_value(uint32_t m)
     return m < 2u ? lo : hi;
 }
 
-// Stochastic rounding of t = |T| / 2^24 onto the grid: between neighbours lo < hi the
-// result is hi with probability (t - lo) / (hi - lo), realised as
-// u16 < frac * 2^16 with u16 uniform in [0, 2^16) ("fp4-train" README,
-// Method).  Grid points and t >= 6 are deterministic.
-//
-// Integer form.  Let pos(t) be the position of t on the grid: the code of the
-// lower neighbour plus the fraction (pos = 2t on [0, 2), t + 2 on [2, 4),
-// t/2 + 4 on [4, 6]), and P = pos * 2^23.  For u16 an integer,
-// u16 < frac * 2^16 is 128 u16 < P mod 2^23, i.e. 128 u16 + 1 <= ceil(P) mod
-// 2^23, so the rounded code is floor((ceil(P) + 2^23 - 1 - 128 u16) / 2^23):
-// the carry out of the low 23 bits is the round-up.  With nu = 0xFFFF - u16,
-// 2^23 - 1 - 128 u16 = 128 nu + 127.  The caller passes T = t * 2^24:
-//   t < 2:   P = 2t * 2^23 = T;
-//   t >= 2:  within a binade the bit pattern of t is linear in t with the
-//            grid's own slope, so P = 2 bits(t) - 504 * 2^22
-//            = 2 bits(T) - 600 * 2^22 (bits(T) = bits(t) + 24 * 2^23).
-// t is clamped to 6 first (code 7, no round-up).  T may also be the binary32
-// rounding of t * 2^24 where t itself is below the normal range: then t > 0
-// exactly when T > 2^-126 (no binary32 quotient lies between the two
-// roundings' thresholds), and every positive subnormal t rounds up exactly
-// when u16 == 0.  ceil(T - 2^-126) gives both: 0 for T <= 2^-126, 1 above it
-// (T - 2^-126 is exact there), and ceil(T) from 2^-100 on, where subtracting
-// 2^-126 cannot cross an integer.
-__device__ __forceinline__ uint32_t e2m1_sr_code(float T, uint32_t nu)
-{
-    // |T| clamped to [0, 6 * 2^24] (t <= 6); the sign of T is ignored
-    const uint32_t b = __float_as_uint(__builtin_amdgcn_fmed3f(__builtin_fabsf(T), 0.0f, 0x1.8p26f));
-    const int32_t m = (int32_t)__builtin_floorf(0x1p-126f - __uint_as_float(b));   // -ceil(T - 2^-126)
-    const uint32_t nf = 127u - (uint32_t)m;                    // 127 + P, t < 2
-    const uint32_t ni = 2u * b + (127u - 600u * (1u << 22));  // 127 + P, t >= 2
-    const uint32_t n = b < 0x4C000000u ? nf : ni;             // bits(2^25): t = 2
-    return (n + (nu << 7)) >> 23;
-}
-
 // Two E2M1 codes (RNE, ties to the even code, saturating at 6, sign kept,
 // signed zero kept) of a and b, written into byte SEL of `old` (a in the low
 // nibble).  This is gfx950's v_cvt_scalef32_pk_fp4_f32 with scale 1; its

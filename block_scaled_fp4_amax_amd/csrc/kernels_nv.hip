@@ -133,7 +133,7 @@ __global__ __launch_bounds__(kThreads) void k_nv_rows(RowArgs a, uint32_t nblock
         normalize16(v, s_o, outer_inv(s_o), vn, true);
     }
     const BlockScale<BIAS> sc = block_scale<BIAS>(max_abs16(vn), rtab);
-    const uint2 packed = SR ? codes16_sr<BIAS>(vn, u, sc) : codes16_rne(vn, ktab[sc.code]);
+    const uint2 packed = SR ? codes16_sr<BIAS, OUTER == kOuterNone>(vn, u, sc) : codes16_rne(vn, ktab[sc.code]);
     if (a.codes) st_nt64(a.codes + e0 / 2, packed);
     if (a.scales) st_nt8(a.scales + (int64_t)i * bpr + jb, sc.code);
     if (a.y || EF) {

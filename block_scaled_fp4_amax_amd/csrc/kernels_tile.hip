@@ -98,24 +98,25 @@ __device__ __forceinline__ float tile16_max(float m)
     return __uint_as_float(v);
 }
 
-// Codes of 16 normalised values with a given inner scale.
-template <int BIAS, bool SR>
+// Codes of 16 normalised values with a given inner scale (CLAMP: no outer
+// scale bounds the quotients, see codes16_sr).
+template <int BIAS, bool SR, bool CLAMP>
 __device__ __forceinline__ uint2 encode16(const float (&vn)[16], const uint32_t (&u)[8], const float2* ktab,
                                           const BlockScale<BIAS>& sc)
 {
-    if (SR) return codes16_sr<BIAS>(vn, u, sc);
+    if (SR) return codes16_sr<BIAS, CLAMP>(vn, u, sc);
     return codes16_rne(vn, ktab[sc.code]);
 }
 
 // One block's scale and codes; with I2D the scale comes from the 16 x 16 tile
 // (tile16_max) instead of the lane's own 16 values.
-template <int BIAS, bool SR, bool I2D>
+template <int BIAS, bool SR, bool I2D, bool CLAMP>
 __device__ __forceinline__ uint2 quant16(const float (&vn)[16], const uint32_t (&u)[8], const double* tab,
                                          const float2* ktab, BlockScale<BIAS>& sc)
 {
     const float b = max_abs16(vn);
     sc = block_scale<BIAS>(I2D ? tile16_max(b) : b, tab);
-    return encode16<BIAS, SR>(vn, u, ktab, sc);
+    return encode16<BIAS, SR, CLAMP>(vn, u, ktab, sc);
 }
 
 // Super-tiles: the unit a workgroup walks is a 2 x 2 block of 64 x 64 tiles
@@ -279,12 +280,14 @@ constexpr bool tile_unrolled()
 // Register budget per lane: 128 VGPRs (4 waves per SIMD) wherever the kernel
 // fits in them without scratch spills, 168 (3 waves) for the stochastic-
 // rounding variants that do not (2D / tensorwise / no outer scale without a
-// residual, and tensorwise with one): a spill reload inside the tile loop
-// waits for every load in flight, the next tile's prefetch included.
-template <int BIAS, int OUTER, bool SR, bool COLS, bool EF>
+// residual, tensorwise with one, and 16 x 16 inner tiles with a residual and a
+// 2D outer scale): a spill reload inside the tile loop waits for every load in
+// flight, the next tile's prefetch included.
+template <int BIAS, int OUTER, bool SR, bool COLS, bool EF, bool I2D>
 constexpr int tile_waves_per_simd()
 {
-    const bool tight = SR && ((!EF && OUTER != kOuter1D) || (EF && OUTER == kOuterTensor));
+    const bool tight = SR && ((!EF && OUTER != kOuter1D) || (EF && OUTER == kOuterTensor) ||
+                              (EF && I2D && COLS && OUTER == kOuter2D));
     return tight ? 3 : 4;
 }
 
@@ -298,7 +301,7 @@ constexpr float kNoSubnormalScale = 0x1p-7f;
 // memory instructions with no branch around any of them, so the compiler's
 // wait for the next tile's loads never waits for earlier stores.
 template <int BIAS, int OUTER, bool SR, bool COLS, bool EF, bool GIVEN, bool Y, bool I2D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(tile_waves_per_simd<BIAS, OUTER, SR, COLS, EF>())))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(tile_waves_per_simd<BIAS, OUTER, SR, COLS, EF, I2D>())))
 void k_tile(TileArgs a)
 {
     __shared__ float4 lds_v[COLS ? kTile * kTile / 4 : 1];
@@ -447,7 +450,7 @@ void k_tile(TileArgs a)
         }
         {
             BlockScale<BIAS> sc;
-            const uint2 packed = quant16<BIAS, SR, I2D>(vn, u, rtab, ktab, sc);
+            const uint2 packed = quant16<BIAS, SR, I2D, OUTER == kOuterNone>(vn, u, rtab, ktab, sc);
             ro.codes = packed;
             ro.scale = sc.code;
             if (EF || Y) {
@@ -542,11 +545,11 @@ void k_tile(TileArgs a)
                 sc.code = lds_tsc[rs * 4 + (cc >> 4)];
                 sc.d = 0.0f;   // not needed for encoding
                 sc.rd = inner_recip<BIAS>(sc.code, rtab);
-                co.codes = encode16<BIAS, SR>(cv, cu, ktab, sc);
+                co.codes = encode16<BIAS, SR, OUTER == kOuterNone>(cv, cu, ktab, sc);
                 co.scale = sc.code;
             } else {
                 BlockScale<BIAS> sc;
-                co.codes = quant16<BIAS, SR, false>(cv, cu, rtab, ktab, sc);
+                co.codes = quant16<BIAS, SR, false, OUTER == kOuterNone>(cv, cu, rtab, ktab, sc);
                 co.scale = sc.code;
             }
         }

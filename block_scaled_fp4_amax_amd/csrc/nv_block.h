@@ -149,31 +149,97 @@ __device__ __forceinline__ uint2 codes16_rne(const float (&vn)[16], float2 k)
     return make_uint2(lo, hi);
 }
 
-template <int BIAS>
-__device__ __forceinline__ uint32_t codes8_sr(const float* vn, const uint32_t* u, double rd24)
+// ---------------------------------------------------------------- stochastic-rounding codes
+// Stochastic rounding of t = RN32(|v_n| / d) onto the E2M1 grid ("fp4-train"
+// README, Method): between neighbours lo < hi round up iff u16 < frac * 2^16,
+// frac = (t - lo) / (hi - lo), with grid points and t >= 6 deterministic.
+//
+// gfx950's v_cvt_scalef32_sr_pk_fp4_f32 does this in one instruction once its
+// inputs are arranged (every case checked on the device: all 65536 u16 against
+// about 3100 t values covering every binade, the fractions next to each k/2^16
+// and the subnormal range).  Measured behaviour of the instruction with the
+// value in its first slot: it sees t on a grid of 2^-23 (below 1, lower bits of
+// t are dropped), and rounds up iff the 22 bits of t's fraction below the E2M1
+// step plus the top 22 bits of the seed carry.  So:
+//   - the value passed is c = ceil(t * 2^23) with the instruction's exact
+//     power-of-two scale 2^23 (t' = c / 2^23; for t >= 1, t' = t): rounding a
+//     dropped remainder up makes "u16 < frac * 2^16" and "carry" agree for
+//     every fraction, since u16 * 2^(k-16) and the kept bits are multiples of
+//     the grid step;
+//   - seed = (~u16 << 16) | 0xFFFF: its top 22 bits are 2^22 - 1 - 64 u16, so
+//     the carry happens iff the kept fraction exceeds 64 u16;
+//   - the instruction's second slot draws from the seed shifted by one bit, so
+//     each element goes through a first slot of its own: even elements into one
+//     word, odd elements into another, merged by a shift.
+// c comes from T = RN32(v_n * RN64(1/d) * 2^23), which is t * 2^23 exactly while
+// t is a normal binary32.  Below that only "t > 0" matters (c = 1 rounds up iff
+// u16 == 0), and t > 0 exactly when T > 2^-127: the quotient v_n / d is either
+// 2^-150 exactly (T = 2^-127, t = 0) or at least 2^-7 of itself away from it
+// (v_n is then subnormal and d has 4 significant bits).  ceil(|T| - 2^-127)
+// gives both cases, and ceil(t * 2^23) from T = 2^-100 on.  Without an outer
+// scale t can exceed 2^104 (saturated inner scales), so CLAMP bounds T to
+// [2^-127, 6 * 2^23] first; otherwise t stays near 6 and the instruction
+// saturates by itself.  Magnitude nibbles carry no sign (the masks drop the -0
+// that ceil gives for T == 0); the sign nibbles come from the hardware RNE pack
+// of v_n / 2^125, which is a zero of v_n's sign unless |v_n| >= 2^123, and such
+// values saturate (code 7) under every inner scale, so OR-ing stays exact.
+
+// The code of c / 2^23 (first slot, seed as above) in bits 8 SEL .. 8 SEL + 2,
+// every other bit zero.  Only those magnitude bits of the result are used: the
+// compiler does not tie the builtin's first operand to the destination, so
+// the other bytes of the result are not defined.
+template <int SEL>
+__device__ __forceinline__ uint32_t sr_code_at(float c, uint32_t seed)
 {
-    constexpr float kSignOnly = 0x1p125f;
-    uint32_t w = 0;
-    w = fp4x2_rne_scaled<0>(w, vn[0], vn[1], kSignOnly);
-    w = fp4x2_rne_scaled<1>(w, vn[2], vn[3], kSignOnly);
-    w = fp4x2_rne_scaled<2>(w, vn[4], vn[5], kSignOnly);
-    w = fp4x2_rne_scaled<3>(w, vn[6], vn[7], kSignOnly);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const float T = div_inv64(vn[k], rd24);               // +-t * 2^24
-        const uint32_t nw = ~u[k >> 1];                       // element k's variate: half (k & 1)
-        const uint32_t nu = (k & 1) ? (nw >> 16) : (nw & 0xFFFFu);
-        w |= e2m1_sr_code(T, nu) << (4 * k);
-    }
-    return w;
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    f32x2_t v;
+    v.x = c;
+    v.y = 0.0f;
+    return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, v, seed, 0x1p23f, SEL) & (0x7u << (8 * SEL));
 }
 
-template <int BIAS>
+template <bool CLAMP>
+__device__ __forceinline__ float sr_fixed23(float T)
+{
+    float a = __builtin_fabsf(T);
+    if (CLAMP) a = __builtin_amdgcn_fmed3f(a, 0x1p-127f, 0x1.8p25f);
+    return __builtin_ceilf(a - 0x1p-127f);
+}
+
+template <bool CLAMP>
+__device__ __forceinline__ uint32_t codes8_sr(const float* vn, const uint32_t* u, double rd23)
+{
+    constexpr float kSignOnly = 0x1p125f;
+    uint32_t sg = 0;
+    sg = fp4x2_rne_scaled<0>(sg, vn[0], vn[1], kSignOnly);
+    sg = fp4x2_rne_scaled<1>(sg, vn[2], vn[3], kSignOnly);
+    sg = fp4x2_rne_scaled<2>(sg, vn[4], vn[5], kSignOnly);
+    sg = fp4x2_rne_scaled<3>(sg, vn[6], vn[7], kSignOnly);
+    // element 2j takes the low 16 bits of u[j], element 2j + 1 the high 16 bits
+    uint32_t ev, od, nw;
+    nw = ~u[0];
+    ev = sr_code_at<0>(sr_fixed23<CLAMP>(div_inv64(vn[0], rd23)), (nw << 16) | 0xFFFFu);
+    od = sr_code_at<0>(sr_fixed23<CLAMP>(div_inv64(vn[1], rd23)), nw | 0xFFFFu);
+    nw = ~u[1];
+    ev |= sr_code_at<1>(sr_fixed23<CLAMP>(div_inv64(vn[2], rd23)), (nw << 16) | 0xFFFFu);
+    od |= sr_code_at<1>(sr_fixed23<CLAMP>(div_inv64(vn[3], rd23)), nw | 0xFFFFu);
+    nw = ~u[2];
+    ev |= sr_code_at<2>(sr_fixed23<CLAMP>(div_inv64(vn[4], rd23)), (nw << 16) | 0xFFFFu);
+    od |= sr_code_at<2>(sr_fixed23<CLAMP>(div_inv64(vn[5], rd23)), nw | 0xFFFFu);
+    nw = ~u[3];
+    ev |= sr_code_at<3>(sr_fixed23<CLAMP>(div_inv64(vn[6], rd23)), (nw << 16) | 0xFFFFu);
+    od |= sr_code_at<3>(sr_fixed23<CLAMP>(div_inv64(vn[7], rd23)), nw | 0xFFFFu);
+    return sg | ev | (od << 4);
+}
+
+// SR codes of 16 normalised values with the block's scale; CLAMP when no
+// outer scale bounds the quotients.
+template <int BIAS, bool CLAMP>
 __device__ __forceinline__ uint2 codes16_sr(const float (&vn)[16], const uint32_t (&u)[8], const BlockScale<BIAS>& s)
 {
-    const double rd24 = s.rd * 0x1p24;
-    const uint32_t lo = codes8_sr<BIAS>(vn, u, rd24);
-    const uint32_t hi = codes8_sr<BIAS>(vn + 8, u + 4, rd24);
+    const double rd23 = s.rd * 0x1p23;
+    const uint32_t lo = codes8_sr<CLAMP>(vn, u, rd23);
+    const uint32_t hi = codes8_sr<CLAMP>(vn + 8, u + 4, rd23);
     return make_uint2(lo, hi);
 }
 
