@@ -70,6 +70,17 @@ int orc_max_threads(void)
 #endif
 }
 
+/* Thread count for the parallel loops that follow (timing only: the loops
+ * split independent rows, so results do not depend on it). */
+void orc_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* E2M1 magnitude grid, [FP4T] Method: {0, .5, 1, 1.5, 2, 3, 4, 6}; the 3-bit
  * magnitude code m indexes it and the sign is a separate bit (code = s*8+m). */
 static const double E2M1_GRID[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};

@@ -53,6 +53,8 @@ def lib():
         L.orc_sr_u16.argtypes = [ct.c_uint64, ct.c_uint64, ct.c_uint64]
         L.orc_max_threads.restype = ct.c_int
         L.orc_max_threads.argtypes = []
+        L.orc_set_threads.restype = None
+        L.orc_set_threads.argtypes = [ct.c_int]
         for name in ("orc_f32_to_bf16_array", "orc_e2m1_rne_array"):
             getattr(L, name).restype = None
             getattr(L, name).argtypes = [P, ct.c_int64, P]
@@ -85,6 +87,11 @@ def _p(a):
 
 def threads() -> int:
     return lib().orc_max_threads()
+
+
+def set_threads(n: int) -> None:
+    """OpenMP thread count of the oracle's parallel loops (timing only)."""
+    lib().orc_set_threads(int(n))
 
 
 # ---------------------------------------------------------------- primitives
