@@ -745,3 +745,140 @@ int orc_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t R, in
         }
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* FP8 re-encodings of the MXFP4 projection ([TEQAT] Overview, Design,       */
+/* Correctness: the projected weight goes to the MXFP8 (1x32 UE8M0 scale,    */
+/* E4M3 payload) and Float8 128x128 block-scaling hosts; the rowwise MXFP8   */
+/* encoding is bitwise lossless, the 128x128 encoding is lossless within a   */
+/* tile's E4M3 headroom, the columnwise 32x1 encoding is a bounded           */
+/* re-quantisation).                                                         */
+/* ------------------------------------------------------------------------ */
+
+/* E4M3 (OCP E4M3FN) payload byte of v: RNE onto the finite grid with
+ * subnormals (orc_scale_encode on |v|), sign bit 0x80 kept also for zero.
+ * NaN encodes as 0xFF (an E4M3FN NaN; reading: the pages fix no NaN payload).
+ * Above 448 the code saturates to 0x7E (never reached below: every encoding
+ * here keeps |v| <= 384). */
+static uint8_t e4m3_payload(double v)
+{
+    if (isnan(v)) return 0xFF;
+    const uint8_t s = signbit(v) ? 0x80 : 0x00;
+    return (uint8_t)(s | (uint8_t)orc_scale_encode(1, (float)fabs(v)));
+}
+
+uint8_t orc_e4m3_payload(double v) { return e4m3_payload(v); }
+
+/* MXFP8 shared exponent of a block (OCP Microscaling formats v1.0: the scale
+ * is 2^(floor(log2(amax)) - emax) with emax = 8 for E4M3), clamped to the
+ * UE8M0 range [-127, 127]; a block with no nonzero finite element takes -127
+ * (code 0).  Reading: amax is over the finite elements. */
+static int mx8_exponent(double amax)
+{
+    if (!(amax > 0.0)) return -127;
+    int e;
+    (void)frexp(amax, &e);          /* amax = f * 2^e, f in [0.5, 1) */
+    int E = (e - 1) - 8;
+    if (E < -127) E = -127;
+    if (E > 127) E = 127;
+    return E;
+}
+
+/* Power-of-two scale exponent of a 128 x 128 block: the smallest e with
+ * amax <= 448 * 2^e (reading of "lossless within each tile's E4M3 headroom":
+ * a power-of-two scale keeps the E4M3 payload grid exact down to 2^14 below
+ * the tile maximum); amax == 0 (no nonzero finite element) gives e = 0. */
+static int blk_exponent(double amax)
+{
+    if (!(amax > 0.0)) return 0;
+    int e = -300;
+    while (amax > ldexp(448.0, e)) ++e;
+    return e;
+}
+
+#define F8BLK 128
+
+/* MXFP4 projection of X [R, C] (bf16 bits) and its FP8 re-encodings, every
+ * output optional (NULL skips it):
+ *   y        bf16 [R, C]        the projection (orc_mx_qdq)
+ *   mx8_row  E4M3 [R, C], mx8_row_sc UE8M0 [R, C/32]: 1 x 32 blocks of y along rows
+ *   mx8_col  E4M3 [C, R], mx8_col_sc UE8M0 [C, R/32]: 32 x 1 blocks of y down the
+ *            columns, stored as the rowwise layout of y^T
+ *   blk      E4M3 [R, C], blk_t E4M3 [C, R] (its transpose), blk_sc FP32
+ *            [R/128, C/128]: 128 x 128 blocks with a power-of-two scale
+ * Payload = e4m3(y / scale) with the scale of the element's block. */
+int orc_mx_project_encode(const uint16_t* X, int64_t R, int64_t C, uint16_t* y_out,
+                          uint8_t* mx8_row, uint8_t* mx8_row_sc, uint8_t* mx8_col, uint8_t* mx8_col_sc,
+                          uint8_t* blk, uint8_t* blk_t, float* blk_sc)
+{
+    if (R < 0 || C < 0 || C % MXB) return -2;
+    if ((mx8_col || mx8_col_sc) && R % MXB) return -2;
+    if ((blk || blk_t || blk_sc) && (R % F8BLK || C % F8BLK)) return -2;
+    const int64_t N = R * C;
+    uint16_t* y = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(N ? N : 1));
+    orc_mx_qdq(X, R, C, NULL, NULL, y);
+    if (y_out) memcpy(y_out, y, sizeof(uint16_t) * (size_t)N);
+
+    /* rowwise MXFP8: the 1 x 32 blocks of y along each row */
+    if (mx8_row || mx8_row_sc) {
+#pragma omp parallel for schedule(static)
+        for (int64_t b = 0; b < R * (C / MXB); ++b) {
+            const uint16_t* yb = y + b * MXB;
+            double A = 0.0;
+            for (int k = 0; k < MXB; ++k) {
+                double v = (double)orc_bf16_to_f32(yb[k]);
+                if (!isnan(v) && fabs(v) > A) A = fabs(v);
+            }
+            const int E = mx8_exponent(A);
+            if (mx8_row_sc) mx8_row_sc[b] = (uint8_t)(E + 127);
+            if (mx8_row)
+                for (int k = 0; k < MXB; ++k)
+                    mx8_row[b * MXB + k] = e4m3_payload((double)orc_bf16_to_f32(yb[k]) * ldexp(1.0, -E));
+        }
+    }
+
+    /* columnwise MXFP8: 32 x 1 blocks down each column, i.e. the rowwise
+     * encoding of y^T */
+    if (mx8_col || mx8_col_sc) {
+#pragma omp parallel for schedule(static)
+        for (int64_t j = 0; j < C; ++j)
+            for (int64_t g = 0; g < R / MXB; ++g) {
+                double A = 0.0;
+                for (int64_t i = g * MXB; i < (g + 1) * MXB; ++i) {
+                    double v = (double)orc_bf16_to_f32(y[i * C + j]);
+                    if (!isnan(v) && fabs(v) > A) A = fabs(v);
+                }
+                const int E = mx8_exponent(A);
+                if (mx8_col_sc) mx8_col_sc[j * (R / MXB) + g] = (uint8_t)(E + 127);
+                if (mx8_col)
+                    for (int64_t i = g * MXB; i < (g + 1) * MXB; ++i)
+                        mx8_col[j * R + i] = e4m3_payload((double)orc_bf16_to_f32(y[i * C + j]) * ldexp(1.0, -E));
+            }
+    }
+
+    /* 128 x 128 blocks with one power-of-two FP32 scale each; blk_t is the
+     * same payload transposed (a square block is transpose-consistent) */
+    if (blk || blk_t || blk_sc) {
+        const int64_t TR = R / F8BLK, TC = C / F8BLK;
+#pragma omp parallel for schedule(static)
+        for (int64_t t = 0; t < TR * TC; ++t) {
+            const int64_t ti = t / TC, tj = t % TC;
+            double A = 0.0;
+            for (int64_t i = ti * F8BLK; i < (ti + 1) * F8BLK; ++i)
+                for (int64_t j = tj * F8BLK; j < (tj + 1) * F8BLK; ++j) {
+                    double v = (double)orc_bf16_to_f32(y[i * C + j]);
+                    if (!isnan(v) && fabs(v) > A) A = fabs(v);
+                }
+            const int e = blk_exponent(A);
+            if (blk_sc) blk_sc[t] = (float)ldexp(1.0, e);
+            for (int64_t i = ti * F8BLK; i < (ti + 1) * F8BLK; ++i)
+                for (int64_t j = tj * F8BLK; j < (tj + 1) * F8BLK; ++j) {
+                    const uint8_t p = e4m3_payload((double)orc_bf16_to_f32(y[i * C + j]) * ldexp(1.0, -e));
+                    if (blk) blk[i * C + j] = p;
+                    if (blk_t) blk_t[j * R + i] = p;
+                }
+        }
+    }
+    free(y);
+    return 0;
+}

@@ -75,6 +75,10 @@ def lib():
                                         ct.c_int64, ct.c_int64, P]
         L.orc_mx_qdq.restype = ct.c_int
         L.orc_mx_qdq.argtypes = [P, ct.c_int64, ct.c_int64, P, P, P]
+        L.orc_mx_project_encode.restype = ct.c_int
+        L.orc_mx_project_encode.argtypes = [P, ct.c_int64, ct.c_int64, P, P, P, P, P, P, P, P]
+        L.orc_e4m3_payload.restype = ct.c_uint8
+        L.orc_e4m3_payload.argtypes = [ct.c_double]
         L.orc_mx_dequantize.restype = ct.c_int
         L.orc_mx_dequantize.argtypes = [P, P, ct.c_int64, ct.c_int64, P]
         _lib = L
@@ -285,6 +289,43 @@ def mx_qdq(x):
     if rc != 0:
         raise ValueError("oracle rejected the shape (%d)" % rc)
     return codes, scales, y
+
+
+def e4m3_payload(v):
+    """E4M3 payload byte of one value (RNE, subnormals, sign kept, NaN -> 0xFF)."""
+    return int(lib().orc_e4m3_payload(float(v)))
+
+
+def mx_project_encode(x, *, y=True, mx8_row=True, mx8_col=True, blk=True):
+    """MXFP4 projection of x (bf16 bits [R, C]) and its FP8 re-encodings.
+
+    Returns a dict with any of: y (bf16 bits [R, C]); mx8_row (E4M3 [R, C]) and
+    mx8_row_scales (UE8M0 [R, C/32]); mx8_col (E4M3 [C, R]) and mx8_col_scales
+    (UE8M0 [C, R/32]); blk (E4M3 [R, C]), blk_t (E4M3 [C, R]) and blk_scales
+    (FP32 [R/128, C/128]).
+    """
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    R, C = x.shape
+    out = {}
+    if y:
+        out["y"] = np.zeros((R, C), np.uint16)
+    if mx8_row:
+        out["mx8_row"] = np.zeros((R, C), np.uint8)
+        out["mx8_row_scales"] = np.zeros((R, C // 32), np.uint8)
+    if mx8_col:
+        out["mx8_col"] = np.zeros((C, R), np.uint8)
+        out["mx8_col_scales"] = np.zeros((C, R // 32), np.uint8)
+    if blk:
+        out["blk"] = np.zeros((R, C), np.uint8)
+        out["blk_t"] = np.zeros((C, R), np.uint8)
+        out["blk_scales"] = np.zeros((R // 128, C // 128), np.float32)
+    g = out.get
+    rc = lib().orc_mx_project_encode(_p(x), R, C, _p(g("y")), _p(g("mx8_row")), _p(g("mx8_row_scales")),
+                                     _p(g("mx8_col")), _p(g("mx8_col_scales")), _p(g("blk")), _p(g("blk_t")),
+                                     _p(g("blk_scales")))
+    if rc != 0:
+        raise ValueError("oracle rejected the shape (%d)" % rc)
+    return out
 
 
 def mx_dequantize(codes, scales, R, C):
