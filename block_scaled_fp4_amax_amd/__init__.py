@@ -15,7 +15,7 @@ import os
 __all__ = [
     "Fp4Error", "Cfg", "Sizes", "make_cfg", "lib", "fp4q_abi_version", "fp4q_status_str", "fp4q_buffer_sizes",
     "fp4q_workspace_bytes", "fp4_quantize", "fp4_dequantize", "fp4_qdq", "fp4_cast_transpose",
-    "fp4_cast_transpose_grouped", "LIB_PATH",
+    "fp4_cast_transpose_grouped", "fp4_mx_project_fp8", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp4q.so")
@@ -92,6 +92,8 @@ def lib():
         L.fp4_cast_transpose.argtypes = [C, P, I64, I64, I64, P, P, P, P, P, P, P, P, SZ, P]
         L.fp4_cast_transpose_grouped.restype = ct.c_int
         L.fp4_cast_transpose_grouped.argtypes = [C, ct.c_int32, P, I64, P, I64, P, P, P, P, P, P, P, P, SZ, P]
+        L.fp4_mx_project_fp8.restype = ct.c_int
+        L.fp4_mx_project_fp8.argtypes = [C, P, I64, I64, I64, P, P, P, P, P, P, P, P, P]
         if L.fp4q_abi_version() != ABI_VERSION:
             raise ImportError("libfp4q.so ABI %d, binding expects %d" % (L.fp4q_abi_version(), ABI_VERSION))
         _lib = L
@@ -287,3 +289,31 @@ def fp4_cast_transpose_grouped(x, rows_per_group, cfg, *, residual=None, stream=
                                             _ptr(out["col_scales"]), _ptr(out["col_outer"]), _ptr(residual), None, 0,
                                             _stream(stream)), "fp4_cast_transpose_grouped")
     return out
+
+
+def fp4_mx_project_fp8(x, cfg=None, *, y=True, mx8_row=True, mx8_col=True, blk=True, stream=None, out=None):
+    """MXFP4 projection of x and its FP8 re-encodings in one pass.  Returns a
+    dict with the requested outputs: "y" (bf16 [R, C]); "mx8_row" (uint8 E4M3
+    [R, C]) and "mx8_row_scales" (uint8 UE8M0 [R, C/32]); "mx8_col" ([C, R]) and
+    "mx8_col_scales" ([C, R/32]); "blk" ([R, C]), "blk_t" ([C, R]) and
+    "blk_scales" (float32 [R/128, C/128]).  `out` may supply any of them."""
+    torch = _torch()
+    x, R, C, ld = _src(x)
+    dev = x.device
+    cfg = cfg if cfg is not None else make_cfg(format="mxfp4")
+    out = dict(out or {})
+    want = {"y": (y, (R, C), torch.bfloat16), "mx8_row": (mx8_row, (R, C), torch.uint8),
+            "mx8_row_scales": (mx8_row, (R, C // 32), torch.uint8), "mx8_col": (mx8_col, (C, R), torch.uint8),
+            "mx8_col_scales": (mx8_col, (C, R // 32), torch.uint8), "blk": (blk, (R, C), torch.uint8),
+            "blk_t": (blk, (C, R), torch.uint8), "blk_scales": (blk, (R // 128, C // 128), torch.float32)}
+    for k, (on, shp, dt) in want.items():
+        if on and out.get(k) is None:
+            out[k] = torch.empty(shp, dtype=dt, device=dev)
+        if not on:
+            out[k] = None
+    g = out.get
+    _check(lib().fp4_mx_project_fp8(ct.byref(cfg), _ptr(x), R, C, ld, _ptr(g("y")), _ptr(g("mx8_row")),
+                                    _ptr(g("mx8_row_scales")), _ptr(g("mx8_col")), _ptr(g("mx8_col_scales")),
+                                    _ptr(g("blk")), _ptr(g("blk_t")), _ptr(g("blk_scales")), _stream(stream)),
+           "fp4_mx_project_fp8")
+    return {k: v for k, v in out.items() if v is not None}

@@ -389,6 +389,45 @@ int fp4_cast_transpose(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int
     return hip_status(launch_tiles(r.bias, r.outer_kind, r.sr, a, s));
 }
 
+int fp4_mx_project_fp8(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                       uint16_t* y, uint8_t* mx8_row, uint8_t* mx8_row_scales, uint8_t* mx8_col,
+                       uint8_t* mx8_col_scales, uint8_t* blk, uint8_t* blk_t, float* blk_scales, void* stream)
+{
+    Resolved r;
+    int st = resolve(cfg, r);
+    if (st) return st;
+    if (r.fmt != FP4Q_MXFP4) return FP4Q_ERR_MODE;
+    st = check_shape(r, rows, cols, ld_x, false);
+    if (st) return st;
+    if ((mx8_row == nullptr) != (mx8_row_scales == nullptr)) return FP4Q_ERR_NULL;
+    if ((mx8_col == nullptr) != (mx8_col_scales == nullptr)) return FP4Q_ERR_NULL;
+    const bool want_blk = blk || blk_t || blk_scales;
+    if (mx8_col && rows % 32) return FP4Q_ERR_SHAPE;
+    if (want_blk && (rows % 128 || cols % 128)) return FP4Q_ERR_SHAPE;
+    // 32-bit byte offsets inside a 128-row tile
+    if (rows > ((int64_t)1 << 22) || ld_x > ((int64_t)1 << 22)) return FP4Q_ERR_UNSUPPORTED;
+    if (rows == 0 || cols == 0) return FP4Q_OK;
+    if (!x) return FP4Q_ERR_NULL;
+    if (misaligned(x, 16) || misaligned(y, 16) || misaligned(mx8_row, 16) || misaligned(mx8_col, 16) ||
+        misaligned(blk, 16) || misaligned(blk_t, 16) || misaligned(blk_scales, 4))
+        return FP4Q_ERR_ALIGN;
+    if (!y && !mx8_row && !mx8_col && !want_blk) return FP4Q_OK;   // nothing asked
+    Mx8Args a;
+    a.x = x;
+    a.rows = rows;
+    a.cols = cols;
+    a.ld = ld_x;
+    a.y = y;
+    a.mx8_row = mx8_row;
+    a.mx8_row_sc = mx8_row_scales;
+    a.mx8_col = mx8_col;
+    a.mx8_col_sc = mx8_col_scales;
+    a.blk = blk;
+    a.blk_t = blk_t;
+    a.blk_sc = blk_scales;
+    return hip_status(launch_mx_fp8(a, (hipStream_t)stream));
+}
+
 int fp4_cast_transpose_grouped(const fp4q_cfg* cfg, int32_t groups, const int64_t* rows_per_group, int64_t cols,
                                const uint16_t* x, int64_t ld_x, uint8_t* row_codes, uint8_t* row_scales,
                                float* row_outer, uint8_t* col_codes, uint8_t* col_scales, float* col_outer,

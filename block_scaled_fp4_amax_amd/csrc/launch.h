@@ -64,6 +64,22 @@ struct TileArgs {
 
 enum OuterKind { kOuterNone = 0, kOuterTensor = 1, kOuter1D = 2, kOuter2D = 3 };
 
+// MXFP4 projection and FP8 re-encodings (every output may be null).
+struct Mx8Args {
+    const uint16_t* x;
+    int64_t rows, cols, ld;
+    uint16_t* y;               // bf16 [rows, cols]
+    uint8_t* mx8_row;          // E4M3 [rows, cols]
+    uint8_t* mx8_row_sc;       // UE8M0 [rows, cols / 32]
+    uint8_t* mx8_col;          // E4M3 [cols, rows]
+    uint8_t* mx8_col_sc;       // UE8M0 [cols, rows / 32]
+    uint8_t* blk;              // E4M3 [rows, cols]
+    uint8_t* blk_t;            // E4M3 [cols, rows]
+    float* blk_sc;             // FP32 [rows / 128, cols / 128]
+};
+
+hipError_t launch_mx_fp8(const Mx8Args& a, hipStream_t s);
+
 hipError_t launch_mx_qdq(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, uint16_t* y,
                          uint8_t* codes, uint8_t* scales, hipStream_t s);
 

@@ -258,6 +258,40 @@ int fp4_cast_transpose_grouped(const fp4q_cfg* cfg, int32_t groups, const int64_
                                uint8_t* col_codes, uint8_t* col_scales, float* col_outer,
                                float* residual, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * fp4_mx_project_fp8 -- the MXFP4 projection of a bf16 weight and its FP8
+ * re-encodings from one read of the weight ("MXFP4 weight QAT recipes on MXFP8
+ * and FP8 block-scaling hosts", Overview, Design, Correctness: the projected
+ * weight feeds MXFP8 and Float8 128x128 block-scaling hosts; the rowwise MXFP8
+ * encoding is bitwise lossless, the 128x128 encoding lossless within a tile's
+ * E4M3 headroom, the columnwise MXFP8 encoding a bounded re-quantisation).
+ * cfg: format MXFP4 (RNE, no two-level mode).  With y the bf16 projection
+ * (as fp4_qdq writes it) every output is optional (NULL skips it):
+ *   y              bf16 [rows, cols]
+ *   mx8_row        E4M3 [rows, cols] and mx8_row_scales UE8M0 [rows, cols/32]:
+ *                  1 x 32 blocks along rows, scale 2^E with
+ *                  E = floor(log2(amax)) - 8 (the OCP microscaling rule for
+ *                  E4M3) clamped to [-127, 127], amax over the block's finite
+ *                  values (code 0 when there is none);
+ *   mx8_col        E4M3 [cols, rows] and mx8_col_scales UE8M0 [cols, rows/32]:
+ *                  the same on 32 x 1 blocks, stored as the rowwise layout of
+ *                  y^T (needs rows % 32 == 0);
+ *   blk            E4M3 [rows, cols], blk_t E4M3 [cols, rows] (its transpose)
+ *                  and blk_scales FP32 [rows/128, cols/128]: 128 x 128 blocks
+ *                  with the smallest power-of-two scale s for which
+ *                  amax / s <= 448 (1 for a block without a finite nonzero
+ *                  value); needs rows % 128 == 0 and cols % 128 == 0.
+ * Payload = E4M3 of y / scale, round to nearest even with subnormals, sign kept
+ * (also for zero); a NaN element of y (a poisoned MXFP4 block) encodes as 0xFF.
+ * mx8_row and mx8_row_scales are given together or not at all, likewise
+ * mx8_col and mx8_col_scales.  Needs cols % 32 == 0; rows and ld_x up to 2^22
+ * (FP4Q_ERR_UNSUPPORTED beyond).  x, y, mx8_row, mx8_col, blk and blk_t
+ * 16-byte aligned, blk_scales 4-byte aligned.
+ */
+int fp4_mx_project_fp8(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                       uint16_t* y, uint8_t* mx8_row, uint8_t* mx8_row_scales, uint8_t* mx8_col,
+                       uint8_t* mx8_col_scales, uint8_t* blk, uint8_t* blk_t, float* blk_scales, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

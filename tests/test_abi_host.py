@@ -158,6 +158,30 @@ def test_inner_2d_rules():
     assert q(C(inner_2d=True), rows=0, x=None, codes=None, scales=None, outer=None) == fq.OK
 
 
+def test_mx_project_fp8_rules():
+    """The MXFP4 projection with FP8 re-encodings: MXFP4 only, 1x32 blocks,
+    32x1 columnwise blocks and 128x128 blocks must tile the tensor."""
+    C = fq.make_cfg
+    L = fq.lib()
+
+    def call(cfg, rows=128, cols=128, ld=None, x=FAKE, y=FAKE, r8=FAKE, r8s=FAKE, c8=FAKE, c8s=FAKE, b=FAKE,
+             bt=FAKE, bs=FAKE):
+        return L.fp4_mx_project_fp8(ct.byref(cfg), x, rows, cols, cols if ld is None else ld, y, r8, r8s, c8, c8s,
+                                    b, bt, bs, None)
+    mx = C(format="mxfp4")
+    assert call(C()) == fq.ERR_MODE                                     # NVFP4 is not the projection
+    assert call(C(format="mxfp4", rounding="stochastic")) == fq.ERR_UNSUPPORTED
+    assert call(mx, cols=144) == fq.ERR_SHAPE                           # cols % 32
+    assert call(mx, rows=48, b=None, bt=None, bs=None) == fq.ERR_SHAPE  # rows % 32 for the columnwise blocks
+    assert call(mx, rows=96) == fq.ERR_SHAPE                            # rows % 128 for 128x128 blocks
+    assert call(mx, r8s=None) == fq.ERR_NULL                            # payload without its scales
+    assert call(mx, c8=None) == fq.ERR_NULL
+    assert call(mx, x=None) == fq.ERR_NULL
+    assert call(mx, x=FAKE_MIS) == fq.ERR_ALIGN
+    assert call(mx, rows=(1 << 22) + 128) == fq.ERR_UNSUPPORTED
+    assert call(mx, rows=0, x=None) == fq.OK                            # empty: validated, nothing launched
+
+
 def test_empty_tensors_are_accepted_without_launch():
     C = fq.make_cfg
     for cfg in (C(), C(format="mxfp4"), C(two_level="outer_block", outer_block_size=64, outer_2d=True)):
