@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU oracle time for the baseline")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 256 MiB device copy (counter calibration) and exit")
-    ap.add_argument("--only", default=None, help="time a single workload (nv_tensorwise_qdq_256, nv_2d_cast_transpose_4096, mx_fake_quant_8192, amd_1d_sr_cast_transpose_16384x2880, nv_grouped_sr_ef_32x2880, nv_2d_inner16_cast_transpose_4096) and exit")
+    ap.add_argument("--only", default=None, help="time a single workload (nv_tensorwise_qdq_256, nv_2d_cast_transpose_4096, mx_fake_quant_8192, amd_1d_sr_cast_transpose_16384x2880, nv_grouped_sr_ef_32x2880, nv_2d_inner16_cast_transpose_4096, mx_project_fp8_8192) and exit")
     ap.add_argument("--eager", action="store_true", help="launch every step from the host (no graph replay)")
     ap.add_argument("--pmc-summary", nargs=5, metavar=("KEY", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     default=None,
@@ -60,7 +60,8 @@ def parse():
 KERNEL_NAME_PREFIX = {"nv_tensorwise_qdq_256": "fp4q::(anonymous namespace)::k_nv_rows", "nv_2d_cast_transpose_4096": "fp4q::(anonymous namespace)::k_tile",
                       "mx_fake_quant_8192": "fp4q::(anonymous namespace)::k_mx_qdq", "amd_1d_sr_cast_transpose_16384x2880": "fp4q::(anonymous namespace)::k_tile",
                       "nv_grouped_sr_ef_32x2880": "fp4q::(anonymous namespace)::k_tile",
-                      "nv_2d_inner16_cast_transpose_4096": "fp4q::(anonymous namespace)::k_tile"}
+                      "nv_2d_inner16_cast_transpose_4096": "fp4q::(anonymous namespace)::k_tile",
+                      "mx_project_fp8_8192": "fp4q::(anonymous namespace)::k_mx_fp8"}
 COPY_PROBE_BYTES = 256 << 20
 
 
@@ -241,6 +242,35 @@ def make_mx_fake_quant(torch, fq, W):
                  R * C)
 
 
+def make_mx_project_fp8(torch, fq, W):
+    R = C = 8192
+    x = W.mx_weight_8192_edges()
+    cfg = fq.make_cfg(format="mxfp4")
+    n = R * C
+    # read bf16; write bf16 y, MXFP8 row and column payloads + UE8M0 scales,
+    # 128x128 payload and its transpose, one FP32 scale per tile
+    alg = n * 2 + n * 2 + 2 * (n + n // 32) + 2 * n + 4 * (n // (128 * 128))
+    nset = n_sets_for(alg, cap=4)
+    src = torch.from_numpy(x.view("int16")).cuda()
+
+    def outs():
+        u8 = lambda m: torch.empty(m, dtype=torch.uint8, device="cuda")
+        return dict(x=src.clone(), y=torch.empty(n, dtype=torch.int16, device="cuda"), r=u8(n), rs=u8(n // 32),
+                    c=u8(n), cs=u8(n // 32), b=u8(n), bt=u8(n),
+                    bs=torch.empty(n // (128 * 128), dtype=torch.float32, device="cuda"))
+    sets = [outs() for _ in range(nset)]
+    L = fq.lib()
+
+    def launch(s):
+        st = L.fp4_mx_project_fp8(ct.byref(cfg), s["x"].data_ptr(), R, C, C, s["y"].data_ptr(), s["r"].data_ptr(),
+                                  s["rs"].data_ptr(), s["c"].data_ptr(), s["cs"].data_ptr(), s["b"].data_ptr(),
+                                  s["bt"].data_ptr(), s["bs"].data_ptr(), torch.cuda.current_stream().cuda_stream)
+        if st:
+            raise fq.Fp4Error(st, "fp4_mx_project_fp8")
+    return Timed("mx_project_fp8_8192", "MXFP4 projection 8192x8192 bf16 -> bf16 y + MXFP8 1x32 / 32x1 + FP8 128x128 (+T)",
+                 alg, sets, launch, "k_mx_fp8<true, true, true, true>", n)
+
+
 def make_cast_transpose_1d_sr(torch, fq, W):
     R, C = 16384, 2880
     x = W.activations_16384x2880()
@@ -403,7 +433,8 @@ def main():
               "mx_fake_quant_8192": make_mx_fake_quant,
               "amd_1d_sr_cast_transpose_16384x2880": make_cast_transpose_1d_sr,
               "nv_grouped_sr_ef_32x2880": make_grouped_sr_ef,
-              "nv_2d_inner16_cast_transpose_4096": make_cast_transpose_2d_inner16}[args.only]
+              "nv_2d_inner16_cast_transpose_4096": make_cast_transpose_2d_inner16,
+              "mx_project_fp8_8192": make_mx_project_fp8}[args.only]
         w = mk(torch, fq, W)
         ms = run_timed(torch, w, args.steps, args.warmup, graph=not args.eager)
         per = ms / args.steps
@@ -438,7 +469,8 @@ def main():
     if not args.no_extra:
         extra = {}
         for mk, steps in ((make_mx_fake_quant, 400), (make_cast_transpose_1d_sr, 400), (make_grouped_sr_ef, 20),
-                          (make_tensorwise_qdq, 400), (make_cast_transpose_2d_inner16, 2000)):
+                          (make_tensorwise_qdq, 400), (make_cast_transpose_2d_inner16, 2000),
+                          (make_mx_project_fp8, 200)):
             e = mk(torch, fq, W)
             print("# extra %s" % e.name, file=sys.stderr, flush=True)
             ems = run_timed(torch, e, steps, min(20, steps))
