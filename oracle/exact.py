@@ -165,14 +165,38 @@ def _bf16max():
     return bf16_to_frac(0x7F7F)
 
 
+def _source_cell(b: int, f32: bool):
+    """(kind, value, negative) of one source element given by its bf16 or
+    binary32 bit pattern; kind is "nan", "inf" or "fin"."""
+    ebits, mbits, sbit = (23, 0x7FFFFF, 31) if f32 else (7, 0x7F, 15)
+    e = (b >> ebits) & 0xFF
+    m = b & mbits
+    neg = bool((b >> sbit) & 1)
+    if e == 0xFF:
+        return ("nan" if m else "inf"), None, neg
+    return "fin", (f32_bits_to_frac(b) if f32 else bf16_to_frac(b)), neg
+
+
+def _out_value(w: F, neg_zero: bool, f32: bool):
+    """bf16 bits (RNE) or the float32 of a binary32-valued rational."""
+    if not f32:
+        return frac_to_bf16(w, neg_zero=neg_zero)
+    if w == 0:
+        return np.float32(-0.0 if neg_zero else 0.0)
+    return np.float32(float(w))
+
+
 def nv_quantize(x_bits, *, scale_fmt="e4m3", two_level="none", obs=0, outer_2d=False,
-                stochastic=False, u16=None, residual=None, cols=False, inner_2d=False):
+                stochastic=False, u16=None, residual=None, cols=False, inner_2d=False, y_f32=False):
     """Exact model of the NVFP4 / AMD-FP4 pipeline on a small [R, C] input.
 
-    x_bits: uint16 bf16 bits.  residual: float32 array (read, not written; the
-    new residual is returned).  u16: uint16 [R, C] SR draws.  Returns a dict
-    with the same buffers as the C oracle (numpy arrays)."""
-    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    x_bits: uint16 bf16 bits, or uint32 binary32 bits (a binary32 source).
+    residual: float32 array (read, not written; the new residual is returned).
+    u16: uint16 [R, C] SR draws.  y_f32: dequantised outputs as float32 values
+    instead of bf16 bits.  Returns a dict with the same buffers as the C oracle
+    (numpy arrays)."""
+    x_f32 = np.asarray(x_bits).dtype == np.uint32
+    x_bits = np.asarray(x_bits, dtype=np.uint32 if x_f32 else np.uint16)
     R, C = x_bits.shape
     D = (F(448) if scale_fmt == "e4m3" else F(114688)) * 6
     D = rn32(D)
@@ -181,20 +205,16 @@ def nv_quantize(x_bits, *, scale_fmt="e4m3", two_level="none", obs=0, outer_2d=F
     vneg = [[False] * C for _ in range(R)]
     for i in range(R):
         for j in range(C):
-            b = int(x_bits[i, j])
-            e = (b >> 7) & 0xFF
-            m = b & 0x7F
+            kind, xv, xn = _source_cell(int(x_bits[i, j]), x_f32)
             # sanitisation applies to the value being quantised: NaN -> +0,
             # +-inf -> +-largest bf16 (a non-finite x stays non-finite after
             # adding a finite residual, so it is sanitised directly)
-            if e == 0xFF and m != 0:
+            if kind == "nan":
                 v[i][j], vneg[i][j] = F(0), False
                 continue
-            if e == 0xFF:
-                xn = bool(bf16_sign(b))
+            if kind == "inf":
                 v[i][j], vneg[i][j] = (-_bf16max() if xn else _bf16max()), xn
                 continue
-            xv, xn = bf16_to_frac(b), bool(bf16_sign(b))
             if residual is not None:
                 zb = int(np.float32(residual[i, j]).view(np.uint32))
                 z = f32_bits_to_frac(zb)
@@ -275,7 +295,7 @@ def nv_quantize(x_bits, *, scale_fmt="e4m3", two_level="none", obs=0, outer_2d=F
     out = {}
     row_codes = np.zeros((R, C // 2), np.uint8)
     row_scales = np.zeros((R, C // 16), np.uint8)
-    row_y = np.zeros((R, C), np.uint16)
+    row_y = np.zeros((R, C), np.float32 if y_f32 else np.uint16)
     new_res = np.zeros((R, C), np.float32) if residual is not None else None
     for i in range(R):
         for j0 in range(0, C, 16):
@@ -291,7 +311,7 @@ def nv_quantize(x_bits, *, scale_fmt="e4m3", two_level="none", obs=0, outer_2d=F
                 w = p if so_r is None else rn32(p * so_r(i, j))
                 neg = bool(code & 8)
                 wv = -w if neg else w
-                row_y[i, j] = frac_to_bf16(wv, neg_zero=neg and w == 0)
+                row_y[i, j] = _out_value(wv, neg and w == 0, y_f32)
                 if new_res is not None:
                     r = rn32(v[i][j] - wv)
                     if r == 0:
@@ -308,7 +328,7 @@ def nv_quantize(x_bits, *, scale_fmt="e4m3", two_level="none", obs=0, outer_2d=F
     if cols:
         col_codes = np.zeros((C, R // 2), np.uint8)
         col_scales = np.zeros((C, R // 16), np.uint8)
-        col_y = np.zeros((C, R), np.uint16)
+        col_y = np.zeros((C, R), np.float32 if y_f32 else np.uint16)
         for j in range(C):
             for i0 in range(0, R, 16):
                 vals = []
@@ -322,7 +342,7 @@ def nv_quantize(x_bits, *, scale_fmt="e4m3", two_level="none", obs=0, outer_2d=F
                     col_codes[j, i // 2] |= (code << 4) if (i & 1) else code
                     w = p if so_c is None else rn32(p * so_c(i, j))
                     neg = bool(code & 8)
-                    col_y[j, i] = frac_to_bf16(-w if neg else w, neg_zero=neg and w == 0)
+                    col_y[j, i] = _out_value(-w if neg else w, neg and w == 0, y_f32)
         out.update(col_codes=col_codes, col_scales=col_scales, col_y=col_y)
         if col_outer is not None:
             out["col_outer"] = col_outer
@@ -330,21 +350,24 @@ def nv_quantize(x_bits, *, scale_fmt="e4m3", two_level="none", obs=0, outer_2d=F
 
 
 # --------------------------------------------------------------- MXFP4
-def mx_qdq(x_bits):
-    """Exact model of the MXFP4 1x32 fake-quant: (codes, scales, y bits)."""
-    x_bits = np.asarray(x_bits, dtype=np.uint16)
+def mx_qdq(x_bits, y_f32=False):
+    """Exact model of the MXFP4 1x32 fake-quant: (codes, scales, y).  x_bits:
+    uint16 bf16 bits or uint32 binary32 bits; y as bf16 bits, or float32
+    values with y_f32."""
+    x_f32 = np.asarray(x_bits).dtype == np.uint32
+    x_bits = np.asarray(x_bits, dtype=np.uint32 if x_f32 else np.uint16)
     R, C = x_bits.shape
     codes = np.zeros((R, C // 2), np.uint8)
     scales = np.zeros((R, C // 32), np.uint8)
-    y = np.zeros((R, C), np.uint16)
+    y = np.zeros((R, C), np.float32 if y_f32 else np.uint16)
     for i in range(R):
         for j0 in range(0, C, 32):
-            blk = [int(b) for b in x_bits[i, j0:j0 + 32]]
-            if any(((b >> 7) & 0xFF) == 0xFF for b in blk):
+            cells = [_source_cell(int(b), x_f32) for b in x_bits[i, j0:j0 + 32]]
+            if any(kind != "fin" for kind, _, _ in cells):
                 scales[i, j0 // 32] = 0xFF
-                y[i, j0:j0 + 32] = 0x7FC0
+                y[i, j0:j0 + 32] = np.float32("nan") if y_f32 else 0x7FC0
                 continue
-            A = max(abs(bf16_to_frac(b)) for b in blk)
+            A = max(abs(val) for _, val, _ in cells)
             if A == 0:
                 k = -126
             else:
@@ -354,13 +377,12 @@ def mx_qdq(x_bits):
                     k += 1
                 k = min(max(k, -126), 125)
             scales[i, j0 // 32] = k + 127
-            for kk, b in enumerate(blk):
+            for kk, (_, val, neg) in enumerate(cells):
                 j = j0 + kk
-                t = abs(bf16_to_frac(b)) / F(2) ** k
+                t = abs(val) / F(2) ** k
                 m = e2m1_rne(t)
-                neg = bool(bf16_sign(b))
                 code = (8 if neg else 0) | m
                 codes[i, j // 2] |= (code << 4) if (j & 1) else code
                 w = E2M1[m] * F(2) ** k
-                y[i, j] = frac_to_bf16(-w if neg else w, neg_zero=neg and w == 0)
+                y[i, j] = _out_value(-w if neg else w, neg and w == 0, y_f32)
     return codes, scales, y

@@ -278,6 +278,21 @@ static float sanitize(float v)
     return v;
 }
 
+/* Element e of a source held as bf16 bits or as binary32 ([FP4T] Requirements:
+ * float32 or bfloat16 input; a bf16 value widens to binary32 exactly). */
+static float load_x(const void* X, int x_f32, int64_t e)
+{
+    return x_f32 ? ((const float*)X)[e] : orc_bf16_to_f32(((const uint16_t*)X)[e]);
+}
+
+/* Store a binary32 result as bf16 (RNE) or as binary32 itself ([TEQAT]
+ * Correctness: bf16 and fp32 fake-quant and dequantise targets). */
+static void store_y(void* Y, int y_f32, int64_t e, float w)
+{
+    if (y_f32) ((float*)Y)[e] = w;
+    else ((uint16_t*)Y)[e] = orc_f32_to_bf16(w);
+}
+
 /* Quantise the rows of an [R, C] fp32 matrix of normalised values vn with
  * per-16 inner blocks along each row ([FP4T] Method; [ALTO] Technical design
  * level 2 and 3).  u holds each element's SR variate (ignored for RNE).
@@ -419,10 +434,10 @@ static void tile_maxima(const float* vn, int64_t R, int64_t C, float* tmax)
  *     ([FP4T] Method: residual x - dequant(quantize(x))).
  * SR draws: element (i, j) uses u16(seed, step, index_base + i*C + j) in both
  * directions.  Returns 0 or a negative error. */
-int orc_nv_quantize(const orc_nv_params* prm, const uint16_t* X, int64_t R, int64_t C,
-                    float* residual,
-                    uint8_t* row_codes, uint8_t* row_scales, float* row_outer, uint16_t* row_y,
-                    uint8_t* col_codes, uint8_t* col_scales, float* col_outer, uint16_t* col_y)
+static int nv_quantize_impl(const orc_nv_params* prm, const void* X, int x_f32, int64_t R, int64_t C,
+                            float* residual,
+                            uint8_t* row_codes, uint8_t* row_scales, float* row_outer, void* row_y,
+                            uint8_t* col_codes, uint8_t* col_scales, float* col_outer, void* col_y, int y_f32)
 {
     int want_cols = (col_codes != NULL);
     int rc = check_params(prm, R, C, want_cols);
@@ -442,7 +457,7 @@ int orc_nv_quantize(const orc_nv_params* prm, const uint16_t* X, int64_t R, int6
     /* step 1 */
 #pragma omp parallel for schedule(static)
     for (int64_t e = 0; e < N; ++e) {
-        float x = orc_bf16_to_f32(X[e]);
+        float x = load_x(X, x_f32, e);
         float ve = residual ? x + residual[e] : x;
         v[e] = sanitize(ve);
     }
@@ -537,7 +552,7 @@ int orc_nv_quantize(const orc_nv_params* prm, const uint16_t* X, int64_t R, int6
         for (int64_t j = 0; j < C; ++j) {
             float so = has_outer ? outer_at(&om_r, R, C, i, j) : 1.0f;
             float w = dequant_value(p_r[i * C + j], has_outer, so);
-            if (row_y) row_y[i * C + j] = orc_f32_to_bf16(w);
+            if (row_y) store_y(row_y, y_f32, i * C + j, w);
             if (residual) residual[i * C + j] = v[i * C + j] - w;
         }
 
@@ -556,7 +571,7 @@ int orc_nv_quantize(const orc_nv_params* prm, const uint16_t* X, int64_t R, int6
                 if (i % INNER == 0) col_scales[j * (R / INNER) + i / INNER] = rc_scales[i * (C / INNER) + j / INNER];
                 if (col_y) {
                     float so = has_outer ? outer_at(&om_r, R, C, i, j) : 1.0f;
-                    col_y[j * R + i] = orc_f32_to_bf16(dequant_value(p_r[i * C + j], has_outer, so));
+                    store_y(col_y, y_f32, j * R + i, dequant_value(p_r[i * C + j], has_outer, so));
                 }
             }
     }
@@ -581,7 +596,7 @@ int orc_nv_quantize(const orc_nv_params* prm, const uint16_t* X, int64_t R, int6
             for (int64_t j = 0; j < C; ++j)
                 for (int64_t i = 0; i < R; ++i) {
                     float so = has_outer ? outer_at(&om_c, C, R, j, i) : 1.0f;
-                    col_y[j * R + i] = orc_f32_to_bf16(dequant_value(pT[j * R + i], has_outer, so));
+                    store_y(col_y, y_f32, j * R + i, dequant_value(pT[j * R + i], has_outer, so));
                 }
         }
         free(vT); free(uT); free(pT);
@@ -594,6 +609,27 @@ int orc_nv_quantize(const orc_nv_params* prm, const uint16_t* X, int64_t R, int6
     if (!row_scales) free(rc_scales);
     free(v); free(u); free(vn_r); free(p_r);
     return 0;
+}
+
+int orc_nv_quantize(const orc_nv_params* prm, const uint16_t* X, int64_t R, int64_t C,
+                    float* residual,
+                    uint8_t* row_codes, uint8_t* row_scales, float* row_outer, uint16_t* row_y,
+                    uint8_t* col_codes, uint8_t* col_scales, float* col_outer, uint16_t* col_y)
+{
+    return nv_quantize_impl(prm, X, 0, R, C, residual, row_codes, row_scales, row_outer, row_y,
+                            col_codes, col_scales, col_outer, col_y, 0);
+}
+
+/* The same with the source's and the outputs' dtypes chosen: x_f32 = 1 reads
+ * X as binary32, y_f32 = 1 writes the dequantised outputs as binary32 (the
+ * FP32 value w itself, no bf16 rounding). */
+int orc_nv_quantize_ex(const orc_nv_params* prm, const void* X, int x_f32, int64_t R, int64_t C,
+                       float* residual,
+                       uint8_t* row_codes, uint8_t* row_scales, float* row_outer, void* row_y,
+                       uint8_t* col_codes, uint8_t* col_scales, float* col_outer, void* col_y, int y_f32)
+{
+    return nv_quantize_impl(prm, X, x_f32, R, C, residual, row_codes, row_scales, row_outer, row_y,
+                            col_codes, col_scales, col_outer, col_y, y_f32);
 }
 
 /* Grouped (per-expert) quantisation ([ALTO] Implementation: grouped MoE GEMM
@@ -629,13 +665,14 @@ int orc_nv_quantize_grouped(const orc_nv_params* prm, int32_t G, const int64_t* 
 }
 
 /* Dequantise stored NVFP4 / AMD-FP4 buffers of a logical [R, C] matrix:
- * y = bf16(RN(+-G[m] * dec(s_i) * s_o)) with the inner product exact.
+ * y = bf16(RN(+-G[m] * dec(s_i) * s_o)) with the inner product exact (with
+ * y_f32 the binary32 value itself).
  * outer_kind: 0 none, 1 tensorwise, 2 1D [R, C/obs], 3 2D [R/obs, C/obs],
  * 4 2D stored transposed [C/obs, R/obs] (the shared tile scale read from the
  * columnwise buffer's frame). */
-int orc_nv_dequantize(int sfmt, int outer_kind, int64_t obs,
-                      const uint8_t* codes, const uint8_t* scales, const float* outer,
-                      int64_t R, int64_t C, uint16_t* y)
+int orc_nv_dequantize_ex(int sfmt, int outer_kind, int64_t obs,
+                         const uint8_t* codes, const uint8_t* scales, const float* outer,
+                         int64_t R, int64_t C, void* y, int y_f32)
 {
     if (C % INNER) return -2;
     outer_map om = {outer_kind, obs, outer};
@@ -648,9 +685,16 @@ int orc_nv_dequantize(int sfmt, int outer_kind, int64_t obs,
             float p = (float)E2M1_GRID[code & 7] * d;
             float w = (outer_kind != 0) ? p * outer_at(&om, R, C, i, j) : p;
             if (code & 8) w = -w;
-            y[i * C + j] = orc_f32_to_bf16(w);
+            store_y(y, y_f32, i * C + j, w);
         }
     return 0;
+}
+
+int orc_nv_dequantize(int sfmt, int outer_kind, int64_t obs,
+                      const uint8_t* codes, const uint8_t* scales, const float* outer,
+                      int64_t R, int64_t C, uint16_t* y)
+{
+    return orc_nv_dequantize_ex(sfmt, outer_kind, obs, codes, scales, outer, R, C, y, 0);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -675,40 +719,40 @@ static int mx_exponent(double amax)
     return k;
 }
 
-/* MXFP4 fake-quant of X [R, C] (bf16 bits): codes [R, C/2], scale bytes
- * [R, C/32], y bf16 [R, C].  A block holding any NaN or +-inf is poisoned
- * ([TEQAT] Correctness: inf/NaN block poisoning): scale byte 0xFF (the NaN
- * code), codes 0, every y = 0x7FC0.  Otherwise t = |x| * 2^-k (exact),
+/* MXFP4 fake-quant of X [R, C] (bf16 bits, or binary32 with x_f32): codes
+ * [R, C/2], scale bytes [R, C/32], y [R, C] as bf16 (or binary32 with y_f32).
+ * A block holding any NaN or +-inf is poisoned ([TEQAT] Correctness: inf/NaN
+ * block poisoning): scale byte 0xFF (the NaN code), codes 0, every y the quiet
+ * NaN (0x7FC0, or 0x7FC00000 as binary32).  Otherwise t = |x| * 2^-k (exact),
  * m = RNE(t) saturating at 6, sign kept (also for zero), y = +-G[m] * 2^k,
  * which bf16 represents exactly ([TEQAT] Design). */
-int orc_mx_qdq(const uint16_t* X, int64_t R, int64_t C, uint8_t* codes, uint8_t* scales, uint16_t* y)
+int orc_mx_qdq_ex(const void* X, int x_f32, int64_t R, int64_t C, uint8_t* codes, uint8_t* scales, void* y,
+                  int y_f32)
 {
     if (C % MXB) return -2;
     const int64_t nb = R * (C / MXB);
 #pragma omp parallel for schedule(static)
     for (int64_t b = 0; b < nb; ++b) {
-        const uint16_t* xb = X + b * MXB;
         int poisoned = 0;
         double A = 0.0;
         for (int k = 0; k < MXB; ++k) {
-            float f = orc_bf16_to_f32(xb[k]);
+            float f = load_x(X, x_f32, b * MXB + k);
             if (isnan(f) || isinf(f)) poisoned = 1;
             else if (fabs((double)f) > A) A = fabs((double)f);
         }
         uint8_t* cb = codes ? codes + b * (MXB / 2) : NULL;
-        uint16_t* yb = y ? y + b * MXB : NULL;
         if (poisoned) {
             if (scales) scales[b] = 0xFF;
             for (int k = 0; k < MXB; ++k) {
                 if (cb && (k & 1) == 0) cb[k / 2] = 0;
-                if (yb) yb[k] = 0x7FC0;
+                if (y) store_y(y, y_f32, b * MXB + k, f_from_bits(0x7FC00000u));
             }
             continue;
         }
         int e = mx_exponent(A);
         if (scales) scales[b] = (uint8_t)(e + 127);
         for (int k = 0; k < MXB; ++k) {
-            float f = orc_bf16_to_f32(xb[k]);
+            float f = load_x(X, x_f32, b * MXB + k);
             double t = fabs((double)f) * ldexp(1.0, -e);
             int m = orc_e2m1_rne(t);
             int s = signbit(f) ? 1 : 0;
@@ -717,19 +761,24 @@ int orc_mx_qdq(const uint16_t* X, int64_t R, int64_t C, uint8_t* codes, uint8_t*
                 if ((k & 1) == 0) cb[k / 2] = (uint8_t)code;
                 else cb[k / 2] = (uint8_t)(cb[k / 2] | (code << 4));
             }
-            if (yb) {
+            if (y) {
                 double w = E2M1_GRID[m] * ldexp(1.0, e);
                 float wf = (float)(s ? -w : w);
-                yb[k] = orc_f32_to_bf16(wf);
+                store_y(y, y_f32, b * MXB + k, wf);
             }
         }
     }
     return 0;
 }
 
-/* MXFP4 dequantise from stored codes and UE8M0 scales: y = +-G[m] * 2^(c-127),
- * scale byte 0xFF (NaN) gives 0x7FC0. */
-int orc_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t R, int64_t C, uint16_t* y)
+int orc_mx_qdq(const uint16_t* X, int64_t R, int64_t C, uint8_t* codes, uint8_t* scales, uint16_t* y)
+{
+    return orc_mx_qdq_ex(X, 0, R, C, codes, scales, y, 0);
+}
+
+/* MXFP4 dequantise from stored codes and UE8M0 scales: y = +-G[m] * 2^(c-127)
+ * as bf16 (or binary32 with y_f32); scale byte 0xFF (NaN) gives the quiet NaN. */
+int orc_mx_dequantize_ex(const uint8_t* codes, const uint8_t* scales, int64_t R, int64_t C, void* y, int y_f32)
 {
     if (C % MXB) return -2;
 #pragma omp parallel for schedule(static)
@@ -738,12 +787,17 @@ int orc_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t R, in
             uint8_t byte = codes[i * (C / 2) + j / 2];
             int code = (j & 1) ? (byte >> 4) : (byte & 0xF);
             int sc = scales[i * (C / MXB) + j / MXB];
-            if (sc == 255) { y[i * C + j] = 0x7FC0; continue; }
+            if (sc == 255) { store_y(y, y_f32, i * C + j, f_from_bits(0x7FC00000u)); continue; }
             double w = E2M1_GRID[code & 7] * orc_ue8m0_decode(sc);
             float wf = (float)((code & 8) ? -w : w);
-            y[i * C + j] = orc_f32_to_bf16(wf);
+            store_y(y, y_f32, i * C + j, wf);
         }
     return 0;
+}
+
+int orc_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t R, int64_t C, uint16_t* y)
+{
+    return orc_mx_dequantize_ex(codes, scales, R, C, y, 0);
 }
 
 /* ------------------------------------------------------------------------ */

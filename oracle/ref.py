@@ -67,6 +67,16 @@ def lib():
         L.orc_nv_quantize.restype = ct.c_int
         L.orc_nv_quantize.argtypes = [ct.POINTER(_NvParams), P, ct.c_int64, ct.c_int64, P,
                                       P, P, P, P, P, P, P, P]
+        L.orc_nv_quantize_ex.restype = ct.c_int
+        L.orc_nv_quantize_ex.argtypes = [ct.POINTER(_NvParams), P, ct.c_int, ct.c_int64, ct.c_int64, P,
+                                         P, P, P, P, P, P, P, P, ct.c_int]
+        L.orc_nv_dequantize_ex.restype = ct.c_int
+        L.orc_nv_dequantize_ex.argtypes = [ct.c_int, ct.c_int, ct.c_int64, P, P, P,
+                                           ct.c_int64, ct.c_int64, P, ct.c_int]
+        L.orc_mx_qdq_ex.restype = ct.c_int
+        L.orc_mx_qdq_ex.argtypes = [P, ct.c_int, ct.c_int64, ct.c_int64, P, P, P, ct.c_int]
+        L.orc_mx_dequantize_ex.restype = ct.c_int
+        L.orc_mx_dequantize_ex.argtypes = [P, P, ct.c_int64, ct.c_int64, P, ct.c_int]
         L.orc_nv_quantize_grouped.restype = ct.c_int
         L.orc_nv_quantize_grouped.argtypes = [ct.POINTER(_NvParams), ct.c_int32, P, ct.c_int64,
                                               P, P, P, P, P, P, P, P]
@@ -193,10 +203,24 @@ def outer_shapes(two_level, obs, outer_2d, R, C):
     return (R, C // obs), (C, R // obs)
 
 
+def _source(x):
+    """(contiguous array, 1 if binary32) of a source given as uint16 bf16 bits
+    or as float32 values."""
+    if np.asarray(x).dtype == np.float32:
+        return np.ascontiguousarray(x, dtype=np.float32), 1
+    return np.ascontiguousarray(x, dtype=np.uint16), 0
+
+
+_Y_DT = {"bf16": np.uint16, "fp32": np.float32}
+
+
 def nv_quantize(x, *, scale_fmt="e4m3", two_level="none", obs=0, outer_2d=False,
                 stochastic=False, seed=0, step=0, index_base=0, residual=None,
-                given_outer=None, cols=False, want_y=True, inner_2d=False):
-    """Oracle NVFP4 / AMD-FP4 quantisation of x (uint16 bf16 bits, [R, C]).
+                given_outer=None, cols=False, want_y=True, inner_2d=False, y_dtype="bf16"):
+    """Oracle NVFP4 / AMD-FP4 quantisation of x ([R, C]: uint16 bf16 bits, or
+    float32 values for a binary32 source).
+
+    y_dtype: "bf16" (row_y / col_y as uint16 bits) or "fp32" (float32 values).
 
     residual: float32 [R, C] updated in place (error feedback) or None.
     given_outer: (row_outer, col_outer) supplied by the caller instead of computed.
@@ -204,7 +228,8 @@ def nv_quantize(x, *, scale_fmt="e4m3", two_level="none", obs=0, outer_2d=False,
     rows of row_scales; the columnwise buffers are the transposes).
     Returns a dict of numpy arrays.
     """
-    x = np.ascontiguousarray(x, dtype=np.uint16)
+    x, x_f32 = _source(x)
+    ydt = _Y_DT[y_dtype]
     R, C = x.shape
     out = {"row_codes": np.zeros((R, C // 2), np.uint8), "row_scales": np.zeros((R, C // 16), np.uint8)}
     rs, cs = outer_shapes(two_level, obs, outer_2d, R, C)
@@ -218,20 +243,20 @@ def nv_quantize(x, *, scale_fmt="e4m3", two_level="none", obs=0, outer_2d=False,
         if cs is not None and cols:
             out["col_outer"] = np.zeros(cs, np.float32)
     if want_y:
-        out["row_y"] = np.zeros((R, C), np.uint16)
+        out["row_y"] = np.zeros((R, C), ydt)
     if cols:
         out["col_codes"] = np.zeros((C, R // 2), np.uint8)
         out["col_scales"] = np.zeros((C, R // 16), np.uint8)
         if want_y:
-            out["col_y"] = np.zeros((C, R), np.uint16)
+            out["col_y"] = np.zeros((C, R), ydt)
     if residual is not None:
         assert residual.dtype == np.float32 and residual.flags.c_contiguous and residual.shape == (R, C)
     prm = _params(scale_fmt, two_level, obs, outer_2d, stochastic, seed, step, index_base, given_outer is not None,
                   inner_2d)
-    rc = lib().orc_nv_quantize(ct.byref(prm), _p(x), R, C, _p(residual),
-                               _p(out["row_codes"]), _p(out["row_scales"]), _p(out.get("row_outer")),
-                               _p(out.get("row_y")), _p(out.get("col_codes")), _p(out.get("col_scales")),
-                               _p(out.get("col_outer")), _p(out.get("col_y")))
+    rc = lib().orc_nv_quantize_ex(ct.byref(prm), _p(x), x_f32, R, C, _p(residual),
+                                  _p(out["row_codes"]), _p(out["row_scales"]), _p(out.get("row_outer")),
+                                  _p(out.get("row_y")), _p(out.get("col_codes")), _p(out.get("col_scales")),
+                                  _p(out.get("col_outer")), _p(out.get("col_y")), int(y_dtype == "fp32"))
     if rc != 0:
         raise ValueError("oracle rejected the configuration (%d)" % rc)
     return out
@@ -266,26 +291,27 @@ def nv_quantize_grouped(x, rows, *, scale_fmt="e4m3", two_level="outer", obs=64,
 OUTER_KIND = {"none": 0, "tensorwise": 1, "1d": 2, "2d": 3, "2d_t": 4}
 
 
-def nv_dequantize(codes, scales, outer, R, C, *, scale_fmt="e4m3", outer_kind="none", obs=0):
+def nv_dequantize(codes, scales, outer, R, C, *, scale_fmt="e4m3", outer_kind="none", obs=0, y_dtype="bf16"):
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
     scales = np.ascontiguousarray(scales, dtype=np.uint8)
     outer = None if outer is None else np.ascontiguousarray(outer, dtype=np.float32)
-    y = np.zeros((R, C), np.uint16)
-    rc = lib().orc_nv_dequantize(SCALE_FMT[scale_fmt], OUTER_KIND[outer_kind], int(obs),
-                                 _p(codes), _p(scales), _p(outer), R, C, _p(y))
+    y = np.zeros((R, C), _Y_DT[y_dtype])
+    rc = lib().orc_nv_dequantize_ex(SCALE_FMT[scale_fmt], OUTER_KIND[outer_kind], int(obs),
+                                    _p(codes), _p(scales), _p(outer), R, C, _p(y), int(y_dtype == "fp32"))
     if rc != 0:
         raise ValueError("oracle rejected the configuration (%d)" % rc)
     return y
 
 
-def mx_qdq(x):
-    """MXFP4 fake-quant: returns (codes [R, C/2], scales [R, C/32], y bf16 bits [R, C])."""
-    x = np.ascontiguousarray(x, dtype=np.uint16)
+def mx_qdq(x, y_dtype="bf16"):
+    """MXFP4 fake-quant of x (uint16 bf16 bits, or float32 values): returns
+    (codes [R, C/2], scales [R, C/32], y [R, C] as bf16 bits or float32)."""
+    x, x_f32 = _source(x)
     R, C = x.shape
     codes = np.zeros((R, C // 2), np.uint8)
     scales = np.zeros((R, C // 32), np.uint8)
-    y = np.zeros((R, C), np.uint16)
-    rc = lib().orc_mx_qdq(_p(x), R, C, _p(codes), _p(scales), _p(y))
+    y = np.zeros((R, C), _Y_DT[y_dtype])
+    rc = lib().orc_mx_qdq_ex(_p(x), x_f32, R, C, _p(codes), _p(scales), _p(y), int(y_dtype == "fp32"))
     if rc != 0:
         raise ValueError("oracle rejected the shape (%d)" % rc)
     return codes, scales, y
@@ -328,11 +354,11 @@ def mx_project_encode(x, *, y=True, mx8_row=True, mx8_col=True, blk=True):
     return out
 
 
-def mx_dequantize(codes, scales, R, C):
+def mx_dequantize(codes, scales, R, C, y_dtype="bf16"):
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
     scales = np.ascontiguousarray(scales, dtype=np.uint8)
-    y = np.zeros((R, C), np.uint16)
-    rc = lib().orc_mx_dequantize(_p(codes), _p(scales), R, C, _p(y))
+    y = np.zeros((R, C), _Y_DT[y_dtype])
+    rc = lib().orc_mx_dequantize_ex(_p(codes), _p(scales), R, C, _p(y), int(y_dtype == "fp32"))
     if rc != 0:
         raise ValueError("oracle rejected the shape (%d)" % rc)
     return y
