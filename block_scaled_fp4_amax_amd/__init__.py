@@ -15,13 +15,13 @@ import os
 __all__ = [
     "Fp4Error", "Cfg", "Sizes", "make_cfg", "lib", "fp4q_abi_version", "fp4q_status_str", "fp4q_buffer_sizes",
     "fp4q_workspace_bytes", "fp4_quantize", "fp4_dequantize", "fp4_qdq", "fp4_cast_transpose",
-    "fp4_cast_transpose_grouped", "fp4_mx_project_fp8", "LIB_PATH",
+    "fp4_cast_transpose_grouped", "fp4_mx_project_fp8", "ErrorFeedback", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp4q.so")
 
 OK, ERR_NULL, ERR_DTYPE, ERR_SHAPE, ERR_MODE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP, ERR_ABI = range(10)
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 FORMATS = {"nvfp4": 0, "amdfp4": 1, "mxfp4": 2}
 SCALE_FORMATS = {None: 0, "default": 0, "e4m3": 1, "ue5m3": 2, "ue8m0": 3}
@@ -40,8 +40,8 @@ class Cfg(ct.Structure):
     _fields_ = [("abi_version", ct.c_uint32), ("format", ct.c_int32), ("scale_format", ct.c_int32),
                 ("two_level", ct.c_int32), ("outer_block_size", ct.c_int32), ("outer_2d", ct.c_int32),
                 ("rounding", ct.c_int32), ("outer_mode", ct.c_int32), ("input_dtype", ct.c_int32),
-                ("inner_2d", ct.c_int32), ("seed", ct.c_uint64), ("step", ct.c_uint64),
-                ("index_base", ct.c_uint64)]
+                ("inner_2d", ct.c_int32), ("output_dtype", ct.c_int32), ("seed", ct.c_uint64),
+                ("step", ct.c_uint64), ("index_base", ct.c_uint64)]
 
 
 class Sizes(ct.Structure):
@@ -50,15 +50,29 @@ class Sizes(ct.Structure):
 
 
 def make_cfg(format="nvfp4", scale_format=None, two_level="none", outer_block_size=0, outer_2d=False,
-             rounding="rne", outer_mode=0, seed=0, step=0, index_base=0, input_dtype="bf16", inner_2d=False):
+             rounding="rne", outer_mode=0, seed=0, step=0, index_base=0, input_dtype="bf16", inner_2d=False,
+             output_dtype="bf16"):
     """Build an fp4q_cfg (string names or the raw integers of include/fp4q.h).
 
-    inner_2d: one inner scale per 16 x 16 tile instead of per 1 x 16 block."""
+    inner_2d: one inner scale per 16 x 16 tile instead of per 1 x 16 block.
+    input_dtype / output_dtype: "bf16" or "fp32" (the entry points below set
+    them from the tensors they are given)."""
     def pick(table, v):
         return v if isinstance(v, int) and not isinstance(v, bool) else table[v]
     return Cfg(ABI_VERSION, pick(FORMATS, format), pick(SCALE_FORMATS, scale_format), pick(TWO_LEVEL, two_level),
                int(outer_block_size), int(bool(outer_2d)), pick(ROUNDING, rounding), int(outer_mode),
-               pick(DTYPES, input_dtype), int(inner_2d), int(seed), int(step), int(index_base))
+               pick(DTYPES, input_dtype), int(inner_2d), pick(DTYPES, output_dtype), int(seed), int(step),
+               int(index_base))
+
+
+def _with_dtypes(cfg, input_dtype=None, output_dtype=None):
+    """A copy of cfg with its dtype fields set from the tensors of a call."""
+    c = Cfg.from_buffer_copy(cfg)
+    if input_dtype is not None:
+        c.input_dtype = DTYPES[input_dtype]
+    if output_dtype is not None:
+        c.output_dtype = DTYPES[output_dtype]
+    return c
 
 
 _lib = None
@@ -127,7 +141,13 @@ def _torch():
 
 
 def _ptr(t):
-    return None if t is None else ct.c_void_p(t.data_ptr())
+    """Device address of a tensor (None for None).  Host tensors are refused:
+    every pointer the library takes is a device pointer."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("fp4q takes device tensors; got one on %s" % t.device)
+    return ct.c_void_p(t.data_ptr())
 
 
 def _stream(stream):
@@ -144,17 +164,23 @@ def _check(st, where):
         raise Fp4Error(st, where)
 
 
-def _src(x):
-    """(tensor, rows, cols, ld) for a 2-D bf16 (or 16-bit integer) source."""
+def _src(x, allow_f32=False):
+    """(tensor, rows, cols, ld) for a 2-D bf16 (or 16-bit integer) source, or
+    a float32 one where the entry point takes FP32."""
     torch = _torch()
     if x.dim() != 2:
         raise ValueError("expected a 2-D tensor")
-    if x.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+    ok = (torch.bfloat16, torch.int16, torch.uint16) + ((torch.float32,) if allow_f32 else ())
+    if x.dtype not in ok:
         raise Fp4Error(ERR_DTYPE, "source dtype %s" % x.dtype)
     if x.shape[1] > 1 and x.stride(1) != 1:
         raise ValueError("source rows must be contiguous (stride(1) == 1)")
     ld = x.stride(0) if x.shape[0] > 1 else x.shape[1]
     return x, x.shape[0], x.shape[1], ld
+
+
+def _dtype_name(t):
+    return "fp32" if t.dtype == _torch().float32 else "bf16"
 
 
 def _empty(n, dtype, device):
@@ -177,11 +203,13 @@ def _workspace(cfg, rows, cols, device, workspace):
 
 # ------------------------------------------------------------------ entry points
 def fp4_quantize(x, cfg, *, residual=None, outer=None, workspace=None, stream=None, out=None):
-    """Rowwise quantisation.  Returns {"codes", "scales", "outer"} (outer None
-    without a two-level mode).  `outer` is read when cfg.outer_mode == 1.
-    `out` may supply preallocated "codes" / "scales" tensors."""
+    """Rowwise quantisation of a bf16 or float32 x (views with any storage
+    offset and row pitch are accepted).  Returns {"codes", "scales", "outer"}
+    (outer None without a two-level mode).  `outer` is read when
+    cfg.outer_mode == 1.  `out` may supply preallocated "codes" / "scales"."""
     torch = _torch()
-    x, R, C, ld = _src(x)
+    x, R, C, ld = _src(x, allow_f32=True)
+    cfg = _with_dtypes(cfg, _dtype_name(x))
     dev = x.device
     sizes = fp4q_buffer_sizes(cfg, R, C)
     out = out or {}
@@ -199,14 +227,20 @@ def fp4_quantize(x, cfg, *, residual=None, outer=None, workspace=None, stream=No
     return {"codes": codes, "scales": scales, "outer": outer}
 
 
-def fp4_qdq(x, cfg, *, residual=None, outer=None, with_codes=False, workspace=None, stream=None, y=None):
-    """Quantise-dequantise rowwise.  Returns {"y", "codes", "scales", "outer"}."""
+def fp4_qdq(x, cfg, *, residual=None, outer=None, with_codes=False, workspace=None, stream=None, y=None,
+            y_dtype=None):
+    """Quantise-dequantise rowwise (bf16 or float32 x; y in y_dtype, default
+    x's dtype, or the dtype of a given y).  Returns {"y", "codes", "scales", "outer"}."""
     torch = _torch()
-    x, R, C, ld = _src(x)
+    x, R, C, ld = _src(x, allow_f32=True)
     dev = x.device
+    if y is not None:
+        y_dtype = y.dtype
+    ydt = torch.float32 if (y_dtype if y_dtype is not None else x.dtype) == torch.float32 else torch.bfloat16
+    cfg = _with_dtypes(cfg, _dtype_name(x), "fp32" if ydt == torch.float32 else "bf16")
     sizes = fp4q_buffer_sizes(cfg, R, C)
     if y is None:
-        y = torch.empty((R, C), dtype=torch.bfloat16, device=dev)
+        y = torch.empty((R, C), dtype=ydt, device=dev)
     codes = scales = None
     if with_codes:
         codes = _empty(sizes["row_codes"], torch.uint8, dev).view(R, C // 2)
@@ -219,11 +253,14 @@ def fp4_qdq(x, cfg, *, residual=None, outer=None, with_codes=False, workspace=No
     return {"y": y, "codes": codes, "scales": scales, "outer": outer}
 
 
-def fp4_dequantize(codes, scales, outer, rows, cols, cfg, *, outer_transposed=False, stream=None, y=None):
-    """bf16 [rows, cols] from stored codes, scales and outer scales."""
+def fp4_dequantize(codes, scales, outer, rows, cols, cfg, *, outer_transposed=False, stream=None, y=None,
+                   dtype=None):
+    """bf16 (or float32: dtype=torch.float32, or a float32 y) [rows, cols]
+    from stored codes, scales and outer scales."""
     torch = _torch()
     if y is None:
-        y = torch.empty((rows, cols), dtype=torch.bfloat16, device=codes.device)
+        y = torch.empty((rows, cols), dtype=dtype if dtype is not None else torch.bfloat16, device=codes.device)
+    cfg = _with_dtypes(cfg, output_dtype=_dtype_name(y))
     _check(lib().fp4_dequantize(ct.byref(cfg), _ptr(codes), _ptr(scales), _ptr(outer), int(rows), int(cols),
                                 int(bool(outer_transposed)), _ptr(y), _stream(stream)), "fp4_dequantize")
     return y
@@ -317,3 +354,70 @@ def fp4_mx_project_fp8(x, cfg=None, *, y=True, mx8_row=True, mx8_col=True, blk=T
                                     _ptr(g("blk")), _ptr(g("blk_t")), _ptr(g("blk_scales")), _stream(stream)),
            "fp4_mx_project_fp8")
     return {k: v for k, v in out.items() if v is not None}
+
+
+class ErrorFeedback:
+    """Per-tensor error-feedback state for quantised weights ("fp4-train"
+    README, API: ErrorFeedback; Method: error feedback carries each step's
+    quantisation error into the next step's value).
+
+    One FP32 residual per name, created as zeros on the first call with the
+    tensor's shape and device.  qdq(name, w, step) quantises RN(w + residual)
+    and returns the dequantised tensor (w's dtype); the same kernel rewrites the
+    residual in place with RN(value - dequantised value).  quantize() does the
+    same and returns the packed codes and scales instead.  `step` is the
+    stochastic-rounding counter of that call.  NVFP4 / AMD-FP4 only (MXFP4 has
+    no error-feedback path).
+    """
+
+    def __init__(self, cfg=None, *, stochastic=False, seed=0, **cfg_kw):
+        if cfg is None:
+            cfg = make_cfg(rounding="stochastic" if stochastic else "rne", seed=seed, **cfg_kw)
+        elif cfg_kw or stochastic or seed:
+            raise ValueError("pass either cfg or its keyword settings, not both")
+        if cfg.format == FORMATS["mxfp4"]:
+            raise Fp4Error(ERR_UNSUPPORTED, "ErrorFeedback with MXFP4")
+        self.cfg = cfg
+        self._res = {}
+
+    def _cfg(self, step):
+        c = Cfg.from_buffer_copy(self.cfg)
+        c.step = int(step)
+        return c
+
+    def residual(self, name, like=None):
+        """The residual of `name` (created as zeros shaped like `like`)."""
+        r = self._res.get(name)
+        if r is None:
+            if like is None:
+                raise KeyError(name)
+            torch = _torch()
+            r = torch.zeros(like.shape, dtype=torch.float32, device=like.device)
+            self._res[name] = r
+        elif like is not None and (tuple(r.shape) != tuple(like.shape) or r.device != like.device):
+            raise ValueError("residual of %r is %s on %s, tensor is %s on %s"
+                             % (name, tuple(r.shape), r.device, tuple(like.shape), like.device))
+        return r
+
+    def qdq(self, name, w, step=0, **kw):
+        return fp4_qdq(w, self._cfg(step), residual=self.residual(name, w), **kw)["y"]
+
+    def quantize(self, name, w, step=0, **kw):
+        return fp4_quantize(w, self._cfg(step), residual=self.residual(name, w), **kw)
+
+    def reset(self, name=None):
+        """Forget one residual (or all of them)."""
+        if name is None:
+            self._res.clear()
+        else:
+            self._res.pop(name, None)
+
+    def state_dict(self):
+        return {k: v.clone() for k, v in self._res.items()}
+
+    def load_state_dict(self, state):
+        torch = _torch()
+        for k, v in state.items():
+            if v.dtype != torch.float32 or v.dim() != 2:
+                raise ValueError("residual %r must be a 2-D float32 tensor" % k)
+        self._res = {k: v.clone().contiguous() for k, v in state.items()}

@@ -22,6 +22,8 @@ struct Resolved {
     bool sr;
     bool given;       // outer scales supplied by the caller
     bool inner2d;     // 16 x 16 inner tiles
+    bool x_f32;       // FP32 source (else bf16)
+    bool y_f32;       // FP32 dequantised output (else bf16)
 };
 
 bool misaligned(const void* p, uintptr_t a) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) % a) != 0; }
@@ -35,8 +37,8 @@ int resolve(const fp4q_cfg* c, Resolved& r)
     if (!c) return FP4Q_ERR_NULL;
     if (c->abi_version != FP4Q_ABI_VERSION) return FP4Q_ERR_ABI;
     if (c->inner_2d != 0 && c->inner_2d != 1) return FP4Q_ERR_MODE;
-    if (c->input_dtype == FP4Q_DTYPE_FP32) return FP4Q_ERR_UNSUPPORTED;
-    if (c->input_dtype != FP4Q_DTYPE_BF16) return FP4Q_ERR_DTYPE;
+    if (c->input_dtype != FP4Q_DTYPE_BF16 && c->input_dtype != FP4Q_DTYPE_FP32) return FP4Q_ERR_DTYPE;
+    if (c->output_dtype != FP4Q_DTYPE_BF16 && c->output_dtype != FP4Q_DTYPE_FP32) return FP4Q_ERR_DTYPE;
     if (c->rounding != FP4Q_RNE && c->rounding != FP4Q_STOCHASTIC) return FP4Q_ERR_MODE;
     if (c->outer_mode != 0 && c->outer_mode != 1) return FP4Q_ERR_MODE;
     if (c->outer_2d != 0 && c->outer_2d != 1) return FP4Q_ERR_MODE;
@@ -44,6 +46,8 @@ int resolve(const fp4q_cfg* c, Resolved& r)
     r.sr = c->rounding == FP4Q_STOCHASTIC;
     r.given = c->outer_mode == 1;
     r.inner2d = c->inner_2d == 1;
+    r.x_f32 = c->input_dtype == FP4Q_DTYPE_FP32;
+    r.y_f32 = c->output_dtype == FP4Q_DTYPE_FP32;
     r.obs = 0;
     r.bias = 0;
     r.outer_kind = kOuterNone;
@@ -95,7 +99,6 @@ int check_shape(const Resolved& r, int64_t rows, int64_t cols, int64_t ld, bool 
     const int inner = r.fmt == FP4Q_MXFP4 ? 32 : 16;
     if (cols % inner) return FP4Q_ERR_SHAPE;
     if (rows > 0 && ld < cols) return FP4Q_ERR_SHAPE;
-    if (ld % 8) return FP4Q_ERR_ALIGN;
     if ((columnwise || r.inner2d) && rows % 16) return FP4Q_ERR_SHAPE;
     if (r.outer_kind == kOuter1D || r.outer_kind == kOuter2D) {
         if (cols % r.obs) return FP4Q_ERR_SHAPE;
@@ -105,6 +108,15 @@ int check_shape(const Resolved& r, int64_t rows, int64_t cols, int64_t ld, bool 
     // a 64-row tile (x rows of ld_x bf16, residual rows of cols FP32)
     if (rows * (cols / 8) >= (int64_t)1 << 31) return FP4Q_ERR_UNSUPPORTED;
     if (ld > ((int64_t)1 << 24) || cols > ((int64_t)1 << 23)) return FP4Q_ERR_UNSUPPORTED;
+    return FP4Q_OK;
+}
+
+// Sources read in 16-byte row chunks (the 64 x 64 tile kernels and the FP8
+// re-encode): bf16 only, every row start 16-byte aligned.
+int check_vector_source(const Resolved& r, int64_t ld)
+{
+    if (r.x_f32) return FP4Q_ERR_UNSUPPORTED;
+    if (ld % 8) return FP4Q_ERR_ALIGN;
     return FP4Q_OK;
 }
 
@@ -145,7 +157,7 @@ TileArgs tile_args_single(const uint16_t* x, int64_t rows, int64_t cols, int64_t
 }
 
 // Rowwise quantisation shared by fp4_quantize and fp4_qdq.
-int rowwise(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, uint16_t* y,
+int rowwise(const fp4q_cfg* cfg, const void* x, int64_t rows, int64_t cols, int64_t ld, void* y,
             uint8_t* codes, uint8_t* scales, float* outer, float* residual, void* ws, size_t ws_bytes, void* stream,
             bool is_qdq)
 {
@@ -158,6 +170,14 @@ int rowwise(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int64_t cols, 
     if (r.outer_kind == kOuter1D && r.obs != 16 && r.obs != 32 && r.obs != 64 && r.obs != 128)
         return FP4Q_ERR_UNSUPPORTED;
     if (r.fmt == FP4Q_MXFP4 && residual) return FP4Q_ERR_UNSUPPORTED;
+    // the 64 x 64 tile modes read bf16 in 16-byte row chunks and write bf16
+    const bool tile_mode = r.fmt != FP4Q_MXFP4 && (r.outer_kind == kOuter2D || r.inner2d);
+    if (tile_mode) {
+        if (r.y_f32 && is_qdq) return FP4Q_ERR_UNSUPPORTED;
+        st = check_vector_source(r, ld);
+        if (st) return st;
+    }
+    const uintptr_t esize = r.x_f32 ? 4 : 2;
     const bool empty = rows == 0 || cols == 0;
     const size_t need_ws = ws_bytes_for(r);
     if (!empty) {
@@ -171,24 +191,28 @@ int rowwise(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int64_t cols, 
         }
         if (need_ws && !ws) return FP4Q_ERR_NULL;
         if ((codes == nullptr) != (scales == nullptr)) return FP4Q_ERR_NULL;
-        if (misaligned(x, 16) || misaligned(y, 16) || misaligned(codes, 16) || misaligned(residual, 16) ||
-            misaligned(outer, 4) || misaligned(ws, 16))
+        // a misaligned view: x aligned to its element size only (not in the tile modes)
+        if (misaligned(x, tile_mode ? 16 : esize) || misaligned(y, 16) || misaligned(codes, 16) ||
+            misaligned(residual, 16) || misaligned(outer, 4) || misaligned(ws, 16))
             return FP4Q_ERR_ALIGN;
     }
     if (ws_bytes < need_ws) return FP4Q_ERR_WORKSPACE;
     if (empty) return FP4Q_OK;
     hipStream_t s = (hipStream_t)stream;
+    // 16-byte vector loads when x and every row start are 16-byte aligned
+    const bool x_vec = !misaligned(x, 16) && ((uint64_t)ld * esize) % 16 == 0;
 
-    if (r.fmt == FP4Q_MXFP4) return hip_status(launch_mx_qdq(x, rows, cols, ld, y, codes, scales, s));
+    if (r.fmt == FP4Q_MXFP4)
+        return hip_status(launch_mx_qdq(x, r.x_f32, x_vec, rows, cols, ld, y, r.y_f32, codes, scales, s));
 
-    if (r.outer_kind == kOuter2D || r.inner2d) {
+    if (tile_mode) {
         // 64 x 64 tiles: the 2D outer tile, and the 16 x 16 inner tiles
-        TileArgs a = tile_args_single(x, rows, cols, ld);
+        TileArgs a = tile_args_single(static_cast<const uint16_t*>(x), rows, cols, ld);
         a.row_codes = codes;
         a.row_scales = scales;
         a.row_outer = outer;
         a.residual = residual;
-        a.y = y;
+        a.y = static_cast<uint16_t*>(y);
         a.seed = cfg->seed;
         a.step = cfg->step;
         a.index_base = cfg->index_base;
@@ -200,7 +224,8 @@ int rowwise(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int64_t cols, 
                 a.tensor_scale = outer;
             } else {
                 float* wsf = (float*)ws;
-                hipError_t e = launch_amax(r.bias, x, rows, cols, ld, residual, wsf + 1, kAmaxPartials, wsf, outer, s);
+                hipError_t e = launch_amax(r.bias, x, false, true, rows, cols, ld, residual, wsf + 1, kAmaxPartials, wsf,
+                                           outer, s);
                 if (e != hipSuccess) return FP4Q_ERR_HIP;
                 a.tensor_scale = wsf;
             }
@@ -223,17 +248,20 @@ int rowwise(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int64_t cols, 
     a.index_base = cfg->index_base;
     a.obs16 = r.obs / 16;
     a.outer_given = r.given;
+    a.x_vec = x_vec ? 1 : 0;
+    a.y_f32 = r.y_f32 ? 1 : 0;
     if (r.outer_kind == kOuterTensor) {
         if (r.given) {
             a.tensor_scale = outer;
         } else {
             float* wsf = (float*)ws;
-            hipError_t e = launch_amax(r.bias, x, rows, cols, ld, residual, wsf + 1, kAmaxPartials, wsf, outer, s);
+            hipError_t e = launch_amax(r.bias, x, r.x_f32, x_vec, rows, cols, ld, residual, wsf + 1, kAmaxPartials, wsf,
+                                       outer, s);
             if (e != hipSuccess) return FP4Q_ERR_HIP;
             a.tensor_scale = wsf;
         }
     }
-    return hip_status(launch_rows(r.bias, r.outer_kind, r.sr, a, s));
+    return hip_status(launch_rows(r.bias, r.outer_kind, r.sr, r.x_f32, a, s));
 }
 
 }  // namespace
@@ -247,7 +275,7 @@ const char* fp4q_status_str(int status)
     switch (status) {
     case FP4Q_OK: return "ok";
     case FP4Q_ERR_NULL: return "a required pointer is NULL";
-    case FP4Q_ERR_DTYPE: return "input dtype not accepted (bf16 only; fp16 is rejected)";
+    case FP4Q_ERR_DTYPE: return "dtype not accepted (bf16 or fp32; fp16 is rejected)";
     case FP4Q_ERR_SHAPE: return "shape violates the block or outer-block divisibility rules";
     case FP4Q_ERR_MODE: return "illegal combination of format, scale format and two-level mode";
     case FP4Q_ERR_UNSUPPORTED: return "configuration valid but not implemented";
@@ -288,20 +316,20 @@ int fp4q_buffer_sizes(const fp4q_cfg* cfg, int64_t rows, int64_t cols, fp4q_size
         out->col_scales = n / 16;
         out->col_outer = (r.outer_kind == kOuter1D && rows % r.obs == 0) ? outer_count(r, rows, cols, true) * sizeof(float) : 0;
     }
-    out->y = n * 2;
+    out->y = n * (r.y_f32 ? 4 : 2);
     out->residual = r.fmt == FP4Q_MXFP4 ? 0 : n * 4;
     out->workspace = ws_bytes_for(r);
     return FP4Q_OK;
 }
 
-int fp4_quantize(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* codes,
+int fp4_quantize(const fp4q_cfg* cfg, const void* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* codes,
                  uint8_t* scales, float* outer, float* residual, void* workspace, size_t workspace_bytes, void* stream)
 {
     return rowwise(cfg, x, rows, cols, ld_x, nullptr, codes, scales, outer, residual, workspace, workspace_bytes,
                    stream, false);
 }
 
-int fp4_qdq(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint16_t* y,
+int fp4_qdq(const fp4q_cfg* cfg, const void* x, int64_t rows, int64_t cols, int64_t ld_x, void* y,
             uint8_t* codes, uint8_t* scales, float* outer, float* residual, void* workspace, size_t workspace_bytes,
             void* stream)
 {
@@ -310,7 +338,7 @@ int fp4_qdq(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int64_t cols, 
 }
 
 int fp4_dequantize(const fp4q_cfg* cfg, const uint8_t* codes, const uint8_t* scales, const float* outer, int64_t rows,
-                   int64_t cols, int32_t outer_transposed, uint16_t* y, void* stream)
+                   int64_t cols, int32_t outer_transposed, void* y, void* stream)
 {
     Resolved r;
     int st = resolve(cfg, r);
@@ -328,9 +356,9 @@ int fp4_dequantize(const fp4q_cfg* cfg, const uint8_t* codes, const uint8_t* sca
     if (r.outer_kind != kOuterNone && !outer) return FP4Q_ERR_NULL;
     if (misaligned(codes, 16) || misaligned(y, 16) || misaligned(outer, 4)) return FP4Q_ERR_ALIGN;
     hipStream_t s = (hipStream_t)stream;
-    if (r.fmt == FP4Q_MXFP4) return hip_status(launch_dequant_mx(codes, scales, rows, cols, y, s));
+    if (r.fmt == FP4Q_MXFP4) return hip_status(launch_dequant_mx(codes, scales, rows, cols, y, r.y_f32, s));
     return hip_status(launch_dequant_nv(r.bias, r.outer_kind, outer_transposed, r.obs, codes, scales, outer, rows, cols,
-                                        y, s));
+                                        y, r.y_f32, s));
 }
 
 int fp4_cast_transpose(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
@@ -343,6 +371,8 @@ int fp4_cast_transpose(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int
     if (st) return st;
     if (r.fmt == FP4Q_MXFP4) return FP4Q_ERR_UNSUPPORTED;
     st = check_shape(r, rows, cols, ld_x, true);
+    if (st) return st;
+    st = check_vector_source(r, ld_x);
     if (st) return st;
     if (r.outer_kind == kOuter2D && r.obs != 64) return FP4Q_ERR_UNSUPPORTED;
     if (r.outer_kind == kOuter1D && r.obs != 16 && r.obs != 32 && r.obs != 64) return FP4Q_ERR_UNSUPPORTED;
@@ -381,7 +411,8 @@ int fp4_cast_transpose(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int
             a.tensor_scale = row_outer;
         } else {
             float* wsf = (float*)workspace;
-            hipError_t e = launch_amax(r.bias, x, rows, cols, ld_x, residual, wsf + 1, kAmaxPartials, wsf, row_outer, s);
+            hipError_t e = launch_amax(r.bias, x, false, true, rows, cols, ld_x, residual, wsf + 1, kAmaxPartials, wsf,
+                                       row_outer, s);
             if (e != hipSuccess) return FP4Q_ERR_HIP;
             a.tensor_scale = wsf;
         }
@@ -398,6 +429,9 @@ int fp4_mx_project_fp8(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int
     if (st) return st;
     if (r.fmt != FP4Q_MXFP4) return FP4Q_ERR_MODE;
     st = check_shape(r, rows, cols, ld_x, false);
+    if (st) return st;
+    if (r.y_f32) return FP4Q_ERR_UNSUPPORTED;
+    st = check_vector_source(r, ld_x);
     if (st) return st;
     if ((mx8_row == nullptr) != (mx8_row_scales == nullptr)) return FP4Q_ERR_NULL;
     if ((mx8_col == nullptr) != (mx8_col_scales == nullptr)) return FP4Q_ERR_NULL;
@@ -439,6 +473,8 @@ int fp4_cast_transpose_grouped(const fp4q_cfg* cfg, int32_t groups, const int64_
     int st = resolve(cfg, r);
     if (st) return st;
     if (r.fmt == FP4Q_MXFP4 || r.outer_kind == kOuterTensor) return FP4Q_ERR_UNSUPPORTED;
+    st = check_vector_source(r, ld_x);
+    if (st) return st;
     if (groups < 0) return FP4Q_ERR_SHAPE;
     if (groups > 0 && !rows_per_group) return FP4Q_ERR_NULL;
     int64_t total = 0;

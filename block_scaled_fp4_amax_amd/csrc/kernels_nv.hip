@@ -14,9 +14,14 @@
 //   w   = G[m] * d * s_o                    dequantised value (G[m]*d exact)
 //   residual' = v - (+-w)
 //
+// Sources are bf16 or FP32 ("fp4-train" README, Requirements and limits:
+// float32 or bfloat16 input); a bf16 value widens to binary32 exactly, so the
+// arithmetic is the same.  Dequantised outputs are bf16 (RNE of w) or FP32 (w).
+//
 // Work decomposition: one lane owns one 16-element inner block (two 16-byte
-// loads); the obs/16 lanes of a 1D outer group are neighbours and combine
-// their maxima with cross-lane steps.
+// loads of bf16, four of FP32; one load per element for a view whose start or
+// row pitch is not 16-byte aligned); the obs/16 lanes of a 1D outer group are
+// neighbours and combine their maxima with cross-lane steps.
 #include "launch.h"
 #include "nv_block.h"
 
@@ -26,15 +31,6 @@ namespace {
 
 constexpr int kThreads = 256;
 
-
-__device__ __forceinline__ void load16_bf16(const uint16_t* p, float (&v)[16])
-{
-    const uint4 a = ld_nt16(p);
-    const uint4 b = ld_nt16(p + 8);
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int k = 0; k < 8; ++k) { v[2 * k] = bf16_lo(w[k]); v[2 * k + 1] = bf16_hi(w[k]); }
-}
 
 __device__ __forceinline__ void load16_f32(const float* p, float (&z)[16])
 {
@@ -53,7 +49,41 @@ __device__ __forceinline__ void store16_f32(float* p, const float (&z)[16])
                                       __float_as_uint(z[4 * q + 3])));
 }
 
-template <int BIAS, int OUTER, bool SR, bool EF>
+// Sixteen consecutive source values from element offset off, as binary32, and
+// the largest |value| bit pattern among them (a non-finite value compares above
+// every finite one).  vec (uniform): 16-byte loads; otherwise one load per
+// element, for views aligned only to the element size.
+template <bool XF32>
+__device__ __forceinline__ uint32_t load_src16(const void* x, int64_t off, bool vec, float (&v)[16])
+{
+    uint32_t am = 0;
+    if (!XF32) {
+        const uint16_t* p = static_cast<const uint16_t*>(x) + off;
+        if (vec) {
+            const uint4 w0 = ld_nt16(p);
+            const uint4 w1 = ld_nt16(p + 8);
+            const uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+            for (int k = 0; k < 8; ++k) { v[2 * k] = bf16_lo(w[k]); v[2 * k + 1] = bf16_hi(w[k]); }
+            return bf16_absmax_bits(w) << 16;
+        }
+#pragma unroll
+        for (int k = 0; k < 16; ++k) v[k] = __uint_as_float((uint32_t)__builtin_nontemporal_load(p + k) << 16);
+    } else {
+        const float* p = static_cast<const float*>(x) + off;
+        if (vec) {
+            load16_f32(p, v);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 16; ++k) v[k] = __builtin_nontemporal_load(p + k);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) am = max(am, __float_as_uint(v[k]) & 0x7FFFFFFFu);
+    return am;
+}
+
+template <int BIAS, int OUTER, bool SR, bool EF, bool XF32>
 __global__ __launch_bounds__(kThreads) void k_nv_rows(RowArgs a, uint32_t nblocks, uint32_t bpr)
 {
     __shared__ double rtab[16];
@@ -74,22 +104,16 @@ __global__ __launch_bounds__(kThreads) void k_nv_rows(RowArgs a, uint32_t nblock
     float z[16];
     uint32_t am_bits = 0;
     {
-        const uint16_t* px = a.x + (int64_t)i * a.ld + j0;
-        const uint4 w0 = ld_nt16(px);
-        const uint4 w1 = ld_nt16(px + 8);
-        const uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-        for (int k = 0; k < 8; ++k) { v[2 * k] = bf16_lo(w[k]); v[2 * k + 1] = bf16_hi(w[k]); }
+        am_bits = load_src16<XF32>(a.x, (int64_t)i * a.ld + j0, a.x_vec != 0, v);
         if (EF) {
             load16_f32(a.residual + e0, z);
+            am_bits = 0;
 #pragma unroll
             for (int k = 0; k < 16; ++k) {
                 v[k] = v[k] + z[k];
                 const uint32_t bb = __float_as_uint(v[k]) & 0x7FFFFFFFu;
                 am_bits = am_bits > bb ? am_bits : bb;
             }
-        } else {
-            am_bits = bf16_absmax_bits(w) << 16;
         }
         if (__builtin_expect(am_bits >= 0x7F800000u, 0)) {
             am_bits = 0;
@@ -143,12 +167,15 @@ __global__ __launch_bounds__(kThreads) void k_nv_rows(RowArgs a, uint32_t nblock
 #pragma unroll
             for (int k = 0; k < 16; ++k) w[k] = w[k] * s_o;
         }
-        if (a.y) {
+        if (a.y && a.y_f32) {
+            store16_f32(static_cast<float*>(a.y) + e0, w);
+        } else if (a.y) {
+            uint16_t* y = static_cast<uint16_t*>(a.y);
             uint32_t o[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k) o[k] = f32_to_bf16(w[2 * k]) | (f32_to_bf16(w[2 * k + 1]) << 16);
-            st_nt16(a.y + e0, make_uint4(o[0], o[1], o[2], o[3]));
-            st_nt16(a.y + e0 + 8, make_uint4(o[4], o[5], o[6], o[7]));
+            st_nt16(y + e0, make_uint4(o[0], o[1], o[2], o[3]));
+            st_nt16(y + e0 + 8, make_uint4(o[4], o[5], o[6], o[7]));
         }
         if (EF) {
 #pragma unroll
@@ -159,16 +186,17 @@ __global__ __launch_bounds__(kThreads) void k_nv_rows(RowArgs a, uint32_t nblock
 }
 
 // Tensorwise pass 1: per-workgroup maxima of |sanitise(x (+ residual))|.
-__global__ __launch_bounds__(kThreads) void k_amax_partial(const uint16_t* __restrict__ x, const float* __restrict__ res,
-                                                           int64_t cols, int64_t ld, uint32_t nblocks, uint32_t bpr,
-                                                           float* __restrict__ partials)
+template <bool XF32>
+__global__ __launch_bounds__(kThreads) void k_amax_partial(const void* __restrict__ x, int x_vec,
+                                                           const float* __restrict__ res, int64_t cols, int64_t ld,
+                                                           uint32_t nblocks, uint32_t bpr, float* __restrict__ partials)
 {
     float am = 0.0f;
     for (uint32_t b = blockIdx.x * kThreads + threadIdx.x; b < nblocks; b += gridDim.x * kThreads) {
         const uint32_t i = b / bpr;
         const int64_t j0 = (int64_t)(b - i * bpr) * 16;
         float v[16];
-        load16_bf16(x + (int64_t)i * ld + j0, v);
+        (void)load_src16<XF32>(x, (int64_t)i * ld + j0, x_vec != 0, v);
         if (res) {
             float z[16];
             load16_f32(res + (int64_t)i * cols + j0, z);
@@ -209,13 +237,14 @@ __global__ __launch_bounds__(kThreads) void k_tensor_scale(const float* __restri
     }
 }
 
-// Dequantise one 16-code block: y = bf16(+-G[m] * d [* s_o]).
-template <int BIAS>
+// Dequantise one 16-code block: y = bf16(+-G[m] * d [* s_o]), or the FP32
+// value itself (YF32).
+template <int BIAS, bool YF32>
 __global__ __launch_bounds__(kThreads) void k_nv_dequant(const uint8_t* __restrict__ codes,
                                                          const uint8_t* __restrict__ scales,
                                                          const float* __restrict__ outer, int outer_kind,
                                                          int outer_t, int obs, uint32_t nblocks, uint32_t bpr,
-                                                         int64_t rows, int64_t cols, uint16_t* __restrict__ y)
+                                                         int64_t rows, int64_t cols, void* __restrict__ y)
 {
     const uint32_t b = blockIdx.x * kThreads + threadIdx.x;
     if (b >= nblocks) return;
@@ -229,31 +258,39 @@ __global__ __launch_bounds__(kThreads) void k_nv_dequant(const uint8_t* __restri
     else if (outer_kind == kOuter1D) s_o = outer[(int64_t)i * (cols / obs) + j0 / obs];
     else if (outer_kind == kOuter2D)
         s_o = outer_t ? outer[(j0 / obs) * (rows / obs) + i / obs] : outer[(int64_t)(i / obs) * (cols / obs) + j0 / obs];
-    uint32_t o[8];
+    float w[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
         const uint32_t code = ((k < 8 ? cw.x : cw.y) >> (4 * (k & 7))) & 0xFu;
-        float w = e2m1_value(code & 7u) * d;
-        if (outer_kind != kOuterNone) w = w * s_o;
-        if (code & 8u) w = -w;
-        const uint32_t h = f32_to_bf16(w);
-        if (k & 1) o[k >> 1] |= h << 16;
-        else o[k >> 1] = h;
+        float wk = e2m1_value(code & 7u) * d;
+        if (outer_kind != kOuterNone) wk = wk * s_o;
+        w[k] = (code & 8u) ? -wk : wk;
     }
-    st_nt16(y + e0, make_uint4(o[0], o[1], o[2], o[3]));
-    st_nt16(y + e0 + 8, make_uint4(o[4], o[5], o[6], o[7]));
+    if (YF32) {
+        store16_f32(static_cast<float*>(y) + e0, w);
+    } else {
+        uint32_t o[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[k] = f32_to_bf16(w[2 * k]) | (f32_to_bf16(w[2 * k + 1]) << 16);
+        uint16_t* yb = static_cast<uint16_t*>(y);
+        st_nt16(yb + e0, make_uint4(o[0], o[1], o[2], o[3]));
+        st_nt16(yb + e0 + 8, make_uint4(o[4], o[5], o[6], o[7]));
+    }
 }
 
 }  // namespace
 
-hipError_t launch_rows(int bias, int outer_kind, bool sr, const RowArgs& a, hipStream_t s)
+hipError_t launch_rows(int bias, int outer_kind, bool sr, bool x_f32, const RowArgs& a, hipStream_t s)
 {
     const uint32_t bpr = (uint32_t)(a.cols / 16);
     const uint32_t nblocks = (uint32_t)(a.rows * bpr);
     const uint32_t grid = (nblocks + kThreads - 1) / kThreads;
     const bool ef = a.residual != nullptr;
-#define FP4Q_ROWS(B, O, S, E) \
-    hipLaunchKernelGGL((k_nv_rows<B, O, S, E>), dim3(grid), dim3(kThreads), 0, s, a, nblocks, bpr)
+#define FP4Q_ROWS(B, O, S, E)                                                                                   \
+    do {                                                                                                        \
+        if (x_f32) hipLaunchKernelGGL((k_nv_rows<B, O, S, E, true>), dim3(grid), dim3(kThreads), 0, s, a, nblocks, bpr); \
+        else hipLaunchKernelGGL((k_nv_rows<B, O, S, E, false>), dim3(grid), dim3(kThreads), 0, s, a, nblocks, bpr); \
+    } while (0)
 #define FP4Q_ROWS_E(B, O, S)                     \
     do {                                         \
         if (ef) FP4Q_ROWS(B, O, S, true);        \
@@ -273,15 +310,21 @@ hipError_t launch_rows(int bias, int outer_kind, bool sr, const RowArgs& a, hipS
     return hipGetLastError();
 }
 
-hipError_t launch_amax(int bias, const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, const float* residual,
-                       float* partials, int npartials, float* scale_out, float* user_outer, hipStream_t s)
+hipError_t launch_amax(int bias, const void* x, bool x_f32, bool x_vec, int64_t rows, int64_t cols, int64_t ld,
+                       const float* residual, float* partials, int npartials, float* scale_out, float* user_outer,
+                       hipStream_t s)
 {
     const uint32_t bpr = (uint32_t)(cols / 16);
     const uint32_t nblocks = (uint32_t)(rows * bpr);
     uint32_t grid = (nblocks + kThreads - 1) / kThreads;
     if (grid > (uint32_t)npartials) grid = (uint32_t)npartials;
     if (grid == 0) grid = 1;
-    hipLaunchKernelGGL(k_amax_partial, dim3(grid), dim3(kThreads), 0, s, x, residual, cols, ld, nblocks, bpr, partials);
+    if (x_f32)
+        hipLaunchKernelGGL(k_amax_partial<true>, dim3(grid), dim3(kThreads), 0, s, x, (int)x_vec, residual, cols, ld,
+                           nblocks, bpr, partials);
+    else
+        hipLaunchKernelGGL(k_amax_partial<false>, dim3(grid), dim3(kThreads), 0, s, x, (int)x_vec, residual, cols, ld,
+                           nblocks, bpr, partials);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (bias == 7)
@@ -292,18 +335,18 @@ hipError_t launch_amax(int bias, const uint16_t* x, int64_t rows, int64_t cols, 
 }
 
 hipError_t launch_dequant_nv(int bias, int outer_kind, int outer_t, int obs, const uint8_t* codes,
-                             const uint8_t* scales, const float* outer, int64_t rows, int64_t cols, uint16_t* y,
-                             hipStream_t s)
+                             const uint8_t* scales, const float* outer, int64_t rows, int64_t cols, void* y,
+                             bool y_f32, hipStream_t s)
 {
     const uint32_t bpr = (uint32_t)(cols / 16);
     const uint32_t nblocks = (uint32_t)(rows * bpr);
     const uint32_t grid = (nblocks + kThreads - 1) / kThreads;
-    if (bias == 7)
-        hipLaunchKernelGGL(k_nv_dequant<7>, dim3(grid), dim3(kThreads), 0, s, codes, scales, outer, outer_kind, outer_t,
-                           obs, nblocks, bpr, rows, cols, y);
-    else
-        hipLaunchKernelGGL(k_nv_dequant<15>, dim3(grid), dim3(kThreads), 0, s, codes, scales, outer, outer_kind,
-                           outer_t, obs, nblocks, bpr, rows, cols, y);
+#define FP4Q_DQ(B, F)                                                                                        \
+    hipLaunchKernelGGL((k_nv_dequant<B, F>), dim3(grid), dim3(kThreads), 0, s, codes, scales, outer, outer_kind, \
+                       outer_t, obs, nblocks, bpr, rows, cols, y)
+    if (bias == 7) { if (y_f32) FP4Q_DQ(7, true); else FP4Q_DQ(7, false); }
+    else { if (y_f32) FP4Q_DQ(15, true); else FP4Q_DQ(15, false); }
+#undef FP4Q_DQ
     return hipGetLastError();
 }
 

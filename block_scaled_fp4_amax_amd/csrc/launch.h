@@ -21,17 +21,19 @@ inline void set_tile_grid(int32_t total_tiles, int32_t& per_xcd, int32_t& wgs_pe
 
 // Rowwise NVFP4 / AMDFP4 parameters (modes none, tensorwise, 1D outer).
 struct RowArgs {
-    const uint16_t* x;
+    const void* x;           // bf16 or FP32 (the launcher's x_f32), [rows, ld]
     int64_t rows, cols, ld;
     uint8_t* codes;          // may be null (qdq without codes)
     uint8_t* scales;         // may be null
     float* outer;            // 1D: [rows, cols/obs]; tensorwise: [1]
     float* residual;         // may be null
-    uint16_t* y;             // may be null
+    void* y;                 // bf16 or FP32 (y_f32) [rows, cols], may be null
     const float* tensor_scale;  // tensorwise: device scalar holding s_g
     uint64_t seed, step, index_base;
     int32_t obs16;           // 1D outer: obs / 16 (1, 2, 4, 8)
     int32_t outer_given;     // 1: read outer instead of computing it
+    int32_t x_vec;           // 1: x and every row start 16-byte aligned (vector loads)
+    int32_t y_f32;           // 1: y is FP32
 };
 
 // Tile parameters (64 x 64 tiles walked as 2 x 2 super-tiles): cast-transpose,
@@ -80,23 +82,26 @@ struct Mx8Args {
 
 hipError_t launch_mx_fp8(const Mx8Args& a, hipStream_t s);
 
-hipError_t launch_mx_qdq(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, uint16_t* y,
-                         uint8_t* codes, uint8_t* scales, hipStream_t s);
+// x: bf16 (x_f32 = false) or FP32 [rows, ld]; x_vec: x and every row start
+// 16-byte aligned.  y: bf16 or FP32 (y_f32) [rows, cols].
+hipError_t launch_mx_qdq(const void* x, bool x_f32, bool x_vec, int64_t rows, int64_t cols, int64_t ld, void* y,
+                         bool y_f32, uint8_t* codes, uint8_t* scales, hipStream_t s);
 
-hipError_t launch_amax(int scale_bias, const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+hipError_t launch_amax(int scale_bias, const void* x, bool x_f32, bool x_vec, int64_t rows, int64_t cols, int64_t ld,
                        const float* residual, float* partials, int npartials, float* scale_out,
                        float* user_outer, hipStream_t s);
 
-hipError_t launch_rows(int scale_bias, int outer_kind, bool stochastic, const RowArgs& a, hipStream_t s);
+hipError_t launch_rows(int scale_bias, int outer_kind, bool stochastic, bool x_f32, const RowArgs& a,
+                       hipStream_t s);
 
 hipError_t launch_tiles(int scale_bias, int outer_kind, bool stochastic, const TileArgs& a, hipStream_t s);
 
 hipError_t launch_dequant_nv(int scale_bias, int outer_kind, int outer_transposed, int obs,
                              const uint8_t* codes, const uint8_t* scales, const float* outer,
-                             int64_t rows, int64_t cols, uint16_t* y, hipStream_t s);
+                             int64_t rows, int64_t cols, void* y, bool y_f32, hipStream_t s);
 
 hipError_t launch_dequant_mx(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
-                             uint16_t* y, hipStream_t s);
+                             void* y, bool y_f32, hipStream_t s);
 
 // partial maxima used by the tensorwise amax pass
 constexpr int kAmaxPartials = 512;

@@ -130,6 +130,48 @@ def apply_expert_update(w_bits, dw):
     return to_bf16(from_bf16(w_bits) + dw)
 
 
+
+# ------------------------------------------------------------------ binary32 sources
+def fp32_weights(seed, rows, cols, std=0.02):
+    """A binary32 source with full 24-bit significands: N(0, std) x per-row
+    lognormal(0, 2), one seeded row x300, one seeded column x1e-3, seeded
+    signed zeros and binary32 subnormals (float32 array; no inf / NaN)."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((rows, cols), dtype=np.float32) * np.float32(std)
+    x *= rng.lognormal(0.0, 2.0, (rows, 1)).astype(np.float32)
+    x[rng.integers(0, rows), :] *= np.float32(300)
+    x[:, rng.integers(0, cols)] *= np.float32(1e-3)
+    n = rows * cols
+    k = max(1, n // 512)
+    x.ravel()[rng.integers(0, n, k)] = 0.0
+    x.ravel()[rng.integers(0, n, k)] = -0.0
+    sub = rng.integers(1, 1 << 23, k, dtype=np.uint64).astype(np.uint32)
+    sub |= rng.integers(0, 2, k, dtype=np.uint64).astype(np.uint32) << np.uint32(31)
+    x.ravel()[rng.integers(0, n, k)] = sub.view(np.float32)
+    return x
+
+
+def fp32_raw_bit_blocks(seed, rows, cols):
+    """Raw binary32 bit patterns in 1 x 32 blocks (uint32): every fourth block
+    uniformly random bits (NaN / inf / subnormal patterns included), the others
+    random significands and signs within one to four binades drawn per block,
+    or binary32 subnormals."""
+    rng = np.random.default_rng(seed)
+    x = np.zeros((rows, cols), np.uint32)
+    for i in range(rows):
+        for j0 in range(0, cols, 32):
+            kind = (i * (cols // 32) + j0 // 32) % 4
+            raw = rng.integers(0, 1 << 32, 32, dtype=np.uint64).astype(np.uint32)
+            if kind == 0:
+                x[i, j0:j0 + 32] = raw
+                continue
+            e = int(rng.integers(1, 250)) if kind != 3 else 0
+            span = int(rng.integers(0, 4))
+            exps = (e + (raw >> np.uint32(24)) % np.uint32(span + 1)) if kind != 3 else np.zeros(32, np.uint32)
+            x[i, j0:j0 + 32] = (raw & np.uint32(0x807FFFFF)) | (exps.astype(np.uint32) << np.uint32(23))
+    return x
+
+
 CONFIGS = {
     "nv_tensorwise_qdq_256": dict(name="nvfp4_tensorwise_qdq_256x256", rows=256, cols=256),
     "nv_2d_cast_transpose_4096": dict(name="nvfp4_outer2d64_cast_transpose_4096x4096", rows=4096, cols=4096),

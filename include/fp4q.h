@@ -66,15 +66,15 @@
 extern "C" {
 #endif
 
-#define FP4Q_ABI_VERSION 1
+#define FP4Q_ABI_VERSION 2
 
 /* Status codes. */
 enum {
     FP4Q_OK = 0,
     FP4Q_ERR_NULL = 1,        /* a required pointer is NULL                               */
-    FP4Q_ERR_DTYPE = 2,       /* input dtype other than bf16 (fp16 is rejected: its range
-                                 is smaller than the FP4 grid times the scales, "MXFP4
-                                 weight QAT recipes", Guards)                              */
+    FP4Q_ERR_DTYPE = 2,       /* input or output dtype other than bf16 / fp32 (fp16 is
+                                 rejected: its range is smaller than the FP4 grid times
+                                 the scales, "MXFP4 weight QAT recipes", Guards)          */
     FP4Q_ERR_SHAPE = 3,       /* cols % 16 (32 for MXFP4), rows % 16 for columnwise,
                                  outer_block_size not a multiple of 16 or not dividing a
                                  reduction dimension (ALTO page, Technical design),
@@ -85,7 +85,9 @@ enum {
                                  precomputed outer scale without a two-level mode,
                                  16 x 16 inner tiles with MXFP4 or 1D outer blocks        */
     FP4Q_ERR_UNSUPPORTED = 5, /* valid on the pages but not built here (see the function) */
-    FP4Q_ERR_ALIGN = 6,       /* a pointer not 16-byte aligned, ld_x % 8 != 0             */
+    FP4Q_ERR_ALIGN = 6,       /* a pointer not 16-byte aligned, ld_x % 8 != 0 (the
+                                 rowwise entry points accept any x aligned to its element
+                                 size and any ld_x >= cols)                               */
     FP4Q_ERR_WORKSPACE = 7,   /* workspace smaller than fp4q_workspace_bytes()            */
     FP4Q_ERR_HIP = 8,         /* the HIP runtime reported a launch error                  */
     FP4Q_ERR_ABI = 9          /* cfg->abi_version != FP4Q_ABI_VERSION                     */
@@ -110,7 +112,13 @@ typedef struct {
     int32_t outer_mode;        /* 0: compute and write the outer scales; 1: read them from the
                                   outer buffers (a precomputed scale, ALTO page,
                                   Implementation: precomputed_outer_scale)                     */
-    int32_t input_dtype;       /* fp4q_dtype of x; only FP4Q_DTYPE_BF16 is accepted            */
+    int32_t input_dtype;       /* fp4q_dtype of x: BF16, or FP32 for fp4_quantize / fp4_qdq in
+                                  modes NONE, TENSORWISE and 1D OUTER_BLOCK and for MXFP4
+                                  ("fp4-train" README, Requirements and limits: float32 or
+                                  bfloat16 input; "MXFP4 weight QAT recipes", Correctness:
+                                  fake-quant on bf16 and fp32).  A bf16 value widens to FP32
+                                  exactly, so both give the same result on bf16 values.
+                                  FP16: FP4Q_ERR_DTYPE.                                        */
     int32_t inner_2d;          /* NVFP4 / AMDFP4 inner scale geometry: 0 = one scale per 1 x 16
                                   block along the quantisation axis; 1 = one scale per 16 x 16
                                   tile of the source, from the largest normalised magnitude of
@@ -122,6 +130,12 @@ typedef struct {
                                   per element serves both directions.  Needs rows % 16 == 0;
                                   not with MXFP4 or 1D outer blocks (their scales differ per
                                   direction): FP4Q_ERR_MODE.                                   */
+    int32_t output_dtype;      /* fp4q_dtype of y in fp4_qdq and fp4_dequantize: BF16 (RNE of
+                                  the FP32 dequantised value) or FP32 (that value itself;
+                                  "MXFP4 weight QAT recipes", Correctness: bf16 and fp32
+                                  dequantise targets); FP32 with the 64 x 64 tile modes (2D
+                                  outer, inner_2d): FP4Q_ERR_UNSUPPORTED; FP16: FP4Q_ERR_DTYPE.
+                                  Ignored by entry points without a y of this kind.            */
     uint64_t seed;             /* SR key                                                       */
     uint64_t step;             /* SR step (counter high word)                                  */
     uint64_t index_base;       /* SR global index of element (0, 0): element (i, j) draws with
@@ -133,7 +147,7 @@ typedef struct {
 typedef struct {
     size_t row_codes, row_scales, row_outer;
     size_t col_codes, col_scales, col_outer;   /* col_outer == 0 when it is shared */
-    size_t y;                                  /* bf16 dequantised output            */
+    size_t y;                                  /* dequantised output (output_dtype)  */
     size_t residual;                           /* FP32 error-feedback residual       */
     size_t workspace;                          /* scratch the caller must provide    */
 } fp4q_sizes;
@@ -156,7 +170,12 @@ size_t fp4q_workspace_bytes(const fp4q_cfg* cfg, int64_t rows, int64_t cols);
 /*
  * fp4_quantize -- rowwise quantisation ("fp4-train" README, API: quantize(x,
  * stochastic, residual, seed, step)).
- *   x         bf16 [rows, ld_x] device, read.
+ *   x         bf16 or FP32 (cfg->input_dtype) [rows, ld_x] device, read.  In
+ *             modes NONE, TENSORWISE, 1D OUTER_BLOCK and MXFP4, x may be a view
+ *             aligned only to its element size with any ld_x >= cols (a
+ *             misaligned view: "MXFP4 weight QAT recipes", Correctness); the
+ *             64 x 64 tile modes (2D outer, inner_2d) need bf16, a 16-byte
+ *             aligned x and ld_x % 8 == 0.
  *   codes     uint8 [rows, cols/2] device, written.
  *   scales    uint8 [rows, cols/16] (cols/32 for MXFP4) device, written.
  *   outer     FP32 outer scales (layout above) device; written when
@@ -171,39 +190,43 @@ size_t fp4q_workspace_bytes(const fp4q_cfg* cfg, int64_t rows, int64_t cols);
  * only and no residual.  With cfg->inner_2d, rows % 16 == 0 (FP4Q_ERR_SHAPE
  * otherwise) and scales hold each 16 x 16 tile's byte in every one of its rows.
  */
-int fp4_quantize(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+int fp4_quantize(const fp4q_cfg* cfg, const void* x, int64_t rows, int64_t cols, int64_t ld_x,
                  uint8_t* codes, uint8_t* scales, float* outer, float* residual,
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * fp4_dequantize -- bf16 from stored codes and scales ("fp4-train" README,
- * API: dequantize(packed, scale, M, K); ALTO page, Implementation:
- * convert_from).  y = bf16(RN(+-G[m] * dec(s_i) [* s_o])); an MXFP4 scale byte
- * 0xFF (NaN) gives the quiet NaN 0x7FC0.
+ * fp4_dequantize -- bf16 or FP32 from stored codes and scales ("fp4-train"
+ * README, API: dequantize(packed, scale, M, K); ALTO page, Implementation:
+ * convert_from).  w = RN(+-G[m] * dec(s_i) [* s_o]), y = bf16(w) or, with
+ * cfg->output_dtype FP32, w itself; an MXFP4 scale byte 0xFF (NaN) gives the
+ * quiet NaN (0x7FC0, 0x7FC00000).
  *   codes, scales, outer  as written by the entry points for a logical
  *                         [rows, cols] buffer (device, read).
  *   outer_transposed      1 when a 2D outer array belongs to the transpose of
  *                         this buffer, i.e. is [cols/obs, rows/obs] -- the case
  *                         of a columnwise buffer sharing its source's 2D outer
  *                         scale; 0 otherwise.
- *   y                     bf16 [rows, cols] device, written.
- * rounding, seed, step and index_base are ignored; so is inner_2d, whose
- * replicated scale layout dequantises exactly like 1 x 16 blocks.
+ *   y                     bf16 or FP32 [rows, cols] device, 16-byte aligned,
+ *                         written.
+ * rounding, seed, step, index_base and input_dtype are ignored; so is inner_2d,
+ * whose replicated scale layout dequantises exactly like 1 x 16 blocks.
  */
 int fp4_dequantize(const fp4q_cfg* cfg, const uint8_t* codes, const uint8_t* scales, const float* outer,
-                   int64_t rows, int64_t cols, int32_t outer_transposed, uint16_t* y, void* stream);
+                   int64_t rows, int64_t cols, int32_t outer_transposed, void* y, void* stream);
 
 /*
  * fp4_qdq -- quantise then dequantise, rowwise ("fp4-train" README, API: qdq;
  * "MXFP4 weight QAT recipes", Design: the fused bf16 -> mxfp4 -> bf16
  * projection is fp4_qdq with format MXFP4).
- *   y         bf16 [rows, cols] device, written.
+ *   x         as in fp4_quantize (bf16 or FP32, misaligned views).
+ *   y         bf16 or FP32 (cfg->output_dtype) [rows, cols] device, 16-byte
+ *             aligned, written.
  *   codes, scales, outer  optional outputs as in fp4_quantize (NULL to skip;
  *             outer is required when outer_mode == 1).
  *   residual, workspace   as in fp4_quantize.
  */
-int fp4_qdq(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
-            uint16_t* y, uint8_t* codes, uint8_t* scales, float* outer, float* residual,
+int fp4_qdq(const fp4q_cfg* cfg, const void* x, int64_t rows, int64_t cols, int64_t ld_x,
+            void* y, uint8_t* codes, uint8_t* scales, float* outer, float* residual,
             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -211,7 +234,8 @@ int fp4_qdq(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int64_t cols, 
  * columnwise buffers (the rowwise layout of X^T) ("Block-Scaled FP8 and FP4
  * Weight Quantization", sections 2-3: fused cast-transpose; ALTO page,
  * Implementation: an axis-invariant 2D outer scale computed once and used by
- * both directions).  NVFP4 / AMDFP4 only.
+ * both directions).  NVFP4 / AMDFP4 only; x bf16 [rows, ld_x] (input_dtype
+ * FP32: FP4Q_ERR_UNSUPPORTED), 16-byte aligned, ld_x % 8 == 0.
  *   row_codes [rows, cols/2], row_scales [rows, cols/16], row_outer (layout
  *   above) -- device, written (row_outer read when outer_mode == 1).
  *   col_codes [cols, rows/2], col_scales [cols, rows/16] -- device, written.
@@ -238,7 +262,8 @@ int fp4_cast_transpose(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int
  *   groups          G >= 0.
  *   rows_per_group  HOST array of G row counts (each a multiple of 16, and of
  *                   obs in OUTER_BLOCK mode).
- *   x               bf16 [sum(rows), ld_x] device.
+ *   x               bf16 [sum(rows), ld_x] device (16-byte aligned, ld_x % 8 == 0;
+ *                   input_dtype FP32: FP4Q_ERR_UNSUPPORTED).
  *   row_codes/row_scales/residual  stacked along rows exactly as for one tensor
  *                   of sum(rows) rows.
  *   col_codes, col_scales  group g's [cols, rows_g/2] and [cols, rows_g/16]
@@ -265,7 +290,8 @@ int fp4_cast_transpose_grouped(const fp4q_cfg* cfg, int32_t groups, const int64_
  * weight feeds MXFP8 and Float8 128x128 block-scaling hosts; the rowwise MXFP8
  * encoding is bitwise lossless, the 128x128 encoding lossless within a tile's
  * E4M3 headroom, the columnwise MXFP8 encoding a bounded re-quantisation).
- * cfg: format MXFP4 (RNE, no two-level mode).  With y the bf16 projection
+ * cfg: format MXFP4 (RNE, no two-level mode), input and output dtype BF16
+ * (FP32: FP4Q_ERR_UNSUPPORTED).  With y the bf16 projection
  * (as fp4_qdq writes it) every output is optional (NULL skips it):
  *   y              bf16 [rows, cols]
  *   mx8_row        E4M3 [rows, cols] and mx8_row_scales UE8M0 [rows, cols/32]:
@@ -286,7 +312,7 @@ int fp4_cast_transpose_grouped(const fp4q_cfg* cfg, int32_t groups, const int64_
  * mx8_row and mx8_row_scales are given together or not at all, likewise
  * mx8_col and mx8_col_scales.  Needs cols % 32 == 0; rows and ld_x up to 2^22
  * (FP4Q_ERR_UNSUPPORTED beyond).  x, y, mx8_row, mx8_col, blk and blk_t
- * 16-byte aligned, blk_scales 4-byte aligned.
+ * 16-byte aligned, ld_x % 8 == 0, blk_scales 4-byte aligned.
  */
 int fp4_mx_project_fp8(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                        uint16_t* y, uint8_t* mx8_row, uint8_t* mx8_row_scales, uint8_t* mx8_col,

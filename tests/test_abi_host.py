@@ -1,14 +1,22 @@
 """Host-side tests of the C ABI (no GPU): the library loads, exports every
 function include/fp4q.h declares, and rejects every invalid configuration
 with its documented status before anything is enqueued (no compute call is
-made: every call here either fails validation or has an empty tensor)."""
+made: every call here either fails validation or has an empty tensor).
+
+The calls pass placeholder device addresses; a call that validated would
+launch on them, so where a GPU is visible these tests do not run (without
+one such a launch fails with FP4Q_ERR_HIP, which every helper rejects)."""
 import ctypes as ct
 import os
 import re
 
 import pytest
+import torch
 
 import block_scaled_fp4_amax_amd as fq
+
+pytestmark = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                                reason="placeholder device pointers: host-only validation tests")
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fp4q.h")
@@ -39,15 +47,25 @@ def test_status_strings():
     assert fq.fp4q_status_str(123) == "unknown status"
 
 
+def _validated(st):
+    assert st != fq.ERR_HIP, "a call reached a launch"
+    return st
+
+
 def q(cfg, rows=64, cols=64, ld=None, x=FAKE, codes=FAKE, scales=FAKE, outer=FAKE, residual=None, ws=None, wsb=0):
-    return fq.lib().fp4_quantize(ct.byref(cfg), x, rows, cols, cols if ld is None else ld, codes, scales, outer,
-                                 residual, ws, wsb, None)
+    return _validated(fq.lib().fp4_quantize(ct.byref(cfg), x, rows, cols, cols if ld is None else ld, codes, scales,
+                                            outer, residual, ws, wsb, None))
+
+
+def qdq(cfg, rows=64, cols=64, ld=None, x=FAKE, y=FAKE):
+    return _validated(fq.lib().fp4_qdq(ct.byref(cfg), x, rows, cols, cols if ld is None else ld, y, None, None, None,
+                                       None, None, 0, None))
 
 
 def ct_(cfg, rows=64, cols=64, ld=None, x=FAKE, row_outer=FAKE, col_outer=None, residual=None, ws=None, wsb=0,
         col_codes=FAKE):
-    return fq.lib().fp4_cast_transpose(ct.byref(cfg), x, rows, cols, cols if ld is None else ld, FAKE, FAKE,
-                                       row_outer, col_codes, FAKE, col_outer, residual, ws, wsb, None)
+    return _validated(fq.lib().fp4_cast_transpose(ct.byref(cfg), x, rows, cols, cols if ld is None else ld, FAKE, FAKE,
+                                                  row_outer, col_codes, FAKE, col_outer, residual, ws, wsb, None))
 
 
 def test_mode_rules():
@@ -70,9 +88,19 @@ def test_mode_rules():
     assert q(C(format=9)) == fq.ERR_MODE
     # precomputed outer without a two-level mode
     assert q(C(outer_mode=1)) == fq.ERR_MODE
-    # dtype guard: fp16 rejected, fp32 valid on the pages but not built
+    # dtype guard: fp16 rejected as input and as output ("MXFP4 weight QAT
+    # recipes", Guards); fp32 accepted by the rowwise paths only
     assert q(C(input_dtype="fp16")) == fq.ERR_DTYPE
-    assert q(C(input_dtype="fp32")) == fq.ERR_UNSUPPORTED
+    assert q(C(input_dtype=7)) == fq.ERR_DTYPE
+    assert qdq(C(output_dtype="fp16")) == fq.ERR_DTYPE
+    assert qdq(C(format="mxfp4", output_dtype=5)) == fq.ERR_DTYPE
+    for f32 in (C(input_dtype="fp32"), C(format="mxfp4", input_dtype="fp32", output_dtype="fp32")):
+        assert q(f32, rows=0, x=None, codes=None, scales=None, outer=None) == fq.OK
+    tile2d = dict(two_level="outer_block", outer_block_size=64, outer_2d=True)
+    assert q(C(input_dtype="fp32", **tile2d)) == fq.ERR_UNSUPPORTED
+    assert q(C(input_dtype="fp32", inner_2d=True)) == fq.ERR_UNSUPPORTED
+    assert qdq(C(output_dtype="fp32", **tile2d)) == fq.ERR_UNSUPPORTED
+    assert ct_(C(input_dtype="fp32")) == fq.ERR_UNSUPPORTED
     bad = C()
     bad.abi_version = 99
     assert q(bad) == fq.ERR_ABI
@@ -85,11 +113,21 @@ def test_shape_and_pointer_rules():
     assert q(C(format="mxfp4"), cols=48) == fq.ERR_SHAPE        # cols % 32
     assert q(C(), rows=-1) == fq.ERR_SHAPE
     assert q(C(), cols=64, ld=32) == fq.ERR_SHAPE               # ld < cols
-    assert q(C(), cols=64, ld=68) == fq.ERR_ALIGN               # ld % 8
+    # any row pitch for the rowwise paths (views), 16-byte rows for the tile kernels
+    assert q(C(), rows=0, cols=64, ld=68, x=None, codes=None, scales=None, outer=None) == fq.OK
+    tile2d = C(two_level="outer_block", outer_block_size=64, outer_2d=True)
+    assert q(tile2d, cols=64, ld=68) == fq.ERR_ALIGN
+    assert ct_(C(), cols=64, ld=68) == fq.ERR_ALIGN
     assert q(C(), x=None) == fq.ERR_NULL
     assert q(C(), codes=None) == fq.ERR_NULL
     assert q(C(two_level="tensorwise"), outer=None) == fq.ERR_NULL
-    assert q(C(), x=FAKE_MIS) == fq.ERR_ALIGN
+    # misaligned views: x aligned to its element size is enough for the rowwise paths
+    assert q(C(), x=FAKE + 1) == fq.ERR_ALIGN
+    assert q(C(input_dtype="fp32"), x=FAKE + 2) == fq.ERR_ALIGN
+    assert q(C(format="mxfp4", input_dtype="fp32"), x=FAKE + 6) == fq.ERR_ALIGN
+    assert q(tile2d, x=FAKE_MIS) == fq.ERR_ALIGN
+    assert ct_(C(), x=FAKE_MIS) == fq.ERR_ALIGN
+    assert qdq(C(), y=FAKE_MIS) == fq.ERR_ALIGN                 # outputs stay 16-byte aligned
     assert q(C(format="mxfp4"), residual=FAKE) == fq.ERR_UNSUPPORTED
     # 2D outer needs rows % obs; only obs 64 is built for 2D
     assert q(C(two_level="outer_block", outer_block_size=64, outer_2d=True), rows=80) == fq.ERR_SHAPE
@@ -166,8 +204,8 @@ def test_mx_project_fp8_rules():
 
     def call(cfg, rows=128, cols=128, ld=None, x=FAKE, y=FAKE, r8=FAKE, r8s=FAKE, c8=FAKE, c8s=FAKE, b=FAKE,
              bt=FAKE, bs=FAKE):
-        return L.fp4_mx_project_fp8(ct.byref(cfg), x, rows, cols, cols if ld is None else ld, y, r8, r8s, c8, c8s,
-                                    b, bt, bs, None)
+        return _validated(L.fp4_mx_project_fp8(ct.byref(cfg), x, rows, cols, cols if ld is None else ld, y, r8, r8s,
+                                               c8, c8s, b, bt, bs, None))
     mx = C(format="mxfp4")
     assert call(C()) == fq.ERR_MODE                                     # NVFP4 is not the projection
     assert call(C(format="mxfp4", rounding="stochastic")) == fq.ERR_UNSUPPORTED
@@ -178,6 +216,9 @@ def test_mx_project_fp8_rules():
     assert call(mx, c8=None) == fq.ERR_NULL
     assert call(mx, x=None) == fq.ERR_NULL
     assert call(mx, x=FAKE_MIS) == fq.ERR_ALIGN
+    assert call(mx, ld=132) == fq.ERR_ALIGN                              # 16-byte rows
+    assert call(C(format="mxfp4", input_dtype="fp32")) == fq.ERR_UNSUPPORTED
+    assert call(C(format="mxfp4", output_dtype="fp32")) == fq.ERR_UNSUPPORTED
     assert call(mx, rows=(1 << 22) + 128) == fq.ERR_UNSUPPORTED
     assert call(mx, rows=0, x=None) == fq.OK                            # empty: validated, nothing launched
 
@@ -197,6 +238,12 @@ def test_dequantize_rules():
     o2 = C(two_level="outer_block", outer_block_size=64, outer_2d=True)
     assert L.fp4_dequantize(ct.byref(o2), FAKE, FAKE, None, 64, 64, 0, FAKE, None) == fq.ERR_NULL
     assert L.fp4_dequantize(ct.byref(o2), FAKE, FAKE, FAKE, 48, 64, 0, FAKE, None) == fq.ERR_SHAPE
+    assert L.fp4_dequantize(ct.byref(C(output_dtype="fp16")), FAKE, FAKE, None, 16, 32, 0, FAKE, None) == fq.ERR_DTYPE
+    assert L.fp4_dequantize(ct.byref(C(output_dtype="fp32")), FAKE, FAKE, None, 16, 32, 0, FAKE_MIS,
+                            None) == fq.ERR_ALIGN
+    # buffer sizes follow the output dtype
+    assert fq.fp4q_buffer_sizes(C(output_dtype="fp32"), 32, 64)["y"] == 32 * 64 * 4
+    assert fq.fp4q_buffer_sizes(C(), 32, 64)["y"] == 32 * 64 * 2
 
 
 def test_buffer_sizes():

@@ -1,0 +1,47 @@
+"""Host-side checks of the Python binding (no GPU, no launch): the
+error-feedback state manager's bookkeeping and argument rules ("fp4-train"
+README, API: ErrorFeedback), and the refusal of host tensors before any
+pointer reaches the library."""
+import pytest
+import torch
+
+import block_scaled_fp4_amax_amd as fq
+
+
+def test_host_tensors_are_refused():
+    x = torch.zeros(16, 32, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device tensors"):
+        fq.fp4_qdq(x, fq.make_cfg())
+    with pytest.raises(ValueError, match="device tensors"):
+        fq.fp4_quantize(x.float(), fq.make_cfg(format="mxfp4"))
+    with pytest.raises(ValueError, match="device tensors"):
+        fq.fp4_mx_project_fp8(x)
+
+
+def test_error_feedback_rules():
+    with pytest.raises(fq.Fp4Error):
+        fq.ErrorFeedback(format="mxfp4")
+    with pytest.raises(ValueError):
+        fq.ErrorFeedback(fq.make_cfg(), stochastic=True)
+    ef = fq.ErrorFeedback(stochastic=True, seed=7, two_level="tensorwise")
+    assert ef.cfg.rounding == fq.ROUNDING["stochastic"] and ef.cfg.seed == 7
+    assert ef.cfg.two_level == fq.TWO_LEVEL["tensorwise"]
+    assert ef._cfg(5).step == 5 and ef.cfg.step == 0          # per-call step, stored cfg untouched
+    with pytest.raises(KeyError):
+        ef.residual("w")
+    like = torch.zeros(32, 64, dtype=torch.bfloat16)
+    r = ef.residual("w", like)
+    assert r.dtype == torch.float32 and tuple(r.shape) == (32, 64) and not r.any()
+    assert ef.residual("w", like) is r
+    with pytest.raises(ValueError):
+        ef.residual("w", torch.zeros(16, 64))
+    sd = ef.state_dict()
+    sd["w"] += 1
+    assert not ef.residual("w").any()                          # state_dict holds copies
+    ef.load_state_dict(sd)
+    assert bool((ef.residual("w") == 1).all())
+    with pytest.raises(ValueError):
+        ef.load_state_dict({"w": torch.zeros(4, dtype=torch.float32)})
+    ef.reset("w")
+    with pytest.raises(KeyError):
+        ef.residual("w")
