@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU oracle time for the baseline")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 256 MiB device copy (counter calibration) and exit")
-    ap.add_argument("--only", default=None, help="time a single workload (nv_tensorwise_qdq_256, nv_2d_cast_transpose_4096, mx_fake_quant_8192, amd_1d_sr_cast_transpose_16384x2880, nv_grouped_sr_ef_32x2880, nv_2d_inner16_cast_transpose_4096, mx_project_fp8_8192) and exit")
+    ap.add_argument("--only", default=None, help="time a single workload (nv_tensorwise_qdq_256, nv_2d_cast_transpose_4096, mx_fake_quant_8192, amd_1d_sr_cast_transpose_16384x2880, nv_grouped_sr_ef_32x2880, nv_2d_inner16_cast_transpose_4096, mx_project_fp8_8192, mx_fake_quant_fp32_8192) and exit")
     ap.add_argument("--eager", action="store_true", help="launch every step from the host (no graph replay)")
     ap.add_argument("--pmc-summary", nargs=5, metavar=("KEY", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     default=None,
@@ -61,7 +61,8 @@ KERNEL_NAME_PREFIX = {"nv_tensorwise_qdq_256": "fp4q::(anonymous namespace)::k_n
                       "mx_fake_quant_8192": "fp4q::(anonymous namespace)::k_mx_qdq", "amd_1d_sr_cast_transpose_16384x2880": "fp4q::(anonymous namespace)::k_tile",
                       "nv_grouped_sr_ef_32x2880": "fp4q::(anonymous namespace)::k_tile",
                       "nv_2d_inner16_cast_transpose_4096": "fp4q::(anonymous namespace)::k_tile",
-                      "mx_project_fp8_8192": "fp4q::(anonymous namespace)::k_mx_fp8"}
+                      "mx_project_fp8_8192": "fp4q::(anonymous namespace)::k_mx_fp8",
+                      "mx_fake_quant_fp32_8192": "fp4q::(anonymous namespace)::k_mx_qdq_f32"}
 COPY_PROBE_BYTES = 256 << 20
 
 
@@ -271,6 +272,25 @@ def make_mx_project_fp8(torch, fq, W):
                  alg, sets, launch, "k_mx_fp8<true, true, true, true>", n)
 
 
+def make_mx_fake_quant_fp32(torch, fq, W):
+    R = C = 8192
+    x = W.from_bf16(W.mx_weight_8192_edges())
+    cfg = fq.make_cfg(format="mxfp4", input_dtype="fp32", output_dtype="fp32")
+    alg = R * C * 4 * 2
+    nset = n_sets_for(alg, cap=4)
+    src = torch.from_numpy(x.copy()).cuda()
+    sets = [dict(x=src.clone(), y=torch.empty(R * C, dtype=torch.float32, device="cuda")) for _ in range(nset)]
+    L = fq.lib()
+
+    def launch(s):
+        st = L.fp4_qdq(ct.byref(cfg), s["x"].data_ptr(), R, C, C, s["y"].data_ptr(), None, None, None, None, None, 0,
+                       torch.cuda.current_stream().cuda_stream)
+        if st:
+            raise fq.Fp4Error(st, "fp4_qdq")
+    return Timed("mx_fake_quant_fp32_8192", "MXFP4 1x32 fake-quant 8192x8192 fp32 -> fp32", alg, sets, launch,
+                 "k_mx_qdq_f32<true, true, false>", R * C)
+
+
 def make_cast_transpose_1d_sr(torch, fq, W):
     R, C = 16384, 2880
     x = W.activations_16384x2880()
@@ -434,7 +454,8 @@ def main():
               "amd_1d_sr_cast_transpose_16384x2880": make_cast_transpose_1d_sr,
               "nv_grouped_sr_ef_32x2880": make_grouped_sr_ef,
               "nv_2d_inner16_cast_transpose_4096": make_cast_transpose_2d_inner16,
-              "mx_project_fp8_8192": make_mx_project_fp8}[args.only]
+              "mx_project_fp8_8192": make_mx_project_fp8,
+              "mx_fake_quant_fp32_8192": make_mx_fake_quant_fp32}[args.only]
         w = mk(torch, fq, W)
         ms = run_timed(torch, w, args.steps, args.warmup, graph=not args.eager)
         per = ms / args.steps
@@ -470,7 +491,7 @@ def main():
         extra = {}
         for mk, steps in ((make_mx_fake_quant, 400), (make_cast_transpose_1d_sr, 400), (make_grouped_sr_ef, 20),
                           (make_tensorwise_qdq, 400), (make_cast_transpose_2d_inner16, 2000),
-                          (make_mx_project_fp8, 200)):
+                          (make_mx_project_fp8, 200), (make_mx_fake_quant_fp32, 200)):
             e = mk(torch, fq, W)
             print("# extra %s" % e.name, file=sys.stderr, flush=True)
             ems = run_timed(torch, e, steps, min(20, steps))
