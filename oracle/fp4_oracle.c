@@ -936,3 +936,44 @@ int orc_mx_project_encode(const uint16_t* X, int64_t R, int64_t C, uint16_t* y_o
     free(y);
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* FP4 GEMM consumer: C = A . B^T with MXFP4 operands ("fp4-train" README,   */
+/* API: fp4_mm(a, b) is a @ b^T on FP4 operands; Correctness: the FP4 GEMM   */
+/* equals the dequantise-then-multiply path).                                */
+/* ------------------------------------------------------------------------ */
+
+/* Value of element (i, k) of an MXFP4 operand stored as rowwise codes
+ * [rows, K/2] and UE8M0 scale bytes [rows, K/32]: +-G[m] * 2^(s-127), NaN for
+ * scale byte 0xFF. */
+static double mx_operand(const uint8_t* codes, const uint8_t* scales, int64_t K, int64_t i, int64_t k)
+{
+    const uint8_t byte = codes[i * (K / 2) + k / 2];
+    const int code = (k & 1) ? (byte >> 4) : (byte & 0xF);
+    const int sc = scales[i * (K / MXB) + k / MXB];
+    if (sc == 255) return NAN;
+    const double v = E2M1_GRID[code & 7] * orc_ue8m0_decode(sc);
+    return (code & 8) ? -v : v;
+}
+
+/* c[i, j] = sum_k a(i, k) * b(j, k) and s[i, j] = sum_k |a(i, k) * b(j, k)|,
+ * both in binary64, k ascending (each product is exact in binary64).  The
+ * absolute sum bounds the rounding error of any binary32 evaluation order. */
+int orc_mx_mm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes, const uint8_t* b_scales,
+              int64_t M, int64_t N, int64_t K, double* c, double* s)
+{
+    if (K % MXB || M < 0 || N < 0) return -2;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < N; ++j) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const double p = mx_operand(a_codes, a_scales, K, i, k) * mx_operand(b_codes, b_scales, K, j, k);
+                acc += p;
+                mag += fabs(p);
+            }
+            c[i * N + j] = acc;
+            if (s) s[i * N + j] = mag;
+        }
+    return 0;
+}

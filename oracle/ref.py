@@ -77,6 +77,8 @@ def lib():
         L.orc_mx_qdq_ex.argtypes = [P, ct.c_int, ct.c_int64, ct.c_int64, P, P, P, ct.c_int]
         L.orc_mx_dequantize_ex.restype = ct.c_int
         L.orc_mx_dequantize_ex.argtypes = [P, P, ct.c_int64, ct.c_int64, P, ct.c_int]
+        L.orc_mx_mm.restype = ct.c_int
+        L.orc_mx_mm.argtypes = [P, P, P, P, ct.c_int64, ct.c_int64, ct.c_int64, P, P]
         L.orc_nv_quantize_grouped.restype = ct.c_int
         L.orc_nv_quantize_grouped.argtypes = [ct.POINTER(_NvParams), ct.c_int32, P, ct.c_int64,
                                               P, P, P, P, P, P, P, P]
@@ -362,3 +364,18 @@ def mx_dequantize(codes, scales, R, C, y_dtype="bf16"):
     if rc != 0:
         raise ValueError("oracle rejected the shape (%d)" % rc)
     return y
+
+
+def mx_mm(a_codes, a_scales, b_codes, b_scales, M, N, K):
+    """C = A . B^T of MXFP4 operands (rowwise codes [*, K/2], UE8M0 scales
+    [*, K/32]) in binary64: returns (c, s), s the sum of |products| per entry."""
+    a_codes = np.ascontiguousarray(a_codes, dtype=np.uint8)
+    a_scales = np.ascontiguousarray(a_scales, dtype=np.uint8)
+    b_codes = np.ascontiguousarray(b_codes, dtype=np.uint8)
+    b_scales = np.ascontiguousarray(b_scales, dtype=np.uint8)
+    c = np.zeros((M, N), np.float64)
+    s = np.zeros((M, N), np.float64)
+    rc = lib().orc_mx_mm(_p(a_codes), _p(a_scales), _p(b_codes), _p(b_scales), M, N, K, _p(c), _p(s))
+    if rc != 0:
+        raise ValueError("oracle rejected the shape (%d)" % rc)
+    return c, s
