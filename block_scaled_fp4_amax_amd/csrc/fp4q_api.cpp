@@ -462,6 +462,35 @@ int fp4_mx_project_fp8(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int
     return hip_status(launch_mx_fp8(a, (hipStream_t)stream));
 }
 
+int fp4_mm(const fp4q_cfg* cfg, const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+           const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* c, int64_t ldc, void* stream)
+{
+    Resolved r;
+    int st = resolve(cfg, r);
+    if (st) return st;
+    if (r.fmt != FP4Q_MXFP4) return FP4Q_ERR_MODE;
+    if (M < 0 || N < 0 || K < 0 || K % 64) return FP4Q_ERR_SHAPE;
+    if (M > 0 && N > 0 && ldc < N) return FP4Q_ERR_SHAPE;
+    if (K > ((int64_t)1 << 22) || M > ((int64_t)1 << 24) || N > ((int64_t)1 << 24)) return FP4Q_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return FP4Q_OK;
+    if (!c || (K > 0 && (!a_codes || !a_scales || !b_codes || !b_scales))) return FP4Q_ERR_NULL;
+    if (misaligned(a_codes, 16) || misaligned(b_codes, 16) || misaligned(c, r.y_f32 ? 4 : 2)) return FP4Q_ERR_ALIGN;
+    GemmArgs g;
+    g.a = a_codes;
+    g.as = a_scales;
+    g.b = b_codes;
+    g.bs = b_scales;
+    g.M = (int32_t)M;
+    g.N = (int32_t)N;
+    g.K = (int32_t)K;
+    g.tiles_m = (int32_t)((M + 255) / 256);
+    g.tiles_n = (int32_t)((N + 255) / 256);
+    g.c_f32 = r.y_f32 ? 1 : 0;
+    g.c = c;
+    g.ldc = ldc;
+    return hip_status(launch_mx_gemm(g, (hipStream_t)stream));
+}
+
 int fp4_cast_transpose_grouped(const fp4q_cfg* cfg, int32_t groups, const int64_t* rows_per_group, int64_t cols,
                                const uint16_t* x, int64_t ld_x, uint8_t* row_codes, uint8_t* row_scales,
                                float* row_outer, uint8_t* col_codes, uint8_t* col_scales, float* col_outer,

@@ -1,0 +1,229 @@
+// kernels_gemm.hip -- the FP4 GEMM consumer: C = A . B^T with MXFP4 operands
+// on gfx950's block-scaled matrix cores.
+//
+// "fp4-train" README, API: fp4_mm(a, b) computes a @ b^T on FP4 operands with
+// the hardware's FP4 matrix instructions; Correctness: the result equals the
+// dequantise-then-multiply path.  On gfx950 the FP4 matrix instruction is
+// v_mfma_scale_f32_32x32x64_f8f6f4, which takes one UE8M0 scale per 32
+// K-values of each operand row: exactly the MXFP4 rowwise layout the quantiser
+// writes (codes [rows, K/2], low nibble first; scales [rows, K/32]).  Both
+// operands are K-major (A [M, K], B [N, K]), so no transpose is needed.
+//
+// Operand layout of the instruction (checked on the device): lane l supplies
+// row l % 32 of its 32 x 64 operand, 32 FP4 values (16 bytes, the low four of
+// its eight operand dwords) that all take lane l's scale byte, and the two
+// lanes l and l + 32 together cover the 64 K-values; A and B lanes pair
+// position by position.  Accumulator register r of lane l holds
+// C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32].  So lane l's operand is one MX
+// block: 16 contiguous bytes of a row, with that block's scale byte.
+//
+// Work decomposition: one workgroup of 256 lanes (4 waves, 2 x 2) per 256 x 256
+// tile of C; each wave owns 128 x 128 (4 x 4 instructions, 256 accumulators).
+// K advances in tiles of 256 values (128 bytes of codes per row) staged in LDS
+// through registers, double-buffered: the next tile's global loads are issued
+// before the current tile's 64 instructions per wave, and written to the other
+// LDS buffer after them (one barrier per K-tile).  In LDS a row's eight 16-byte
+// chunks are XOR-swizzled by the row (chunk ^ (row & 7)), so the 32 rows a
+// wave reads for one operand spread over all banks.  Rows beyond M or N and
+// K-values beyond K load as zero codes with scale byte 0 (2^-127), adding
+// exact zeros.  Workgroup ids are remapped so each XCD (ids dealt round-robin)
+// works on a contiguous run of tiles that share operand panels in its L2.
+#include "fp4q_device.h"
+#include "launch.h"
+
+namespace fp4q {
+
+namespace {
+
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+typedef float v16f_t __attribute__((ext_vector_type(16)));
+
+constexpr int kThreads = 256;
+constexpr int kBM = 256;                       // tile rows (A) = tile columns (B)
+constexpr int kBK = 256;                       // K-values per K-tile
+constexpr int kRowB = kBK / 2;                 // code bytes per row and K-tile (128)
+constexpr int kChunks = kBM * kRowB / 16;      // 16-byte chunks per operand tile (2048)
+constexpr int kScB = kBK / 32;                 // scale bytes per row and K-tile (8)
+
+struct Smem {
+    uint4 code[2][2][kChunks];                 // [buffer][A, B][chunk]   128 KiB
+    uint2 scale[2][2][kBM];                    // [buffer][A, B][row]       8 KiB
+};
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
+
+// Global loads of one K-tile: 8 code chunks of A and of B per lane (rows
+// q / 8, chunk q % 8 for q = i * 256 + lane: eight lanes read one row's 128
+// bytes), and the lane's row of 8 scale bytes of A and of B.
+struct Stage {
+    uint4 a[8], b[8];
+    uint32_t as[8], bs[8];
+};
+
+__device__ __forceinline__ void load_tile(const GemmArgs& g, const rsrc_t& ra, const rsrc_t& rb, const rsrc_t& ras,
+                                          const rsrc_t& rbs, int kt, int rows_a, int rows_b, Stage& st)
+{
+    const int tid = (int)threadIdx.x;
+    const int kb0 = kt * kRowB;                // byte offset of the K-tile in a code row
+    const int kb_end = g.K / 2;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int q = i * kThreads + tid;
+        const int row = q >> 3, c = q & 7;
+        const int kb = kb0 + 16 * c;
+        const bool kin = kb < kb_end;
+        st.a[i] = buf_load16<0>(ra, (row < rows_a && kin) ? (uint32_t)(row * kb_end + kb) : kOff);
+        st.b[i] = buf_load16<0>(rb, (row < rows_b && kin) ? (uint32_t)(row * kb_end + kb) : kOff);
+    }
+    const int sb0 = kt * kScB, sb_end = g.K / 32;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const bool kin = sb0 + j < sb_end;
+        st.as[j] = __builtin_amdgcn_raw_buffer_load_b8(ras, (tid < rows_a && kin) ? (uint32_t)(tid * sb_end + sb0 + j)
+                                                                                   : kOff, 0, 0);
+        st.bs[j] = __builtin_amdgcn_raw_buffer_load_b8(rbs, (tid < rows_b && kin) ? (uint32_t)(tid * sb_end + sb0 + j)
+                                                                                   : kOff, 0, 0);
+    }
+}
+
+__device__ __forceinline__ void store_tile(Smem& sm, int buf, const Stage& st)
+{
+    const int tid = (int)threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int q = i * kThreads + tid;
+        const int row = q >> 3, c = q & 7;
+        sm.code[buf][0][swz(row, c)] = st.a[i];
+        sm.code[buf][1][swz(row, c)] = st.b[i];
+    }
+    uint2 a, b;
+    a.x = st.as[0] | (st.as[1] << 8) | (st.as[2] << 16) | (st.as[3] << 24);
+    a.y = st.as[4] | (st.as[5] << 8) | (st.as[6] << 16) | (st.as[7] << 24);
+    b.x = st.bs[0] | (st.bs[1] << 8) | (st.bs[2] << 16) | (st.bs[3] << 24);
+    b.y = st.bs[4] | (st.bs[5] << 8) | (st.bs[6] << 16) | (st.bs[7] << 24);
+    sm.scale[buf][0][tid] = a;
+    sm.scale[buf][1][tid] = b;
+}
+
+__device__ __forceinline__ uint32_t scale_byte(uint2 s, int idx)
+{
+    // byte idx (0..7) of the row's K-tile scales
+    const uint32_t w = idx < 4 ? s.x : s.y;
+    return (w >> (8 * (idx & 3))) & 0xFFu;
+}
+
+template <bool CF32>
+__global__ __launch_bounds__(kThreads) void k_mx_gemm(GemmArgs g)
+{
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
+
+    // tile of this workgroup: XCD x takes the contiguous run x * T/8 .. of the
+    // tile order when T % 8 == 0 (ids are dealt round-robin to the 8 XCDs);
+    // within the order, groups of 4 tile rows are walked column by column
+    const int T = g.tiles_m * g.tiles_n;
+    int t = (int)blockIdx.x;
+    if (T % 8 == 0) t = (t & 7) * (T >> 3) + (t >> 3);
+    const int gm = 4;
+    const int group = t / (gm * g.tiles_n);
+    const int first_m = group * gm;
+    const int rows_in_group = min(gm, g.tiles_m - first_m);
+    const int in_group = t - group * gm * g.tiles_n;
+    const int tm = first_m + in_group % rows_in_group;
+    const int tn = in_group / rows_in_group;
+
+    const int m0 = tm * kBM, n0 = tn * kBM;
+    const int rows_a = min(kBM, g.M - m0), rows_b = min(kBM, g.N - n0);
+    const int64_t lda = g.K / 2;
+    const rsrc_t ra = make_rsrc(g.a + (int64_t)m0 * lda);
+    const rsrc_t rb = make_rsrc(g.b + (int64_t)n0 * lda);
+    const rsrc_t ras = make_rsrc(g.as + (int64_t)m0 * (g.K / 32));
+    const rsrc_t rbs = make_rsrc(g.bs + (int64_t)n0 * (g.K / 32));
+
+    const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int lr = lane & 31, lh = lane >> 5;
+
+    v16f_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = v16f_t{};
+
+    const int nk = (g.K + kBK - 1) / kBK;
+    Stage st;
+    load_tile(g, ra, rb, ras, rbs, 0, rows_a, rows_b, st);
+    store_tile(sm, 0, st);
+    __syncthreads();
+
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        const bool more = kt + 1 < nk;
+        if (more) load_tile(g, ra, rb, ras, rbs, kt + 1, rows_a, rows_b, st);
+
+        uint2 sa[4], sb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sa[i] = sm.scale[cur][0][wm * 128 + i * 32 + lr];
+            sb[i] = sm.scale[cur][1][wn * 128 + i * 32 + lr];
+        }
+#pragma unroll
+        for (int ks = 0; ks < kBK / 64; ++ks) {
+            const int chunk = 2 * ks + lh;
+            v8i_t av[4], bv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint4 x = sm.code[cur][0][swz(wm * 128 + i * 32 + lr, chunk)];
+                const uint4 y = sm.code[cur][1][swz(wn * 128 + i * 32 + lr, chunk)];
+                av[i] = v8i_t{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
+                bv[i] = v8i_t{(int)y.x, (int)y.y, (int)y.z, (int)y.w, 0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int sai = (int)scale_byte(sa[i], chunk);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        av[i], bv[j], acc[i][j], 4, 4, 0, sai, 0, (int)scale_byte(sb[j], chunk));
+            }
+        }
+        if (more) {
+            store_tile(sm, cur ^ 1, st);
+        }
+        __syncthreads();
+    }
+
+    // epilogue: accumulator r of lane l is C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32]
+    const int64_t ldc = g.ldc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int col = n0 + wn * 128 + j * 32 + lr;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                if (row < g.M && col < g.N) {
+                    const float v = acc[i][j][r];
+                    if (CF32) static_cast<float*>(g.c)[(int64_t)row * ldc + col] = v;
+                    else static_cast<uint16_t*>(g.c)[(int64_t)row * ldc + col] = (uint16_t)f32_to_bf16(v);
+                }
+            }
+        }
+}
+
+}  // namespace
+
+hipError_t launch_mx_gemm(const GemmArgs& g, hipStream_t s)
+{
+    const int T = g.tiles_m * g.tiles_n;
+    const size_t lds = sizeof(Smem);   // 136 KiB of the CU's 160 KiB
+    auto fn = g.c_f32 ? k_mx_gemm<true> : k_mx_gemm<false>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(fn, dim3(T), dim3(kThreads), lds, s, g);
+    return hipGetLastError();
+}
+
+}  // namespace fp4q

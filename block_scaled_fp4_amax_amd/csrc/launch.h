@@ -82,6 +82,22 @@ struct Mx8Args {
 
 hipError_t launch_mx_fp8(const Mx8Args& a, hipStream_t s);
 
+// C = A . B^T with MXFP4 operands (rowwise codes [rows, K/2], UE8M0 scales
+// [rows, K/32]); K % 64 == 0.
+struct GemmArgs {
+    const uint8_t* a;          // codes of A [M, K/2]
+    const uint8_t* as;         // scales of A [M, K/32]
+    const uint8_t* b;          // codes of B [N, K/2]
+    const uint8_t* bs;         // scales of B [N, K/32]
+    int32_t M, N, K;
+    int32_t tiles_m, tiles_n;  // 256 x 256 tiles of C
+    int32_t c_f32;             // 1: C is FP32, 0: bf16
+    void* c;                   // [M, ldc]
+    int64_t ldc;
+};
+
+hipError_t launch_mx_gemm(const GemmArgs& g, hipStream_t s);
+
 // x: bf16 (x_f32 = false) or FP32 [rows, ld]; x_vec: x and every row start
 // 16-byte aligned.  y: bf16 or FP32 (y_f32) [rows, cols].
 hipError_t launch_mx_qdq(const void* x, bool x_f32, bool x_vec, int64_t rows, int64_t cols, int64_t ld, void* y,

@@ -318,6 +318,29 @@ int fp4_mx_project_fp8(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int
                        uint16_t* y, uint8_t* mx8_row, uint8_t* mx8_row_scales, uint8_t* mx8_col,
                        uint8_t* mx8_col_scales, uint8_t* blk, uint8_t* blk_t, float* blk_scales, void* stream);
 
+/*
+ * fp4_mm -- C = A . B^T with MXFP4 operands on gfx950's FP4 matrix cores
+ * ("fp4-train" README, API: fp4_mm(a, b) is a @ b^T on the FP4 tensor cores;
+ * Correctness: the FP4 GEMM equals the dequantise-then-multiply path).
+ *   cfg        format MXFP4; output_dtype BF16 or FP32 is the type of C; the
+ *              other fields are ignored.
+ *   a_codes    uint8 [M, K/2] and a_scales uint8 [M, K/32]: A's rowwise MXFP4
+ *              buffers as fp4_quantize writes them (device, read).
+ *   b_codes    uint8 [N, K/2] and b_scales uint8 [N, K/32]: B's, B being
+ *              [N, K] (both operands K-major).
+ *   c          [M, ldc] device (ldc >= N), written, not accumulated into; bf16
+ *              is the RNE of the FP32 sum.
+ * Every product of two E2M1 values and two power-of-two scales is exact; the
+ * sums accumulate in binary32 in an order of the kernel's choosing, so
+ * |C - exact| <= (K - 1) 2^-24 sum_k |a_ik b_jk| (plus the bf16 rounding).
+ * Needs K % 64 == 0 (FP4Q_ERR_SHAPE), K <= 2^22 and M, N <= 2^24
+ * (FP4Q_ERR_UNSUPPORTED), code buffers 16-byte aligned and c aligned to its
+ * element (FP4Q_ERR_ALIGN).  M == 0 or N == 0 writes nothing; K == 0 writes
+ * zeros.
+ */
+int fp4_mm(const fp4q_cfg* cfg, const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+           const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* c, int64_t ldc, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

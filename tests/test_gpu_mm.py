@@ -1,0 +1,121 @@
+"""GPU parity of the FP4 GEMM consumer fp4_mm (C = A . B^T with MXFP4
+operands, "fp4-train" README, API: fp4_mm; Correctness: equal to the
+dequantise-then-multiply path) against the oracle's binary64 GEMM.
+
+Products are exact; the binary32 accumulation order is the kernel's, so the
+bar is |C - c| <= (K - 1) 2^-24 s with s = sum_k |a_ik b_jk| from the oracle
+(the standard bound for any summation order), and bit-exact where every
+partial sum is a binary32 number (operand scales within 2^-1 .. 2^1 and
+K <= 1024: all sums are multiples of 2^-4 below 2^18)."""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp4_amax_amd as fq
+from block_scaled_fp4_amax_amd import workloads as W
+from oracle import ref
+
+pytestmark = [pytest.mark.gpu, pytest.mark.filterwarnings("ignore::RuntimeWarning")]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fq.lib()
+
+
+def operand(rng, rows, K, lo, hi):
+    return (rng.integers(0, 256, (rows, K // 2), dtype=np.uint8), rng.integers(lo, hi, (rows, K // 32), dtype=np.uint8))
+
+
+def gpu_mm(a, b, dtype=torch.float32, ldc=None):
+    d = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()  # noqa: E731
+    M, N = a[0].shape[0], b[0].shape[0]
+    c = None
+    if ldc is not None:
+        c = torch.full((M, ldc), float("nan"), dtype=dtype, device="cuda")[:, :N]
+    out = fq.fp4_mm({"codes": d(a[0]), "scales": d(a[1])}, {"codes": d(b[0]), "scales": d(b[1])},
+                    out_dtype=dtype, c=c)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64)
+
+
+def within_bound(got, c, s, K, what, bf16=False):
+    bound = (K - 1) * 2.0 ** -24 * s + 2.0 ** -140
+    if bf16:
+        bound = bound + 2.0 ** -8 * np.abs(c)
+    bad = np.flatnonzero(~(np.abs(got - c) <= bound))
+    assert bad.size == 0, "%s: %d of %d outside the bound; first flat %d: gpu %r oracle %r bound %r" % (
+        what, bad.size, c.size, bad[0], got.ravel()[bad[0]], c.ravel()[bad[0]], bound.ravel()[bad[0]])
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 290, 1024), (256, 256, 64), (1, 515, 960), (37, 1, 128)])
+def test_exact_when_every_partial_sum_is_representable(M, N, K):
+    rng = np.random.default_rng(M * 7 + N + K)
+    a, b = operand(rng, M, K, 126, 129), operand(rng, N, K, 126, 129)
+    c, _ = ref.mx_mm(*a, *b, M, N, K)
+    got = gpu_mm(a, b)
+    np.testing.assert_array_equal(got, c)
+
+
+@pytest.mark.parametrize("M,N,K", [(333, 517, 2880), (512, 512, 512), (64, 768, 4096), (700, 90, 192)])
+def test_within_the_accumulation_bound(M, N, K):
+    rng = np.random.default_rng(M + N * 3 + K)
+    a, b = operand(rng, M, K, 100, 150), operand(rng, N, K, 100, 150)
+    c, s = ref.mx_mm(*a, *b, M, N, K)
+    within_bound(gpu_mm(a, b), c, s, K, "fp32 C")
+    within_bound(gpu_mm(a, b, torch.bfloat16), c, s, K, "bf16 C", bf16=True)
+
+
+def test_strided_output_and_untouched_padding():
+    rng = np.random.default_rng(9)
+    M, N, K = 130, 200, 256
+    a, b = operand(rng, M, K, 120, 135), operand(rng, N, K, 120, 135)
+    c, s = ref.mx_mm(*a, *b, M, N, K)
+    d = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()  # noqa: E731
+    full = torch.full((M, 232), -7.0, dtype=torch.float32, device="cuda")
+    fq.fp4_mm({"codes": d(a[0]), "scales": d(a[1])}, {"codes": d(b[0]), "scales": d(b[1])}, c=full[:, :N])
+    torch.cuda.synchronize()
+    f = full.cpu().numpy().astype(np.float64)
+    within_bound(f[:, :N], c, s, K, "strided C")
+    assert np.all(f[:, N:] == -7.0)
+
+
+def test_quantise_then_multiply_tensors():
+    """fp4_mm on bf16 / fp32 tensors quantises them (MXFP4) first: the result
+    is the product of the oracle's quantised operands."""
+    rng = np.random.default_rng(11)
+    M, N, K = 257, 300, 2880
+    xa = W.to_bf16(rng.standard_normal((M, K)).astype(np.float32))
+    xb = rng.standard_normal((N, K)).astype(np.float32) * np.float32(0.02)
+    ac, asc, _ = ref.mx_qdq(xa)
+    bc, bsc, _ = ref.mx_qdq(xb)
+    c, s = ref.mx_mm(ac, asc, bc, bsc, M, N, K)
+    ta = torch.from_numpy(xa.view(np.int16)).cuda().view(torch.bfloat16)
+    tb = torch.from_numpy(xb).cuda()
+    got = fq.fp4_mm(ta, tb, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    within_bound(got.cpu().numpy().astype(np.float64), c, s, K, "quantise-then-multiply")
+
+
+def test_k_zero_writes_zeros():
+    d = torch.full((5, 7), 3.0, dtype=torch.float32, device="cuda")
+    z = torch.empty((5, 0), dtype=torch.uint8, device="cuda")
+    e = torch.empty((7, 0), dtype=torch.uint8, device="cuda")
+    fq.fp4_mm({"codes": z, "scales": z}, {"codes": e, "scales": e}, c=d)
+    torch.cuda.synchronize()
+    assert bool((d == 0).all())
+
+
+def test_gemm_8192_sampled_rows():
+    """The 8192 x 8192 x 8192 GEMM at full size; 48 sampled rows of C (rows
+    are independent) against the oracle."""
+    rng = np.random.default_rng(12)
+    M = N = K = 8192
+    a, b = operand(rng, M, K, 115, 135), operand(rng, N, K, 115, 135)
+    got = gpu_mm(a, b)
+    rows = np.sort(rng.choice(M, 48, replace=False))
+    rows[0], rows[-1] = 0, M - 1
+    c, s = ref.mx_mm(a[0][rows], a[1][rows], *b, len(rows), N, K)
+    within_bound(got[rows], c, s, K, "8192^3 sampled rows")
