@@ -15,7 +15,8 @@ import os
 __all__ = [
     "Fp4Error", "Cfg", "Sizes", "make_cfg", "lib", "fp4q_abi_version", "fp4q_status_str", "fp4q_buffer_sizes",
     "fp4q_workspace_bytes", "fp4_quantize", "fp4_dequantize", "fp4_qdq", "fp4_cast_transpose",
-    "fp4_cast_transpose_grouped", "fp4_mx_project_fp8", "fp4_mm", "ErrorFeedback", "LIB_PATH",
+    "fp4_cast_transpose_grouped", "fp4_mx_project_fp8", "fp4_mm", "fp4_mx_scales_tiled",
+    "fp4q_mx_scales_tiled_bytes", "ErrorFeedback", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp4q.so")
@@ -107,7 +108,11 @@ def lib():
         L.fp4_cast_transpose_grouped.restype = ct.c_int
         L.fp4_cast_transpose_grouped.argtypes = [C, ct.c_int32, P, I64, P, I64, P, P, P, P, P, P, P, P, SZ, P]
         L.fp4_mm.restype = ct.c_int
-        L.fp4_mm.argtypes = [C, P, P, P, P, I64, I64, I64, P, I64, P]
+        L.fp4_mm.argtypes = [C, P, P, P, P, I64, I64, I64, ct.c_int32, P, I64, P]
+        L.fp4q_mx_scales_tiled_bytes.restype = SZ
+        L.fp4q_mx_scales_tiled_bytes.argtypes = [I64, I64]
+        L.fp4_mx_scales_tiled.restype = ct.c_int
+        L.fp4_mx_scales_tiled.argtypes = [P, I64, I64, P, P]
         L.fp4_mx_project_fp8.restype = ct.c_int
         L.fp4_mx_project_fp8.argtypes = [C, P, I64, I64, I64, P, P, P, P, P, P, P, P, P]
         if L.fp4q_abi_version() != ABI_VERSION:
@@ -358,28 +363,49 @@ def fp4_mx_project_fp8(x, cfg=None, *, y=True, mx8_row=True, mx8_col=True, blk=T
     return {k: v for k, v in out.items() if v is not None}
 
 
+def fp4q_mx_scales_tiled_bytes(rows, K):
+    return lib().fp4q_mx_scales_tiled_bytes(int(rows), int(K))
+
+
+def fp4_mx_scales_tiled(scales, K, stream=None, out=None):
+    """GEMM-ready layout of rowwise MXFP4 scales [rows, K/32] (uint8, flat)."""
+    torch = _torch()
+    rows = scales.shape[0]
+    if out is None:
+        out = torch.empty(fp4q_mx_scales_tiled_bytes(rows, K), dtype=torch.uint8, device=scales.device)
+    _check(lib().fp4_mx_scales_tiled(_ptr(scales), int(rows), int(K), _ptr(out), _stream(stream)),
+           "fp4_mx_scales_tiled")
+    return out
+
+
 def fp4_mm(a, b, cfg=None, *, out_dtype=None, c=None, stream=None):
     """C = a @ b^T on the FP4 matrix cores with MXFP4 operands.  a ([M, K]) and
-    b ([N, K]) are either dicts {"codes", "scales"} as fp4_quantize returns them
-    for MXFP4, or bf16 / float32 tensors, which are quantised first (two
-    library calls).  C is bf16 unless out_dtype (or a given c) is float32."""
+    b ([N, K]) are dicts {"codes", "scales"} as fp4_quantize returns them for
+    MXFP4 (rowwise scales), or {"codes", "scales_tiled"} with GEMM-ready
+    scales (fp4_mx_scales_tiled), or bf16 / float32 tensors, which are
+    quantised and their scales tiled first.  C is bf16 unless out_dtype (or a
+    given c) is float32."""
     torch = _torch()
     cfg = cfg if cfg is not None else make_cfg(format="mxfp4")
 
     def operand(x):
         if isinstance(x, dict):
-            return x["codes"], x["scales"]
+            if "scales_tiled" in x:
+                return x["codes"], x["scales_tiled"], 1
+            return x["codes"], x["scales"], 0
         q = fp4_quantize(x, cfg, stream=stream)
-        return q["codes"], q["scales"]
-    ac, asc = operand(a)
-    bc, bsc = operand(b)
+        return q["codes"], fp4_mx_scales_tiled(q["scales"], x.shape[1], stream=stream), 1
+    ac, asc, la = operand(a)
+    bc, bsc, lb = operand(b)
+    if la != lb:
+        raise ValueError("both operands need the same scale layout")
     M, N, K = ac.shape[0], bc.shape[0], ac.shape[1] * 2
     if bc.shape[1] * 2 != K:
         raise ValueError("operands disagree on K (%d vs %d)" % (K, bc.shape[1] * 2))
     if c is None:
         c = torch.empty((M, N), dtype=out_dtype if out_dtype is not None else torch.bfloat16, device=ac.device)
     ccfg = _with_dtypes(cfg, output_dtype=_dtype_name(c))
-    _check(lib().fp4_mm(ct.byref(ccfg), _ptr(ac), _ptr(asc), _ptr(bc), _ptr(bsc), M, N, K, _ptr(c),
+    _check(lib().fp4_mm(ct.byref(ccfg), _ptr(ac), _ptr(asc), _ptr(bc), _ptr(bsc), M, N, K, la, _ptr(c),
                         c.stride(0) if M > 1 else N, _stream(stream)), "fp4_mm")
     return c
 

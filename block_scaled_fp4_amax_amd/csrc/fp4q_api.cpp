@@ -462,19 +462,38 @@ int fp4_mx_project_fp8(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int
     return hip_status(launch_mx_fp8(a, (hipStream_t)stream));
 }
 
+size_t fp4q_mx_scales_tiled_bytes(int64_t rows, int64_t K)
+{
+    if (rows <= 0 || K <= 0) return 0;
+    return (size_t)((rows + 255) / 256) * (size_t)((K + 255) / 256) * 256 * 8;
+}
+
+int fp4_mx_scales_tiled(const uint8_t* scales, int64_t rows, int64_t K, uint8_t* out, void* stream)
+{
+    if (rows < 0 || K < 0 || K % 32) return FP4Q_ERR_SHAPE;
+    if (K > ((int64_t)1 << 22) || rows > ((int64_t)1 << 24)) return FP4Q_ERR_UNSUPPORTED;
+    if (rows == 0 || K == 0) return FP4Q_OK;
+    if (!scales || !out) return FP4Q_ERR_NULL;
+    if (misaligned(out, 8)) return FP4Q_ERR_ALIGN;
+    return hip_status(launch_mx_scales_tiled(scales, rows, K, out, (hipStream_t)stream));
+}
+
 int fp4_mm(const fp4q_cfg* cfg, const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
-           const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* c, int64_t ldc, void* stream)
+           const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, int32_t scale_layout, void* c, int64_t ldc,
+           void* stream)
 {
     Resolved r;
     int st = resolve(cfg, r);
     if (st) return st;
     if (r.fmt != FP4Q_MXFP4) return FP4Q_ERR_MODE;
+    if (scale_layout != 0 && scale_layout != 1) return FP4Q_ERR_MODE;
     if (M < 0 || N < 0 || K < 0 || K % 64) return FP4Q_ERR_SHAPE;
     if (M > 0 && N > 0 && ldc < N) return FP4Q_ERR_SHAPE;
     if (K > ((int64_t)1 << 22) || M > ((int64_t)1 << 24) || N > ((int64_t)1 << 24)) return FP4Q_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return FP4Q_OK;
     if (!c || (K > 0 && (!a_codes || !a_scales || !b_codes || !b_scales))) return FP4Q_ERR_NULL;
     if (misaligned(a_codes, 16) || misaligned(b_codes, 16) || misaligned(c, r.y_f32 ? 4 : 2)) return FP4Q_ERR_ALIGN;
+    if (scale_layout == 1 && (misaligned(a_scales, 8) || misaligned(b_scales, 8))) return FP4Q_ERR_ALIGN;
     GemmArgs g;
     g.a = a_codes;
     g.as = a_scales;
@@ -486,6 +505,10 @@ int fp4_mm(const fp4q_cfg* cfg, const uint8_t* a_codes, const uint8_t* a_scales,
     g.tiles_m = (int32_t)((M + 255) / 256);
     g.tiles_n = (int32_t)((N + 255) / 256);
     g.c_f32 = r.y_f32 ? 1 : 0;
+    // rowwise scales with whole 256-value K-tiles and 8-byte aligned bases take
+    // one 8-byte load per row and K-tile, otherwise one load per byte
+    if (scale_layout == 1) g.scale_layout = 2;
+    else g.scale_layout = (K % 256 == 0 && !misaligned(a_scales, 8) && !misaligned(b_scales, 8)) ? 1 : 0;
     g.c = c;
     g.ldc = ldc;
     return hip_status(launch_mx_gemm(g, (hipStream_t)stream));

@@ -52,6 +52,16 @@ struct Smem {
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
 
+// Scale layouts the kernel reads (SL):
+//   kScaleRowBytes   rowwise [rows, K/32] as the quantiser writes it, any K:
+//                    one byte load per scale;
+//   kScaleRow8       the same when K % 256 == 0 and the base is 8-byte aligned:
+//                    one 8-byte load per row and K-tile;
+//   kScaleTiled      the GEMM-ready layout [ceil(rows/256)][ceil(K/256)][256][8]
+//                    (zero-padded): a workgroup's 2 KiB of scales for one K-tile
+//                    are contiguous, one coalesced 8-byte load per lane.
+enum { kScaleRowBytes = 0, kScaleRow8 = 1, kScaleTiled = 2 };
+
 // Global loads of one K-tile: 8 code chunks of A and of B per lane (rows
 // q / 8, chunk q % 8 for q = i * 256 + lane: eight lanes read one row's 128
 // bytes), and the lane's row of 8 scale bytes of A and of B.
@@ -60,6 +70,7 @@ struct Stage {
     uint32_t as[8], bs[8];
 };
 
+template <int SL>
 __device__ __forceinline__ void load_tile(const GemmArgs& g, const rsrc_t& ra, const rsrc_t& rb, const rsrc_t& ras,
                                           const rsrc_t& rbs, int kt, int rows_a, int rows_b, Stage& st)
 {
@@ -76,16 +87,32 @@ __device__ __forceinline__ void load_tile(const GemmArgs& g, const rsrc_t& ra, c
         st.b[i] = buf_load16<0>(rb, (row < rows_b && kin) ? (uint32_t)(row * kb_end + kb) : kOff);
     }
     const int sb0 = kt * kScB, sb_end = g.K / 32;
+    if (SL == kScaleRowBytes) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const bool kin = sb0 + j < sb_end;
-        st.as[j] = __builtin_amdgcn_raw_buffer_load_b8(ras, (tid < rows_a && kin) ? (uint32_t)(tid * sb_end + sb0 + j)
-                                                                                   : kOff, 0, 0);
-        st.bs[j] = __builtin_amdgcn_raw_buffer_load_b8(rbs, (tid < rows_b && kin) ? (uint32_t)(tid * sb_end + sb0 + j)
-                                                                                   : kOff, 0, 0);
+        for (int j = 0; j < 8; ++j) {
+            const bool kin = sb0 + j < sb_end;
+            st.as[j] = __builtin_amdgcn_raw_buffer_load_b8(ras, (tid < rows_a && kin) ? (uint32_t)(tid * sb_end + sb0 + j)
+                                                                                       : kOff, 0, 0);
+            st.bs[j] = __builtin_amdgcn_raw_buffer_load_b8(rbs, (tid < rows_b && kin) ? (uint32_t)(tid * sb_end + sb0 + j)
+                                                                                       : kOff, 0, 0);
+        }
+    } else {
+        // 8 bytes of the lane's row: rowwise (K % 256 == 0, so no K-tile is
+        // partial) or the tiled block of this K-tile (padded: always whole)
+        const uint32_t oa = SL == kScaleRow8 ? (tid < rows_a ? (uint32_t)(tid * sb_end + sb0) : kOff)
+                                             : (uint32_t)((kt * kBM + tid) * 8);
+        const uint32_t ob = SL == kScaleRow8 ? (tid < rows_b ? (uint32_t)(tid * sb_end + sb0) : kOff)
+                                             : (uint32_t)((kt * kBM + tid) * 8);
+        const u32x2_t va = __builtin_amdgcn_raw_buffer_load_b64(ras, oa, 0, 0);
+        const u32x2_t vb = __builtin_amdgcn_raw_buffer_load_b64(rbs, ob, 0, 0);
+        st.as[0] = va[0];
+        st.as[1] = va[1];
+        st.bs[0] = vb[0];
+        st.bs[1] = vb[1];
     }
 }
 
+template <int SL>
 __device__ __forceinline__ void store_tile(Smem& sm, int buf, const Stage& st)
 {
     const int tid = (int)threadIdx.x;
@@ -97,10 +124,15 @@ __device__ __forceinline__ void store_tile(Smem& sm, int buf, const Stage& st)
         sm.code[buf][1][swz(row, c)] = st.b[i];
     }
     uint2 a, b;
-    a.x = st.as[0] | (st.as[1] << 8) | (st.as[2] << 16) | (st.as[3] << 24);
-    a.y = st.as[4] | (st.as[5] << 8) | (st.as[6] << 16) | (st.as[7] << 24);
-    b.x = st.bs[0] | (st.bs[1] << 8) | (st.bs[2] << 16) | (st.bs[3] << 24);
-    b.y = st.bs[4] | (st.bs[5] << 8) | (st.bs[6] << 16) | (st.bs[7] << 24);
+    if (SL == kScaleRowBytes) {
+        a.x = st.as[0] | (st.as[1] << 8) | (st.as[2] << 16) | (st.as[3] << 24);
+        a.y = st.as[4] | (st.as[5] << 8) | (st.as[6] << 16) | (st.as[7] << 24);
+        b.x = st.bs[0] | (st.bs[1] << 8) | (st.bs[2] << 16) | (st.bs[3] << 24);
+        b.y = st.bs[4] | (st.bs[5] << 8) | (st.bs[6] << 16) | (st.bs[7] << 24);
+    } else {
+        a = make_uint2(st.as[0], st.as[1]);
+        b = make_uint2(st.bs[0], st.bs[1]);
+    }
     sm.scale[buf][0][tid] = a;
     sm.scale[buf][1][tid] = b;
 }
@@ -112,7 +144,7 @@ __device__ __forceinline__ uint32_t scale_byte(uint2 s, int idx)
     return (w >> (8 * (idx & 3))) & 0xFFu;
 }
 
-template <bool CF32>
+template <bool CF32, int SL>
 __global__ __launch_bounds__(kThreads) void k_mx_gemm(GemmArgs g)
 {
     extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -137,8 +169,10 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemm(GemmArgs g)
     const int64_t lda = g.K / 2;
     const rsrc_t ra = make_rsrc(g.a + (int64_t)m0 * lda);
     const rsrc_t rb = make_rsrc(g.b + (int64_t)n0 * lda);
-    const rsrc_t ras = make_rsrc(g.as + (int64_t)m0 * (g.K / 32));
-    const rsrc_t rbs = make_rsrc(g.bs + (int64_t)n0 * (g.K / 32));
+    // tiled scales: the workgroup's row tile is block tm (tn) of ceil(K/256) K-tiles
+    const int kts = (g.K + kBK - 1) / kBK;
+    const rsrc_t ras = make_rsrc(SL == kScaleTiled ? g.as + (int64_t)tm * kts * kBM * 8 : g.as + (int64_t)m0 * (g.K / 32));
+    const rsrc_t rbs = make_rsrc(SL == kScaleTiled ? g.bs + (int64_t)tn * kts * kBM * 8 : g.bs + (int64_t)n0 * (g.K / 32));
 
     const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -152,14 +186,14 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemm(GemmArgs g)
 
     const int nk = (g.K + kBK - 1) / kBK;
     Stage st;
-    load_tile(g, ra, rb, ras, rbs, 0, rows_a, rows_b, st);
-    store_tile(sm, 0, st);
+    load_tile<SL>(g, ra, rb, ras, rbs, 0, rows_a, rows_b, st);
+    store_tile<SL>(sm, 0, st);
     __syncthreads();
 
     for (int kt = 0; kt < nk; ++kt) {
         const int cur = kt & 1;
         const bool more = kt + 1 < nk;
-        if (more) load_tile(g, ra, rb, ras, rbs, kt + 1, rows_a, rows_b, st);
+        if (more) load_tile<SL>(g, ra, rb, ras, rbs, kt + 1, rows_a, rows_b, st);
 
         uint2 sa[4], sb[4];
 #pragma unroll
@@ -188,7 +222,7 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemm(GemmArgs g)
             }
         }
         if (more) {
-            store_tile(sm, cur ^ 1, st);
+            store_tile<SL>(sm, cur ^ 1, st);
         }
         __syncthreads();
     }
@@ -212,13 +246,49 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemm(GemmArgs g)
         }
 }
 
+// GEMM-ready scales: out[(t * kts + kt) * 256 + r][j] = in[t * 256 + r][kt * 8 + j],
+// zero outside [rows, K/32].  One lane per 8 output bytes.
+__global__ __launch_bounds__(256) void k_mx_scales_tiled(const uint8_t* __restrict__ in, int32_t rows, int32_t nsb,
+                                                         int32_t kts, int64_t total, uint8_t* __restrict__ out)
+{
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;   // 8-byte group
+    if (q >= total) return;
+    const int r = (int)(q % kBM);
+    const int64_t tk = q / kBM;
+    const int kt = (int)(tk % kts);
+    const int t = (int)(tk / kts);
+    const int row = t * kBM + r;
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int col = kt * 8 + j;
+        const uint32_t v = (row < rows && col < nsb) ? (uint32_t)in[(int64_t)row * nsb + col] : 0u;
+        w[j >> 2] |= v << (8 * (j & 3));
+    }
+    *reinterpret_cast<uint2*>(out + q * 8) = make_uint2(w[0], w[1]);
+}
+
 }  // namespace
+
+hipError_t launch_mx_scales_tiled(const uint8_t* in, int64_t rows, int64_t K, uint8_t* out, hipStream_t s)
+{
+    const int32_t kts = (int32_t)((K + kBK - 1) / kBK);
+    const int64_t tiles = (rows + kBM - 1) / kBM;
+    const int64_t total = tiles * kts * kBM;
+    const int64_t grid = (total + 255) / 256;
+    hipLaunchKernelGGL(k_mx_scales_tiled, dim3((uint32_t)grid), dim3(256), 0, s, in, (int32_t)rows, (int32_t)(K / 32),
+                       kts, total, out);
+    return hipGetLastError();
+}
 
 hipError_t launch_mx_gemm(const GemmArgs& g, hipStream_t s)
 {
     const int T = g.tiles_m * g.tiles_n;
     const size_t lds = sizeof(Smem);   // 136 KiB of the CU's 160 KiB
-    auto fn = g.c_f32 ? k_mx_gemm<true> : k_mx_gemm<false>;
+    void (*fn)(GemmArgs) = nullptr;
+    if (g.scale_layout == kScaleTiled) fn = g.c_f32 ? k_mx_gemm<true, kScaleTiled> : k_mx_gemm<false, kScaleTiled>;
+    else if (g.scale_layout == kScaleRow8) fn = g.c_f32 ? k_mx_gemm<true, kScaleRow8> : k_mx_gemm<false, kScaleRow8>;
+    else fn = g.c_f32 ? k_mx_gemm<true, kScaleRowBytes> : k_mx_gemm<false, kScaleRowBytes>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)lds);
     if (e != hipSuccess) return e;

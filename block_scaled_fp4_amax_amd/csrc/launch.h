@@ -92,11 +92,17 @@ struct GemmArgs {
     int32_t M, N, K;
     int32_t tiles_m, tiles_n;  // 256 x 256 tiles of C
     int32_t c_f32;             // 1: C is FP32, 0: bf16
+    int32_t scale_layout;      // 0: rowwise, byte loads; 1: rowwise, 8-byte loads
+                               // (K % 256 == 0, 8-byte aligned); 2: GEMM-ready tiled
     void* c;                   // [M, ldc]
     int64_t ldc;
 };
 
 hipError_t launch_mx_gemm(const GemmArgs& g, hipStream_t s);
+
+// GEMM-ready scale layout [ceil(rows/256)][ceil(K/256)][256][8] from rowwise
+// UE8M0 scales [rows, K/32] (zero padding).
+hipError_t launch_mx_scales_tiled(const uint8_t* in, int64_t rows, int64_t K, uint8_t* out, hipStream_t s);
 
 // x: bf16 (x_f32 = false) or FP32 [rows, ld]; x_vec: x and every row start
 // 16-byte aligned.  y: bf16 or FP32 (y_f32) [rows, cols].

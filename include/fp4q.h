@@ -328,6 +328,9 @@ int fp4_mx_project_fp8(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int
  *              buffers as fp4_quantize writes them (device, read).
  *   b_codes    uint8 [N, K/2] and b_scales uint8 [N, K/32]: B's, B being
  *              [N, K] (both operands K-major).
+ *   scale_layout  0: a_scales / b_scales are the rowwise [rows, K/32] buffers
+ *              above; 1: both are in the GEMM-ready layout fp4_mx_scales_tiled
+ *              writes (the faster path for every K).
  *   c          [M, ldc] device (ldc >= N), written, not accumulated into; bf16
  *              is the RNE of the FP32 sum.
  * Every product of two E2M1 values and two power-of-two scales is exact; the
@@ -339,7 +342,26 @@ int fp4_mx_project_fp8(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int
  * zeros.
  */
 int fp4_mm(const fp4q_cfg* cfg, const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
-           const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* c, int64_t ldc, void* stream);
+           const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, int32_t scale_layout, void* c, int64_t ldc,
+           void* stream);
+
+/*
+ * fp4_mx_scales_tiled -- the GEMM-ready ("MFMA-ready") layout of MXFP4 scales
+ * ("Block-Scaled FP8 and FP4 Weight Quantization", section 2: the scale tensor
+ * indexed in the block order the matrix-core kernel consumes, materialised
+ * once and cached while the weight is unchanged).
+ *   scales     uint8 [rows, K/32] rowwise UE8M0 scales (device, read).
+ *   out        uint8 [ceil(rows/256)][ceil(K/256)][256][8] (device, written,
+ *              8-byte aligned): byte j of entry (t, kt, r) is scale
+ *              [256 t + r][8 kt + j], and 0 where that lies outside the input.
+ *              Each 2 KiB block holds the scales of one 256-row tile for one
+ *              256-value K-tile of fp4_mm, so a workgroup reads it with one
+ *              coalesced 8-byte load per lane.
+ * fp4q_mx_scales_tiled_bytes gives the size of out.  Needs K % 32 == 0
+ * (FP4Q_ERR_SHAPE), K <= 2^22, rows <= 2^24 (FP4Q_ERR_UNSUPPORTED).
+ */
+size_t fp4q_mx_scales_tiled_bytes(int64_t rows, int64_t K);
+int fp4_mx_scales_tiled(const uint8_t* scales, int64_t rows, int64_t K, uint8_t* out, void* stream);
 
 #ifdef __cplusplus
 }

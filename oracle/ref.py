@@ -379,3 +379,23 @@ def mx_mm(a_codes, a_scales, b_codes, b_scales, M, N, K):
     if rc != 0:
         raise ValueError("oracle rejected the shape (%d)" % rc)
     return c, s
+
+
+def mx_scales_tiled(scales, rows, K):
+    """GEMM-ready scale layout (a byte layout convention; parity unpinned):
+    entry [t][kt][r][j] = scales[256 t + r][8 kt + j], 0 outside the input;
+    returned flat (uint8)."""
+    scales = np.asarray(scales, dtype=np.uint8).reshape(rows, K // 32)
+    T, KT = -(-rows // 256), -(-K // 256)
+    out = np.zeros((T, KT, 256, 8), np.uint8)
+    for t in range(T):
+        for kt in range(KT):
+            for r in range(256):
+                row = 256 * t + r
+                if row >= rows:
+                    break
+                for j in range(8):
+                    col = 8 * kt + j
+                    if col < K // 32:
+                        out[t, kt, r, j] = scales[row, col]
+    return out.ravel()

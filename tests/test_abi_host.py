@@ -259,3 +259,33 @@ def test_buffer_sizes():
     assert fq.fp4q_buffer_sizes(C(two_level="tensorwise"), 256, 256)["workspace"] > 0
     with pytest.raises(fq.Fp4Error):
         fq.fp4q_buffer_sizes(C(), 16, 40)
+
+
+def test_mm_rules():
+    """fp4_mm (MXFP4 operands, K % 64 == 0) and the GEMM-ready scale layout."""
+    C = fq.make_cfg
+    L = fq.lib()
+    mx = C(format="mxfp4")
+
+    def mm(cfg, M=64, N=64, K=128, layout=0, a=FAKE, asc=FAKE, b=FAKE, bsc=FAKE, c=FAKE, ldc=None):
+        return _validated(L.fp4_mm(ct.byref(cfg), a, asc, b, bsc, M, N, K, layout, c, N if ldc is None else ldc, None))
+    assert mm(C()) == fq.ERR_MODE                                       # NVFP4 operands: not this consumer
+    assert mm(mx, layout=2) == fq.ERR_MODE
+    assert mm(mx, K=96) == fq.ERR_SHAPE                                 # K % 64
+    assert mm(mx, M=-1) == fq.ERR_SHAPE
+    assert mm(mx, ldc=32) == fq.ERR_SHAPE                               # ldc < N
+    assert mm(mx, K=(1 << 22) + 64) == fq.ERR_UNSUPPORTED
+    assert mm(mx, a=None) == fq.ERR_NULL
+    assert mm(mx, c=None) == fq.ERR_NULL
+    assert mm(mx, a=FAKE_MIS) == fq.ERR_ALIGN
+    assert mm(mx, layout=1, asc=FAKE + 4) == fq.ERR_ALIGN
+    assert mm(C(format="mxfp4", output_dtype="fp32"), c=FAKE + 2) == fq.ERR_ALIGN
+    assert mm(C(format="mxfp4", output_dtype="fp16")) == fq.ERR_DTYPE
+    assert mm(mx, M=0, a=None, asc=None, b=None, bsc=None, c=None) == fq.OK
+    # the GEMM-ready scale layout: 2 KiB per 256-row tile and 256-value K-tile
+    assert fq.fp4q_mx_scales_tiled_bytes(300, 2880) == 2 * 12 * 2048
+    assert fq.fp4q_mx_scales_tiled_bytes(0, 64) == 0
+    assert _validated(L.fp4_mx_scales_tiled(FAKE, 64, 48, FAKE, None)) == fq.ERR_SHAPE
+    assert _validated(L.fp4_mx_scales_tiled(FAKE, 64, 64, FAKE + 4, None)) == fq.ERR_ALIGN
+    assert _validated(L.fp4_mx_scales_tiled(None, 64, 64, FAKE, None)) == fq.ERR_NULL
+    assert _validated(L.fp4_mx_scales_tiled(None, 0, 64, None, None)) == fq.OK

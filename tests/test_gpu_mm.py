@@ -29,14 +29,25 @@ def operand(rng, rows, K, lo, hi):
     return (rng.integers(0, 256, (rows, K // 2), dtype=np.uint8), rng.integers(lo, hi, (rows, K // 32), dtype=np.uint8))
 
 
-def gpu_mm(a, b, dtype=torch.float32, ldc=None):
-    d = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()  # noqa: E731
-    M, N = a[0].shape[0], b[0].shape[0]
-    c = None
-    if ldc is not None:
-        c = torch.full((M, ldc), float("nan"), dtype=dtype, device="cuda")[:, :N]
-    out = fq.fp4_mm({"codes": d(a[0]), "scales": d(a[1])}, {"codes": d(b[0]), "scales": d(b[1])},
-                    out_dtype=dtype, c=c)
+def dev_operand(x, layout, check_tiled=False):
+    """{"codes", "scales"} (rowwise scales) or {"codes", "scales_tiled"} (the
+    GEMM-ready layout, converted on the device and, when asked, compared with
+    the oracle's definition of the layout)."""
+    d = lambda v: torch.from_numpy(np.ascontiguousarray(v)).cuda()  # noqa: E731
+    codes, scales = x
+    if layout == "row":
+        return {"codes": d(codes), "scales": d(scales)}
+    K = codes.shape[1] * 2
+    tiled = fq.fp4_mx_scales_tiled(d(scales), K)
+    if check_tiled:
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(tiled.cpu().numpy(), ref.mx_scales_tiled(scales, scales.shape[0], K))
+    return {"codes": d(codes), "scales_tiled": tiled}
+
+
+def gpu_mm(a, b, dtype=torch.float32, layout="row"):
+    small = a[0].size + b[0].size < (1 << 22)
+    out = fq.fp4_mm(dev_operand(a, layout, small), dev_operand(b, layout, small), out_dtype=dtype)
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64)
 
@@ -50,22 +61,24 @@ def within_bound(got, c, s, K, what, bf16=False):
         what, bad.size, c.size, bad[0], got.ravel()[bad[0]], c.ravel()[bad[0]], bound.ravel()[bad[0]])
 
 
+@pytest.mark.parametrize("layout", ["row", "tiled"])
 @pytest.mark.parametrize("M,N,K", [(300, 290, 1024), (256, 256, 64), (1, 515, 960), (37, 1, 128)])
-def test_exact_when_every_partial_sum_is_representable(M, N, K):
+def test_exact_when_every_partial_sum_is_representable(M, N, K, layout):
     rng = np.random.default_rng(M * 7 + N + K)
     a, b = operand(rng, M, K, 126, 129), operand(rng, N, K, 126, 129)
     c, _ = ref.mx_mm(*a, *b, M, N, K)
-    got = gpu_mm(a, b)
+    got = gpu_mm(a, b, layout=layout)
     np.testing.assert_array_equal(got, c)
 
 
+@pytest.mark.parametrize("layout", ["row", "tiled"])
 @pytest.mark.parametrize("M,N,K", [(333, 517, 2880), (512, 512, 512), (64, 768, 4096), (700, 90, 192)])
-def test_within_the_accumulation_bound(M, N, K):
+def test_within_the_accumulation_bound(M, N, K, layout):
     rng = np.random.default_rng(M + N * 3 + K)
     a, b = operand(rng, M, K, 100, 150), operand(rng, N, K, 100, 150)
     c, s = ref.mx_mm(*a, *b, M, N, K)
-    within_bound(gpu_mm(a, b), c, s, K, "fp32 C")
-    within_bound(gpu_mm(a, b, torch.bfloat16), c, s, K, "bf16 C", bf16=True)
+    within_bound(gpu_mm(a, b, layout=layout), c, s, K, "fp32 C")
+    within_bound(gpu_mm(a, b, torch.bfloat16, layout=layout), c, s, K, "bf16 C", bf16=True)
 
 
 def test_strided_output_and_untouched_padding():
@@ -108,13 +121,14 @@ def test_k_zero_writes_zeros():
     assert bool((d == 0).all())
 
 
-def test_gemm_8192_sampled_rows():
+@pytest.mark.parametrize("layout", ["row", "tiled"])
+def test_gemm_8192_sampled_rows(layout):
     """The 8192 x 8192 x 8192 GEMM at full size; 48 sampled rows of C (rows
     are independent) against the oracle."""
     rng = np.random.default_rng(12)
     M = N = K = 8192
     a, b = operand(rng, M, K, 115, 135), operand(rng, N, K, 115, 135)
-    got = gpu_mm(a, b)
+    got = gpu_mm(a, b, layout=layout)
     rows = np.sort(rng.choice(M, 48, replace=False))
     rows[0], rows[-1] = 0, M - 1
     c, s = ref.mx_mm(a[0][rows], a[1][rows], *b, len(rows), N, K)
