@@ -64,21 +64,24 @@ enum { kScaleRowBytes = 0, kScaleRow8 = 1, kScaleTiled = 2 };
 
 // Global loads of one K-tile: 8 code chunks of A and of B per lane (rows
 // q / 8, chunk q % 8 for q = i * 256 + lane: eight lanes read one row's 128
-// bytes), and the lane's row of 8 scale bytes of A and of B.
+// bytes), and the lane's row of 8 scale bytes of A and of B.  The main loop
+// moves a tile in quarters (chunks 2 Q and 2 Q + 1 of each operand; the scales
+// with the last quarter) so that loads and LDS writes interleave with the
+// matrix instructions.  A K-tile at or beyond the end of K loads zeros.
 struct Stage {
     uint4 a[8], b[8];
     uint32_t as[8], bs[8];
 };
 
 template <int SL>
-__device__ __forceinline__ void load_tile(const GemmArgs& g, const rsrc_t& ra, const rsrc_t& rb, const rsrc_t& ras,
-                                          const rsrc_t& rbs, int kt, int rows_a, int rows_b, Stage& st)
+__device__ __forceinline__ void load_quarter(const GemmArgs& g, const rsrc_t& ra, const rsrc_t& rb, const rsrc_t& ras,
+                                             const rsrc_t& rbs, int kt, int rows_a, int rows_b, int Q, Stage& st)
 {
     const int tid = (int)threadIdx.x;
     const int kb0 = kt * kRowB;                // byte offset of the K-tile in a code row
     const int kb_end = g.K / 2;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 2 * Q; i < 2 * Q + 2; ++i) {
         const int q = i * kThreads + tid;
         const int row = q >> 3, c = q & 7;
         const int kb = kb0 + 16 * c;
@@ -86,6 +89,7 @@ __device__ __forceinline__ void load_tile(const GemmArgs& g, const rsrc_t& ra, c
         st.a[i] = buf_load16<0>(ra, (row < rows_a && kin) ? (uint32_t)(row * kb_end + kb) : kOff);
         st.b[i] = buf_load16<0>(rb, (row < rows_b && kin) ? (uint32_t)(row * kb_end + kb) : kOff);
     }
+    if (Q != 3) return;
     const int sb0 = kt * kScB, sb_end = g.K / 32;
     if (SL == kScaleRowBytes) {
 #pragma unroll
@@ -97,12 +101,13 @@ __device__ __forceinline__ void load_tile(const GemmArgs& g, const rsrc_t& ra, c
                                                                                        : kOff, 0, 0);
         }
     } else {
-        // 8 bytes of the lane's row: rowwise (K % 256 == 0, so no K-tile is
-        // partial) or the tiled block of this K-tile (padded: always whole)
-        const uint32_t oa = SL == kScaleRow8 ? (tid < rows_a ? (uint32_t)(tid * sb_end + sb0) : kOff)
-                                             : (uint32_t)((kt * kBM + tid) * 8);
-        const uint32_t ob = SL == kScaleRow8 ? (tid < rows_b ? (uint32_t)(tid * sb_end + sb0) : kOff)
-                                             : (uint32_t)((kt * kBM + tid) * 8);
+        // 8 bytes of the lane's row: rowwise (K % 256 == 0, so a K-tile is
+        // whole or beyond K) or the tiled block of this K-tile (padded)
+        const bool kin = sb0 < sb_end;
+        const uint32_t oa = !kin ? kOff : SL == kScaleRow8 ? (tid < rows_a ? (uint32_t)(tid * sb_end + sb0) : kOff)
+                                                            : (uint32_t)((kt * kBM + tid) * 8);
+        const uint32_t ob = !kin ? kOff : SL == kScaleRow8 ? (tid < rows_b ? (uint32_t)(tid * sb_end + sb0) : kOff)
+                                                            : (uint32_t)((kt * kBM + tid) * 8);
         const u32x2_t va = __builtin_amdgcn_raw_buffer_load_b64(ras, oa, 0, 0);
         const u32x2_t vb = __builtin_amdgcn_raw_buffer_load_b64(rbs, ob, 0, 0);
         st.as[0] = va[0];
@@ -113,16 +118,17 @@ __device__ __forceinline__ void load_tile(const GemmArgs& g, const rsrc_t& ra, c
 }
 
 template <int SL>
-__device__ __forceinline__ void store_tile(Smem& sm, int buf, const Stage& st)
+__device__ __forceinline__ void store_quarter(Smem& sm, int buf, const Stage& st, int Q)
 {
     const int tid = (int)threadIdx.x;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 2 * Q; i < 2 * Q + 2; ++i) {
         const int q = i * kThreads + tid;
         const int row = q >> 3, c = q & 7;
         sm.code[buf][0][swz(row, c)] = st.a[i];
         sm.code[buf][1][swz(row, c)] = st.b[i];
     }
+    if (Q != 3) return;
     uint2 a, b;
     if (SL == kScaleRowBytes) {
         a.x = st.as[0] | (st.as[1] << 8) | (st.as[2] << 16) | (st.as[3] << 24);
@@ -186,43 +192,59 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemm(GemmArgs g)
 
     const int nk = (g.K + kBK - 1) / kBK;
     Stage st;
-    load_tile<SL>(g, ra, rb, ras, rbs, 0, rows_a, rows_b, st);
-    store_tile<SL>(sm, 0, st);
+    // prologue: tile 0 into LDS buffer 0, tile 1 in flight into the registers
+#pragma unroll
+    for (int Q = 0; Q < 4; ++Q) load_quarter<SL>(g, ra, rb, ras, rbs, 0, rows_a, rows_b, Q, st);
+#pragma unroll
+    for (int Q = 0; Q < 4; ++Q) store_quarter<SL>(sm, 0, st, Q);
+#pragma unroll
+    for (int Q = 0; Q < 4; ++Q) load_quarter<SL>(g, ra, rb, ras, rbs, 1, rows_a, rows_b, Q, st);
     __syncthreads();
 
+    // iteration kt: LDS buffer kt % 2 holds tile kt, the registers receive
+    // tile kt + 1; during the 64 instructions of each wave, tile kt + 1 goes
+    // to the other buffer and tile kt + 2 is requested, a quarter per K-step
     for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        const bool more = kt + 1 < nk;
-        if (more) load_tile<SL>(g, ra, rb, ras, rbs, kt + 1, rows_a, rows_b, st);
-
+        const int cur = kt & 1, nxt = cur ^ 1;
         uint2 sa[4], sb[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             sa[i] = sm.scale[cur][0][wm * 128 + i * 32 + lr];
             sb[i] = sm.scale[cur][1][wn * 128 + i * 32 + lr];
         }
-#pragma unroll
-        for (int ks = 0; ks < kBK / 64; ++ks) {
+        v8i_t av[2][4], bv[2][4];
+        auto read_ops = [&](int ks, int p) __attribute__((always_inline)) {
             const int chunk = 2 * ks + lh;
-            v8i_t av[4], bv[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const uint4 x = sm.code[cur][0][swz(wm * 128 + i * 32 + lr, chunk)];
                 const uint4 y = sm.code[cur][1][swz(wn * 128 + i * 32 + lr, chunk)];
-                av[i] = v8i_t{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
-                bv[i] = v8i_t{(int)y.x, (int)y.y, (int)y.z, (int)y.w, 0, 0, 0, 0};
+                av[p][i] = v8i_t{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
+                bv[p][i] = v8i_t{(int)y.x, (int)y.y, (int)y.z, (int)y.w, 0, 0, 0, 0};
             }
+        };
+        read_ops(0, 0);
+#pragma unroll
+        for (int ks = 0; ks < kBK / 64; ++ks) {
+            const int p = ks & 1;
+            // the next K-step's operand reads go out a whole K-step (16
+            // instructions) before their use; the fences keep the scheduler
+            // from moving them next to their consumers
+            if (ks + 1 < kBK / 64) read_ops(ks + 1, p ^ 1);
+            __builtin_amdgcn_sched_barrier(0);
+            const int chunk = 2 * ks + lh;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int sai = (int)scale_byte(sa[i], chunk);
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        av[i], bv[j], acc[i][j], 4, 4, 0, sai, 0, (int)scale_byte(sb[j], chunk));
+                        av[p][i], bv[p][j], acc[i][j], 4, 4, 0, sai, 0, (int)scale_byte(sb[j], chunk));
             }
-        }
-        if (more) {
-            store_tile<SL>(sm, cur ^ 1, st);
+            __builtin_amdgcn_sched_barrier(0);
+            store_quarter<SL>(sm, nxt, st, ks);
+            load_quarter<SL>(g, ra, rb, ras, rbs, kt + 2, rows_a, rows_b, ks, st);
+            __builtin_amdgcn_sched_barrier(0);
         }
         __syncthreads();
     }
