@@ -23,7 +23,7 @@
 // through registers, double-buffered: the next tile's global loads are issued
 // before the current tile's 64 instructions per wave, and written to the other
 // LDS buffer after them (one barrier per K-tile).  In LDS a row's eight 16-byte
-// chunks are XOR-swizzled by the row (chunk ^ (row & 7)), so the 32 rows a
+// chunks are XOR-swizzled by the row (chunk ^ ((row / 2) & 7)), so the rows a
 // wave reads for one operand spread over all banks.  Rows beyond M or N and
 // K-values beyond K load as zero codes with scale byte 0 (2^-127), adding
 // exact zeros.  Workgroup ids are remapped so each XCD (ids dealt round-robin)
@@ -50,7 +50,9 @@ struct Smem {
     uint2 scale[2][2][kBM];                    // [buffer][A, B][row]       8 KiB
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
+// 16-byte chunk c of a row lives at chunk c ^ ((row / 2) & 7): the 16 rows one
+// quarter-wave reads (two rows per 256-byte bank window) land on distinct banks.
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ ((row >> 1) & 7)); }
 
 // Scale layouts the kernel reads (SL):
 //   kScaleRowBytes   rowwise [rows, K/32] as the quantiser writes it, any K:
