@@ -34,6 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+FP4_MFMA_PEAK_TFLOPS = 10100.0   # MI355X dense FP4 / FP6 matrix peak
 METRIC = "quantize GB/s (HBM bytes read+written) and fraction of MI355X HBM peak"
 
 
@@ -47,7 +48,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU oracle time for the baseline")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 256 MiB device copy (counter calibration) and exit")
-    ap.add_argument("--only", default=None, help="time a single workload (nv_tensorwise_qdq_256, nv_2d_cast_transpose_4096, mx_fake_quant_8192, amd_1d_sr_cast_transpose_16384x2880, nv_grouped_sr_ef_32x2880, nv_2d_inner16_cast_transpose_4096, mx_project_fp8_8192, mx_fake_quant_fp32_8192) and exit")
+    ap.add_argument("--only", default=None, help="time a single workload (nv_tensorwise_qdq_256, nv_2d_cast_transpose_4096, mx_fake_quant_8192, amd_1d_sr_cast_transpose_16384x2880, nv_grouped_sr_ef_32x2880, nv_2d_inner16_cast_transpose_4096, mx_project_fp8_8192, mx_fake_quant_fp32_8192, mx_gemm_8192) and exit")
     ap.add_argument("--eager", action="store_true", help="launch every step from the host (no graph replay)")
     ap.add_argument("--pmc-summary", nargs=5, metavar=("KEY", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     default=None,
@@ -62,7 +63,8 @@ KERNEL_NAME_PREFIX = {"nv_tensorwise_qdq_256": "fp4q::(anonymous namespace)::k_n
                       "nv_grouped_sr_ef_32x2880": "fp4q::(anonymous namespace)::k_tile",
                       "nv_2d_inner16_cast_transpose_4096": "fp4q::(anonymous namespace)::k_tile",
                       "mx_project_fp8_8192": "fp4q::(anonymous namespace)::k_mx_fp8",
-                      "mx_fake_quant_fp32_8192": "fp4q::(anonymous namespace)::k_mx_qdq_f32"}
+                      "mx_fake_quant_fp32_8192": "fp4q::(anonymous namespace)::k_mx_qdq_f32",
+                      "mx_gemm_8192": "fp4q::(anonymous namespace)::k_mx_gemm"}
 COPY_PROBE_BYTES = 256 << 20
 
 
@@ -145,9 +147,11 @@ def measured_traffic(kernel_key):
 class Timed:
     """A workload: rotating buffer sets and a launch closure per set."""
 
-    def __init__(self, name, desc, bytes_per_step, sets, launch, kernel, elements=0):
+    def __init__(self, name, desc, bytes_per_step, sets, launch, kernel, elements=0, flops=0, graph=True):
         self.name, self.desc, self.bytes, self.sets, self.launch, self.kernel = name, desc, bytes_per_step, sets, launch, kernel
         self.elements = elements
+        self.flops = flops          # MFMA-bound workloads: algorithmic flops per launch
+        self.graph = graph
 
 
 def run_timed(torch, w, steps, warmup, graph=True):
@@ -289,6 +293,35 @@ def make_mx_fake_quant_fp32(torch, fq, W):
             raise fq.Fp4Error(st, "fp4_qdq")
     return Timed("mx_fake_quant_fp32_8192", "MXFP4 1x32 fake-quant 8192x8192 fp32 -> fp32", alg, sets, launch,
                  "k_mx_qdq_f32<true, true, false>", R * C)
+
+
+def make_mx_gemm(torch, fq, W):
+    """C = A . B^T, 8192^3, MXFP4 operands (quantised from seeded bf16 with the
+    library's MXFP4 quantiser), GEMM-ready tiled scales, bf16 C."""
+    import numpy as np
+    M = N = K = 8192
+    cfg = fq.make_cfg(format="mxfp4")
+    sets = []
+    for k in range(2):
+        rng = np.random.default_rng(60 + k)
+        xa = torch.from_numpy(W.to_bf16(rng.standard_normal((M, K), dtype=np.float32)).view("int16")).cuda()
+        xb = torch.from_numpy(W.to_bf16(rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02)).view("int16")).cuda()
+        qa, qb = fq.fp4_quantize(xa, cfg), fq.fp4_quantize(xb, cfg)
+        del xa, xb
+        sets.append(dict(a=qa["codes"], at=fq.fp4_mx_scales_tiled(qa["scales"], K), b=qb["codes"],
+                         bt=fq.fp4_mx_scales_tiled(qb["scales"], K), c=torch.empty((M, N), dtype=torch.bfloat16,
+                                                                                     device="cuda")))
+    torch.cuda.synchronize()
+    L = fq.lib()
+
+    def launch(s):
+        st = L.fp4_mm(ct.byref(cfg), s["a"].data_ptr(), s["at"].data_ptr(), s["b"].data_ptr(), s["bt"].data_ptr(),
+                      M, N, K, 1, s["c"].data_ptr(), N, torch.cuda.current_stream().cuda_stream)
+        if st:
+            raise fq.Fp4Error(st, "fp4_mm")
+    alg = M * K // 2 * 2 + 2 * 8 * ((M + 255) // 256) * ((K + 255) // 256) * 256 + M * N * 2
+    return Timed("mx_gemm_8192", "MXFP4 GEMM C = A.B^T 8192x8192x8192, tiled scales, bf16 C", alg, sets, launch,
+                 "k_mx_gemm<false, 2>", M * N, flops=2 * M * N * K, graph=False)
 
 
 def make_cast_transpose_1d_sr(torch, fq, W):
@@ -455,12 +488,17 @@ def main():
               "nv_grouped_sr_ef_32x2880": make_grouped_sr_ef,
               "nv_2d_inner16_cast_transpose_4096": make_cast_transpose_2d_inner16,
               "mx_project_fp8_8192": make_mx_project_fp8,
-              "mx_fake_quant_fp32_8192": make_mx_fake_quant_fp32}[args.only]
+              "mx_fake_quant_fp32_8192": make_mx_fake_quant_fp32,
+              "mx_gemm_8192": make_mx_gemm}[args.only]
         w = mk(torch, fq, W)
-        ms = run_timed(torch, w, args.steps, args.warmup, graph=not args.eager)
+        ms = run_timed(torch, w, args.steps, args.warmup, graph=w.graph and not args.eager)
         per = ms / args.steps
-        print(json.dumps({"workload": w.name, "desc": w.desc, "ms_per_launch": per,
-                          "GB/s": w.bytes / (per * 1e-3) / 1e9, "frac": w.bytes / (per * 1e-3) / 1e9 / HBM_PEAK_GBS}))
+        rec = {"workload": w.name, "desc": w.desc, "ms_per_launch": per,
+               "GB/s": w.bytes / (per * 1e-3) / 1e9, "frac": w.bytes / (per * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        if w.flops:
+            tf = w.flops / (per * 1e-3) / 1e12
+            rec.update({"TFLOP/s": tf, "frac": tf / FP4_MFMA_PEAK_TFLOPS, "bound": "mfma"})
+        print(json.dumps(rec))
         return
 
     w = make_cast_transpose_2d(torch, fq, W)
@@ -491,15 +529,19 @@ def main():
         extra = {}
         for mk, steps in ((make_mx_fake_quant, 400), (make_cast_transpose_1d_sr, 400), (make_grouped_sr_ef, 20),
                           (make_tensorwise_qdq, 400), (make_cast_transpose_2d_inner16, 2000),
-                          (make_mx_project_fp8, 200), (make_mx_fake_quant_fp32, 200)):
+                          (make_mx_project_fp8, 200), (make_mx_fake_quant_fp32, 200), (make_mx_gemm, 50)):
             e = mk(torch, fq, W)
             print("# extra %s" % e.name, file=sys.stderr, flush=True)
-            ems = run_timed(torch, e, steps, min(20, steps))
+            ems = run_timed(torch, e, steps, min(20, steps), graph=e.graph)
             per = ems / steps
             eg = e.bytes / (per * 1e-3) / 1e9
             extra[e.name] = {"desc": e.desc, "us_per_step": round(per * 1e3, 3), "GB/s": round(eg, 2),
                              "frac": round(eg / HBM_PEAK_GBS, 4), "algorithmic_bytes": e.bytes, "kernel": e.kernel,
                              "elements_per_s": round(e.elements / (per * 1e-3), 1)}
+            if e.flops:
+                tf = e.flops / (per * 1e-3) / 1e12
+                extra[e.name].update({"bound": "mfma", "TFLOP/s": round(tf, 1), "peak_TFLOP/s": FP4_MFMA_PEAK_TFLOPS,
+                                      "frac": round(tf / FP4_MFMA_PEAK_TFLOPS, 4), "flops": e.flops})
             del e
             torch.cuda.empty_cache()
         line["extra"] = extra
