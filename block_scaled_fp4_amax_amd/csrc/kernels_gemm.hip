@@ -17,11 +17,13 @@
 // C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32].  So lane l's operand is one MX
 // block: 16 contiguous bytes of a row, with that block's scale byte.
 //
-// Work decomposition: one workgroup of 256 lanes (4 waves, 2 x 2) per 256 x 256
-// tile of C; each wave owns 128 x 128 (4 x 4 instructions, 256 accumulators).
+// Work decomposition: one workgroup of 512 lanes (8 waves, 2 x 4, two per
+// SIMD so that one wave's loads and LDS traffic overlap the other's matrix
+// instructions) per 256 x 256 tile of C; each wave owns 128 x 64 (4 x 2
+// instructions, 128 accumulators).
 // K advances in tiles of 256 values (128 bytes of codes per row) staged in LDS
 // through registers, double-buffered: the next tile's global loads are issued
-// before the current tile's 64 instructions per wave, and written to the other
+// before the current tile's 32 instructions per wave, and written to the other
 // LDS buffer after them (one barrier per K-tile).  In LDS a row's eight 16-byte
 // chunks are XOR-swizzled by the row (chunk ^ ((row / 2) & 7)), so the rows a
 // wave reads for one operand spread over all banks.  Rows beyond M or N and
@@ -38,7 +40,9 @@ namespace {
 typedef int v8i_t __attribute__((ext_vector_type(8)));
 typedef float v16f_t __attribute__((ext_vector_type(16)));
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;                  // 8 waves, two per SIMD
+constexpr int kWaveM = 2, kWaveN = 4;          // wave grid over the tile
+constexpr int kTM = 4, kTN = 2;                // 32 x 32 blocks per wave: 128 x 64
 constexpr int kBM = 256;                       // tile rows (A) = tile columns (B)
 constexpr int kBK = 256;                       // K-values per K-tile
 constexpr int kRowB = kBK / 2;                 // code bytes per row and K-tile (128)
@@ -64,17 +68,18 @@ __device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk
 //                    are contiguous, one coalesced 8-byte load per lane.
 enum { kScaleRowBytes = 0, kScaleRow8 = 1, kScaleTiled = 2 };
 
-// Global loads of one K-tile: 8 code chunks of A and of B per lane (rows
-// q / 8, chunk q % 8 for q = i * 256 + lane: eight lanes read one row's 128
-// bytes), and the lane's row of 8 scale bytes of A and of B.  The main loop
-// moves a tile in quarters (chunks 2 Q and 2 Q + 1 of each operand; the scales
-// with the last quarter) so that loads and LDS writes interleave with the
-// matrix instructions.  A K-tile at or beyond the end of K loads zeros.
+// The main loop moves a K-tile in quarters so that its global loads and LDS
+// writes interleave with the matrix instructions.  A K-tile at or beyond the
+// end of K loads zeros.
 struct Stage {
-    uint4 a[8], b[8];
-    uint32_t as[8], bs[8];
+    uint4 a[4], b[4];
+    uint32_t sc[8];                            // scale bytes (or two words) of the lane's scale row
 };
 
+// Quarter Q of a K-tile: code chunk Q of A and of B per lane (rows q / 8,
+// chunk q % 8 for q = Q * 512 + lane: eight lanes read one row's 128 bytes);
+// with the last quarter, lanes 0..255 fetch the scale row of A row `lane`,
+// lanes 256..511 that of B row `lane - 256`.
 template <int SL>
 __device__ __forceinline__ void load_quarter(const GemmArgs& g, const rsrc_t& ra, const rsrc_t& rb, const rsrc_t& ras,
                                              const rsrc_t& rbs, int kt, int rows_a, int rows_b, int Q, Stage& st)
@@ -82,40 +87,36 @@ __device__ __forceinline__ void load_quarter(const GemmArgs& g, const rsrc_t& ra
     const int tid = (int)threadIdx.x;
     const int kb0 = kt * kRowB;                // byte offset of the K-tile in a code row
     const int kb_end = g.K / 2;
-#pragma unroll
-    for (int i = 2 * Q; i < 2 * Q + 2; ++i) {
-        const int q = i * kThreads + tid;
+    {
+        const int q = Q * kThreads + tid;
         const int row = q >> 3, c = q & 7;
         const int kb = kb0 + 16 * c;
         const bool kin = kb < kb_end;
-        st.a[i] = buf_load16<0>(ra, (row < rows_a && kin) ? (uint32_t)(row * kb_end + kb) : kOff);
-        st.b[i] = buf_load16<0>(rb, (row < rows_b && kin) ? (uint32_t)(row * kb_end + kb) : kOff);
+        st.a[Q] = buf_load16<0>(ra, (row < rows_a && kin) ? (uint32_t)(row * kb_end + kb) : kOff);
+        st.b[Q] = buf_load16<0>(rb, (row < rows_b && kin) ? (uint32_t)(row * kb_end + kb) : kOff);
     }
     if (Q != 3) return;
     const int sb0 = kt * kScB, sb_end = g.K / 32;
+    const bool is_b = tid >= kBM;
+    const int srow = is_b ? tid - kBM : tid;
+    const int srows = is_b ? rows_b : rows_a;
+    const rsrc_t rs = is_b ? rbs : ras;
     if (SL == kScaleRowBytes) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const bool kin = sb0 + j < sb_end;
-            st.as[j] = __builtin_amdgcn_raw_buffer_load_b8(ras, (tid < rows_a && kin) ? (uint32_t)(tid * sb_end + sb0 + j)
-                                                                                       : kOff, 0, 0);
-            st.bs[j] = __builtin_amdgcn_raw_buffer_load_b8(rbs, (tid < rows_b && kin) ? (uint32_t)(tid * sb_end + sb0 + j)
-                                                                                       : kOff, 0, 0);
+            st.sc[j] = __builtin_amdgcn_raw_buffer_load_b8(rs, (srow < srows && kin) ? (uint32_t)(srow * sb_end + sb0 + j)
+                                                                                      : kOff, 0, 0);
         }
     } else {
         // 8 bytes of the lane's row: rowwise (K % 256 == 0, so a K-tile is
         // whole or beyond K) or the tiled block of this K-tile (padded)
         const bool kin = sb0 < sb_end;
-        const uint32_t oa = !kin ? kOff : SL == kScaleRow8 ? (tid < rows_a ? (uint32_t)(tid * sb_end + sb0) : kOff)
-                                                            : (uint32_t)((kt * kBM + tid) * 8);
-        const uint32_t ob = !kin ? kOff : SL == kScaleRow8 ? (tid < rows_b ? (uint32_t)(tid * sb_end + sb0) : kOff)
-                                                            : (uint32_t)((kt * kBM + tid) * 8);
-        const u32x2_t va = __builtin_amdgcn_raw_buffer_load_b64(ras, oa, 0, 0);
-        const u32x2_t vb = __builtin_amdgcn_raw_buffer_load_b64(rbs, ob, 0, 0);
-        st.as[0] = va[0];
-        st.as[1] = va[1];
-        st.bs[0] = vb[0];
-        st.bs[1] = vb[1];
+        const uint32_t o = !kin ? kOff : SL == kScaleRow8 ? (srow < srows ? (uint32_t)(srow * sb_end + sb0) : kOff)
+                                                           : (uint32_t)((kt * kBM + srow) * 8);
+        const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rs, o, 0, 0);
+        st.sc[0] = v[0];
+        st.sc[1] = v[1];
     }
 }
 
@@ -123,26 +124,22 @@ template <int SL>
 __device__ __forceinline__ void store_quarter(Smem& sm, int buf, const Stage& st, int Q)
 {
     const int tid = (int)threadIdx.x;
-#pragma unroll
-    for (int i = 2 * Q; i < 2 * Q + 2; ++i) {
-        const int q = i * kThreads + tid;
+    {
+        const int q = Q * kThreads + tid;
         const int row = q >> 3, c = q & 7;
-        sm.code[buf][0][swz(row, c)] = st.a[i];
-        sm.code[buf][1][swz(row, c)] = st.b[i];
+        sm.code[buf][0][swz(row, c)] = st.a[Q];
+        sm.code[buf][1][swz(row, c)] = st.b[Q];
     }
     if (Q != 3) return;
-    uint2 a, b;
+    uint2 w;
     if (SL == kScaleRowBytes) {
-        a.x = st.as[0] | (st.as[1] << 8) | (st.as[2] << 16) | (st.as[3] << 24);
-        a.y = st.as[4] | (st.as[5] << 8) | (st.as[6] << 16) | (st.as[7] << 24);
-        b.x = st.bs[0] | (st.bs[1] << 8) | (st.bs[2] << 16) | (st.bs[3] << 24);
-        b.y = st.bs[4] | (st.bs[5] << 8) | (st.bs[6] << 16) | (st.bs[7] << 24);
+        w.x = st.sc[0] | (st.sc[1] << 8) | (st.sc[2] << 16) | (st.sc[3] << 24);
+        w.y = st.sc[4] | (st.sc[5] << 8) | (st.sc[6] << 16) | (st.sc[7] << 24);
     } else {
-        a = make_uint2(st.as[0], st.as[1]);
-        b = make_uint2(st.bs[0], st.bs[1]);
+        w = make_uint2(st.sc[0], st.sc[1]);
     }
-    sm.scale[buf][0][tid] = a;
-    sm.scale[buf][1][tid] = b;
+    const bool is_b = tid >= kBM;
+    sm.scale[buf][is_b ? 1 : 0][is_b ? tid - kBM : tid] = w;
 }
 
 __device__ __forceinline__ uint32_t scale_byte(uint2 s, int idx)
@@ -183,14 +180,14 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemm(GemmArgs g)
     const rsrc_t rbs = make_rsrc(SL == kScaleTiled ? g.bs + (int64_t)tn * kts * kBM * 8 : g.bs + (int64_t)n0 * (g.K / 32));
 
     const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / kWaveN, wn = wave % kWaveN;   // wave rows 128 wm.., columns 64 wn..
     const int lr = lane & 31, lh = lane >> 5;
 
-    v16f_t acc[4][4];
+    v16f_t acc[kTM][kTN];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kTM; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = v16f_t{};
+        for (int j = 0; j < kTN; ++j) acc[i][j] = v16f_t{};
 
     const int nk = (g.K + kBK - 1) / kBK;
     Stage st;
@@ -208,21 +205,23 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemm(GemmArgs g)
     // to the other buffer and tile kt + 2 is requested, a quarter per K-step
     for (int kt = 0; kt < nk; ++kt) {
         const int cur = kt & 1, nxt = cur ^ 1;
-        uint2 sa[4], sb[4];
+        uint2 sa[kTM], sb[kTN];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            sa[i] = sm.scale[cur][0][wm * 128 + i * 32 + lr];
-            sb[i] = sm.scale[cur][1][wn * 128 + i * 32 + lr];
-        }
-        v8i_t av[2][4], bv[2][4];
+        for (int i = 0; i < kTM; ++i) sa[i] = sm.scale[cur][0][wm * 32 * kTM + i * 32 + lr];
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) sb[j] = sm.scale[cur][1][wn * 32 * kTN + j * 32 + lr];
+        v8i_t av[2][kTM], bv[2][kTN];
         auto read_ops = [&](int ks, int p) __attribute__((always_inline)) {
             const int chunk = 2 * ks + lh;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint4 x = sm.code[cur][0][swz(wm * 128 + i * 32 + lr, chunk)];
-                const uint4 y = sm.code[cur][1][swz(wn * 128 + i * 32 + lr, chunk)];
+            for (int i = 0; i < kTM; ++i) {
+                const uint4 x = sm.code[cur][0][swz(wm * 32 * kTM + i * 32 + lr, chunk)];
                 av[p][i] = v8i_t{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
-                bv[p][i] = v8i_t{(int)y.x, (int)y.y, (int)y.z, (int)y.w, 0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int j = 0; j < kTN; ++j) {
+                const uint4 y = sm.code[cur][1][swz(wn * 32 * kTN + j * 32 + lr, chunk)];
+                bv[p][j] = v8i_t{(int)y.x, (int)y.y, (int)y.z, (int)y.w, 0, 0, 0, 0};
             }
         };
         read_ops(0, 0);
@@ -236,10 +235,10 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemm(GemmArgs g)
             __builtin_amdgcn_sched_barrier(0);
             const int chunk = 2 * ks + lh;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < kTM; ++i) {
                 const int sai = (int)scale_byte(sa[i], chunk);
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < kTN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                         av[p][i], bv[p][j], acc[i][j], 4, 4, 0, sai, 0, (int)scale_byte(sb[j], chunk));
             }
@@ -254,13 +253,13 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemm(GemmArgs g)
     // epilogue: accumulator r of lane l is C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32]
     const int64_t ldc = g.ldc;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kTM; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int col = n0 + wn * 128 + j * 32 + lr;
+        for (int j = 0; j < kTN; ++j) {
+            const int col = n0 + wn * 32 * kTN + j * 32 + lr;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                const int row = m0 + wm * 32 * kTM + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
                 if (row < g.M && col < g.N) {
                     const float v = acc[i][j][r];
                     if (CF32) static_cast<float*>(g.c)[(int64_t)row * ldc + col] = v;
