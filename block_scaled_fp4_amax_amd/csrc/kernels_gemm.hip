@@ -252,6 +252,49 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemm(GemmArgs g)
 
     // epilogue: accumulator r of lane l is C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32]
     const int64_t ldc = g.ldc;
+    constexpr int kES = CF32 ? 4 : 2;                  // bytes per element of C
+    const bool whole = m0 + kBM <= g.M && n0 + kBM <= g.N && ((uint64_t)ldc * kES) % 16 == 0 &&
+                       (reinterpret_cast<uintptr_t>(g.c) & 15) == 0;
+    if (whole) {
+        // a whole tile and 16-byte aligned rows of C (uniform over the
+        // workgroup): each wave stages its block in its own 16 KiB of the now
+        // idle LDS (bf16: all 128 rows; FP32: 64 rows at a time), rows of 64
+        // elements with the 16-byte chunk index XOR-swizzled by the row, then
+        // writes 16-byte chunks, eight or sixteen lanes per row of C
+        constexpr int kRowB = 64 * kES;                // staged row bytes
+        constexpr int kCpr = kRowB / 16;               // chunks per staged row
+        constexpr int kHalves = CF32 ? 2 : 1;
+        constexpr int kTMh = kTM / kHalves;
+        unsigned char* stage = smem_raw + wave * 16384;
+#pragma unroll
+        for (int h = 0; h < kHalves; ++h) {
+            __syncthreads();                           // the LDS is free (operands, previous half)
+#pragma unroll
+            for (int ii = 0; ii < kTMh; ++ii)
+#pragma unroll
+                for (int j = 0; j < kTN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int lrow = ii * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                        const int cb = (j * 32 + lr) * kES;
+                        unsigned char* dst = stage + lrow * kRowB + (((cb >> 4) ^ (lrow & (kCpr - 1))) << 4) + (cb & 15);
+                        const float v = acc[h * kTMh + ii][j][r];
+                        if (CF32) *reinterpret_cast<float*>(dst) = v;
+                        else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)f32_to_bf16(v);
+                    }
+            __syncthreads();
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int ch = q * 64 + lane;
+                const int lrow = ch / kCpr, c = ch % kCpr;
+                const uint4 v = *reinterpret_cast<const uint4*>(stage + lrow * kRowB + ((c ^ (lrow & (kCpr - 1))) << 4));
+                const int64_t grow = m0 + wm * 32 * kTM + h * kTMh * 32 + lrow;
+                const int64_t gcol = n0 + wn * 32 * kTN + c * (16 / kES);
+                st_nt16(static_cast<unsigned char*>(g.c) + (grow * ldc + gcol) * kES, v);
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < kTM; ++i)
 #pragma unroll

@@ -133,3 +133,21 @@ def test_gemm_8192_sampled_rows(layout):
     rows[0], rows[-1] = 0, M - 1
     c, s = ref.mx_mm(a[0][rows], a[1][rows], *b, len(rows), N, K)
     within_bound(got[rows], c, s, K, "8192^3 sampled rows")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("ldc", [520, 517])
+def test_whole_tiles_into_padded_c(dtype, ldc):
+    """512 x 512 (whole 256 x 256 tiles) into C with row pitch ldc: 16-byte
+    aligned rows take the staged 16-byte stores, odd pitches the per-element
+    stores; the padding columns stay untouched."""
+    rng = np.random.default_rng(ldc)
+    M, N, K = 512, 512, 384
+    a, b = operand(rng, M, K, 120, 135), operand(rng, N, K, 120, 135)
+    c, s = ref.mx_mm(*a, *b, M, N, K)
+    full = torch.full((M, ldc), -7.0, dtype=dtype, device="cuda")
+    fq.fp4_mm(dev_operand(a, "tiled"), dev_operand(b, "tiled"), c=full[:, :N])
+    torch.cuda.synchronize()
+    f = full.float().cpu().numpy().astype(np.float64)
+    within_bound(f[:, :N], c, s, K, "C ldc=%d" % ldc, bf16=dtype == torch.bfloat16)
+    assert np.all(f[:, N:] == -7.0)
