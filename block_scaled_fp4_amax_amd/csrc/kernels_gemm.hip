@@ -30,6 +30,8 @@
 // K-values beyond K load as zero codes with scale byte 0 (2^-127), adding
 // exact zeros.  Workgroup ids are remapped so each XCD (ids dealt round-robin)
 // works on a contiguous run of tiles that share operand panels in its L2.
+#include <mutex>
+
 #include "fp4q_device.h"
 #include "launch.h"
 
@@ -351,14 +353,20 @@ hipError_t launch_mx_gemm(const GemmArgs& g, hipStream_t s)
 {
     const int T = g.tiles_m * g.tiles_n;
     const size_t lds = sizeof(Smem);   // 136 KiB of the CU's 160 KiB
-    void (*fn)(GemmArgs) = nullptr;
-    if (g.scale_layout == kScaleTiled) fn = g.c_f32 ? k_mx_gemm<true, kScaleTiled> : k_mx_gemm<false, kScaleTiled>;
-    else if (g.scale_layout == kScaleRow8) fn = g.c_f32 ? k_mx_gemm<true, kScaleRow8> : k_mx_gemm<false, kScaleRow8>;
-    else fn = g.c_f32 ? k_mx_gemm<true, kScaleRowBytes> : k_mx_gemm<false, kScaleRowBytes>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(fn, dim3(T), dim3(kThreads), lds, s, g);
+    const int variant = (g.scale_layout == kScaleTiled ? 4 : g.scale_layout == kScaleRow8 ? 2 : 0) + (g.c_f32 ? 1 : 0);
+    static void (*const fns[6])(GemmArgs) = {
+        k_mx_gemm<false, kScaleRowBytes>, k_mx_gemm<true, kScaleRowBytes>, k_mx_gemm<false, kScaleRow8>,
+        k_mx_gemm<true, kScaleRow8>,      k_mx_gemm<false, kScaleTiled>,   k_mx_gemm<true, kScaleTiled>};
+    // the dynamic-LDS limit is a property of the kernel function: raise it once
+    // per variant (not per launch, so launches stay capturable in a HIP graph)
+    static std::once_flag once[6];
+    static hipError_t attr_status[6];
+    std::call_once(once[variant], [&] {
+        attr_status[variant] = hipFuncSetAttribute(reinterpret_cast<const void*>(fns[variant]),
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    });
+    if (attr_status[variant] != hipSuccess) return attr_status[variant];
+    hipLaunchKernelGGL(fns[variant], dim3(T), dim3(kThreads), lds, s, g);
     return hipGetLastError();
 }
 

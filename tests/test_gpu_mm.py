@@ -151,3 +151,33 @@ def test_whole_tiles_into_padded_c(dtype, ldc):
     f = full.float().cpu().numpy().astype(np.float64)
     within_bound(f[:, :N], c, s, K, "C ldc=%d" % ldc, bf16=dtype == torch.bfloat16)
     assert np.all(f[:, N:] == -7.0)
+
+
+def test_graph_replays_equal_eager():
+    """fp4_mm captured in a HIP graph (after one eager call of the variant):
+    three replays, with eager launches in between, each equal to the eager C."""
+    rng = np.random.default_rng(21)
+    M, N, K = 512, 768, 512
+    a, b = operand(rng, M, K, 120, 135), operand(rng, N, K, 120, 135)
+    A, B = dev_operand(a, "tiled"), dev_operand(b, "tiled")
+    eager = fq.fp4_mm(A, B, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    want = eager.cpu().numpy().view(np.uint32).copy()
+    c = torch.zeros((M, N), dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fq.fp4_mm(A, B, c=c)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fq.fp4_mm(A, B, c=c)
+    for rep in range(3):
+        c.fill_(-1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(c.cpu().numpy().view(np.uint32), want, err_msg="replay %d" % rep)
+        fq.fp4_mm(B, A, out_dtype=torch.float32)          # unrelated eager work between replays
+        torch.cuda.synchronize()
