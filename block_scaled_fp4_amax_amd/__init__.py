@@ -186,6 +186,26 @@ def _src(x, allow_f32=False):
     return x, x.shape[0], x.shape[1], ld
 
 
+def _need(t, nbytes, what):
+    """A caller-supplied buffer must be contiguous and hold at least nbytes
+    (the library trusts its buffer sizes, so this is checked before any call)."""
+    if t is None:
+        return
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % what)
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError("%s holds %d bytes, needs %d" % (what, have, nbytes))
+
+
+def _need_residual(residual, R, C):
+    if residual is None:
+        return
+    if residual.dtype != _torch().float32 or tuple(residual.shape) != (R, C):
+        raise ValueError("residual must be a float32 [%d, %d] tensor" % (R, C))
+    _need(residual, R * C * 4, "residual")
+
+
 def _dtype_name(t):
     return "fp32" if t.dtype == _torch().float32 else "bf16"
 
@@ -228,6 +248,10 @@ def fp4_quantize(x, cfg, *, residual=None, outer=None, workspace=None, stream=No
         scales = _empty(sizes["row_scales"], torch.uint8, dev).view(R, C // _inner(cfg))
     if outer is None and sizes["row_outer"]:
         outer = _empty(sizes["row_outer"] // 4, torch.float32, dev)
+    _need(codes, sizes["row_codes"], "codes")
+    _need(scales, sizes["row_scales"], "scales")
+    _need(outer, sizes["row_outer"], "outer")
+    _need_residual(residual, R, C)
     ws, wsb = _workspace(cfg, R, C, dev, workspace)
     _check(lib().fp4_quantize(ct.byref(cfg), _ptr(x), R, C, ld, _ptr(codes), _ptr(scales), _ptr(outer),
                               _ptr(residual), _ptr(ws), wsb, _stream(stream)), "fp4_quantize")
@@ -254,6 +278,9 @@ def fp4_qdq(x, cfg, *, residual=None, outer=None, with_codes=False, workspace=No
         scales = _empty(sizes["row_scales"], torch.uint8, dev).view(R, C // _inner(cfg))
     if outer is None and sizes["row_outer"] and (with_codes or cfg.outer_mode == 0):
         outer = _empty(sizes["row_outer"] // 4, torch.float32, dev)
+    _need(y, sizes["y"], "y")
+    _need(outer, sizes["row_outer"], "outer")
+    _need_residual(residual, R, C)
     ws, wsb = _workspace(cfg, R, C, dev, workspace)
     _check(lib().fp4_qdq(ct.byref(cfg), _ptr(x), R, C, ld, _ptr(y), _ptr(codes), _ptr(scales), _ptr(outer),
                          _ptr(residual), _ptr(ws), wsb, _stream(stream)), "fp4_qdq")
@@ -268,6 +295,12 @@ def fp4_dequantize(codes, scales, outer, rows, cols, cfg, *, outer_transposed=Fa
     if y is None:
         y = torch.empty((rows, cols), dtype=dtype if dtype is not None else torch.bfloat16, device=codes.device)
     cfg = _with_dtypes(cfg, output_dtype=_dtype_name(y))
+    if rows and cols:
+        sizes = fp4q_buffer_sizes(cfg, rows, cols)
+        _need(codes, sizes["row_codes"], "codes")
+        _need(scales, sizes["row_scales"], "scales")
+        _need(outer, sizes["row_outer"], "outer")
+        _need(y, sizes["y"], "y")
     _check(lib().fp4_dequantize(ct.byref(cfg), _ptr(codes), _ptr(scales), _ptr(outer), int(rows), int(cols),
                                 int(bool(outer_transposed)), _ptr(y), _stream(stream)), "fp4_dequantize")
     return y
@@ -297,6 +330,11 @@ def fp4_cast_transpose(x, cfg, *, residual=None, row_outer=None, col_outer=None,
     if col_outer is None and sizes["col_outer"]:
         col_outer = _empty(sizes["col_outer"] // 4, torch.float32, dev)
     out["row_outer"], out["col_outer"] = row_outer, col_outer
+    for k, shp in shapes.items():
+        _need(out[k], shp[0] * shp[1], k)
+    _need(row_outer, sizes["row_outer"], "row_outer")
+    _need(col_outer, sizes["col_outer"], "col_outer")
+    _need_residual(residual, R, C)
     ws, wsb = _workspace(cfg, R, C, dev, workspace)
     _check(lib().fp4_cast_transpose(ct.byref(cfg), _ptr(x), R, C, ld, _ptr(out["row_codes"]), _ptr(out["row_scales"]),
                                     _ptr(row_outer), _ptr(out["col_codes"]), _ptr(out["col_scales"]), _ptr(col_outer),
@@ -327,6 +365,10 @@ def fp4_cast_transpose_grouped(x, rows_per_group, cfg, *, residual=None, stream=
             "row_outer": _empty(n_ro, torch.float32, dev) if n_ro else None,
             "col_outer": _empty(n_co, torch.float32, dev) if n_co else None,
         }
+    for k, n in (("row_codes", total * C // 2), ("row_scales", total * C // 16), ("col_codes", total * C // 2),
+                 ("col_scales", total * C // 16), ("row_outer", 4 * n_ro), ("col_outer", 4 * n_co)):
+        _need(out.get(k), n, k)
+    _need_residual(residual, total, C)
     arr = (ct.c_int64 * max(len(rows), 1))(*rows)
     _check(lib().fp4_cast_transpose_grouped(ct.byref(cfg), len(rows), arr, C, _ptr(x), ld, _ptr(out["row_codes"]),
                                             _ptr(out["row_scales"]), _ptr(out["row_outer"]), _ptr(out["col_codes"]),
@@ -355,6 +397,8 @@ def fp4_mx_project_fp8(x, cfg=None, *, y=True, mx8_row=True, mx8_col=True, blk=T
             out[k] = torch.empty(shp, dtype=dt, device=dev)
         if not on:
             out[k] = None
+        else:
+            _need(out[k], shp[0] * shp[1] * torch.empty((), dtype=dt).element_size(), k)
     g = out.get
     _check(lib().fp4_mx_project_fp8(ct.byref(cfg), _ptr(x), R, C, ld, _ptr(g("y")), _ptr(g("mx8_row")),
                                     _ptr(g("mx8_row_scales")), _ptr(g("mx8_col")), _ptr(g("mx8_col_scales")),
@@ -371,8 +415,10 @@ def fp4_mx_scales_tiled(scales, K, stream=None, out=None):
     """GEMM-ready layout of rowwise MXFP4 scales [rows, K/32] (uint8, flat)."""
     torch = _torch()
     rows = scales.shape[0]
+    _need(scales, rows * (K // 32), "scales")
     if out is None:
         out = torch.empty(fp4q_mx_scales_tiled_bytes(rows, K), dtype=torch.uint8, device=scales.device)
+    _need(out, fp4q_mx_scales_tiled_bytes(rows, K), "tiled scales")
     _check(lib().fp4_mx_scales_tiled(_ptr(scales), int(rows), int(K), _ptr(out), _stream(stream)),
            "fp4_mx_scales_tiled")
     return out
@@ -402,8 +448,13 @@ def fp4_mm(a, b, cfg=None, *, out_dtype=None, c=None, stream=None):
     M, N, K = ac.shape[0], bc.shape[0], ac.shape[1] * 2
     if bc.shape[1] * 2 != K:
         raise ValueError("operands disagree on K (%d vs %d)" % (K, bc.shape[1] * 2))
+    for nm, codes, sc, rows in (("a", ac, asc, M), ("b", bc, bsc, N)):
+        _need(codes, rows * K // 2, nm + " codes")
+        _need(sc, fp4q_mx_scales_tiled_bytes(rows, K) if la else rows * (K // 32), nm + " scales")
     if c is None:
         c = torch.empty((M, N), dtype=out_dtype if out_dtype is not None else torch.bfloat16, device=ac.device)
+    if tuple(c.shape) != (M, N) or (N > 1 and c.stride(1) != 1) or c.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("c must be a bf16 or float32 [%d, %d] view with contiguous rows" % (M, N))
     ccfg = _with_dtypes(cfg, output_dtype=_dtype_name(c))
     _check(lib().fp4_mm(ct.byref(ccfg), _ptr(ac), _ptr(asc), _ptr(bc), _ptr(bsc), M, N, K, la, _ptr(c),
                         c.stride(0) if M > 1 else N, _stream(stream)), "fp4_mm")

@@ -45,3 +45,27 @@ def test_error_feedback_rules():
     ef.reset("w")
     with pytest.raises(KeyError):
         ef.residual("w")
+
+
+def test_caller_buffers_are_size_checked_before_any_call():
+    """Too-small or non-contiguous caller buffers are refused by the binding
+    (the C ABI trusts its sizes); these checks run before the device check."""
+    u8 = lambda *s: torch.zeros(*s, dtype=torch.uint8)  # noqa: E731
+    with pytest.raises(ValueError, match="a scales"):
+        fq.fp4_mm({"codes": u8(64, 64), "scales": u8(64, 3)}, {"codes": u8(32, 64), "scales": u8(32, 4)})
+    with pytest.raises(ValueError, match="b codes"):
+        fq.fp4_mm({"codes": u8(64, 64), "scales": u8(64, 4)}, {"codes": u8(32, 128)[:, :64], "scales": u8(32, 4)})
+    with pytest.raises(ValueError, match="tiled scales|a scales"):
+        fq.fp4_mm({"codes": u8(64, 64), "scales_tiled": u8(100)}, {"codes": u8(32, 64), "scales_tiled": u8(2048)})
+    with pytest.raises(ValueError, match="c must be"):
+        fq.fp4_mm({"codes": u8(64, 64), "scales": u8(64, 4)}, {"codes": u8(32, 64), "scales": u8(32, 4)},
+                  c=torch.zeros(32, 64, dtype=torch.float32))
+    with pytest.raises(ValueError, match="residual"):
+        fq.fp4_qdq(torch.zeros(16, 32, dtype=torch.bfloat16), fq.make_cfg(), residual=torch.zeros(16, 16))
+    with pytest.raises(ValueError, match="codes holds"):
+        fq.fp4_quantize(torch.zeros(16, 32, dtype=torch.bfloat16), fq.make_cfg(), out={"codes": u8(16, 8)})
+    with pytest.raises(ValueError, match="y holds"):
+        fq.fp4_dequantize(u8(16, 16), u8(16, 2), None, 16, 32, fq.make_cfg(), y=torch.zeros(16, 16, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="blk_scales"):
+        fq.fp4_mx_project_fp8(torch.zeros(128, 128, dtype=torch.bfloat16),
+                              out={"blk_scales": torch.zeros(0, dtype=torch.float32)})
