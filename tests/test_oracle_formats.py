@@ -128,9 +128,19 @@ def _torch_e4m3(y):
 
 
 def test_e4m3_encode_matches_torch_float8_cast():
-    y = _probe_values(-12, 9)
-    y = np.concatenate([y[y <= 448.0], np.float32([0.0, 2.0 ** -10, 2.0 ** -9, 3 * 2.0 ** -11, 448.0])])
-    np.testing.assert_array_equal(ref.scale_encode_array("e4m3", y), _torch_e4m3(y))
+    # every binary32 in [2^-11, 448] (every value that can round to a nonzero
+    # code, and a binade below), in chunks; below 2^-11 (all of which encode to
+    # zero) every 97th pattern
+    lo, hi = int(np.float32(2.0 ** -11).view(np.uint32)), int(np.float32(448.0).view(np.uint32))
+    step = 1 << 24
+    for a in range(lo, hi + 1, step):
+        y = np.arange(a, min(hi + 1, a + step), dtype=np.uint32).view(np.float32)
+        got, want = ref.scale_encode_array("e4m3", y), _torch_e4m3(y)
+        bad = np.flatnonzero(got != want)
+        assert bad.size == 0, (y[bad[:4]], got[bad[:4]], want[bad[:4]])
+    tiny = np.arange(0, lo, 97, dtype=np.uint32).view(np.float32)
+    np.testing.assert_array_equal(ref.scale_encode_array("e4m3", tiny), _torch_e4m3(tiny))
+    assert not ref.scale_encode_array("e4m3", tiny).any()
 
 
 def test_ue5m3_encode_pinned_to_e4m3_by_exponent_shift():
