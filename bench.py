@@ -321,7 +321,7 @@ def make_mx_gemm(torch, fq, W):
             raise fq.Fp4Error(st, "fp4_mm")
     alg = M * K // 2 * 2 + 2 * 8 * ((M + 255) // 256) * ((K + 255) // 256) * 256 + M * N * 2
     return Timed("mx_gemm_8192", "MXFP4 GEMM C = A.B^T 8192x8192x8192, tiled scales, bf16 C", alg, sets, launch,
-                 "k_mx_gemm<false, 2>", M * N, flops=2 * M * N * K, graph=False)
+                 "k_mx_gemm_lds<false>", M * N, flops=2 * M * N * K, graph=False)
 
 
 def make_cast_transpose_1d_sr(torch, fq, W):

@@ -151,15 +151,11 @@ __device__ __forceinline__ uint32_t scale_byte(uint2 s, int idx)
     return (w >> (8 * (idx & 3))) & 0xFFu;
 }
 
-template <bool CF32, int SL>
-__global__ __launch_bounds__(kThreads) void k_mx_gemm(GemmArgs g)
+// Tile of this workgroup: XCD x takes the contiguous run x * T/8 .. of the
+// tile order when T % 8 == 0 (ids are dealt round-robin to the 8 XCDs); within
+// the order, groups of 4 tile rows are walked column by column.
+__device__ __forceinline__ void tile_of_workgroup(const GemmArgs& g, int& tm, int& tn)
 {
-    extern __shared__ __align__(16) unsigned char smem_raw[];
-    Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
-
-    // tile of this workgroup: XCD x takes the contiguous run x * T/8 .. of the
-    // tile order when T % 8 == 0 (ids are dealt round-robin to the 8 XCDs);
-    // within the order, groups of 4 tile rows are walked column by column
     const int T = g.tiles_m * g.tiles_n;
     int t = (int)blockIdx.x;
     if (T % 8 == 0) t = (t & 7) * (T >> 3) + (t >> 3);
@@ -168,9 +164,88 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemm(GemmArgs g)
     const int first_m = group * gm;
     const int rows_in_group = min(gm, g.tiles_m - first_m);
     const int in_group = t - group * gm * g.tiles_n;
-    const int tm = first_m + in_group % rows_in_group;
-    const int tn = in_group / rows_in_group;
+    tm = first_m + in_group % rows_in_group;
+    tn = in_group / rows_in_group;
+}
 
+// C tile: accumulator r of lane l of wave (wm, wn) holds
+// C[m0 + 128 wm + 32 i + 8 (r / 4) + 4 (l / 32) + r % 4][n0 + 64 wn + 32 j + l % 32].
+template <bool CF32>
+__device__ __forceinline__ void store_c(const GemmArgs& g, const v16f_t (&acc)[kTM][kTN], int m0, int n0,
+                                        unsigned char* smem_raw)
+{
+    const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / kWaveN, wn = wave % kWaveN;
+    const int lr = lane & 31, lh = lane >> 5;
+    const int64_t ldc = g.ldc;
+    constexpr int kES = CF32 ? 4 : 2;                  // bytes per element of C
+    const bool whole = m0 + kBM <= g.M && n0 + kBM <= g.N && ((uint64_t)ldc * kES) % 16 == 0 &&
+                       (reinterpret_cast<uintptr_t>(g.c) & 15) == 0;
+    if (whole) {
+        // a whole tile and 16-byte aligned rows of C (uniform over the
+        // workgroup): each wave stages its block in its own 16 KiB of the now
+        // idle LDS (bf16: all 128 rows; FP32: 64 rows at a time), rows of 64
+        // elements with the 16-byte chunk index XOR-swizzled by the row, then
+        // writes 16-byte chunks, eight or sixteen lanes per row of C
+        constexpr int kRowB = 64 * kES;                // staged row bytes
+        constexpr int kCpr = kRowB / 16;               // chunks per staged row
+        constexpr int kHalves = CF32 ? 2 : 1;
+        constexpr int kTMh = kTM / kHalves;
+        unsigned char* stage = smem_raw + wave * 16384;
+#pragma unroll
+        for (int h = 0; h < kHalves; ++h) {
+            __syncthreads();                           // the LDS is free (operands, previous half)
+#pragma unroll
+            for (int ii = 0; ii < kTMh; ++ii)
+#pragma unroll
+                for (int j = 0; j < kTN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int lrow = ii * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                        const int cb = (j * 32 + lr) * kES;
+                        unsigned char* dst = stage + lrow * kRowB + (((cb >> 4) ^ (lrow & (kCpr - 1))) << 4) + (cb & 15);
+                        const float v = acc[h * kTMh + ii][j][r];
+                        if (CF32) *reinterpret_cast<float*>(dst) = v;
+                        else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)f32_to_bf16(v);
+                    }
+            __syncthreads();
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int ch = q * 64 + lane;
+                const int lrow = ch / kCpr, c = ch % kCpr;
+                const uint4 v = *reinterpret_cast<const uint4*>(stage + lrow * kRowB + ((c ^ (lrow & (kCpr - 1))) << 4));
+                const int64_t grow = m0 + wm * 32 * kTM + h * kTMh * 32 + lrow;
+                const int64_t gcol = n0 + wn * 32 * kTN + c * (16 / kES);
+                st_nt16(static_cast<unsigned char*>(g.c) + (grow * ldc + gcol) * kES, v);
+            }
+        }
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) {
+            const int col = n0 + wn * 32 * kTN + j * 32 + lr;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + wm * 32 * kTM + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                if (row < g.M && col < g.N) {
+                    const float v = acc[i][j][r];
+                    if (CF32) static_cast<float*>(g.c)[(int64_t)row * ldc + col] = v;
+                    else static_cast<uint16_t*>(g.c)[(int64_t)row * ldc + col] = (uint16_t)f32_to_bf16(v);
+                }
+            }
+        }
+}
+
+template <bool CF32, int SL>
+__global__ __launch_bounds__(kThreads) void k_mx_gemm(GemmArgs g)
+{
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
+
+    int tm, tn;
+    tile_of_workgroup(g, tm, tn);
     const int m0 = tm * kBM, n0 = tn * kBM;
     const int rows_a = min(kBM, g.M - m0), rows_b = min(kBM, g.N - n0);
     const int64_t lda = g.K / 2;
@@ -252,66 +327,176 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemm(GemmArgs g)
         __syncthreads();
     }
 
-    // epilogue: accumulator r of lane l is C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32]
-    const int64_t ldc = g.ldc;
-    constexpr int kES = CF32 ? 4 : 2;                  // bytes per element of C
-    const bool whole = m0 + kBM <= g.M && n0 + kBM <= g.N && ((uint64_t)ldc * kES) % 16 == 0 &&
-                       (reinterpret_cast<uintptr_t>(g.c) & 15) == 0;
-    if (whole) {
-        // a whole tile and 16-byte aligned rows of C (uniform over the
-        // workgroup): each wave stages its block in its own 16 KiB of the now
-        // idle LDS (bf16: all 128 rows; FP32: 64 rows at a time), rows of 64
-        // elements with the 16-byte chunk index XOR-swizzled by the row, then
-        // writes 16-byte chunks, eight or sixteen lanes per row of C
-        constexpr int kRowB = 64 * kES;                // staged row bytes
-        constexpr int kCpr = kRowB / 16;               // chunks per staged row
-        constexpr int kHalves = CF32 ? 2 : 1;
-        constexpr int kTMh = kTM / kHalves;
-        unsigned char* stage = smem_raw + wave * 16384;
+    store_c<CF32>(g, acc, m0, n0, smem_raw);
+}
+
+// Direct-to-LDS variant for the GEMM-ready scale layout.  gfx950's buffer loads
+// with the LDS flag write a wave's 64 results (16 or 4 bytes each) to 64
+// consecutive LDS slots at a wave-uniform base, bypassing registers, so a
+// K-tile moves into LDS without register staging or LDS write instructions.
+// Two buffers: K-tile kt + 1 is requested right after the barrier that opens
+// K-tile kt (the barrier also retires every wave's reads of the buffer it
+// overwrites); the first two K-tiles are requested before the loop.  Slot l of
+// code block b (1 KiB, rows 8 b .. 8 b + 7) receives row 8 b + l / 8, stored
+// chunk l % 8, i.e. K-chunk (l % 8) ^ ((row / 2) & 7) of the row: the same
+// swizzled layout the register-staged kernel writes.  Scale words go to two
+// planes (low and high four bytes of a row's eight).  The loads are issued from
+// inline assembly with explicit waits: the compiler's own wait insertion cannot
+// tell the two buffers apart and would wait for the next K-tile's loads before
+// every read of the current one.
+struct SmemLds {
+    uint4 code[2][2][kChunks];                 // [buffer][A, B][chunk]         128 KiB
+    uint32_t scale[2][2][2][kBM];              // [buffer][A, B][low, high][row]  8 KiB
+};
+
+// The loads set m0 (the LDS base) themselves; no other instruction of these
+// kernels reads m0, so the reserved-register clobber warning is silenced.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_load16(rsrc_t r, uint32_t voff, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(lds_base), "s"(r)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ void lds_load4(rsrc_t r, uint32_t voff, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dword %0, %2, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(lds_base), "s"(r)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// wait until at most N of this wave's vector-memory loads are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p)
+{
+    return __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p);
+}
+
+// The ten loads of K-tile kt into buffer buf issued by wave w: code blocks
+// 4 w .. 4 w + 3 of A and of B, and the scale words of 64 rows (waves 0..3: A
+// rows 64 w .., waves 4..7: B rows 64 (w - 4) ..).  Codes beyond the rows or K
+// load as zeros; the tiled scales are zero-padded.
+__device__ __forceinline__ void lds_tile(const GemmArgs& g, SmemLds& sm, const rsrc_t& ra, const rsrc_t& rb,
+                                         const rsrc_t& ras, const rsrc_t& rbs, int kt, int rows_a, int rows_b,
+                                         int buf, int wave, int lane)
+{
+    const int kb_end = g.K / 2;
 #pragma unroll
-        for (int h = 0; h < kHalves; ++h) {
-            __syncthreads();                           // the LDS is free (operands, previous half)
+    for (int o = 0; o < 2; ++o) {
+        const int rows = o ? rows_b : rows_a;
 #pragma unroll
-            for (int ii = 0; ii < kTMh; ++ii)
-#pragma unroll
-                for (int j = 0; j < kTN; ++j)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int lrow = ii * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-                        const int cb = (j * 32 + lr) * kES;
-                        unsigned char* dst = stage + lrow * kRowB + (((cb >> 4) ^ (lrow & (kCpr - 1))) << 4) + (cb & 15);
-                        const float v = acc[h * kTMh + ii][j][r];
-                        if (CF32) *reinterpret_cast<float*>(dst) = v;
-                        else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)f32_to_bf16(v);
-                    }
-            __syncthreads();
-#pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const int ch = q * 64 + lane;
-                const int lrow = ch / kCpr, c = ch % kCpr;
-                const uint4 v = *reinterpret_cast<const uint4*>(stage + lrow * kRowB + ((c ^ (lrow & (kCpr - 1))) << 4));
-                const int64_t grow = m0 + wm * 32 * kTM + h * kTMh * 32 + lrow;
-                const int64_t gcol = n0 + wn * 32 * kTN + c * (16 / kES);
-                st_nt16(static_cast<unsigned char*>(g.c) + (grow * ldc + gcol) * kES, v);
-            }
+        for (int h = 0; h < 4; ++h) {
+            const int b = 4 * wave + h;
+            const int row = 8 * b + (lane >> 3);
+            const int c = (lane & 7) ^ ((row >> 1) & 7);
+            const int kb = kt * kRowB + 16 * c;
+            const uint32_t off = (row < rows && kb < kb_end) ? (uint32_t)(row * kb_end + kb) : kOff;
+            lds_load16(o ? rb : ra, off, lds_addr(&sm.code[buf][o][b * 64]));
         }
-        return;
     }
+    const int o = wave >> 2, r0 = 64 * (wave & 3);
+    const uint32_t off = (uint32_t)((kt * kBM + r0 + lane) * 8);
+    lds_load4(o ? rbs : ras, off, lds_addr(&sm.scale[buf][o][0][r0]));
+    lds_load4(o ? rbs : ras, off + 4, lds_addr(&sm.scale[buf][o][1][r0]));
+}
+
+constexpr int kLdsLoadsPerTile = 10;           // per wave
+
+template <bool CF32>
+__global__ __launch_bounds__(kThreads) void k_mx_gemm_lds(GemmArgs g)
+{
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    SmemLds& sm = *reinterpret_cast<SmemLds*>(smem_raw);
+
+    int tm, tn;
+    tile_of_workgroup(g, tm, tn);
+    const int m0 = tm * kBM, n0 = tn * kBM;
+    const int rows_a = min(kBM, g.M - m0), rows_b = min(kBM, g.N - n0);
+    const int64_t lda = g.K / 2;
+    const rsrc_t ra = make_rsrc(g.a + (int64_t)m0 * lda);
+    const rsrc_t rb = make_rsrc(g.b + (int64_t)n0 * lda);
+    const int nk = (g.K + kBK - 1) / kBK;
+    const rsrc_t ras = make_rsrc(g.as + (int64_t)tm * nk * kBM * 8);
+    const rsrc_t rbs = make_rsrc(g.bs + (int64_t)tn * nk * kBM * 8);
+
+    const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int wm = wave / kWaveN, wn = wave % kWaveN;
+    const int lr = lane & 31, lh = lane >> 5;
+
+    v16f_t acc[kTM][kTN];
 #pragma unroll
     for (int i = 0; i < kTM; ++i)
 #pragma unroll
-        for (int j = 0; j < kTN; ++j) {
-            const int col = n0 + wn * 32 * kTN + j * 32 + lr;
+        for (int j = 0; j < kTN; ++j) acc[i][j] = v16f_t{};
+
+    lds_tile(g, sm, ra, rb, ras, rbs, 0, rows_a, rows_b, 0, wave_u, lane);
+    if (nk > 1) lds_tile(g, sm, ra, rb, ras, rbs, 1, rows_a, rows_b, 1, wave_u, lane);
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        // this wave's part of K-tile kt has landed (K-tile 1 may still be in
+        // flight at kt = 0); the barrier makes every wave's part visible
+        if (kt == 0) wait_vm<kLdsLoadsPerTile>();
+        else wait_vm<0>();
+        __syncthreads();
+        if (kt >= 1 && kt + 1 < nk) lds_tile(g, sm, ra, rb, ras, rbs, kt + 1, rows_a, rows_b, cur ^ 1, wave_u, lane);
+        uint2 sa[kTM], sb[kTN];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = m0 + wm * 32 * kTM + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-                if (row < g.M && col < g.N) {
-                    const float v = acc[i][j][r];
-                    if (CF32) static_cast<float*>(g.c)[(int64_t)row * ldc + col] = v;
-                    else static_cast<uint16_t*>(g.c)[(int64_t)row * ldc + col] = (uint16_t)f32_to_bf16(v);
-                }
-            }
+        for (int i = 0; i < kTM; ++i) {
+            const int r = wm * 32 * kTM + i * 32 + lr;
+            sa[i] = make_uint2(sm.scale[cur][0][0][r], sm.scale[cur][0][1][r]);
         }
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) {
+            const int r = wn * 32 * kTN + j * 32 + lr;
+            sb[j] = make_uint2(sm.scale[cur][1][0][r], sm.scale[cur][1][1][r]);
+        }
+        v8i_t av[2][kTM], bv[2][kTN];
+        auto read_ops = [&](int ks, int p) __attribute__((always_inline)) {
+            const int chunk = 2 * ks + lh;
+#pragma unroll
+            for (int i = 0; i < kTM; ++i) {
+                const uint4 x = sm.code[cur][0][swz(wm * 32 * kTM + i * 32 + lr, chunk)];
+                av[p][i] = v8i_t{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int j = 0; j < kTN; ++j) {
+                const uint4 y = sm.code[cur][1][swz(wn * 32 * kTN + j * 32 + lr, chunk)];
+                bv[p][j] = v8i_t{(int)y.x, (int)y.y, (int)y.z, (int)y.w, 0, 0, 0, 0};
+            }
+        };
+        read_ops(0, 0);
+#pragma unroll
+        for (int ks = 0; ks < kBK / 64; ++ks) {
+            const int p = ks & 1;
+            if (ks + 1 < kBK / 64) read_ops(ks + 1, p ^ 1);
+            __builtin_amdgcn_sched_barrier(0);
+            const int chunk = 2 * ks + lh;
+#pragma unroll
+            for (int i = 0; i < kTM; ++i) {
+                const int sai = (int)scale_byte(sa[i], chunk);
+#pragma unroll
+                for (int j = 0; j < kTN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        av[p][i], bv[p][j], acc[i][j], 4, 4, 0, sai, 0, (int)scale_byte(sb[j], chunk));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    // no load is in flight here: the last K-tile's loads were waited for
+    store_c<CF32>(g, acc, m0, n0, smem_raw);
 }
 
 // GEMM-ready scales: out[(t * kts + kt) * 256 + r][j] = in[t * 256 + r][kt * 8 + j],
@@ -352,15 +537,25 @@ hipError_t launch_mx_scales_tiled(const uint8_t* in, int64_t rows, int64_t K, ui
 hipError_t launch_mx_gemm(const GemmArgs& g, hipStream_t s)
 {
     const int T = g.tiles_m * g.tiles_n;
-    const size_t lds = sizeof(Smem);   // 136 KiB of the CU's 160 KiB
-    const int variant = (g.scale_layout == kScaleTiled ? 4 : g.scale_layout == kScaleRow8 ? 2 : 0) + (g.c_f32 ? 1 : 0);
-    static void (*const fns[6])(GemmArgs) = {
+    static_assert(sizeof(Smem) == sizeof(SmemLds), "both kernels take 136 KiB of the CU's 160 KiB");
+    const size_t lds = sizeof(Smem);
+    // The direct-to-LDS kernel keeps one K-tile of loads in flight, the
+    // register-staged one up to two: measured on random operands, the former
+    // is ahead once K >= 8192 and there are at least four 256 x 256 tiles per
+    // CU (8192^3: +9%, 16384^2 x 8192: +15%), behind for shorter K or fewer
+    // tiles (8192^2 x 4096: -11%, 4096^2 x 8192: -6%).
+    const bool direct = g.scale_layout == kScaleTiled && g.K >= 8192 && T >= 1024;
+    const int variant = direct ? 6 + (g.c_f32 ? 1 : 0)
+                               : (g.scale_layout == kScaleTiled ? 4 : g.scale_layout == kScaleRow8 ? 2 : 0) +
+                                     (g.c_f32 ? 1 : 0);
+    static void (*const fns[8])(GemmArgs) = {
         k_mx_gemm<false, kScaleRowBytes>, k_mx_gemm<true, kScaleRowBytes>, k_mx_gemm<false, kScaleRow8>,
-        k_mx_gemm<true, kScaleRow8>,      k_mx_gemm<false, kScaleTiled>,   k_mx_gemm<true, kScaleTiled>};
+        k_mx_gemm<true, kScaleRow8>,      k_mx_gemm<false, kScaleTiled>,   k_mx_gemm<true, kScaleTiled>,
+        k_mx_gemm_lds<false>,             k_mx_gemm_lds<true>};
     // the dynamic-LDS limit is a property of the kernel function: raise it once
     // per variant (not per launch, so launches stay capturable in a HIP graph)
-    static std::once_flag once[6];
-    static hipError_t attr_status[6];
+    static std::once_flag once[8];
+    static hipError_t attr_status[8];
     std::call_once(once[variant], [&] {
         attr_status[variant] = hipFuncSetAttribute(reinterpret_cast<const void*>(fns[variant]),
                                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

@@ -153,11 +153,12 @@ def test_whole_tiles_into_padded_c(dtype, ldc):
     assert np.all(f[:, N:] == -7.0)
 
 
-def test_graph_replays_equal_eager():
+@pytest.mark.parametrize("M,N,K", [(512, 768, 512), (8192, 8192, 8192)])
+def test_graph_replays_equal_eager(M, N, K):
     """fp4_mm captured in a HIP graph (after one eager call of the variant):
-    three replays, with eager launches in between, each equal to the eager C."""
+    three replays, with eager launches in between, each equal to the eager C
+    (the second shape takes the direct-to-LDS kernel)."""
     rng = np.random.default_rng(21)
-    M, N, K = 512, 768, 512
     a, b = operand(rng, M, K, 120, 135), operand(rng, N, K, 120, 135)
     A, B = dev_operand(a, "tiled"), dev_operand(b, "tiled")
     eager = fq.fp4_mm(A, B, out_dtype=torch.float32)
@@ -181,3 +182,28 @@ def test_graph_replays_equal_eager():
         np.testing.assert_array_equal(c.cpu().numpy().view(np.uint32), want, err_msg="replay %d" % rep)
         fq.fp4_mm(B, A, out_dtype=torch.float32)          # unrelated eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("M,N,K,dtype", [(8192, 8192, 8192, torch.bfloat16), (8192, 8192, 8192, torch.float32),
+                                         (8100, 8200, 8256, torch.float32), (8192, 8192, 16384, torch.bfloat16)])
+def test_direct_lds_kernel_equals_register_staged(M, N, K, dtype):
+    """With GEMM-ready scales, K >= 8192 and at least 1024 tiles of 256 x 256
+    the library takes the direct-to-LDS kernel; with rowwise scales the
+    register-staged one.  Both issue the same instructions in the same K order,
+    so C must agree bit for bit over the whole matrix, ragged edges (8100 x
+    8200, a K tail of 64) included; sampled rows of the direct kernel's C are
+    checked against the oracle as well."""
+    rng = np.random.default_rng(M + N + K)
+    a, b = operand(rng, M, K, 115, 135), operand(rng, N, K, 115, 135)
+    A_row, B_row = dev_operand(a, "row"), dev_operand(b, "row")
+    A_til, B_til = dev_operand(a, "tiled"), dev_operand(b, "tiled")
+    staged = fq.fp4_mm(A_row, B_row, out_dtype=dtype)
+    direct = fq.fp4_mm(A_til, B_til, out_dtype=dtype)
+    torch.cuda.synchronize()
+    bits = torch.int16 if dtype == torch.bfloat16 else torch.int32
+    same = staged.view(bits) == direct.view(bits)
+    assert bool(same.all()), "%d of %d elements differ" % (int((~same).sum()), same.numel())
+    rows = np.array([0, 1, 255, 256, M // 2, M - 2, M - 1])
+    c, s = ref.mx_mm(a[0][rows], a[1][rows], *b, len(rows), N, K)
+    got = direct[torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
+    within_bound(got, c, s, K, "direct-to-LDS sampled rows", bf16=dtype == torch.bfloat16)
