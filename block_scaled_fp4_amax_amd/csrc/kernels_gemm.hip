@@ -282,6 +282,7 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemm(GemmArgs g)
     // to the other buffer and tile kt + 2 is requested, a quarter per K-step
     for (int kt = 0; kt < nk; ++kt) {
         const int cur = kt & 1, nxt = cur ^ 1;
+        const int ksteps = min(kBK / 64, (g.K - kt * kBK) >> 6);   // K-steps inside K (K % 64 == 0)
         uint2 sa[kTM], sb[kTN];
 #pragma unroll
         for (int i = 0; i < kTM; ++i) sa[i] = sm.scale[cur][0][wm * 32 * kTM + i * 32 + lr];
@@ -308,16 +309,19 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemm(GemmArgs g)
             // the next K-step's operand reads go out a whole K-step (16
             // instructions) before their use; the fences keep the scheduler
             // from moving them next to their consumers
-            if (ks + 1 < kBK / 64) read_ops(ks + 1, p ^ 1);
+            if (ks + 1 < ksteps) read_ops(ks + 1, p ^ 1);
             __builtin_amdgcn_sched_barrier(0);
             const int chunk = 2 * ks + lh;
+            // a K-tile's K-steps beyond K hold only zero codes: skipped
+            if (ks < ksteps) {
 #pragma unroll
-            for (int i = 0; i < kTM; ++i) {
-                const int sai = (int)scale_byte(sa[i], chunk);
+                for (int i = 0; i < kTM; ++i) {
+                    const int sai = (int)scale_byte(sa[i], chunk);
 #pragma unroll
-                for (int j = 0; j < kTN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        av[p][i], bv[p][j], acc[i][j], 4, 4, 0, sai, 0, (int)scale_byte(sb[j], chunk));
+                    for (int j = 0; j < kTN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            av[p][i], bv[p][j], acc[i][j], 4, 4, 0, sai, 0, (int)scale_byte(sb[j], chunk));
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
             store_quarter<SL>(sm, nxt, st, ks);
