@@ -339,9 +339,12 @@ int fp4_mx_project_fp8(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int
  * Needs K % 64 == 0 (FP4Q_ERR_SHAPE), K <= 2^22 and M, N <= 2^24
  * (FP4Q_ERR_UNSUPPORTED), code buffers 16-byte aligned and c aligned to its
  * element (FP4Q_ERR_ALIGN).  M == 0 or N == 0 writes nothing; K == 0 writes
- * zeros.  The first call of each (scale layout, C dtype) raises that kernel's
- * LDS limit (a host-side attribute); later calls only enqueue, so they may be
- * captured in a HIP graph.
+ * zeros.  The kernel depends on the scale layout and C's dtype and, for
+ * scale_layout 1, on the shape: K >= 8192 with at least 1024 tiles of
+ * 256 x 256 (8192 x 8192 and up) takes a direct-to-LDS kernel, the rest a
+ * register-staged one; both give bit-identical C.  The first call that selects
+ * a kernel raises its LDS limit (a host-side attribute); later calls only
+ * enqueue, so they may be captured in a HIP graph.
  */
 int fp4_mm(const fp4q_cfg* cfg, const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
            const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, int32_t scale_layout, void* c, int64_t ldc,
