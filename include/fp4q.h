@@ -183,7 +183,11 @@ size_t fp4q_workspace_bytes(const fp4q_cfg* cfg, int64_t rows, int64_t cols);
  *   residual  FP32 [rows, cols] device or NULL.  When given, the value quantised
  *             is RN(x + residual) and residual is rewritten in place with
  *             RN(value - dequantised value) (error feedback, "fp4-train"
- *             README, Method).  NVFP4/AMDFP4 only.
+ *             README, Method).  NVFP4/AMDFP4 only.  Its values must be
+ *             finite.  NaN / inf sanitisation (NaN -> +0, +-inf -> +-largest
+ *             bf16; ALTO page, Op-level test coverage) applies to the value
+ *             quantised, the sum: a NaN x gives +0, an infinite x or an
+ *             overflowing sum the signed largest bf16.
  *   workspace device scratch of >= fp4q_workspace_bytes() bytes (NULL if 0).
  * OUTER_BLOCK 2D needs rows % obs == 0 and supports obs == 64; 1D supports
  * obs in {16, 32, 64, 128} (others: FP4Q_ERR_UNSUPPORTED).  MXFP4 supports RNE

@@ -419,9 +419,11 @@ static void tile_maxima(const float* vn, int64_t R, int64_t C, float* tmax)
  * contiguous) in the rowwise direction and, if col_codes != NULL, in the
  * columnwise direction (the rowwise layout of X^T, [BSWQ] sections 1-3).
  *
- *  1. x = f32(X), sanitised; with a residual Z: v = RN(x + Z)  ([FP4T] API,
- *     Method: error feedback adds the carried residual into the next
- *     quantisation).
+ *  1. x = f32(X); with a residual Z: v = RN(x + Z)  ([FP4T] API, Method:
+ *     error feedback adds the carried residual into the next quantisation);
+ *     then v is sanitised (NaN -> +0, +-inf -> +-largest bf16), so a NaN x
+ *     gives +0 and an infinite x or an overflowing sum the signed largest
+ *     bf16 whatever the (finite) residual holds.
  *  2. outer groups ([ALTO] Technical design): tensorwise = the whole tensor;
  *     2D = obs x obs tiles shared by both directions; 1D = 1 x obs along the
  *     row for the rowwise direction and obs x 1 along the column for the

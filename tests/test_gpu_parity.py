@@ -404,31 +404,25 @@ def test_cast_transpose_1d_sr_16384x2880_full_size():
 
 
 def test_grouped_sr_ef_32x2880_four_steps():
+    """The grouped workload at full size: all 32 experts, every output buffer
+    (row / column codes and scale bytes, the per-expert 2D outer scales and the
+    in-place residual) at each of the four error-feedback steps, against the
+    oracle run on the whole stacked tensor."""
     E, R, C = 32, 2880, 2880
     w = W.experts_32x2880()
     g = fq.make_cfg(format="nvfp4", two_level="outer_block", outer_block_size=64, outer_2d=True, rounding="stochastic",
                     seed=5)
     zd = torch.zeros((E * R, C), dtype=torch.float32, device="cuda")
-    sample = (0, 13, 31)
-    z_or = {e: np.zeros((R, C), np.float32) for e in sample}
+    z_or = np.zeros((E * R, C), np.float32)
     for t in range(4):
         g.step = t
         out = fq.fp4_cast_transpose_grouped(dev(w), [R] * E, g, residual=zd)
-        rc = host(out["row_codes"], np.uint8).reshape(E, R, C // 2)
-        rs = host(out["row_scales"], np.uint8).reshape(E, R, C // 16)
-        cc = host(out["col_codes"], np.uint8).reshape(E, C, R // 2)
-        cs = host(out["col_scales"], np.uint8).reshape(E, C, R // 16)
-        ro = host(out["row_outer"], np.float32).reshape(E, R // 64, C // 64)
-        zg = host(zd, np.float32).reshape(E, R, C)
-        for e in sample:
-            want = ref.nv_quantize(w[e * R:(e + 1) * R], two_level="outer", obs=64, outer_2d=True, stochastic=True,
-                                   seed=5, step=t, index_base=e * R * C, residual=z_or[e], cols=True, want_y=False)
-            same(rc[e], want["row_codes"], "grouped step %d expert %d row codes" % (t, e))
-            same(rs[e], want["row_scales"], "grouped step %d expert %d row scales" % (t, e))
-            same(cc[e], want["col_codes"], "grouped step %d expert %d col codes" % (t, e))
-            same(cs[e], want["col_scales"], "grouped step %d expert %d col scales" % (t, e))
-            same(ro[e], want["row_outer"], "grouped step %d expert %d outer" % (t, e))
-            same(zg[e], z_or[e], "grouped step %d expert %d residual" % (t, e))
+        want = ref.nv_quantize_grouped(w, [R] * E, two_level="outer", obs=64, outer_2d=True, stochastic=True, seed=5,
+                                       step=t, residual=z_or)
+        for k in ("row_codes", "row_scales", "col_codes", "col_scales"):
+            same(host(out[k], np.uint8).reshape(want[k].shape), want[k], "grouped step %d %s" % (t, k))
+        same(host(out["row_outer"], np.float32).ravel(), want["row_outer"], "grouped step %d outer" % t)
+        same(host(zd, np.float32), z_or, "grouped step %d residual" % t)
         w = W.apply_expert_update(w, W.expert_update(t, w.shape))
 
 
@@ -446,6 +440,8 @@ def test_grouped_uneven_groups_equal_single_calls():
         out = fq.fp4_cast_transpose_grouped(dev(x), rows, g, residual=zd)
         rc = host(out["row_codes"], np.uint8)
         cc = host(out["col_codes"], np.uint8)
+        rsc = host(out["row_scales"], np.uint8)
+        csc = host(out["col_scales"], np.uint8)
         zg = host(zd, np.float32)
         r0 = 0
         co_off = ro_off = 0
@@ -455,6 +451,8 @@ def test_grouped_uneven_groups_equal_single_calls():
                                    index_base=r0 * C, residual=zo, cols=True, want_y=False)
             same(rc[r0:r0 + R], want["row_codes"], "%s group rows %d row codes" % (tl, R))
             same(cc[r0 * C // 2:(r0 + R) * C // 2], want["col_codes"].ravel(), "%s group %d col codes" % (tl, R))
+            same(rsc[r0:r0 + R], want["row_scales"], "%s group rows %d row scales" % (tl, R))
+            same(csc[r0 * C // 16:(r0 + R) * C // 16], want["col_scales"].ravel(), "%s group %d col scales" % (tl, R))
             same(zg[r0:r0 + R], zo, "%s group %d residual" % (tl, R))
             if "row_outer" in want:
                 n = want["row_outer"].size
@@ -465,3 +463,30 @@ def test_grouped_uneven_groups_equal_single_calls():
                 same(host(out["col_outer"], np.float32)[co_off:co_off + n], want["col_outer"].ravel(), "col outer")
                 co_off += n
             r0 += R
+
+
+@pytest.mark.parametrize("tl,obs,o2d", [("outer", 64, True), ("outer", 64, False), ("outer", 16, False)])
+def test_grouped_more_groups_than_one_launch_holds(tl, obs, o2d):
+    """More groups than one launch's group table (64): the call is split into
+    several launches, each with its own tile numbering but global row offsets.
+    SR + error feedback, groups of uneven height (some empty), every buffer
+    against the oracle's grouped quantisation."""
+    rng = np.random.default_rng(13 + obs)
+    step = 64 if (tl == "outer" and o2d) or obs == 64 else 16
+    rows = list(rng.choice([0, step, 2 * step, 3 * step], size=130))
+    C = 128
+    x = rand_bf16(rng, (sum(rows), C), 0.02)
+    z0 = (rng.standard_normal(x.shape) * 0.01).astype(np.float32)
+    g = fq.make_cfg(format="nvfp4", two_level="outer_block", outer_block_size=obs, outer_2d=o2d, rounding="stochastic",
+                    seed=21, step=4, index_base=40)
+    zd = torch.from_numpy(z0.copy()).cuda()
+    out = fq.fp4_cast_transpose_grouped(dev(x), rows, g, residual=zd)
+    zo = z0.copy()
+    want = ref.nv_quantize_grouped(x, rows, two_level=tl, obs=obs, outer_2d=o2d, stochastic=True, seed=21, step=4,
+                                   index_base=40, residual=zo)
+    for k in ("row_codes", "row_scales", "col_codes", "col_scales"):
+        same(host(out[k], np.uint8).reshape(want[k].shape), want[k], "%d groups %s" % (len(rows), k))
+    same(host(out["row_outer"], np.float32).ravel(), want["row_outer"], "row outer")
+    if not o2d:
+        same(host(out["col_outer"], np.float32).ravel(), want["col_outer"], "col outer")
+    same(host(zd, np.float32), zo, "residual")

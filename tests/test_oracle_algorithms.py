@@ -96,6 +96,66 @@ def test_nv_edge_values_match_exact_model():
             _compare(c_out, e_out, KEYS)
 
 
+NONFINITE_MODES = [
+    # (scale_fmt, two_level, obs, outer_2d, stochastic)
+    ("e4m3", "none", 0, False, False),
+    ("e4m3", "none", 0, False, True),
+    ("e4m3", "tensorwise", 0, False, False),
+    ("ue5m3", "tensorwise", 0, False, True),
+    ("e4m3", "outer", 16, True, True),
+    ("e4m3", "outer", 16, False, False),
+    ("ue5m3", "outer", 32, False, True),
+]
+
+
+@pytest.mark.parametrize("mode", NONFINITE_MODES, ids=lambda m: "-".join(str(v) for v in m))
+def test_nonfinite_and_overflowing_sums_with_residual_match_exact_model(mode):
+    """Sanitisation with error feedback ("NaN-input sanitization", ALTO page,
+    Op-level test coverage; error feedback, fp4-train README, Method): the
+    value quantised is the sum v = x + r, and the rule NaN -> +0, +-inf ->
+    +-largest bf16 applies to that sum.  So a NaN x gives v = +0 whatever the
+    residual, an infinite x gives the signed largest bf16, and a finite x whose
+    sum with r overflows binary32 gives the signed largest bf16 as well.  The
+    C oracle and the exact-rational model must agree on every output, the
+    residual included, and on these closed forms."""
+    sfmt, tl, obs, o2d, sr = mode
+    rng = np.random.default_rng(zlib.crc32(repr(mode).encode()))
+    R, C = 32, 64
+    xb = _rand_bf16(rng, (R, C), 0.5)
+    z = (rng.standard_normal((R, C)) * 0.05).astype(np.float32)
+    big = bf16([3.0e38])[0]                                   # 0x7F62: |x + z| overflows for z ~ +-5e37
+    n = R * C
+    pos = rng.permutation(n)
+    nan_at, pinf_at, ninf_at, ovf_at, nov_at, max_at = np.split(pos[:6 * 24], 6)
+    xb.ravel()[nan_at] = rng.choice(np.array([0x7FC0, 0xFFC0, 0x7F81, 0xFFFF], np.uint16), nan_at.size)
+    xb.ravel()[pinf_at] = 0x7F80
+    xb.ravel()[ninf_at] = 0xFF80
+    xb.ravel()[ovf_at] = big
+    z.ravel()[ovf_at] = np.float32(9.0e37)                     # 3e38 + 9e37 > FLT_MAX: +overflow
+    xb.ravel()[nov_at] = big | np.uint16(0x8000)
+    z.ravel()[nov_at] = np.float32(-9.0e37)                    # -overflow
+    xb.ravel()[max_at] = 0x7F7F                                # bf16max + a small residual stays finite
+    z.ravel()[np.concatenate([nan_at, pinf_at, ninf_at])] = (rng.standard_normal(72) * 7.0).astype(np.float32)
+    kw = dict(scale_fmt=sfmt, two_level=tl, obs=obs, outer_2d=o2d, stochastic=sr, seed=3, step=5, index_base=11)
+    res_c = z.copy()
+    c_out = ref.nv_quantize(xb, residual=res_c, cols=True, **kw)
+    u = ref.sr_u16_array(3, 5, 11, n).reshape(R, C) if sr else None
+    e_out = exact.nv_quantize(xb, scale_fmt=sfmt, two_level=tl, obs=obs, outer_2d=o2d, stochastic=sr, u16=u,
+                              residual=z, cols=True)
+    _compare(c_out, e_out, KEYS)
+    np.testing.assert_array_equal(res_c.view(np.uint32), e_out["residual"].view(np.uint32))
+    # closed forms: a NaN x is quantised as +0 (positive zero code, residual +0 - 0 = +0)
+    codes = c_out["row_codes"].ravel()
+    nib = lambda e: (codes[e // 2] >> (4 * (e % 2))) & 0xF  # noqa: E731
+    assert all(nib(e) == 0 for e in nan_at)
+    assert np.all(res_c.ravel()[nan_at].view(np.uint32) == 0)
+    # an infinite or overflowing sum is the signed largest bf16, which saturates its block's codes
+    for at, sign in ((pinf_at, 0), (ninf_at, 8), (ovf_at, 0), (nov_at, 8)):
+        assert all(nib(e) == (sign | 7) for e in at)
+        w = f32(c_out["row_y"]).ravel()[at]
+        assert np.all(np.isfinite(w)) and np.all(np.sign(w) == (1 if sign == 0 else -1))
+
+
 # ---------------------------------------------------------------- printed SR / EF values
 def _scale_one_block_inputs(n_blocks):
     """Blocks [6.0, 2.0 x 15] with a residual of 0.3f on the 2.0 entries, so the
