@@ -16,7 +16,7 @@ __all__ = [
     "Fp4Error", "Cfg", "Sizes", "make_cfg", "lib", "fp4q_abi_version", "fp4q_status_str", "fp4q_buffer_sizes",
     "fp4q_workspace_bytes", "fp4_quantize", "fp4_dequantize", "fp4_qdq", "fp4_cast_transpose",
     "fp4_cast_transpose_grouped", "fp4_mx_project_fp8", "fp4_mm", "fp4_mx_scales_tiled",
-    "fp4q_mx_scales_tiled_bytes", "ErrorFeedback", "LIB_PATH",
+    "fp4q_mx_scales_tiled_bytes", "fp4_qdq_noalloc", "ErrorFeedback", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp4q.so")
@@ -103,6 +103,8 @@ def lib():
         L.fp4_dequantize.argtypes = [C, P, P, P, I64, I64, ct.c_int32, P, P]
         L.fp4_qdq.restype = ct.c_int
         L.fp4_qdq.argtypes = [C, P, I64, I64, I64, P, P, P, P, P, P, SZ, P]
+        L.fp4_qdq_noalloc.restype = ct.c_int
+        L.fp4_qdq_noalloc.argtypes = [C, P, I64, I64, I64, P, P, P, P, P, P]
         L.fp4_cast_transpose.restype = ct.c_int
         L.fp4_cast_transpose.argtypes = [C, P, I64, I64, I64, P, P, P, P, P, P, P, P, SZ, P]
         L.fp4_cast_transpose_grouped.restype = ct.c_int
@@ -284,6 +286,24 @@ def fp4_qdq(x, cfg, *, residual=None, outer=None, with_codes=False, workspace=No
     ws, wsb = _workspace(cfg, R, C, dev, workspace)
     _check(lib().fp4_qdq(ct.byref(cfg), _ptr(x), R, C, ld, _ptr(y), _ptr(codes), _ptr(scales), _ptr(outer),
                          _ptr(residual), _ptr(ws), wsb, _stream(stream)), "fp4_qdq")
+    return {"y": y, "codes": codes, "scales": scales, "outer": outer}
+
+
+def fp4_qdq_noalloc(x, cfg, *, y, codes=None, scales=None, outer=None, residual=None, stream=None):
+    """fp4_qdq without a workspace (the library's own per-GPU scratch), for
+    callers that cannot allocate: every output tensor is passed in (y, and
+    optionally codes, scales and outer), nothing is allocated here.  Calls that
+    overlap on one GPU race.  Returns {"y", "codes", "scales", "outer"}."""
+    x, R, C, ld = _src(x, allow_f32=True)
+    cfg = _with_dtypes(cfg, _dtype_name(x), _dtype_name(y))
+    sizes = fp4q_buffer_sizes(cfg, R, C)
+    _need(y, sizes["y"], "y")
+    _need(codes, sizes["row_codes"], "codes")
+    _need(scales, sizes["row_scales"], "scales")
+    _need(outer, sizes["row_outer"], "outer")
+    _need_residual(residual, R, C)
+    _check(lib().fp4_qdq_noalloc(ct.byref(cfg), _ptr(x), R, C, ld, _ptr(y), _ptr(codes), _ptr(scales), _ptr(outer),
+                                 _ptr(residual), _stream(stream)), "fp4_qdq_noalloc")
     return {"y": y, "codes": codes, "scales": scales, "outer": outer}
 
 

@@ -234,6 +234,22 @@ int fp4_qdq(const fp4q_cfg* cfg, const void* x, int64_t rows, int64_t cols, int6
             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * fp4_qdq_noalloc -- fp4_qdq for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Same arguments, results and errors as fp4_qdq, without the
+ * workspace: the scratch fp4_qdq would take from it (the tensorwise mode's
+ * partial maxima and global scale, fp4q_workspace_bytes() bytes) is a 4 KiB
+ * device array inside the library, one per GPU, held until the process ends.
+ * A configuration needing more scratch than that returns FP4Q_ERR_WORKSPACE
+ * (none does today).  The library looks up the array's device address once
+ * per device, on the first call made with that device current; it calls no
+ * allocator.  All calls on one GPU share that GPU's array: calls that overlap
+ * in time on one GPU (concurrent streams) race and give undefined results.
+ */
+int fp4_qdq_noalloc(const fp4q_cfg* cfg, const void* x, int64_t rows, int64_t cols, int64_t ld_x,
+                    void* y, uint8_t* codes, uint8_t* scales, float* outer, float* residual, void* stream);
+
+/*
  * fp4_cast_transpose -- one read of x writes the rowwise buffers and the
  * columnwise buffers (the rowwise layout of X^T) ("Block-Scaled FP8 and FP4
  * Weight Quantization", sections 2-3: fused cast-transpose; ALTO page,
