@@ -34,6 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+STAGED = os.environ.get("FP4Q_BENCH_DIRECT", "0") != "1"   # direct-store path for comparison
 FP4_MFMA_PEAK_TFLOPS = 10100.0   # MI355X dense FP4 / FP6 matrix peak
 METRIC = "quantize GB/s (HBM bytes read+written) and fraction of MI355X HBM peak"
 
@@ -340,12 +341,14 @@ def make_cast_transpose_1d_sr(torch, fq, W):
                          cs=torch.empty(R * C // 16, dtype=torch.uint8, device="cuda"),
                          ro=torch.empty(R * (C // 64), dtype=torch.float32, device="cuda"),
                          co=torch.empty(C * (R // 64), dtype=torch.float32, device="cuda")))
+    wsb = fq.fp4q_cast_transpose_workspace_bytes(cfg, [R], C) if STAGED else 0
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
     L = fq.lib()
 
     def launch(s):
         st = L.fp4_cast_transpose(ct.byref(cfg), s["x"].data_ptr(), R, C, C, s["rc"].data_ptr(), s["rs"].data_ptr(),
                                   s["ro"].data_ptr(), s["cc"].data_ptr(), s["cs"].data_ptr(), s["co"].data_ptr(), None,
-                                  None, 0, torch.cuda.current_stream().cuda_stream)
+                                  ws.data_ptr(), wsb, torch.cuda.current_stream().cuda_stream)
         if st:
             raise fq.Fp4Error(st, "fp4_cast_transpose")
     return Timed("amd_1d_sr_cast_transpose_16384x2880", "AMD-FP4 1D 1x64 outer, UE5M3/16, SR, cast-transpose 16384x2880 bf16", alg, sets, launch,
@@ -364,12 +367,15 @@ def make_grouped_sr_ef(torch, fq, W):
              cc=torch.empty(n // 2, dtype=torch.uint8, device="cuda"), cs=torch.empty(n // 16, dtype=torch.uint8, device="cuda"),
              ro=torch.empty(E * (R // 64) * (C // 64), dtype=torch.float32, device="cuda"))
     rows = (ct.c_int64 * E)(*([R] * E))
+    wsb = fq.fp4q_cast_transpose_workspace_bytes(cfg, [R] * E, C, with_residual=True) if STAGED else 0
+    s["ws"] = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
     L = fq.lib()
 
     def launch(s):
         st = L.fp4_cast_transpose_grouped(ct.byref(cfg), E, rows, C, s["x"].data_ptr(), C, s["rc"].data_ptr(),
                                           s["rs"].data_ptr(), s["ro"].data_ptr(), s["cc"].data_ptr(), s["cs"].data_ptr(),
-                                          None, s["z"].data_ptr(), None, 0, torch.cuda.current_stream().cuda_stream)
+                                          None, s["z"].data_ptr(), s["ws"].data_ptr(), wsb,
+                                          torch.cuda.current_stream().cuda_stream)
         if st:
             raise fq.Fp4Error(st, "fp4_cast_transpose_grouped")
     # the working set (~3 GB per step) is far beyond the last-level cache: one set

@@ -14,7 +14,7 @@ import os
 
 __all__ = [
     "Fp4Error", "Cfg", "Sizes", "make_cfg", "lib", "fp4q_abi_version", "fp4q_status_str", "fp4q_buffer_sizes",
-    "fp4q_workspace_bytes", "fp4_quantize", "fp4_dequantize", "fp4_qdq", "fp4_cast_transpose",
+    "fp4q_workspace_bytes", "fp4q_cast_transpose_workspace_bytes", "fp4_quantize", "fp4_dequantize", "fp4_qdq", "fp4_cast_transpose",
     "fp4_cast_transpose_grouped", "fp4_mx_project_fp8", "fp4_mm", "fp4_mx_scales_tiled",
     "fp4q_mx_scales_tiled_bytes", "fp4_qdq_noalloc", "ErrorFeedback", "LIB_PATH",
 ]
@@ -97,6 +97,8 @@ def lib():
         L.fp4q_buffer_sizes.argtypes = [C, I64, I64, ct.POINTER(Sizes)]
         L.fp4q_workspace_bytes.restype = SZ
         L.fp4q_workspace_bytes.argtypes = [C, I64, I64]
+        L.fp4q_cast_transpose_workspace_bytes.restype = SZ
+        L.fp4q_cast_transpose_workspace_bytes.argtypes = [C, ct.c_int32, P, I64, ct.c_int32]
         L.fp4_quantize.restype = ct.c_int
         L.fp4_quantize.argtypes = [C, P, I64, I64, I64, P, P, P, P, P, SZ, P]
         L.fp4_dequantize.restype = ct.c_int
@@ -141,6 +143,27 @@ def fp4q_buffer_sizes(cfg, rows, cols):
 
 def fp4q_workspace_bytes(cfg, rows, cols):
     return lib().fp4q_workspace_bytes(ct.byref(cfg), int(rows), int(cols))
+
+
+def fp4q_cast_transpose_workspace_bytes(cfg, rows_per_group, cols, with_residual=False):
+    """Workspace that lets the cast-transpose stage its outputs (see
+    include/fp4q.h); rows_per_group is a list of row counts (one entry for a
+    single tensor)."""
+    rows = [int(r) for r in rows_per_group]
+    arr = (ct.c_int64 * max(len(rows), 1))(*rows)
+    return lib().fp4q_cast_transpose_workspace_bytes(ct.byref(cfg), len(rows), arr, int(cols), int(bool(with_residual)))
+
+
+def _ct_workspace(cfg, rows, cols, residual, device, workspace, staged):
+    """(workspace, bytes) for a cast-transpose call: the caller's, or one
+    sized for staged outputs (staged=True) or for the tensorwise scratch only."""
+    if workspace is not None:
+        return workspace, workspace.numel() * workspace.element_size()
+    nb = fp4q_cast_transpose_workspace_bytes(cfg, rows, cols, residual is not None) if staged else \
+        fp4q_workspace_bytes(cfg, sum(rows), cols)
+    if nb == 0:
+        return None, 0
+    return _empty(nb, _torch().uint8, device), nb
 
 
 # ------------------------------------------------------------------ marshalling helpers
@@ -327,10 +350,12 @@ def fp4_dequantize(codes, scales, outer, rows, cols, cfg, *, outer_transposed=Fa
 
 
 def fp4_cast_transpose(x, cfg, *, residual=None, row_outer=None, col_outer=None, workspace=None, stream=None,
-                       out=None):
+                       out=None, staged=True):
     """Rowwise and columnwise buffers from one read of x.  Returns
     {"row_codes", "row_scales", "row_outer", "col_codes", "col_scales", "col_outer"}.
-    `out` may supply any of the four code / scale tensors preallocated."""
+    `out` may supply any of the four code / scale tensors preallocated.
+    Without a `workspace`, one is allocated: large enough to stage the outputs
+    (staged=True) or only for the tensorwise scratch (staged=False)."""
     torch = _torch()
     x, R, C, ld = _src(x)
     dev = x.device
@@ -355,16 +380,18 @@ def fp4_cast_transpose(x, cfg, *, residual=None, row_outer=None, col_outer=None,
     _need(row_outer, sizes["row_outer"], "row_outer")
     _need(col_outer, sizes["col_outer"], "col_outer")
     _need_residual(residual, R, C)
-    ws, wsb = _workspace(cfg, R, C, dev, workspace)
+    ws, wsb = _ct_workspace(cfg, [R], C, residual, dev, workspace, staged)
     _check(lib().fp4_cast_transpose(ct.byref(cfg), _ptr(x), R, C, ld, _ptr(out["row_codes"]), _ptr(out["row_scales"]),
                                     _ptr(row_outer), _ptr(out["col_codes"]), _ptr(out["col_scales"]), _ptr(col_outer),
                                     _ptr(residual), _ptr(ws), wsb, _stream(stream)), "fp4_cast_transpose")
     return out
 
 
-def fp4_cast_transpose_grouped(x, rows_per_group, cfg, *, residual=None, stream=None, out=None):
+def fp4_cast_transpose_grouped(x, rows_per_group, cfg, *, residual=None, stream=None, out=None, workspace=None,
+                               staged=True):
     """Per-group cast-transpose of groups stacked along rows (one launch per 64
-    groups).  Returns flat stacked buffers (see include/fp4q.h)."""
+    groups).  Returns flat stacked buffers (see include/fp4q.h).  `workspace`
+    and `staged` as for fp4_cast_transpose."""
     torch = _torch()
     x, total, C, ld = _src(x)
     dev = x.device
@@ -390,10 +417,11 @@ def fp4_cast_transpose_grouped(x, rows_per_group, cfg, *, residual=None, stream=
         _need(out.get(k), n, k)
     _need_residual(residual, total, C)
     arr = (ct.c_int64 * max(len(rows), 1))(*rows)
+    ws, wsb = _ct_workspace(cfg, rows, C, residual, dev, workspace, staged)
     _check(lib().fp4_cast_transpose_grouped(ct.byref(cfg), len(rows), arr, C, _ptr(x), ld, _ptr(out["row_codes"]),
                                             _ptr(out["row_scales"]), _ptr(out["row_outer"]), _ptr(out["col_codes"]),
-                                            _ptr(out["col_scales"]), _ptr(out["col_outer"]), _ptr(residual), None, 0,
-                                            _stream(stream)), "fp4_cast_transpose_grouped")
+                                            _ptr(out["col_scales"]), _ptr(out["col_outer"]), _ptr(residual), _ptr(ws),
+                                            wsb, _stream(stream)), "fp4_cast_transpose_grouped")
     return out
 
 

@@ -138,6 +138,94 @@ size_t ws_bytes_for(const Resolved& r)
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FP4Q_OK : FP4Q_ERR_HIP; }
 
+// Cast-transpose workspace: [0, partial) the tensorwise partial maxima (when
+// the scale is computed), then, 128-byte aligned, the staged tile blocks of
+// the largest launch (groups go 64 to a launch; launches run in stream order
+// and reuse the region).
+constexpr size_t kPartialRegion = 4096;
+constexpr size_t kStageAlign = 128;
+
+size_t partial_bytes_for(const Resolved& r)
+{
+    return (r.outer_kind == kOuterTensor && !r.given) ? kPartialRegion : 0;
+}
+
+size_t stage_bytes_for(const Resolved& r, int32_t ngroups, const int64_t* rows, int64_t cols)
+{
+    const int64_t tc = (cols + 63) / 64;
+    const int64_t blk = stage_block_bytes(r.outer_kind, r.obs);
+    size_t most = 0;
+    for (int32_t g0 = 0; g0 < ngroups; g0 += kMaxGroupsPerLaunch) {
+        size_t sum = 0;
+        for (int32_t g = g0; g < ngroups && g < g0 + kMaxGroupsPerLaunch; ++g)
+            sum += (size_t)(((rows[g] + 63) / 64) * tc * blk);
+        most = std::max(most, sum);
+    }
+    return most;
+}
+
+size_t ct_workspace_bytes(const Resolved& r, bool ef, int32_t ngroups, const int64_t* rows, int64_t cols)
+{
+    size_t n = partial_bytes_for(r);
+    if (stage_applies(r.sr, ef, r.outer_kind, r.inner2d) && r.obs <= 64) {
+        const size_t st = stage_bytes_for(r, ngroups, rows, cols);
+        if (st) n += st + kStageAlign;
+    }
+    return n;
+}
+
+// The staged region of a workspace large enough for staging, else null.
+uint8_t* stage_region(const Resolved& r, bool ef, int32_t ngroups, const int64_t* rows, int64_t cols, void* ws,
+                      size_t ws_bytes)
+{
+    if (!ws || !stage_applies(r.sr, ef, r.outer_kind, r.inner2d) || r.obs > 64) return nullptr;
+    const size_t st = stage_bytes_for(r, ngroups, rows, cols);
+    if (st == 0 || ws_bytes < partial_bytes_for(r) + st + kStageAlign) return nullptr;
+    const uintptr_t p = reinterpret_cast<uintptr_t>(ws) + partial_bytes_for(r);
+    return reinterpret_cast<uint8_t*>((p + kStageAlign - 1) & ~(uintptr_t)(kStageAlign - 1));
+}
+
+// Switch a tile launch to the staged walk (one tile per unit) over its groups.
+void use_stage(TileArgs& a, const Resolved& r, uint8_t* stage)
+{
+    a.stage = stage;
+    a.stage_block = stage_block_bytes(r.outer_kind, r.obs);
+    a.tiles_c = (int32_t)((a.cols + 63) / 64);
+    for (int g = 0; g < a.ngroups; ++g) {
+        const int32_t R = a.row0[g + 1] - a.row0[g];
+        a.tile0[g + 1] = a.tile0[g] + ((R + 63) / 64) * a.tiles_c;
+    }
+    a.total_tiles = a.tile0[a.ngroups];
+    set_tile_grid(a.total_tiles, a.per_xcd, a.wgs_per_xcd);
+}
+
+// The gather pass for a staged tile launch.
+hipError_t gather_staged(const TileArgs& a, const Resolved& r, hipStream_t s)
+{
+    GatherArgs gth;
+    std::memset(&gth, 0, sizeof(gth));
+    gth.stage = a.stage;
+    gth.stage_block = a.stage_block;
+    gth.ngroups = a.ngroups;
+    gth.cols = a.cols;
+    gth.tiles_c = a.tiles_c;
+    gth.obs = (r.outer_kind == kOuter1D && !r.given) ? r.obs : 0;
+    bool s4 = a.cols % 64 == 0 && !misaligned(a.row_scales, 4) && !misaligned(a.col_scales, 4);
+    for (int g = 0; g <= a.ngroups; ++g) {
+        gth.row0[g] = a.row0[g];
+        gth.tile0[g] = a.tile0[g];
+        if (g < a.ngroups && (a.row0[g + 1] - a.row0[g]) % 64) s4 = false;
+    }
+    gth.scales4 = s4 ? 1 : 0;
+    gth.row_codes = a.row_codes;
+    gth.row_scales = a.row_scales;
+    gth.row_outer = gth.obs ? a.row_outer : nullptr;
+    gth.col_codes = a.col_codes;
+    gth.col_scales = a.col_scales;
+    gth.col_outer = gth.obs ? a.col_outer : nullptr;
+    return launch_gather(gth, s);
+}
+
 TileArgs tile_args_single(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld)
 {
     TileArgs a;
@@ -378,7 +466,7 @@ int fp4_cast_transpose(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int
     if (r.outer_kind == kOuter1D && r.obs != 16 && r.obs != 32 && r.obs != 64) return FP4Q_ERR_UNSUPPORTED;
     if ((r.outer_kind == kOuter2D || r.outer_kind == kOuterTensor) && col_outer && col_outer != row_outer)
         return FP4Q_ERR_MODE;
-    const size_t need_ws = ws_bytes_for(r);
+    const size_t need_ws = partial_bytes_for(r) ? ws_bytes_for(r) : 0;
     const bool empty = rows == 0 || cols == 0;
     if (!empty) {
         if (!x || !row_codes || !row_scales || !col_codes || !col_scales) return FP4Q_ERR_NULL;
@@ -406,6 +494,8 @@ int fp4_cast_transpose(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int
     a.obs16 = r.obs ? r.obs / 16 : 1;
     a.outer_given = r.given;
     a.inner_2d = r.inner2d ? 1 : 0;
+    uint8_t* stage = stage_region(r, residual != nullptr, 1, &rows, cols, workspace, workspace_bytes);
+    if (stage) use_stage(a, r, stage);
     if (r.outer_kind == kOuterTensor) {
         if (r.given) {
             a.tensor_scale = row_outer;
@@ -417,7 +507,9 @@ int fp4_cast_transpose(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int
             a.tensor_scale = wsf;
         }
     }
-    return hip_status(launch_tiles(r.bias, r.outer_kind, r.sr, a, s));
+    st = hip_status(launch_tiles(r.bias, r.outer_kind, r.sr, a, s));
+    if (st || !stage) return st;
+    return hip_status(gather_staged(a, r, s));
 }
 
 int fp4_mx_project_fp8(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
@@ -519,8 +611,6 @@ int fp4_cast_transpose_grouped(const fp4q_cfg* cfg, int32_t groups, const int64_
                                float* row_outer, uint8_t* col_codes, uint8_t* col_scales, float* col_outer,
                                float* residual, void* workspace, size_t workspace_bytes, void* stream)
 {
-    (void)workspace;
-    (void)workspace_bytes;
     Resolved r;
     int st = resolve(cfg, r);
     if (st) return st;
@@ -551,6 +641,7 @@ int fp4_cast_transpose_grouped(const fp4q_cfg* cfg, int32_t groups, const int64_
         return FP4Q_ERR_ALIGN;
     hipStream_t s = (hipStream_t)stream;
     const int32_t tiles_c = (int32_t)((cols + 127) / 128);
+    uint8_t* stage = stage_region(r, residual != nullptr, groups, rows_per_group, cols, workspace, workspace_bytes);
     int64_t row_before = 0;
     for (int32_t g0 = 0; g0 < groups; g0 += kMaxGroupsPerLaunch) {
         const int32_t ng = std::min<int32_t>(kMaxGroupsPerLaunch, groups - g0);
@@ -589,10 +680,26 @@ int fp4_cast_transpose_grouped(const fp4q_cfg* cfg, int32_t groups, const int64_
         set_tile_grid(tt, a.per_xcd, a.wgs_per_xcd);
         row_before = rr;
         if (tt == 0) continue;
+        if (stage) use_stage(a, r, stage);
         st = hip_status(launch_tiles(r.bias, r.outer_kind, r.sr, a, s));
         if (st) return st;
+        if (stage) {
+            st = hip_status(gather_staged(a, r, s));
+            if (st) return st;
+        }
     }
     return FP4Q_OK;
+}
+
+size_t fp4q_cast_transpose_workspace_bytes(const fp4q_cfg* cfg, int32_t groups, const int64_t* rows_per_group,
+                                           int64_t cols, int32_t with_residual)
+{
+    Resolved r;
+    if (resolve(cfg, r) || r.fmt == FP4Q_MXFP4 || groups < 0 || cols < 0 || (groups > 0 && !rows_per_group))
+        return 0;
+    for (int32_t g = 0; g < groups; ++g)
+        if (rows_per_group[g] < 0) return 0;
+    return ct_workspace_bytes(r, with_residual != 0, groups, rows_per_group, cols);
 }
 
 }  // extern "C"

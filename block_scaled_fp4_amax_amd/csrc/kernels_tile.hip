@@ -190,6 +190,25 @@ __device__ __forceinline__ Tile make_tile(const TileArgs& a, const TileWalk& w, 
     return t;
 }
 
+// The tile of a walk whose unit is one tile (staged output).
+__device__ __forceinline__ Tile make_tile_unit(const TileArgs& a, const TileWalk& w)
+{
+    Tile t;
+    t.g = w.g;
+    t.r0 = w.r0;
+    t.ti = w.si;
+    t.tj = w.sj;
+    t.Rg = w.Rg;
+    t.lrow0 = t.ti * kTile;
+    t.grow0 = w.r0 + t.lrow0;
+    t.c0 = t.tj * kTile;
+    t.rows_valid = max(0, min(kTile, t.Rg - t.lrow0));
+    t.cols_valid = max(0, min(kTile, (int)a.cols - t.c0));
+    t.e_base = (int64_t)t.grow0 * a.cols + t.c0;
+    t.ce_base = (int64_t)w.r0 * a.cols + (int64_t)t.c0 * t.Rg + t.lrow0;
+    return t;
+}
+
 // The lane's raw inputs for one tile: 16 bf16 (two 16-byte loads) and, with
 // error feedback, the 16 FP32 residuals.  Lanes outside the tensor (and every
 // lane when `valid` is false) read zeros.
@@ -296,11 +315,15 @@ constexpr int tile_waves_per_simd()
 // normal binary32 and the reciprocal-product division needs no re-check.
 constexpr float kNoSubnormalScale = 0x1p-7f;
 
+// Largest staged tail: scale bytes (2 x 256) and 1D outer scales of 16-element
+// groups (2 x 1024).
+constexpr int kTailMax = kStageRowOuter - kStageTail + 2 * 64 * 4 * 4;
+
 // Every global access is a buffer instruction whose masked lanes carry an
 // out-of-range offset, and every tile iteration issues the same sequence of
 // memory instructions with no branch around any of them, so the compiler's
 // wait for the next tile's loads never waits for earlier stores.
-template <int BIAS, int OUTER, bool SR, bool COLS, bool EF, bool GIVEN, bool Y, bool I2D>
+template <int BIAS, int OUTER, bool SR, bool COLS, bool EF, bool GIVEN, bool Y, bool I2D, bool STAGED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(tile_waves_per_simd<BIAS, OUTER, SR, COLS, EF, I2D>())))
 void k_tile(TileArgs a)
 {
@@ -310,7 +333,11 @@ void k_tile(TileArgs a)
     __shared__ uint32_t red[2][kThreads / 64];
     __shared__ double rtab[kRecipTableSize];
     __shared__ float2 ktab[SR ? 1 : kRneTableSize];
-    __shared__ PairStage stage;
+    __shared__ PairStage stage[1];
+    // staged output: the tail of each tile's block (scale bytes and 1D outer
+    // scales) gathered here, one buffer per tile parity, and written by the
+    // workgroup as whole lines once every wave has finished the tile
+    __shared__ uint4 tail[STAGED ? 2 * kTailMax / 16 : 1];
 
     const int tid = (int)threadIdx.x;
     const int r = tid >> 2, sg = tid & 3;       // row phase: row, 16-column segment
@@ -327,7 +354,7 @@ void k_tile(TileArgs a)
     walk.dj = W - walk.di * a.tiles_c;
     walk_locate(a, walk);
     TileInput<EF> in;
-    load_tile_input<EF>(a, make_tile(a, walk, 0), true, r, sg, in);
+    load_tile_input<EF>(a, STAGED ? make_tile_unit(a, walk) : make_tile(a, walk, 0), true, r, sg, in);
     fill_recip_table(rtab, tid);
     if (!SR) fill_rne_table<BIAS>(ktab, tid);
     lds_barrier();
@@ -352,6 +379,20 @@ void k_tile(TileArgs a)
     wait_vmem_all();
 
     int iter = 0;   // tiles processed (parity of the reduction slots)
+
+    // staged output: the block of the previous tile, whose tail is written
+    // once every wave is past the current tile's first barrier
+    const uint8_t* prev_blk = nullptr;
+    bool prev_ok = false;
+    uint8_t* const tail8 = reinterpret_cast<uint8_t*>(tail);
+    float* const tailf = reinterpret_cast<float*>(tail);
+    const int opr = 4 / a.obs16;                                   // 1D outer groups per tile row
+    const int tail_bytes = (kStageRowOuter - kStageTail) + (OUTER == kOuter1D ? 2 * 64 * opr * 4 : 0);
+    auto emit_tail = [&](int par) {
+        const int n16 = tail_bytes / 16;
+        const uint4 v = tail[par * (kTailMax / 16) + min(tid, n16 - 1)];
+        buf_store16(make_rsrc(prev_blk), (prev_ok && tid < n16) ? (uint32_t)(kStageTail + 16 * tid) : kOff, v);
+    };
 
     // One tile: row phase, LDS transpose, column phase.  Writes the dequantised
     // output, the residual and 2D outer scales itself; returns the codes, scale
@@ -453,6 +494,12 @@ void k_tile(TileArgs a)
             const uint2 packed = quant16<BIAS, SR, I2D, OUTER == kOuterNone>(vn, u, rtab, ktab, sc);
             ro.codes = packed;
             ro.scale = sc.code;
+            if (STAGED) {
+                const int par = iter & 1;
+                tail8[par * kTailMax + r * 4 + sg] = (uint8_t)sc.code;
+                if (OUTER == kOuter1D && !GIVEN && (sg % a.obs16) == 0)
+                    tailf[par * (kTailMax / 4) + 128 + r * opr + sg / a.obs16] = ro.outer;
+            }
             if (EF || Y) {
                 float w[16];
                 decode16(packed, sc.d, w);
@@ -485,6 +532,7 @@ void k_tile(TileArgs a)
         if (COLS) {
             // ---------------- stage through LDS
             if (!barrier_done) lds_barrier();   // previous tile's column reads are done
+            if (STAGED) emit_tail((iter & 1) ^ 1);
             const float* src = (OUTER == kOuter1D) ? v : vn;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
@@ -552,6 +600,12 @@ void k_tile(TileArgs a)
                 co.codes = quant16<BIAS, SR, false, OUTER == kOuterNone>(cv, cu, rtab, ktab, sc);
                 co.scale = sc.code;
             }
+            if (STAGED) {
+                const int par = iter & 1;
+                tail8[par * kTailMax + 256 + cc * 4 + rs] = (uint8_t)co.scale;
+                if (OUTER == kOuter1D && !GIVEN && (rs % a.obs16) == 0)
+                    tailf[par * (kTailMax / 4) + 128 + 64 * opr + cc * opr + rs / a.obs16] = co.outer;
+            }
         }
         ++iter;
     };
@@ -575,7 +629,7 @@ void k_tile(TileArgs a)
         const bool line_ok = enable && r < ta.rows_valid;
         const rsrc_t rc = make_rsrc(a.row_codes ? a.row_codes + ta.e_base / 2 : nullptr);
         const rsrc_t rsc = make_rsrc(a.row_scales ? a.row_scales + ta.e_base / 16 : nullptr);
-        store_pair(stage, r, sg, A, B, line_ok, nvalid, rc, (uint32_t)(r * cols) / 2u, rsc,
+        store_pair(stage[0], r, sg, A, B, line_ok, nvalid, rc, (uint32_t)(r * cols) / 2u, rsc,
                    (uint32_t)(r * cols) / 16u);
         if (OUTER == kOuter1D && !GIVEN) {
             const int gpr = cols / obs;
@@ -592,7 +646,7 @@ void k_tile(TileArgs a)
         const int nvalid = ta.rows_valid / 16 + tb.rows_valid / 16;
         const bool line_ok = enable && cc < ta.cols_valid;
         const uint32_t ecol = (uint32_t)(cc * ta.Rg);   // lane's column, relative to the run start
-        store_pair(stage, cc, rs, A, B, line_ok, nvalid, make_rsrc(a.col_codes + ta.ce_base / 2), ecol / 2u,
+        store_pair(stage[0], cc, rs, A, B, line_ok, nvalid, make_rsrc(a.col_codes + ta.ce_base / 2), ecol / 2u,
                    make_rsrc(a.col_scales + ta.ce_base / 16), ecol / 16u);
         if (OUTER == kOuter1D && !GIVEN) {
             const int gpc = ta.Rg / obs;
@@ -637,7 +691,33 @@ void k_tile(TileArgs a)
     };
 
     TileWalk st = walk;
-    if constexpr (tile_unrolled<OUTER, SR, EF>()) {
+    if constexpr (STAGED) {
+        // One tile per iteration in row-major tile order; codes go to the
+        // tile's block as whole lines (a wave's 64 lanes write 512 contiguous
+        // bytes), the tail through LDS (emit_tail).
+        for (;;) {
+            const Tile cur = make_tile_unit(a, st);
+            const bool has_next = st.t + W < slice_end;
+            TileWalk nst = st;
+            if (has_next) walk_next(a, nst, W);
+            TileInput<EF> nin;
+            load_tile_input<EF>(a, make_tile_unit(a, nst), has_next, r, sg, nin);
+            DirOut ro, co;
+            tile_body(cur, in, ro, co);
+            const bool ok = cur.rows_valid > 0 && cur.cols_valid > 0;
+            const uint8_t* blk = a.stage + (int64_t)st.t * a.stage_block;
+            const rsrc_t rb = make_rsrc(blk);
+            buf_store8(rb, ok ? (uint32_t)(r * 32 + sg * 8) : kOff, ro.codes);
+            buf_store8(rb, ok ? (uint32_t)(kStageColCodes + cc * 32 + rs * 8) : kOff, co.codes);
+            prev_blk = blk;
+            prev_ok = ok;
+            if (!has_next) break;
+            st = nst;
+            in = nin;
+        }
+        lds_barrier();
+        emit_tail((iter & 1) ^ 1);
+    } else if constexpr (tile_unrolled<OUTER, SR, EF>()) {
         // RTNE: the four tiles of a super-tile as straight-line code; the row
         // runs of tiles (0, 1) and (2, 3) are stored after tiles 1 and 3, the
         // column runs of tiles (0, 2) and (1, 3) after tiles 2 and 3.
@@ -771,21 +851,30 @@ hipError_t pick_given_y(const TileArgs& a, hipStream_t s)
 {
     const bool given = a.outer_given != 0;
     const bool y = a.y != nullptr;
+    if constexpr (C && !I && !tile_unrolled<O, S, E>()) {
+        if (a.stage) {
+            if constexpr (O == kOuterNone || O == kOuterTensor)
+                return launch_persistent(k_tile<B, O, S, C, E, false, false, I, true>, a, s);
+            else
+                return given ? launch_persistent(k_tile<B, O, S, C, E, true, false, I, true>, a, s)
+                             : launch_persistent(k_tile<B, O, S, C, E, false, false, I, true>, a, s);
+        }
+    }
     if constexpr (C) {
         if constexpr (O == kOuterNone || O == kOuterTensor) {
-            return launch_persistent(k_tile<B, O, S, C, E, false, false, I>, a, s);
+            return launch_persistent(k_tile<B, O, S, C, E, false, false, I, false>, a, s);
         } else {
-            return given ? launch_persistent(k_tile<B, O, S, C, E, true, false, I>, a, s)
-                         : launch_persistent(k_tile<B, O, S, C, E, false, false, I>, a, s);
+            return given ? launch_persistent(k_tile<B, O, S, C, E, true, false, I, false>, a, s)
+                         : launch_persistent(k_tile<B, O, S, C, E, false, false, I, false>, a, s);
         }
     } else if constexpr (O == kOuterNone || O == kOuterTensor) {
-        return y ? launch_persistent(k_tile<B, O, S, C, E, false, true, I>, a, s)
-                 : launch_persistent(k_tile<B, O, S, C, E, false, false, I>, a, s);
+        return y ? launch_persistent(k_tile<B, O, S, C, E, false, true, I, false>, a, s)
+                 : launch_persistent(k_tile<B, O, S, C, E, false, false, I, false>, a, s);
     } else {
-        if (given) return y ? launch_persistent(k_tile<B, O, S, C, E, true, true, I>, a, s)
-                            : launch_persistent(k_tile<B, O, S, C, E, true, false, I>, a, s);
-        return y ? launch_persistent(k_tile<B, O, S, C, E, false, true, I>, a, s)
-                 : launch_persistent(k_tile<B, O, S, C, E, false, false, I>, a, s);
+        if (given) return y ? launch_persistent(k_tile<B, O, S, C, E, true, true, I, false>, a, s)
+                            : launch_persistent(k_tile<B, O, S, C, E, true, false, I, false>, a, s);
+        return y ? launch_persistent(k_tile<B, O, S, C, E, false, true, I, false>, a, s)
+                 : launch_persistent(k_tile<B, O, S, C, E, false, false, I, false>, a, s);
     }
 }
 

@@ -61,10 +61,57 @@ struct TileArgs {
     int32_t per_xcd;         // super-tiles in each XCD's contiguous slice
     int32_t wgs_per_xcd;     // persistent workgroups per XCD (grid = 8 * wgs_per_xcd)
     int32_t row0[kMaxGroupsPerLaunch + 1];   // prefix rows of the groups
-    int32_t tile0[kMaxGroupsPerLaunch + 1];  // prefix super-tile counts of the groups
+    int32_t tile0[kMaxGroupsPerLaunch + 1];  // prefix unit counts of the groups (super-tiles, or tiles when staged)
+    // Staged output (cast-transpose with stochastic rounding, a residual or 1D
+    // outer groups): when `stage` is set, the walk unit is one 64 x 64 tile
+    // (tiles_c = ceil(cols / 64), tile0 in tiles) and every code, scale byte and
+    // 1D outer scale goes to block `unit index` of `stage` (stage_block bytes,
+    // layout in kernels_tile.hip) as whole 128-byte lines; launch_tiles then
+    // gathers the blocks into the row-major outputs.
+    uint8_t* stage;          // 128-byte aligned, or null for direct stores
+    int32_t stage_block;     // bytes per tile block
 };
 
 enum OuterKind { kOuterNone = 0, kOuterTensor = 1, kOuter1D = 2, kOuter2D = 3 };
+
+// Staged tile block (bytes, offsets from the block start; every part a
+// multiple of 128 bytes):
+//   [0, 2048)       rowwise codes   [64 rows][32 bytes]
+//   [2048, 4096)    columnwise codes [64 columns][32 bytes]
+//   [4096, 4352)    rowwise scale bytes [64 rows][4]
+//   [4352, 4608)    columnwise scale bytes [64 columns][4]
+//   1D outer groups of obs (16, 32, 64) elements:
+//   [4608, +ob)     rowwise outer scales [64 rows][64 / obs] FP32
+//   [4608 + ob, +ob) columnwise outer scales [64 columns][64 / obs] FP32
+// with ob = 64 * (64 / obs) * 4.
+constexpr int32_t kStageColCodes = 2048;
+constexpr int32_t kStageTail = 4096;      // scales and outer scales, staged in LDS
+constexpr int32_t kStageRowOuter = 4608;
+
+inline int32_t stage_outer_bytes(int outer_kind, int obs)
+{
+    return outer_kind == kOuter1D ? 64 * (64 / obs) * 4 : 0;
+}
+
+// The cast-transpose calls that stage their outputs when given the scratch:
+// those with an error-feedback residual (without 16 x 16 inner tiles).  There
+// the residual's read and rewrite (8 of ~11 bytes per element) dominate, and
+// the extra pass over the 1.125 bytes per element of codes and scales costs
+// less than the partial-line stores it replaces (grouped 32 x 2880^2 step:
+// 0.90 -> 0.82 ms); without a residual the extra pass costs more than it
+// saves (16384 x 2880 1D SR: 0.100 -> 0.124 ms), so those store directly.
+// Both paths give identical bytes.
+inline bool stage_applies(bool sr, bool ef, int outer_kind, bool inner2d)
+{
+    (void)sr;
+    (void)outer_kind;
+    return ef && !inner2d;
+}
+
+inline int32_t stage_block_bytes(int outer_kind, int obs)
+{
+    return kStageRowOuter + 2 * stage_outer_bytes(outer_kind, obs);
+}
 
 // MXFP4 projection and FP8 re-encodings (every output may be null).
 struct Mx8Args {
@@ -117,6 +164,31 @@ hipError_t launch_rows(int scale_bias, int outer_kind, bool stochastic, bool x_f
                        hipStream_t s);
 
 hipError_t launch_tiles(int scale_bias, int outer_kind, bool stochastic, const TileArgs& a, hipStream_t s);
+
+// Gather pass of the staged cast-transpose (kernels_stage.hip): the blocks of
+// one tile-kernel launch into the rowwise and columnwise buffers.
+struct GatherArgs {
+    const uint8_t* stage;
+    int32_t stage_block;
+    int32_t ngroups;
+    int64_t cols;
+    int32_t tiles_c;         // ceil(cols / 64)
+    int32_t obs;             // 1D outer group size, 0 without 1D outer scales
+    int32_t scales4;         // 1: every scale row is a whole number of 4-byte words, buffers 4-byte aligned
+    int32_t row0[kMaxGroupsPerLaunch + 1];
+    int32_t tile0[kMaxGroupsPerLaunch + 1];   // prefix tile counts (ceil(rows / 64) * tiles_c)
+    uint8_t* row_codes;
+    uint8_t* row_scales;
+    float* row_outer;        // 1D only
+    uint8_t* col_codes;
+    uint8_t* col_scales;
+    float* col_outer;        // 1D only
+    // filled by launch_gather: work units per output kind (prefix) and lines per unit
+    int32_t kind_units[7];
+    int32_t lines[6];
+};
+
+hipError_t launch_gather(GatherArgs a, hipStream_t s);
 
 hipError_t launch_dequant_nv(int scale_bias, int outer_kind, int outer_transposed, int obs,
                              const uint8_t* codes, const uint8_t* scales, const float* outer,

@@ -167,6 +167,23 @@ int fp4q_buffer_sizes(const fp4q_cfg* cfg, int64_t rows, int64_t cols, fp4q_size
  * TENSORWISE computes its scale: then a small array of partial maxima). */
 size_t fp4q_workspace_bytes(const fp4q_cfg* cfg, int64_t rows, int64_t cols);
 
+/* Workspace bytes for fp4_cast_transpose (groups = 1, rows_per_group =
+ * &rows) and fp4_cast_transpose_grouped (host array of the G row counts), for
+ * a call with (with_residual = 1) or without (0) an error-feedback residual:
+ * the tensorwise partial maxima when the scale is computed, plus, for a call
+ * with a residual (outer blocks of up to 64 elements, 16 x 16 inner tiles
+ * excluded), one tile-major block per 64 x 64 tile of the largest launch
+ * (4608 bytes, more with 1D outer scales) and 128 bytes of alignment slack.
+ * Given at least this much, such a call stages its outputs: the tile kernel
+ * writes every code, scale byte and 1D outer scale as whole 128-byte lines of
+ * that scratch and a second kernel writes whole lines of the final buffers.
+ * The results are identical; HBM time is lower where rows of the output
+ * buffers are not whole 128-byte lines.  With less, the outputs are stored
+ * directly (the tensorwise part must still be there).  0 for an invalid
+ * configuration. */
+size_t fp4q_cast_transpose_workspace_bytes(const fp4q_cfg* cfg, int32_t groups, const int64_t* rows_per_group,
+                                           int64_t cols, int32_t with_residual);
+
 /*
  * fp4_quantize -- rowwise quantisation ("fp4-train" README, API: quantize(x,
  * stochastic, residual, seed, step)).
