@@ -167,7 +167,7 @@ size_t stage_bytes_for(const Resolved& r, int32_t ngroups, const int64_t* rows, 
 size_t ct_workspace_bytes(const Resolved& r, bool ef, int32_t ngroups, const int64_t* rows, int64_t cols)
 {
     size_t n = partial_bytes_for(r);
-    if (stage_applies(r.sr, ef, r.outer_kind, r.inner2d) && r.obs <= 64) {
+    if (stage_applies(r.sr, ef, r.outer_kind, r.inner2d)) {
         const size_t st = stage_bytes_for(r, ngroups, rows, cols);
         if (st) n += st + kStageAlign;
     }
@@ -178,7 +178,7 @@ size_t ct_workspace_bytes(const Resolved& r, bool ef, int32_t ngroups, const int
 uint8_t* stage_region(const Resolved& r, bool ef, int32_t ngroups, const int64_t* rows, int64_t cols, void* ws,
                       size_t ws_bytes)
 {
-    if (!ws || !stage_applies(r.sr, ef, r.outer_kind, r.inner2d) || r.obs > 64) return nullptr;
+    if (!ws || !stage_applies(r.sr, ef, r.outer_kind, r.inner2d)) return nullptr;
     const size_t st = stage_bytes_for(r, ngroups, rows, cols);
     if (st == 0 || ws_bytes < partial_bytes_for(r) + st + kStageAlign) return nullptr;
     const uintptr_t p = reinterpret_cast<uintptr_t>(ws) + partial_bytes_for(r);
@@ -341,13 +341,15 @@ int rowwise(const fp4q_cfg* cfg, const void* x, int64_t rows, int64_t cols, int6
     if (r.outer_kind == kOuterTensor) {
         if (r.given) {
             a.tensor_scale = outer;
-        } else {
+        } else if (rows * cols > kSmallTensorElems) {
             float* wsf = (float*)ws;
             hipError_t e = launch_amax(r.bias, x, r.x_f32, x_vec, rows, cols, ld, residual, wsf + 1, kAmaxPartials, wsf,
                                        outer, s);
             if (e != hipSuccess) return FP4Q_ERR_HIP;
             a.tensor_scale = wsf;
         }
+        // else: a small tensor -- one launch, each workgroup takes the amax itself
+        // (tensor_scale stays null; the kernel writes outer when given)
     }
     return hip_status(launch_rows(r.bias, r.outer_kind, r.sr, r.x_f32, a, s));
 }
@@ -463,7 +465,8 @@ int fp4_cast_transpose(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int
     st = check_vector_source(r, ld_x);
     if (st) return st;
     if (r.outer_kind == kOuter2D && r.obs != 64) return FP4Q_ERR_UNSUPPORTED;
-    if (r.outer_kind == kOuter1D && r.obs != 16 && r.obs != 32 && r.obs != 64) return FP4Q_ERR_UNSUPPORTED;
+    if (r.outer_kind == kOuter1D && r.obs != 16 && r.obs != 32 && r.obs != 64 && r.obs != 128)
+        return FP4Q_ERR_UNSUPPORTED;
     if ((r.outer_kind == kOuter2D || r.outer_kind == kOuterTensor) && col_outer && col_outer != row_outer)
         return FP4Q_ERR_MODE;
     const size_t need_ws = partial_bytes_for(r) ? ws_bytes_for(r) : 0;
@@ -494,8 +497,17 @@ int fp4_cast_transpose(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int
     a.obs16 = r.obs ? r.obs / 16 : 1;
     a.outer_given = r.given;
     a.inner_2d = r.inner2d ? 1 : 0;
-    uint8_t* stage = stage_region(r, residual != nullptr, 1, &rows, cols, workspace, workspace_bytes);
-    if (stage) use_stage(a, r, stage);
+    // 1D groups of 128 span two tiles: their scales are computed first and
+    // the tile kernel reads them as precomputed ones
+    Resolved rt = r;
+    if (r.outer_kind == kOuter1D && r.obs == 128 && !r.given) {
+        st = hip_status(launch_outer128(r.bias, a, s));
+        if (st) return st;
+        a.outer_given = 1;
+        rt.given = true;
+    }
+    uint8_t* stage = stage_region(rt, residual != nullptr, 1, &rows, cols, workspace, workspace_bytes);
+    if (stage) use_stage(a, rt, stage);
     if (r.outer_kind == kOuterTensor) {
         if (r.given) {
             a.tensor_scale = row_outer;
@@ -509,7 +521,7 @@ int fp4_cast_transpose(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int
     }
     st = hip_status(launch_tiles(r.bias, r.outer_kind, r.sr, a, s));
     if (st || !stage) return st;
-    return hip_status(gather_staged(a, r, s));
+    return hip_status(gather_staged(a, rt, s));
 }
 
 int fp4_mx_project_fp8(const fp4q_cfg* cfg, const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
@@ -630,7 +642,8 @@ int fp4_cast_transpose_grouped(const fp4q_cfg* cfg, int32_t groups, const int64_
     if (st) return st;
     if (total >= ((int64_t)1 << 31)) return FP4Q_ERR_UNSUPPORTED;
     if (r.outer_kind == kOuter2D && r.obs != 64) return FP4Q_ERR_UNSUPPORTED;
-    if (r.outer_kind == kOuter1D && r.obs != 16 && r.obs != 32 && r.obs != 64) return FP4Q_ERR_UNSUPPORTED;
+    if (r.outer_kind == kOuter1D && r.obs != 16 && r.obs != 32 && r.obs != 64 && r.obs != 128)
+        return FP4Q_ERR_UNSUPPORTED;
     if (r.outer_kind == kOuter2D && col_outer && col_outer != row_outer) return FP4Q_ERR_MODE;
     if (total == 0 || cols == 0) return FP4Q_OK;
     if (!x || !row_codes || !row_scales || !col_codes || !col_scales) return FP4Q_ERR_NULL;
@@ -641,7 +654,10 @@ int fp4_cast_transpose_grouped(const fp4q_cfg* cfg, int32_t groups, const int64_
         return FP4Q_ERR_ALIGN;
     hipStream_t s = (hipStream_t)stream;
     const int32_t tiles_c = (int32_t)((cols + 127) / 128);
-    uint8_t* stage = stage_region(r, residual != nullptr, groups, rows_per_group, cols, workspace, workspace_bytes);
+    const bool outer128 = r.outer_kind == kOuter1D && r.obs == 128 && !r.given;
+    Resolved rt = r;
+    if (outer128) rt.given = true;
+    uint8_t* stage = stage_region(rt, residual != nullptr, groups, rows_per_group, cols, workspace, workspace_bytes);
     int64_t row_before = 0;
     for (int32_t g0 = 0; g0 < groups; g0 += kMaxGroupsPerLaunch) {
         const int32_t ng = std::min<int32_t>(kMaxGroupsPerLaunch, groups - g0);
@@ -680,11 +696,16 @@ int fp4_cast_transpose_grouped(const fp4q_cfg* cfg, int32_t groups, const int64_
         set_tile_grid(tt, a.per_xcd, a.wgs_per_xcd);
         row_before = rr;
         if (tt == 0) continue;
-        if (stage) use_stage(a, r, stage);
+        if (outer128) {
+            st = hip_status(launch_outer128(r.bias, a, s));
+            if (st) return st;
+            a.outer_given = 1;
+        }
+        if (stage) use_stage(a, rt, stage);
         st = hip_status(launch_tiles(r.bias, r.outer_kind, r.sr, a, s));
         if (st) return st;
         if (stage) {
-            st = hip_status(gather_staged(a, r, s));
+            st = hip_status(gather_staged(a, rt, s));
             if (st) return st;
         }
     }

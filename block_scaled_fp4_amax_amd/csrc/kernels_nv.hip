@@ -83,13 +83,123 @@ __device__ __forceinline__ uint32_t load_src16(const void* x, int64_t off, bool 
     return am;
 }
 
-template <int BIAS, int OUTER, bool SR, bool EF, bool XF32>
+// |sanitise(x (+ residual))| bit-pattern maximum of one 16-element block.
+template <bool XF32>
+__device__ __forceinline__ uint32_t amax_block(const void* x, int x_vec, const float* res, int64_t cols, int64_t ld,
+                                               uint32_t b, uint32_t bpr)
+{
+    const uint32_t i = b / bpr;
+    const int64_t j0 = (int64_t)(b - i * bpr) * 16;
+    float v[16];
+    uint32_t m = load_src16<XF32>(x, (int64_t)i * ld + j0, x_vec != 0, v);
+    if (res) {
+        float z[16];
+        load16_f32(res + (int64_t)i * cols + j0, z);
+        m = 0;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            v[k] = v[k] + z[k];
+            m = max(m, __float_as_uint(v[k]) & 0x7FFFFFFFu);
+        }
+    }
+    if (__builtin_expect(m >= 0x7F800000u, 0)) {
+        m = 0;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) m = max(m, __float_as_uint(sanitize(v[k])) & 0x7FFFFFFFu);
+    }
+    return m;
+}
+
+// Largest |sanitise(x (+ residual))| bit pattern over 16-element blocks
+// first, first + stride, ... < nblocks (the tensorwise amax); four blocks per
+// step, their loads issued together (a block past the end re-reads `first`).
+template <bool XF32>
+__device__ __forceinline__ uint32_t amax_blocks(const void* x, int x_vec, const float* res, int64_t cols, int64_t ld,
+                                                uint32_t nblocks, uint32_t bpr, uint32_t first, uint32_t stride)
+{
+    uint32_t am = 0;
+    if (first >= nblocks) return 0;
+    for (uint32_t b = first; b < nblocks; b += 4 * stride) {
+        uint32_t m[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t bb = b + (uint32_t)k * stride;
+            m[k] = amax_block<XF32>(x, x_vec, res, cols, ld, bb < nblocks ? bb : first, bpr);
+        }
+        am = max(am, max(max(m[0], m[1]), max(m[2], m[3])));
+    }
+    return am;
+}
+
+// Largest |x| bf16 bit pattern of a 16-byte aligned bf16 tensor (rows of
+// cols elements, row pitch ld), the workgroup's lanes taking 16-byte chunks in
+// turn, sixteen loads in flight per lane; a NaN / inf anywhere gives >= 0x7F80,
+// and the caller then takes the sanitised maximum the slow way.
+__device__ __forceinline__ uint32_t amax_bf16_chunks(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld)
+{
+    const uint32_t cpr = (uint32_t)(cols / 8);                 // 16-byte chunks per row
+    const uint32_t n = (uint32_t)(rows * cpr);
+    uint32_t m = 0;
+    for (uint32_t c0 = threadIdx.x; c0 < n; c0 += 16 * kThreads) {
+        uint4 w[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            uint32_t c = c0 + (uint32_t)k * kThreads;
+            c = c < n ? c : 0u;
+            const uint32_t i = c / cpr;
+            w[k] = ld_nt16(x + (int64_t)i * ld + (int64_t)(c - i * cpr) * 8);
+        }
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+            m = pk_max_u16(m, pk_max_u16(pk_max_u16(w[k].x & 0x7FFF7FFFu, w[k].y & 0x7FFF7FFFu),
+                                         pk_max_u16(w[k].z & 0x7FFF7FFFu, w[k].w & 0x7FFF7FFFu)));
+    }
+    const uint32_t lo = m & 0xFFFFu, hi = m >> 16;
+    return lo > hi ? lo : hi;
+}
+
+// Rowwise NV / AMD quantisation; SMALL (tensorwise only): every workgroup
+// first takes the amax of the whole tensor itself (a small tensor is read from
+// the caches once per workgroup), so the global scale needs no second launch.
+template <int BIAS, int OUTER, bool SR, bool EF, bool XF32, bool SMALL>
 __global__ __launch_bounds__(kThreads) void k_nv_rows(RowArgs a, uint32_t nblocks, uint32_t bpr)
 {
     __shared__ double rtab[16];
     __shared__ float2 ktab[SR ? 1 : kRneTableSize];
+    __shared__ uint32_t wmax[kThreads / 64];
     fill_recip_table(rtab, (int)threadIdx.x);
     if (!SR) fill_rne_table<BIAS>(ktab, (int)threadIdx.x);
+    float s_small = 0.0f;
+    if (SMALL) {
+        uint32_t m;
+        if (!XF32 && !EF && a.x_vec) {
+            // bf16 without a residual: packed maxima of the raw bits; the
+            // sanitised pass only if a NaN / inf turned up (a uniform branch)
+            m = wave_max_u32(amax_bf16_chunks(static_cast<const uint16_t*>(a.x), a.rows, a.cols, a.ld));
+            if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+            __syncthreads();
+            const uint32_t fast = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3])) << 16;
+            __syncthreads();
+            if (fast < 0x7F800000u) {
+                m = fast;
+            } else {
+                m = wave_max_u32(amax_blocks<XF32>(a.x, a.x_vec, nullptr, a.cols, a.ld, nblocks, bpr, threadIdx.x,
+                                                   kThreads));
+                if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+                __syncthreads();
+                m = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+            }
+        } else {
+            m = amax_blocks<XF32>(a.x, a.x_vec, EF ? a.residual : nullptr, a.cols, a.ld, nblocks, bpr, threadIdx.x,
+                                  kThreads);
+            m = wave_max_u32(m);
+            if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+            __syncthreads();
+            m = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+        }
+        s_small = __uint_as_float(m) / ScaleFmt<BIAS>::outer_den();
+        if (a.outer && blockIdx.x == 0 && threadIdx.x == 0) a.outer[0] = s_small;
+    }
     __syncthreads();
     const uint32_t b = blockIdx.x * kThreads + threadIdx.x;   // inner block id
     // lanes of one 1D outer group are consecutive and bpr % obs16 == 0, so a
@@ -135,7 +245,7 @@ __global__ __launch_bounds__(kThreads) void k_nv_rows(RowArgs a, uint32_t nblock
 
     float s_o = 1.0f;
     if (OUTER == kOuterTensor) {
-        s_o = *a.tensor_scale;
+        s_o = SMALL ? s_small : *a.tensor_scale;
     } else if (OUTER == kOuter1D) {
         const int64_t og = (int64_t)i * (a.cols / (16 * a.obs16)) + jb / (uint32_t)a.obs16;
         if (a.outer_given) {
@@ -191,30 +301,13 @@ __global__ __launch_bounds__(kThreads) void k_amax_partial(const void* __restric
                                                            const float* __restrict__ res, int64_t cols, int64_t ld,
                                                            uint32_t nblocks, uint32_t bpr, float* __restrict__ partials)
 {
-    float am = 0.0f;
-    for (uint32_t b = blockIdx.x * kThreads + threadIdx.x; b < nblocks; b += gridDim.x * kThreads) {
-        const uint32_t i = b / bpr;
-        const int64_t j0 = (int64_t)(b - i * bpr) * 16;
-        float v[16];
-        (void)load_src16<XF32>(x, (int64_t)i * ld + j0, x_vec != 0, v);
-        if (res) {
-            float z[16];
-            load16_f32(res + (int64_t)i * cols + j0, z);
-#pragma unroll
-            for (int k = 0; k < 16; ++k) v[k] = v[k] + z[k];
-        }
-#pragma unroll
-        for (int k = 0; k < 16; ++k) am = fmaxf(am, __builtin_fabsf(sanitize(v[k])));
-    }
-    am = group_max<64>(am);
-    __shared__ float wmax[kThreads / 64];
+    uint32_t am = amax_blocks<XF32>(x, x_vec, res, cols, ld, nblocks, bpr, blockIdx.x * kThreads + threadIdx.x,
+                                    gridDim.x * kThreads);
+    am = wave_max_u32(am);
+    __shared__ uint32_t wmax[kThreads / 64];
     if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = am;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        float m = wmax[0];
-        for (int w = 1; w < kThreads / 64; ++w) m = fmaxf(m, wmax[w]);
-        partials[blockIdx.x] = m;
-    }
+    if (threadIdx.x == 0) partials[blockIdx.x] = __uint_as_float(max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3])));
 }
 
 // Tensorwise pass 2: s_g = RN(max(partials) / (scale_max * 6)).
@@ -286,10 +379,14 @@ hipError_t launch_rows(int bias, int outer_kind, bool sr, bool x_f32, const RowA
     const uint32_t nblocks = (uint32_t)(a.rows * bpr);
     const uint32_t grid = (nblocks + kThreads - 1) / kThreads;
     const bool ef = a.residual != nullptr;
+    const bool small = outer_kind == kOuterTensor && a.tensor_scale == nullptr;
 #define FP4Q_ROWS(B, O, S, E)                                                                                   \
     do {                                                                                                        \
-        if (x_f32) hipLaunchKernelGGL((k_nv_rows<B, O, S, E, true>), dim3(grid), dim3(kThreads), 0, s, a, nblocks, bpr); \
-        else hipLaunchKernelGGL((k_nv_rows<B, O, S, E, false>), dim3(grid), dim3(kThreads), 0, s, a, nblocks, bpr); \
+        if (O == kOuterTensor && small) {                                                                       \
+            if (x_f32) hipLaunchKernelGGL((k_nv_rows<B, O, S, E, true, true>), dim3(grid), dim3(kThreads), 0, s, a, nblocks, bpr); \
+            else hipLaunchKernelGGL((k_nv_rows<B, O, S, E, false, true>), dim3(grid), dim3(kThreads), 0, s, a, nblocks, bpr); \
+        } else if (x_f32) hipLaunchKernelGGL((k_nv_rows<B, O, S, E, true, false>), dim3(grid), dim3(kThreads), 0, s, a, nblocks, bpr); \
+        else hipLaunchKernelGGL((k_nv_rows<B, O, S, E, false, false>), dim3(grid), dim3(kThreads), 0, s, a, nblocks, bpr); \
     } while (0)
 #define FP4Q_ROWS_E(B, O, S)                     \
     do {                                         \

@@ -165,6 +165,11 @@ hipError_t launch_rows(int scale_bias, int outer_kind, bool stochastic, bool x_f
 
 hipError_t launch_tiles(int scale_bias, int outer_kind, bool stochastic, const TileArgs& a, hipStream_t s);
 
+// FP32 scales of 1D outer groups of 128 elements (both directions) for the
+// groups of a tile launch, written to its row_outer / col_outer before the
+// tile kernel reads them as precomputed scales (kernels_outer.hip).
+hipError_t launch_outer128(int scale_bias, const TileArgs& a, hipStream_t s);
+
 // Gather pass of the staged cast-transpose (kernels_stage.hip): the blocks of
 // one tile-kernel launch into the rowwise and columnwise buffers.
 struct GatherArgs {
@@ -199,5 +204,10 @@ hipError_t launch_dequant_mx(const uint8_t* codes, const uint8_t* scales, int64_
 
 // partial maxima used by the tensorwise amax pass
 constexpr int kAmaxPartials = 512;
+
+// Rowwise tensorwise calls on at most this many elements run in one launch:
+// every workgroup reads the whole (cache-resident) tensor for its amax
+// instead of a grid-wide amax pass and a scale pass before the quantiser.
+constexpr int64_t kSmallTensorElems = (int64_t)1 << 18;
 
 }  // namespace fp4q

@@ -283,7 +283,9 @@ int fp4_qdq_noalloc(const fp4q_cfg* cfg, const void* x, int64_t rows, int64_t co
  *              value; the columnwise direction reads the same value but does not
  *              update it.
  * Needs rows % 16 == 0.  OUTER_BLOCK supports obs == 64 (1D and 2D); 1D also
- * obs in {16, 32}.  Element (i, j) draws its SR variate once and uses it in
+ * obs in {16, 32, 128} (groups of 128 span two 64 x 64 tiles: a first kernel
+ * computes their scales, then the tile kernel reads them; one more read of x
+ * and the residual).  Element (i, j) draws its SR variate once and uses it in
  * both directions.  With cfg->inner_2d the columnwise codes and scales are
  * exactly the transposes of the rowwise ones.
  */

@@ -150,7 +150,9 @@ def test_cast_transpose_rules():
     o2 = C(two_level="outer_block", outer_block_size=64, outer_2d=True)
     assert ct_(o2, col_outer=FAKE + 4096) == fq.ERR_MODE        # 2D outer is shared
     assert ct_(o2, col_codes=None) == fq.ERR_NULL
-    assert ct_(C(two_level="outer_block", outer_block_size=128), rows=128, cols=128, col_outer=FAKE) == fq.ERR_UNSUPPORTED
+    # 1D groups of 128 are built (a pre-pass computes their scales); 256 is valid but not built
+    assert ct_(C(two_level="outer_block", outer_block_size=128), rows=64, cols=128, col_outer=FAKE) == fq.ERR_SHAPE
+    assert ct_(C(two_level="outer_block", outer_block_size=256), rows=256, cols=256, col_outer=FAKE) == fq.ERR_UNSUPPORTED
 
 
 def test_grouped_rules():

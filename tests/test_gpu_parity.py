@@ -143,6 +143,8 @@ ROW_CASES = [
     ("nvfp4-ue5m3", "outer", 64, False, False, (70, 2880), 0),
     ("nvfp4", "outer", 128, False, False, (50, 256), 0),
     ("amdfp4", "outer", 128, True, False, (50, 256), 0),
+    ("nvfp4", "tensorwise", 0, True, True, (600, 512), 3),      # above the one-launch size: amax passes
+    ("amdfp4", "tensorwise", 0, False, False, (512, 512), 0),   # exactly the one-launch limit
 ]
 
 
@@ -262,6 +264,9 @@ CT_CASES = [
     ("nvfp4", "none", 0, False, True, True, (144, 208)),
     ("nvfp4", "tensorwise", 0, False, False, False, (80, 48)),
     ("nvfp4-ue5m3", "tensorwise", 0, False, True, True, (112, 96)),
+    ("amdfp4", "outer", 128, False, True, False, (256, 384)),
+    ("nvfp4", "outer", 128, False, False, True, (128, 256)),
+    ("nvfp4", "outer", 128, False, True, True, (384, 128)),
 ]
 
 
@@ -465,14 +470,15 @@ def test_grouped_uneven_groups_equal_single_calls():
             r0 += R
 
 
-@pytest.mark.parametrize("tl,obs,o2d", [("outer", 64, True), ("outer", 64, False), ("outer", 16, False)])
+@pytest.mark.parametrize("tl,obs,o2d", [("outer", 64, True), ("outer", 64, False), ("outer", 16, False),
+                                        ("outer", 128, False)])
 def test_grouped_more_groups_than_one_launch_holds(tl, obs, o2d):
     """More groups than one launch's group table (64): the call is split into
     several launches, each with its own tile numbering but global row offsets.
     SR + error feedback, groups of uneven height (some empty), every buffer
     against the oracle's grouped quantisation."""
     rng = np.random.default_rng(13 + obs)
-    step = 64 if (tl == "outer" and o2d) or obs == 64 else 16
+    step = 64 if (tl == "outer" and o2d) or obs == 64 else obs
     rows = list(rng.choice([0, step, 2 * step, 3 * step], size=130))
     C = 128
     x = rand_bf16(rng, (sum(rows), C), 0.02)
@@ -490,3 +496,17 @@ def test_grouped_more_groups_than_one_launch_holds(tl, obs, o2d):
     if not o2d:
         same(host(out["col_outer"], np.float32).ravel(), want["col_outer"], "col outer")
     same(host(zd, np.float32), zo, "residual")
+
+
+def test_cast_transpose_1d_obs128_sr_16384x4096():
+    """1D outer groups of 128 (1 x 128 along rows, 128 x 1 down columns; ALTO
+    page, Technical design) at full size: AMD-FP4, SR, the 16384-token
+    activation recipe on 4096 channels, every buffer against the oracle."""
+    x = W.activations_16384x2880(cols=4096)
+    g, o = cfgs("amdfp4", "outer", 128, False, True, seed=7, step=3)
+    want = ref.nv_quantize(x, cols=True, want_y=False, **o)
+    out = fq.fp4_cast_transpose(dev(x), g)
+    for k in ("row_codes", "row_scales", "col_codes", "col_scales"):
+        same(host(out[k], np.uint8), want[k], "1D obs128 cast-transpose " + k)
+    same(host(out["row_outer"], np.float32), want["row_outer"], "1D obs128 row outer")
+    same(host(out["col_outer"], np.float32), want["col_outer"], "1D obs128 col outer")

@@ -62,6 +62,7 @@ CASES = [
     ("nvfp4", "tensorwise", 0, False, True, (112, 96)),
     ("amdfp4", "tensorwise", 0, False, False, (64, 64)),
     ("nvfp4", "outer", 64, False, False, (320, 192)),
+    ("amdfp4", "outer", 128, False, True, (256, 384)),
 ]
 
 
