@@ -19,7 +19,8 @@ __all__ = [
     "fp4q_mx_scales_tiled_bytes", "fp4_qdq_noalloc", "ErrorFeedback", "LIB_PATH",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp4q.so")
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                        "libfp4q_ubsan.so" if os.environ.get("FP4Q_SANITIZE") == "1" else "libfp4q.so")
 
 OK, ERR_NULL, ERR_DTYPE, ERR_SHAPE, ERR_MODE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP, ERR_ABI = range(10)
 ABI_VERSION = 2

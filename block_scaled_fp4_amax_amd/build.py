@@ -57,5 +57,68 @@ def build(force: bool = True, verbose: bool = False) -> str:
     return LIB
 
 
+# ---------------------------------------------------------------- sanitizer builds (host code)
+# The host layer (validation, staging plans, the scratch lookup) is built with
+# a sanitizer on its host side and linked with the kernels' objects of the
+# normal build: "ubsan" gives libfp4q_ubsan.so, which the binding loads when
+# FP4Q_SANITIZE=1 (UBSan's runtime needs no preloading into Python); "asan"
+# gives an executable from a C++ driver (ASan's runtime must be in the
+# executable).  Device code is never built with a sanitizer.
+HOST_SOURCES = ("fp4q_api.cpp", "fp4q_noalloc.hip")
+LIB_UBSAN = os.path.join(HERE, "libfp4q_ubsan.so")
+
+
+def _clang_rt_dir():
+    hits = glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.ubsan_standalone-x86_64.so")
+    if not hits:
+        raise RuntimeError("no clang sanitizer runtime under /opt/rocm/llvm")
+    return os.path.dirname(hits[0])
+
+
+def build_sanitized(kind: str, driver: str = None, out: str = None) -> str:
+    """kind "ubsan": libfp4q_ubsan.so; kind "asan": the executable `out` built
+    from `driver` (a C++ source calling the C ABI)."""
+    build(force=False)
+    objdir = os.path.join(HERE, "_build")
+    san = ["-Xarch_host", "-fsanitize=undefined" if kind == "ubsan" else "-fsanitize=address,undefined",
+           "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+    if kind == "ubsan":
+        san += ["-Xarch_host", "-shared-libsan"]
+    objs, procs = [], []
+    for src in sources():
+        base = os.path.basename(src)
+        if base in HOST_SOURCES:
+            obj = os.path.join(objdir, base + "." + kind + ".o")
+            procs.append((src, subprocess.Popen([HIPCC, *FLAGS, *san, "-g", "-c", src, "-o", obj],
+                                                stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+        else:
+            obj = os.path.join(objdir, base + ".o")
+        objs.append(obj)
+    if kind == "asan":
+        obj = os.path.join(objdir, os.path.basename(driver) + ".asan.o")
+        procs.append((driver, subprocess.Popen([HIPCC, *FLAGS, *san, "-g", "-c", driver, "-o", obj],
+                                               stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+        objs.append(obj)
+    for src, p in procs:
+        text = p.communicate()[0].decode()
+        if p.returncode != 0:
+            raise RuntimeError("hipcc failed on %s:\n%s" % (src, text))
+    rt = _clang_rt_dir()
+    if kind == "ubsan":
+        target = LIB_UBSAN
+        cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-Xarch_host", "-fsanitize=undefined",
+               "-Xarch_host", "-shared-libsan", "-Wl,-rpath," + rt, *objs, "-o", target + ".tmp"]
+    else:
+        target = out
+        cmd = [HIPCC, "--offload-arch=" + ARCH, "-Xarch_host", "-fsanitize=address,undefined", *objs, "-o",
+               target + ".tmp"]
+    subprocess.run(cmd, check=True)
+    os.replace(target + ".tmp", target)
+    return target
+
+
 if __name__ == "__main__":
-    print(build(force="--lazy" not in sys.argv, verbose="-v" in sys.argv))
+    if "--ubsan" in sys.argv:
+        print(build_sanitized("ubsan"))
+    else:
+        print(build(force="--lazy" not in sys.argv, verbose="-v" in sys.argv))

@@ -26,5 +26,29 @@ def build(force: bool = True) -> str:
     return LIB
 
 
+# Sanitizer builds (test infrastructure): liboracle_ubsan.so, loaded by
+# oracle/ref.py when FP4Q_SANITIZE=1, and an ASan + UBSan executable from a C
+# driver linked with the oracle's source.
+LIB_UBSAN = os.path.join(HERE, "liboracle_ubsan.so")
+SAN_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fno-sanitize-recover=all"]
+
+
+def build_ubsan() -> str:
+    tmp = LIB_UBSAN + ".tmp%d" % os.getpid()
+    subprocess.run(["gcc", *CFLAGS, *SAN_FLAGS, "-fsanitize=undefined", SRC, "-o", tmp, "-lm"], check=True)
+    os.replace(tmp, LIB_UBSAN)
+    return LIB_UBSAN
+
+
+def build_asan_driver(driver: str, out: str) -> str:
+    flags = [f for f in CFLAGS if f not in ("-shared", "-fPIC")]
+    subprocess.run(["gcc", *flags, *SAN_FLAGS, "-fsanitize=address,undefined", SRC, driver, "-o", out, "-lm"],
+                   check=True)
+    return out
+
+
 if __name__ == "__main__":
-    print(build(force="--lazy" not in sys.argv))
+    if "--ubsan" in sys.argv:
+        print(build_ubsan())
+    else:
+        print(build(force="--lazy" not in sys.argv))

@@ -27,7 +27,12 @@ def lib():
     global _lib
     if _lib is None:
         path = _build.LIB
-        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_build.SRC):
+        if os.environ.get("FP4Q_SANITIZE") == "1":
+            # the UBSan build (sanitizer runs of the CPU suite)
+            path = _build.LIB_UBSAN
+            if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_build.SRC):
+                _build.build_ubsan()
+        elif not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_build.SRC):
             _build.build()
         L = ct.CDLL(path)
         P = ct.c_void_p
