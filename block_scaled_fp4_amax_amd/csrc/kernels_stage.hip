@@ -24,7 +24,7 @@ namespace fp4q {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBatch = 8;    // 16-byte chunks per lane issued before any store
+constexpr int kBatch = 4;    // 16-byte chunks per lane issued before any store (fallback paths)
 
 // One output range [dst, dst + nbytes) filled from staged blocks, by the
 // whole workgroup.  LOC(off) gives the staged address of the G bytes at range
@@ -181,6 +181,62 @@ __device__ __forceinline__ void band_lds(const Band& b, int l0, int cnt, uint8_t
     __syncthreads();
 }
 
+// band_lds for the common shapes, with no division per piece: each tile's run
+// (cnt * U contiguous bytes, 16-byte aligned) is read as 16-byte chunks by R =
+// cnt * U / 16 neighbouring lanes, 256 / R runs per instruction, so a lane's
+// chunk offset within a run, and with it the chunk's line and LDS position,
+// is fixed for the whole unit and only the tile index advances.  W = min(U,
+// 16) is the LDS write width: a chunk holds 16 / W lines (U <= 16) or part of
+// one line (U = 32).  Needs cnt * U % 16 == 0, cnt * U <= 4096, the run start
+// 16-byte aligned, P % W == 0, and the last tile whole (Ulast == U).
+constexpr int kRunBatch = 12;
+
+template <int W>
+__device__ __forceinline__ void band_runs(const Band& b, int l0, int cnt, uint8_t* lds)
+{
+    const int R = cnt * b.U / 16;
+    const int per_it = kThreads / R;
+    const int tid = (int)threadIdx.x;
+    const int ts = tid / R;
+    const int o = (tid - ts * R) * 16;            // chunk offset in the run
+    const bool lane_ok = ts < per_it;
+    const int l = o / b.U;                         // first line of the chunk
+    const int dst0 = l * b.P + (o - l * b.U);      // LDS offset for tile 0
+    const uint8_t* src0 = b.in + (int64_t)l0 * b.U + o;
+    for (int t0 = 0; t0 < b.T; t0 += per_it * kRunBatch) {
+        uint32_t v[kRunBatch][4];    // plain words: an array of uint4 would live in scratch
+#pragma unroll
+        for (int k = 0; k < kRunBatch; ++k) {
+            const int t = t0 + k * per_it + ts;
+            const bool ok = lane_ok && t < b.T;
+            const uint4 w = *reinterpret_cast<const uint4*>(ok ? src0 + (int64_t)t * b.tstride : b.in);
+            v[k][0] = w.x; v[k][1] = w.y; v[k][2] = w.z; v[k][3] = w.w;
+        }
+#pragma unroll
+        for (int k = 0; k < kRunBatch; ++k) {
+            const int t = t0 + k * per_it + ts;
+            if (!(lane_ok && t < b.T)) continue;
+            uint8_t* q = lds + dst0 + t * b.U;
+            if (W == 16) {
+                *reinterpret_cast<uint4*>(q) = make_uint4(v[k][0], v[k][1], v[k][2], v[k][3]);
+            } else if (W == 8) {
+                *reinterpret_cast<uint2*>(q) = make_uint2(v[k][0], v[k][1]);
+                *reinterpret_cast<uint2*>(q + b.P) = make_uint2(v[k][2], v[k][3]);
+            } else {
+                *reinterpret_cast<uint32_t*>(q) = v[k][0];
+                *reinterpret_cast<uint32_t*>(q + b.P) = v[k][1];
+                *reinterpret_cast<uint32_t*>(q + 2 * b.P) = v[k][2];
+                *reinterpret_cast<uint32_t*>(q + 3 * b.P) = v[k][3];
+            }
+        }
+    }
+    __syncthreads();
+    const int nchunks = cnt * b.P / 16;
+    uint4* out = reinterpret_cast<uint4*>(b.dst + (int64_t)l0 * b.P);
+    for (int c = tid; c < nchunks; c += kThreads) out[c] = reinterpret_cast<const uint4*>(lds)[c];
+    __syncthreads();
+}
+
 // Lines [l0, l0 + cnt) of a band without LDS: each 16-byte output chunk
 // gathered from the blocks directly (shapes the LDS path does not take).
 __device__ __forceinline__ void band_direct(const Band& b, int l0, int cnt)
@@ -282,8 +338,17 @@ __global__ __launch_bounds__(kThreads) void k_gather(GatherArgs a)
         const int cnt = min(a.lines[kind], b.lines - l0);
         const bool lds_ok = cnt * b.P <= kLdsBytes && (reinterpret_cast<uintptr_t>(b.dst + (int64_t)l0 * b.P) & 15) == 0 &&
                             (cnt * b.P) % 16 == 0;
+        const int run = cnt * b.U;
+        const bool runs_ok = lds_ok && b.Ulast == b.U && run % 16 == 0 && run <= 16 * kThreads &&
+                             ((reinterpret_cast<uintptr_t>(b.in) + (uintptr_t)l0 * b.U) & 15) == 0 && b.tstride % 16 == 0;
         if (!lds_ok) {
             band_direct(b, l0, cnt);
+        } else if (runs_ok && b.U % 16 == 0 && b.P % 16 == 0) {
+            band_runs<16>(b, l0, cnt, lds);
+        } else if (runs_ok && b.U == 8 && b.P % 8 == 0) {
+            band_runs<8>(b, l0, cnt, lds);
+        } else if (runs_ok && b.U == 4 && b.P % 4 == 0) {
+            band_runs<4>(b, l0, cnt, lds);
         } else if (b.U % 16 == 0 && b.Ulast % 16 == 0 && b.P % 16 == 0) {
             band_lds<16>(b, l0, cnt, lds);
         } else if (b.U % 8 == 0 && b.Ulast % 8 == 0 && b.P % 8 == 0) {

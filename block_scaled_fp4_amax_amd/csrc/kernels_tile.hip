@@ -333,11 +333,19 @@ void k_tile(TileArgs a)
     __shared__ uint32_t red[2][kThreads / 64];
     __shared__ double rtab[kRecipTableSize];
     __shared__ float2 ktab[SR ? 1 : kRneTableSize];
-    __shared__ PairStage stage[1];
+    // paired-tile stores (direct path only)
+    __shared__ uint4 pair_raw[STAGED ? 1 : (sizeof(PairStage) + 15) / 16];
+    PairStage* const stage = reinterpret_cast<PairStage*>(pair_raw);
     // staged output: the tail of each tile's block (scale bytes and 1D outer
     // scales) gathered here, one buffer per tile parity, and written by the
     // workgroup as whole lines once every wave has finished the tile
-    __shared__ uint4 tail[STAGED ? 2 * kTailMax / 16 : 1];
+    constexpr int kTailCap = OUTER == kOuter1D ? kTailMax : kStageRowOuter - kStageTail;
+    __shared__ uint4 tail[STAGED ? 2 * kTailCap / 16 : 1];
+    // error feedback with both directions: the new residual of the tile, so
+    // that it is stored row-coalesced (16 lanes write one row's 256 bytes)
+    // instead of as each lane's 64-byte run (measured on the grouped
+    // 32 x 2880^2 step's traffic: 0.68 -> 0.58 ms)
+    __shared__ float4 lds_res[(COLS && EF) ? kTile * kTile / 4 : 1];
 
     const int tid = (int)threadIdx.x;
     const int r = tid >> 2, sg = tid & 3;       // row phase: row, 16-column segment
@@ -390,7 +398,7 @@ void k_tile(TileArgs a)
     const int tail_bytes = (kStageRowOuter - kStageTail) + (OUTER == kOuter1D ? 2 * 64 * opr * 4 : 0);
     auto emit_tail = [&](int par) {
         const int n16 = tail_bytes / 16;
-        const uint4 v = tail[par * (kTailMax / 16) + min(tid, n16 - 1)];
+        const uint4 v = tail[par * (kTailCap / 16) + min(tid, n16 - 1)];
         buf_store16(make_rsrc(prev_blk), (prev_ok && tid < n16) ? (uint32_t)(kStageTail + 16 * tid) : kOff, v);
     };
 
@@ -480,6 +488,7 @@ void k_tile(TileArgs a)
         }
 
         float vn[16];
+        float res[EF ? 16 : 1];   // the new residual (error feedback)
         if (OUTER == kOuterNone) {
 #pragma unroll
             for (int k = 0; k < 16; ++k) vn[k] = v[k];
@@ -496,9 +505,9 @@ void k_tile(TileArgs a)
             ro.scale = sc.code;
             if (STAGED) {
                 const int par = iter & 1;
-                tail8[par * kTailMax + r * 4 + sg] = (uint8_t)sc.code;
+                tail8[par * kTailCap + r * 4 + sg] = (uint8_t)sc.code;
                 if (OUTER == kOuter1D && !GIVEN && (sg % a.obs16) == 0)
-                    tailf[par * (kTailMax / 4) + 128 + r * opr + sg / a.obs16] = ro.outer;
+                    tailf[par * (kTailCap / 4) + 128 + r * opr + sg / a.obs16] = ro.outer;
             }
             if (EF || Y) {
                 float w[16];
@@ -517,15 +526,17 @@ void k_tile(TileArgs a)
                     buf_store16<kNT>(ry, oy + 16u, make_uint4(o[4], o[5], o[6], o[7]));
                 }
                 if (EF) {
-                    const rsrc_t rz = make_rsrc(a.residual + cur.e_base);
-                    const uint32_t oz = act ? erow * 4u : kOff;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        buf_store16(rz, oz + 16u * q,
-                                    make_uint4(__float_as_uint(v[4 * q] - w[4 * q]),
-                                               __float_as_uint(v[4 * q + 1] - w[4 * q + 1]),
-                                               __float_as_uint(v[4 * q + 2] - w[4 * q + 2]),
-                                               __float_as_uint(v[4 * q + 3] - w[4 * q + 3])));
+                    for (int k = 0; k < 16; ++k) res[k] = v[k] - w[k];
+                    if (!COLS) {
+                        const rsrc_t rz = make_rsrc(a.residual + cur.e_base);
+                        const uint32_t oz = act ? erow * 4u : kOff;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            buf_store16(rz, oz + 16u * q,
+                                        make_uint4(__float_as_uint(res[4 * q]), __float_as_uint(res[4 * q + 1]),
+                                                   __float_as_uint(res[4 * q + 2]), __float_as_uint(res[4 * q + 3])));
+                    }
                 }
             }
         }
@@ -545,7 +556,26 @@ void k_tile(TileArgs a)
                         make_uint4(u[4 * j], u[4 * j + 1], u[4 * j + 2], u[4 * j + 3]);
             }
             if (I2D && (r & 15) == 0) lds_tsc[(r >> 4) * 4 + sg] = ro.scale;
+            if (EF) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    lds_res[lds_row + swz_chunk(r, 4 * sg + j)] =
+                        make_float4(res[4 * j], res[4 * j + 1], res[4 * j + 2], res[4 * j + 3]);
+            }
             lds_barrier();
+            if (EF) {
+                // row-coalesced residual store: pass q, lane t takes row 16 q + t / 16, columns 4 (t % 16) .. + 3
+                const rsrc_t rz = make_rsrc(a.residual + cur.e_base);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int row = 16 * q + (tid >> 4), ch = tid & 15;
+                    const float4 f = lds_res[row * 16 + swz_chunk(row, ch)];
+                    const bool ok = row < cur.rows_valid && 4 * ch < cur.cols_valid;
+                    buf_store16(rz, ok ? (uint32_t)(row * cols + 4 * ch) * 4u : kOff,
+                                make_uint4(__float_as_uint(f.x), __float_as_uint(f.y), __float_as_uint(f.z),
+                                           __float_as_uint(f.w)));
+                }
+            }
 
             // ---------------- column phase
             const float* lf = reinterpret_cast<const float*>(lds_v);
@@ -602,9 +632,9 @@ void k_tile(TileArgs a)
             }
             if (STAGED) {
                 const int par = iter & 1;
-                tail8[par * kTailMax + 256 + cc * 4 + rs] = (uint8_t)co.scale;
+                tail8[par * kTailCap + 256 + cc * 4 + rs] = (uint8_t)co.scale;
                 if (OUTER == kOuter1D && !GIVEN && (rs % a.obs16) == 0)
-                    tailf[par * (kTailMax / 4) + 128 + 64 * opr + cc * opr + rs / a.obs16] = co.outer;
+                    tailf[par * (kTailCap / 4) + 128 + 64 * opr + cc * opr + rs / a.obs16] = co.outer;
             }
         }
         ++iter;
@@ -629,7 +659,7 @@ void k_tile(TileArgs a)
         const bool line_ok = enable && r < ta.rows_valid;
         const rsrc_t rc = make_rsrc(a.row_codes ? a.row_codes + ta.e_base / 2 : nullptr);
         const rsrc_t rsc = make_rsrc(a.row_scales ? a.row_scales + ta.e_base / 16 : nullptr);
-        store_pair(stage[0], r, sg, A, B, line_ok, nvalid, rc, (uint32_t)(r * cols) / 2u, rsc,
+        store_pair(*stage, r, sg, A, B, line_ok, nvalid, rc, (uint32_t)(r * cols) / 2u, rsc,
                    (uint32_t)(r * cols) / 16u);
         if (OUTER == kOuter1D && !GIVEN) {
             const int gpr = cols / obs;
@@ -646,7 +676,7 @@ void k_tile(TileArgs a)
         const int nvalid = ta.rows_valid / 16 + tb.rows_valid / 16;
         const bool line_ok = enable && cc < ta.cols_valid;
         const uint32_t ecol = (uint32_t)(cc * ta.Rg);   // lane's column, relative to the run start
-        store_pair(stage[0], cc, rs, A, B, line_ok, nvalid, make_rsrc(a.col_codes + ta.ce_base / 2), ecol / 2u,
+        store_pair(*stage, cc, rs, A, B, line_ok, nvalid, make_rsrc(a.col_codes + ta.ce_base / 2), ecol / 2u,
                    make_rsrc(a.col_scales + ta.ce_base / 16), ecol / 16u);
         if (OUTER == kOuter1D && !GIVEN) {
             const int gpc = ta.Rg / obs;
