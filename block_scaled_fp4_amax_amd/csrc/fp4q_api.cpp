@@ -341,15 +341,17 @@ int rowwise(const fp4q_cfg* cfg, const void* x, int64_t rows, int64_t cols, int6
     if (r.outer_kind == kOuterTensor) {
         if (r.given) {
             a.tensor_scale = outer;
-        } else if (rows * cols > kSmallTensorElems) {
+        } else if (rows * cols > kSmallTensorElems || residual != nullptr) {
             float* wsf = (float*)ws;
             hipError_t e = launch_amax(r.bias, x, r.x_f32, x_vec, rows, cols, ld, residual, wsf + 1, kAmaxPartials, wsf,
                                        outer, s);
             if (e != hipSuccess) return FP4Q_ERR_HIP;
             a.tensor_scale = wsf;
         }
-        // else: a small tensor -- one launch, each workgroup takes the amax itself
-        // (tensor_scale stays null; the kernel writes outer when given)
+        // else: a small tensor without a residual -- one launch, each workgroup
+        // takes the amax itself (tensor_scale stays null; the kernel writes
+        // outer when given).  With error feedback the amax is over x + r while
+        // other workgroups rewrite r in place, so those calls keep the passes.
     }
     return hip_status(launch_rows(r.bias, r.outer_kind, r.sr, r.x_f32, a, s));
 }

@@ -158,12 +158,15 @@ __device__ __forceinline__ uint32_t amax_bf16_chunks(const uint16_t* x, int64_t 
     return lo > hi ? lo : hi;
 }
 
-// Rowwise NV / AMD quantisation; SMALL (tensorwise only): every workgroup
-// first takes the amax of the whole tensor itself (a small tensor is read from
-// the caches once per workgroup), so the global scale needs no second launch.
+// Rowwise NV / AMD quantisation; SMALL (tensorwise without a residual only):
+// every workgroup first takes the amax of the whole tensor itself (a small
+// tensor is read from the caches once per workgroup), so the global scale
+// needs no second launch.  With a residual it cannot: other workgroups rewrite
+// the residual in place while the amax is being taken.
 template <int BIAS, int OUTER, bool SR, bool EF, bool XF32, bool SMALL>
 __global__ __launch_bounds__(kThreads) void k_nv_rows(RowArgs a, uint32_t nblocks, uint32_t bpr)
 {
+    static_assert(!(SMALL && EF), "the one-launch tensorwise form reads the residual that it rewrites");
     __shared__ double rtab[16];
     __shared__ float2 ktab[SR ? 1 : kRneTableSize];
     __shared__ uint32_t wmax[kThreads / 64];
@@ -172,7 +175,7 @@ __global__ __launch_bounds__(kThreads) void k_nv_rows(RowArgs a, uint32_t nblock
     float s_small = 0.0f;
     if (SMALL) {
         uint32_t m;
-        if (!XF32 && !EF && a.x_vec) {
+        if (!XF32 && a.x_vec) {
             // bf16 without a residual: packed maxima of the raw bits; the
             // sanitised pass only if a NaN / inf turned up (a uniform branch)
             m = wave_max_u32(amax_bf16_chunks(static_cast<const uint16_t*>(a.x), a.rows, a.cols, a.ld));
@@ -190,8 +193,7 @@ __global__ __launch_bounds__(kThreads) void k_nv_rows(RowArgs a, uint32_t nblock
                 m = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
             }
         } else {
-            m = amax_blocks<XF32>(a.x, a.x_vec, EF ? a.residual : nullptr, a.cols, a.ld, nblocks, bpr, threadIdx.x,
-                                  kThreads);
+            m = amax_blocks<XF32>(a.x, a.x_vec, nullptr, a.cols, a.ld, nblocks, bpr, threadIdx.x, kThreads);
             m = wave_max_u32(m);
             if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
             __syncthreads();
@@ -379,13 +381,21 @@ hipError_t launch_rows(int bias, int outer_kind, bool sr, bool x_f32, const RowA
     const uint32_t nblocks = (uint32_t)(a.rows * bpr);
     const uint32_t grid = (nblocks + kThreads - 1) / kThreads;
     const bool ef = a.residual != nullptr;
+    // tensorwise with no scale given: the one-launch small-tensor form, which
+    // the host selects only without a residual (with one, the amax passes run
+    // first and tensor_scale is set)
     const bool small = outer_kind == kOuterTensor && a.tensor_scale == nullptr;
+    if (small && ef) return hipErrorInvalidValue;
 #define FP4Q_ROWS(B, O, S, E)                                                                                   \
     do {                                                                                                        \
-        if (O == kOuterTensor && small) {                                                                       \
-            if (x_f32) hipLaunchKernelGGL((k_nv_rows<B, O, S, E, true, true>), dim3(grid), dim3(kThreads), 0, s, a, nblocks, bpr); \
-            else hipLaunchKernelGGL((k_nv_rows<B, O, S, E, false, true>), dim3(grid), dim3(kThreads), 0, s, a, nblocks, bpr); \
-        } else if (x_f32) hipLaunchKernelGGL((k_nv_rows<B, O, S, E, true, false>), dim3(grid), dim3(kThreads), 0, s, a, nblocks, bpr); \
+        if constexpr (O == kOuterTensor && !E) {                                                                \
+            if (small) {                                                                                        \
+                if (x_f32) hipLaunchKernelGGL((k_nv_rows<B, O, S, E, true, true>), dim3(grid), dim3(kThreads), 0, s, a, nblocks, bpr); \
+                else hipLaunchKernelGGL((k_nv_rows<B, O, S, E, false, true>), dim3(grid), dim3(kThreads), 0, s, a, nblocks, bpr); \
+                break;                                                                                          \
+            }                                                                                                   \
+        }                                                                                                       \
+        if (x_f32) hipLaunchKernelGGL((k_nv_rows<B, O, S, E, true, false>), dim3(grid), dim3(kThreads), 0, s, a, nblocks, bpr); \
         else hipLaunchKernelGGL((k_nv_rows<B, O, S, E, false, false>), dim3(grid), dim3(kThreads), 0, s, a, nblocks, bpr); \
     } while (0)
 #define FP4Q_ROWS_E(B, O, S)                     \

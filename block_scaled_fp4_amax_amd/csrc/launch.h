@@ -205,9 +205,10 @@ hipError_t launch_dequant_mx(const uint8_t* codes, const uint8_t* scales, int64_
 // partial maxima used by the tensorwise amax pass
 constexpr int kAmaxPartials = 512;
 
-// Rowwise tensorwise calls on at most this many elements run in one launch:
-// every workgroup reads the whole (cache-resident) tensor for its amax
-// instead of a grid-wide amax pass and a scale pass before the quantiser.
+// Rowwise tensorwise calls on at most this many elements and without an
+// error-feedback residual run in one launch: every workgroup reads the whole
+// (cache-resident) tensor for its amax instead of a grid-wide amax pass and a
+// scale pass before the quantiser.
 constexpr int64_t kSmallTensorElems = (int64_t)1 << 18;
 
 }  // namespace fp4q
