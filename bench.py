@@ -557,6 +557,8 @@ def main():
                                      "residual_start": "zeros"}},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     # measured HBM bytes per step (staging round trip included) over the same step time
+                     "traffic_GB/s": round(traffic / (per_ms * 1e-3) / 1e9, 2) if traffic else None,
                      "kernel": "one step = k_tile (tile pass) + k_gather (whole-line gather), timed together",
                      "traffic_source": "profiles/traffic_counters.json[%s] (rocprofv3 FETCH_SIZE + WRITE_SIZE of "
                                        "both kernels per step, scaled by a plain copy)" % key},

@@ -168,10 +168,10 @@ __global__ __launch_bounds__(kThreads) void k_nv_rows(RowArgs a, uint32_t nblock
 {
     static_assert(!(SMALL && EF), "the one-launch tensorwise form reads the residual that it rewrites");
     __shared__ double rtab[16];
-    __shared__ float2 ktab[SR ? 1 : kRneTableSize];
+    __shared__ float2 ktab[kRneTableSize];
     __shared__ uint32_t wmax[kThreads / 64];
     fill_recip_table(rtab, (int)threadIdx.x);
-    if (!SR) fill_rne_table<BIAS>(ktab, (int)threadIdx.x);
+    fill_rne_table<BIAS>(ktab, (int)threadIdx.x);
     float s_small = 0.0f;
     if (SMALL) {
         uint32_t m;
@@ -269,7 +269,7 @@ __global__ __launch_bounds__(kThreads) void k_nv_rows(RowArgs a, uint32_t nblock
         normalize16(v, s_o, outer_inv(s_o), vn, true);
     }
     const BlockScale<BIAS> sc = block_scale<BIAS>(max_abs16(vn), rtab);
-    const uint2 packed = SR ? codes16_sr<BIAS, OUTER == kOuterNone>(vn, u, sc) : codes16_rne(vn, ktab[sc.code]);
+    const uint2 packed = SR ? codes16_sr<OUTER == kOuterNone>(vn, u, ktab[sc.code]) : codes16_rne(vn, ktab[sc.code]);
     if (a.codes) st_nt64(a.codes + e0 / 2, packed);
     if (a.scales) st_nt8(a.scales + (int64_t)i * bpr + jb, sc.code);
     if (a.y || EF) {

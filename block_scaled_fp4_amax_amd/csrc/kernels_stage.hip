@@ -11,10 +11,12 @@
 // adding its codes and scale bytes as pieces of 32 or 64 bytes from different
 // workgroups takes it from 0.48 to 0.82 ms, as whole lines to 0.53 ms).  The tile kernel
 // therefore writes whole lines of a tile-major scratch, and this pass writes
-// whole lines of the final buffers: one workgroup per 64-row band (rowwise
-// codes, scale bytes, 1D outer scales: a contiguous range of each buffer) or
-// per 64-column band (the same for the columnwise buffers), gathering each
-// 16-byte chunk from the staged blocks (layout in launch.h).
+// whole lines of the final buffers.  A work unit is a slice of up to 64 lines
+// (rows of a rowwise buffer, columns of a columnwise one) of one 64-line band
+// and one output kind; its bytes are one contiguous range of the buffer.  The
+// workgroup reads the slice's part of every tile block along the band (one
+// contiguous run per tile), places the pieces in LDS in output order and
+// writes the range as 16-byte stores (staged layout in launch.h).
 #include <algorithm>
 
 #include "launch.h"

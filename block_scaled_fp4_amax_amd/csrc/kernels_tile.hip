@@ -104,7 +104,7 @@ template <int BIAS, bool SR, bool CLAMP>
 __device__ __forceinline__ uint2 encode16(const float (&vn)[16], const uint32_t (&u)[8], const float2* ktab,
                                           const BlockScale<BIAS>& sc)
 {
-    if (SR) return codes16_sr<BIAS, CLAMP>(vn, u, sc);
+    if (SR) return codes16_sr<CLAMP>(vn, u, ktab[sc.code]);
     return codes16_rne(vn, ktab[sc.code]);
 }
 
@@ -332,7 +332,7 @@ void k_tile(TileArgs a)
     __shared__ uint32_t lds_tsc[(COLS && I2D) ? 16 : 1];   // 16 x 16 inner scale codes, [tile row][tile col]
     __shared__ uint32_t red[2][kThreads / 64];
     __shared__ double rtab[kRecipTableSize];
-    __shared__ float2 ktab[SR ? 1 : kRneTableSize];
+    __shared__ float2 ktab[kRneTableSize];
     // paired-tile stores (direct path only)
     __shared__ uint4 pair_raw[STAGED ? 1 : (sizeof(PairStage) + 15) / 16];
     PairStage* const stage = reinterpret_cast<PairStage*>(pair_raw);
@@ -364,7 +364,7 @@ void k_tile(TileArgs a)
     TileInput<EF> in;
     load_tile_input<EF>(a, STAGED ? make_tile_unit(a, walk) : make_tile(a, walk, 0), true, r, sg, in);
     fill_recip_table(rtab, tid);
-    if (!SR) fill_rne_table<BIAS>(ktab, tid);
+    fill_rne_table<BIAS>(ktab, tid);
     lds_barrier();
     const float den = ScaleFmt<BIAS>::outer_den();
     const int cols = (int)a.cols;

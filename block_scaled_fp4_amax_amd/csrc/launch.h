@@ -62,12 +62,12 @@ struct TileArgs {
     int32_t wgs_per_xcd;     // persistent workgroups per XCD (grid = 8 * wgs_per_xcd)
     int32_t row0[kMaxGroupsPerLaunch + 1];   // prefix rows of the groups
     int32_t tile0[kMaxGroupsPerLaunch + 1];  // prefix unit counts of the groups (super-tiles, or tiles when staged)
-    // Staged output (cast-transpose with stochastic rounding, a residual or 1D
-    // outer groups): when `stage` is set, the walk unit is one 64 x 64 tile
+    // Staged output (cast-transpose calls with an error-feedback residual, see
+    // stage_applies): when `stage` is set, the walk unit is one 64 x 64 tile
     // (tiles_c = ceil(cols / 64), tile0 in tiles) and every code, scale byte and
     // 1D outer scale goes to block `unit index` of `stage` (stage_block bytes,
-    // layout in kernels_tile.hip) as whole 128-byte lines; launch_tiles then
-    // gathers the blocks into the row-major outputs.
+    // layout below) as whole 128-byte lines; the host then launches the
+    // gather (launch_gather) that moves the blocks into the row-major outputs.
     uint8_t* stage;          // 128-byte aligned, or null for direct stores
     int32_t stage_block;     // bytes per tile block
 };

@@ -171,18 +171,29 @@ __device__ __forceinline__ uint2 codes16_rne(const float (&vn)[16], float2 k)
 //   - the instruction's second slot draws from the seed shifted by one bit, so
 //     each element goes through a first slot of its own: even elements into one
 //     word, odd elements into another, merged by a shift.
-// c comes from T = RN32(v_n * RN64(1/d) * 2^23), which is t * 2^23 exactly while
-// t is a normal binary32.  Below that only "t > 0" matters (c = 1 rounds up iff
-// u16 == 0), and t > 0 exactly when T > 2^-127: the quotient v_n / d is either
-// 2^-150 exactly (T = 2^-127, t = 0) or at least 2^-7 of itself away from it
-// (v_n is then subnormal and d has 4 significant bits).  ceil(|T| - 2^-127)
-// gives both cases, and ceil(t * 2^23) from T = 2^-100 on.  Without an outer
-// scale t can exceed 2^104 (saturated inner scales), so CLAMP bounds T to
-// [2^-127, 6 * 2^23] first; otherwise t stays near 6 and the instruction
-// saturates by itself.  Magnitude nibbles carry no sign (the masks drop the -0
-// that ceil gives for T == 0); the sign nibbles come from the hardware RNE pack
-// of v_n / 2^125, which is a zero of v_n's sign unless |v_n| >= 2^123, and such
-// values saturate (code 7) under every inner scale, so OR-ing stays exact.
+// c = ceil(T - 2^-127) with T = |v_n| / d * 2^23 rounded to binary32: that is
+// t * 2^23 exactly while t is a normal binary32.  Below that only "t > 0"
+// matters (c = 1 rounds up iff u16 == 0), and t > 0 exactly when T > 2^-127:
+// the quotient v_n / d is either 2^-150 exactly (T = 2^-127, t = 0) or at
+// least 2^-7 of itself away from it (v_n is then subnormal and d has 4
+// significant bits).  ceil(T - 2^-127) gives both cases, and ceil(t * 2^23)
+// from T = 2^-100 on.  T comes from the scale code's two-term reciprocal (the
+// RNE table below, times 2^23): with d of at most 4 significant bits, |v_n| / d
+// is never within 2^-29 (relative) of a binary32 rounding midpoint, and
+// |v_n| Kh + RN32(|v_n| Kl) is within 2^-46 of it, so one fma rounds it to the
+// same binary32; the -2^-127 rides in the low term (it is below half an ulp of
+// T from T = 2^-103 on, and below that only T's side of 2^-127 matters, which
+// it keeps).  Two fmas and a ceil per value, checked on the CPU against
+// ceil(RN32(|v_n| RN64(1/d) 2^23) - 2^-127) for every scale code of both inner
+// formats on 6.5e8 values (log-uniform over 2^-160 .. 2^8 times d, the
+// neighbourhoods of decision points, and the subnormal range), with and without
+// the clamp.  Without an outer scale t can exceed 2^104 (saturated inner
+// scales), so CLAMP bounds T to [0, 6 * 2^23]; otherwise t stays near 6 and the
+// instruction saturates by itself.  Magnitude nibbles carry no sign (the masks
+// drop the -0 that ceil gives for T < 0); the sign nibbles come from the
+// hardware RNE pack of v_n / 2^125, which is a zero of v_n's sign unless
+// |v_n| >= 2^123, and such values saturate (code 7) under every inner scale,
+// so OR-ing stays exact.
 
 // The code of c / 2^23 (first slot, seed as above) in bits 8 SEL .. 8 SEL + 2,
 // every other bit zero.  Only those magnitude bits of the result are used: the
@@ -198,16 +209,18 @@ __device__ __forceinline__ uint32_t sr_code_at(float c, uint32_t seed)
     return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, v, seed, 0x1p23f, SEL) & (0x7u << (8 * SEL));
 }
 
+// ceil(|v| / d * 2^23 - 2^-127) from (Kh, Kl) * 2^23 of the block's scale.
 template <bool CLAMP>
-__device__ __forceinline__ float sr_fixed23(float T)
+__device__ __forceinline__ float sr_fixed23(float v, float kh23, float kl23)
 {
-    float a = __builtin_fabsf(T);
-    if (CLAMP) a = __builtin_amdgcn_fmed3f(a, 0x1p-127f, 0x1.8p25f);
-    return __builtin_ceilf(a - 0x1p-127f);
+    const float av = __builtin_fabsf(v);
+    float a = __builtin_fmaf(av, kh23, __builtin_fmaf(av, kl23, -0x1p-127f));
+    if (CLAMP) a = __builtin_amdgcn_fmed3f(a, 0.0f, 0x1.8p25f);
+    return __builtin_ceilf(a);
 }
 
 template <bool CLAMP>
-__device__ __forceinline__ uint32_t codes8_sr(const float* vn, const uint32_t* u, double rd23)
+__device__ __forceinline__ uint32_t codes8_sr(const float* vn, const uint32_t* u, float kh23, float kl23)
 {
     constexpr float kSignOnly = 0x1p125f;
     uint32_t sg = 0;
@@ -218,28 +231,28 @@ __device__ __forceinline__ uint32_t codes8_sr(const float* vn, const uint32_t* u
     // element 2j takes the low 16 bits of u[j], element 2j + 1 the high 16 bits
     uint32_t ev, od, nw;
     nw = ~u[0];
-    ev = sr_code_at<0>(sr_fixed23<CLAMP>(div_inv64(vn[0], rd23)), (nw << 16) | 0xFFFFu);
-    od = sr_code_at<0>(sr_fixed23<CLAMP>(div_inv64(vn[1], rd23)), nw | 0xFFFFu);
+    ev = sr_code_at<0>(sr_fixed23<CLAMP>(vn[0], kh23, kl23), (nw << 16) | 0xFFFFu);
+    od = sr_code_at<0>(sr_fixed23<CLAMP>(vn[1], kh23, kl23), nw | 0xFFFFu);
     nw = ~u[1];
-    ev |= sr_code_at<1>(sr_fixed23<CLAMP>(div_inv64(vn[2], rd23)), (nw << 16) | 0xFFFFu);
-    od |= sr_code_at<1>(sr_fixed23<CLAMP>(div_inv64(vn[3], rd23)), nw | 0xFFFFu);
+    ev |= sr_code_at<1>(sr_fixed23<CLAMP>(vn[2], kh23, kl23), (nw << 16) | 0xFFFFu);
+    od |= sr_code_at<1>(sr_fixed23<CLAMP>(vn[3], kh23, kl23), nw | 0xFFFFu);
     nw = ~u[2];
-    ev |= sr_code_at<2>(sr_fixed23<CLAMP>(div_inv64(vn[4], rd23)), (nw << 16) | 0xFFFFu);
-    od |= sr_code_at<2>(sr_fixed23<CLAMP>(div_inv64(vn[5], rd23)), nw | 0xFFFFu);
+    ev |= sr_code_at<2>(sr_fixed23<CLAMP>(vn[4], kh23, kl23), (nw << 16) | 0xFFFFu);
+    od |= sr_code_at<2>(sr_fixed23<CLAMP>(vn[5], kh23, kl23), nw | 0xFFFFu);
     nw = ~u[3];
-    ev |= sr_code_at<3>(sr_fixed23<CLAMP>(div_inv64(vn[6], rd23)), (nw << 16) | 0xFFFFu);
-    od |= sr_code_at<3>(sr_fixed23<CLAMP>(div_inv64(vn[7], rd23)), nw | 0xFFFFu);
+    ev |= sr_code_at<3>(sr_fixed23<CLAMP>(vn[6], kh23, kl23), (nw << 16) | 0xFFFFu);
+    od |= sr_code_at<3>(sr_fixed23<CLAMP>(vn[7], kh23, kl23), nw | 0xFFFFu);
     return sg | ev | (od << 4);
 }
 
-// SR codes of 16 normalised values with the block's scale; CLAMP when no
-// outer scale bounds the quotients.
-template <int BIAS, bool CLAMP>
-__device__ __forceinline__ uint2 codes16_sr(const float (&vn)[16], const uint32_t (&u)[8], const BlockScale<BIAS>& s)
+// SR codes of 16 normalised values with the block's scale, given as its RNE
+// table entry k = (Kh, Kl); CLAMP when no outer scale bounds the quotients.
+template <bool CLAMP>
+__device__ __forceinline__ uint2 codes16_sr(const float (&vn)[16], const uint32_t (&u)[8], float2 k)
 {
-    const double rd23 = s.rd * 0x1p23;
-    const uint32_t lo = codes8_sr<CLAMP>(vn, u, rd23);
-    const uint32_t hi = codes8_sr<CLAMP>(vn + 8, u + 4, rd23);
+    const float kh23 = k.x * 0x1p23f, kl23 = k.y * 0x1p23f;
+    const uint32_t lo = codes8_sr<CLAMP>(vn, u, kh23, kl23);
+    const uint32_t hi = codes8_sr<CLAMP>(vn + 8, u + 4, kh23, kl23);
     return make_uint2(lo, hi);
 }
 
