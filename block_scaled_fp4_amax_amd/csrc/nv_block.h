@@ -185,9 +185,9 @@ __device__ __forceinline__ uint2 codes16_rne(const float (&vn)[16], float2 k)
 // T from T = 2^-103 on, and below that only T's side of 2^-127 matters, which
 // it keeps).  Two fmas and a ceil per value, checked on the CPU against
 // ceil(RN32(|v_n| RN64(1/d) 2^23) - 2^-127) for every scale code of both inner
-// formats on 6.5e8 values (log-uniform over 2^-160 .. 2^8 times d, the
-// neighbourhoods of decision points, and the subnormal range), with and without
-// the clamp.  Without an outer scale t can exceed 2^104 (saturated inner
+// formats on 3.2e8 values (log-uniform over 2^-160 .. 2^8 times d, the
+// neighbourhoods of decision points, and the subnormal range), each with and
+// without the clamp.  Without an outer scale t can exceed 2^104 (saturated inner
 // scales), so CLAMP bounds T to [0, 6 * 2^23]; otherwise t stays near 6 and the
 // instruction saturates by itself.  Magnitude nibbles carry no sign (the masks
 // drop the -0 that ceil gives for T < 0); the sign nibbles come from the
