@@ -139,15 +139,24 @@ __device__ __forceinline__ uint32_t amax_bf16_chunks(const uint16_t* x, int64_t 
 {
     const uint32_t cpr = (uint32_t)(cols / 8);                 // 16-byte chunks per row
     const uint32_t n = (uint32_t)(rows * cpr);
+    const bool dense = ld == cols;                             // chunk c at x + 8 c (uniform)
     uint32_t m = 0;
     for (uint32_t c0 = threadIdx.x; c0 < n; c0 += 16 * kThreads) {
         uint4 w[16];
+        // ordinary (cached) loads: every workgroup of the launch reads the
+        // same small tensor, so all but the first reads per XCD hit its L2
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
             uint32_t c = c0 + (uint32_t)k * kThreads;
             c = c < n ? c : 0u;
-            const uint32_t i = c / cpr;
-            w[k] = ld_nt16(x + (int64_t)i * ld + (int64_t)(c - i * cpr) * 8);
+            int64_t off;
+            if (dense) {
+                off = (int64_t)c * 8;
+            } else {
+                const uint32_t i = c / cpr;
+                off = (int64_t)i * ld + (int64_t)(c - i * cpr) * 8;
+            }
+            w[k] = *reinterpret_cast<const uint4*>(x + off);
         }
 #pragma unroll
         for (int k = 0; k < 16; ++k)
@@ -172,6 +181,19 @@ __global__ __launch_bounds__(kThreads) void k_nv_rows(RowArgs a, uint32_t nblock
     __shared__ uint32_t wmax[kThreads / 64];
     fill_recip_table(rtab, (int)threadIdx.x);
     fill_rne_table<BIAS>(ktab, (int)threadIdx.x);
+    const uint32_t b = blockIdx.x * kThreads + threadIdx.x;   // inner block id
+    // the small form's bf16 source: the lane's own block is requested before
+    // the amax pass, so its load overlaps that pass (lanes past the end load
+    // block 0 and return below)
+    const bool early = SMALL && !XF32 && a.x_vec;              // uniform
+    uint4 pre0 = make_uint4(0u, 0u, 0u, 0u), pre1 = pre0;
+    if (early) {
+        const uint32_t bb = b < nblocks ? b : 0u;
+        const uint32_t ii = bb / bpr;
+        const uint16_t* p = static_cast<const uint16_t*>(a.x) + (int64_t)ii * a.ld + (int64_t)(bb - ii * bpr) * 16;
+        pre0 = *reinterpret_cast<const uint4*>(p);
+        pre1 = *reinterpret_cast<const uint4*>(p + 8);
+    }
     float s_small = 0.0f;
     if (SMALL) {
         uint32_t m;
@@ -203,7 +225,6 @@ __global__ __launch_bounds__(kThreads) void k_nv_rows(RowArgs a, uint32_t nblock
         if (a.outer && blockIdx.x == 0 && threadIdx.x == 0) a.outer[0] = s_small;
     }
     __syncthreads();
-    const uint32_t b = blockIdx.x * kThreads + threadIdx.x;   // inner block id
     // lanes of one 1D outer group are consecutive and bpr % obs16 == 0, so a
     // group is entirely inside or outside the tensor
     if (b >= nblocks) return;
@@ -216,7 +237,14 @@ __global__ __launch_bounds__(kThreads) void k_nv_rows(RowArgs a, uint32_t nblock
     float z[16];
     uint32_t am_bits = 0;
     {
-        am_bits = load_src16<XF32>(a.x, (int64_t)i * a.ld + j0, a.x_vec != 0, v);
+        if (early) {
+            const uint32_t w[8] = {pre0.x, pre0.y, pre0.z, pre0.w, pre1.x, pre1.y, pre1.z, pre1.w};
+#pragma unroll
+            for (int k = 0; k < 8; ++k) { v[2 * k] = bf16_lo(w[k]); v[2 * k + 1] = bf16_hi(w[k]); }
+            am_bits = bf16_absmax_bits(w) << 16;
+        } else {
+            am_bits = load_src16<XF32>(a.x, (int64_t)i * a.ld + j0, a.x_vec != 0, v);
+        }
         if (EF) {
             load16_f32(a.residual + e0, z);
             am_bits = 0;
