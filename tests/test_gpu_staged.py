@@ -63,6 +63,11 @@ CASES = [
     ("amdfp4", "tensorwise", 0, False, False, (64, 64)),
     ("nvfp4", "outer", 64, False, False, (320, 192)),
     ("amdfp4", "outer", 128, False, True, (256, 384)),
+    # whole 64-column tiles with 1D outer groups of 32 and 16: the gather's
+    # outer-scale runs of 8 and 16 bytes per tile line take its run-copy path
+    ("amdfp4", "outer", 32, False, True, (128, 192)),
+    ("nvfp4", "outer", 16, False, True, (64, 256)),
+    ("nvfp4", "outer", 32, False, False, (96, 128)),
 ]
 
 
