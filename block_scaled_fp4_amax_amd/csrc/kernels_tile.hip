@@ -852,13 +852,20 @@ Residency residency(const void* fn)
     return r;
 }
 
-// Launch one persistent grid: as many workgroups per XCD as fit at once,
-// spread so that every workgroup of a slice takes the same number of tiles
-// (to within one).
+// Staged (error-feedback) launches: workgroups per CU.  Their traffic is the
+// residual's read-modify-write plus bf16 reads and whole-line block stores;
+// measured on the grouped 32 x 2880^2 step with 1 / 2 / 3 (the LDS limit)
+// workgroups per CU: 0.49 / 0.535 / 0.53 of the HBM peak.
+constexpr int kStagedWgsPerCu = 2;
+
+// Launch one persistent grid: as many workgroups per XCD as fit at once
+// (staged launches: at most kStagedWgsPerCu per CU), spread so that every
+// workgroup of a slice takes the same number of tiles (to within one).
 hipError_t launch_persistent(void (*fn)(TileArgs), TileArgs a, hipStream_t s)
 {
     const Residency r = residency(reinterpret_cast<const void*>(fn));
-    const int cap = r.wgs_per_cu * (r.cus / 8);
+    const int per_cu = a.stage ? min(r.wgs_per_cu, kStagedWgsPerCu) : r.wgs_per_cu;
+    const int cap = per_cu * (r.cus / 8);
     int w = a.wgs_per_xcd < cap ? a.wgs_per_xcd : cap;
     if (w < 1) w = 1;
     const int rounds = (a.per_xcd + w - 1) / w;
