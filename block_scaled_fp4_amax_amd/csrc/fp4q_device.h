@@ -267,10 +267,11 @@ __device__ __forceinline__ void buf_store16(rsrc_t r, uint32_t off, uint4 v)
     __builtin_amdgcn_raw_buffer_store_b128(w, r, off, 0, POLICY);
 }
 
+template <int POLICY = 0>
 __device__ __forceinline__ void buf_store8(rsrc_t r, uint32_t off, uint2 v)
 {
     const u32x2_t w = {v.x, v.y};
-    __builtin_amdgcn_raw_buffer_store_b64(w, r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(w, r, off, 0, POLICY);
 }
 
 __device__ __forceinline__ void buf_store_u32(rsrc_t r, uint32_t off, uint32_t v)

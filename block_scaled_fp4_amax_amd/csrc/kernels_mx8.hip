@@ -35,7 +35,9 @@
 //                one 32 x 1 block per column: MXFP8 column payload and scale,
 //                128 x 128 transposed payload.
 // Stores cover whole 128-byte lines per wave instruction wherever the layout
-// allows (row payloads: 4 rows x 128 B; column payloads: 4 columns x 128 B).
+// allows (row payloads: 4 rows x 128 B; column payloads: 4 columns x 128 B),
+// with the non-temporal policy: nothing here is read back (8192^2 with every
+// output: 0.115-0.118 -> 0.112 ms).
 #include "fp4q_device.h"
 #include "launch.h"
 
@@ -168,7 +170,7 @@ __global__ __launch_bounds__(kThreads) void k_mx_fp8(Mx8Args a)
         if (WY) buf_store16<kNT>(ry, act ? (uint32_t)(row * (int)a.cols + 8 * cc) * 2u : kOff, yp);
         if (ROW8) {
             const int E = max(-127, L - 8);
-            buf_store8(rp, act ? (uint32_t)(row * (int)a.cols + 8 * cc) : kOff, fp8x8(yv, pow2f(E)));
+            buf_store8<kNT>(rp, act ? (uint32_t)(row * (int)a.cols + 8 * cc) : kOff, fp8x8(yv, pow2f(E)));
             buf_store_u8(rps, (act && (cc & 3) == 0) ? (uint32_t)(row * ((int)a.cols / 32) + cc / 4) : kOff,
                          (uint32_t)(E + 127));
         }
@@ -222,7 +224,7 @@ __global__ __launch_bounds__(kThreads) void k_mx_fp8(Mx8Args a)
                 yv[2 * q + 1] = bf16_hi(w[q]);
             }
             prescale(yv);
-            buf_store8(rb, act ? (uint32_t)(row * (int)a.cols + 8 * cc) : kOff, fp8x8(yv, sblk));
+            buf_store8<kNT>(rb, act ? (uint32_t)(row * (int)a.cols + 8 * cc) : kOff, fp8x8(yv, sblk));
         }
     }
 
@@ -258,8 +260,8 @@ __global__ __launch_bounds__(kThreads) void k_mx_fp8(Mx8Args a)
             const int El = max(-127, (int)(bl >> 23) - 127 - 8);
             const int Eh = max(-127, (int)(bh >> 23) - 127 - 8);
             const uint32_t ocol = (uint32_t)(2 * dc * rows_c + 8 * rg);
-            buf_store8(rc, act ? ocol : kOff, fp8x8(lo, pow2f(El)));
-            buf_store8(rc, act ? ocol + (uint32_t)rows_c : kOff, fp8x8(hi, pow2f(Eh)));
+            buf_store8<kNT>(rc, act ? ocol : kOff, fp8x8(lo, pow2f(El)));
+            buf_store8<kNT>(rc, act ? ocol + (uint32_t)rows_c : kOff, fp8x8(hi, pow2f(Eh)));
             const uint32_t osc = (uint32_t)(2 * dc * (rows_c / 32) + rg / 4);
             buf_store_u8(rcs, (act && (rg & 3) == 0) ? osc : kOff, (uint32_t)(El + 127));
             buf_store_u8(rcs, (act && (rg & 3) == 0) ? osc + (uint32_t)(rows_c / 32) : kOff, (uint32_t)(Eh + 127));
@@ -268,8 +270,8 @@ __global__ __launch_bounds__(kThreads) void k_mx_fp8(Mx8Args a)
             prescale(lo);
             prescale(hi);
             const uint32_t ocol = (uint32_t)(2 * dc * rows_c + 8 * rg);
-            buf_store8(rbt, act ? ocol : kOff, fp8x8(lo, sblk));
-            buf_store8(rbt, act ? ocol + (uint32_t)rows_c : kOff, fp8x8(hi, sblk));
+            buf_store8<kNT>(rbt, act ? ocol : kOff, fp8x8(lo, sblk));
+            buf_store8<kNT>(rbt, act ? ocol + (uint32_t)rows_c : kOff, fp8x8(hi, sblk));
         }
     }
 }
