@@ -5,8 +5,10 @@ of 16 / 32 / 64 / 128, the 2D 64 x 64 outer tile), RNE or stochastic rounding
 with a random seed, step and index base, an optional error-feedback residual,
 an entry point (fp4_qdq, fp4_quantize, fp4_cast_transpose staged or direct,
 fp4_cast_transpose_grouped) and a shape with ragged tiles where the mode allows
-them.  Every output buffer is compared byte for byte with the oracle.  The
-draws are fixed by the case number, so a failure names a reproducible case."""
+them.  A second family draws the remaining options: FP32 sources and FP32
+outputs, outer scales supplied by the caller, 16 x 16 inner tiles and MXFP4.
+Every output buffer is compared byte for byte with the oracle.  The draws are
+fixed by the case number, so a failure names a reproducible case."""
 import zlib
 
 import numpy as np
@@ -138,5 +140,131 @@ def test_random_configuration_matches_oracle(case):
                 assert w.size == 0, what + " " + k + ": the oracle has outer scales, the call returned none"
             else:
                 _same(_host(out[k], np.float32).ravel(), w, what + " " + k)
+    if c["ef"]:
+        _same(_host(zd, np.float32), zo, what + " residual")
+
+
+# ------------------------------------------------------------------ more options
+N_MORE = 120
+
+
+def draw_more(case):
+    """FP32 sources and FP32 targets (rowwise entry points), precomputed outer
+    scales (outer_mode 1, no residual), 16 x 16 inner tiles, and MXFP4."""
+    rng = np.random.default_rng(5000 + case)
+    kind = str(rng.choice(["f32", "given", "inner2d", "mx"]))
+    c = {"kind": kind, "fmt": str(rng.choice(list(FMT))), "sr": bool(rng.integers(2)),
+         "seed": int(rng.integers(0, 2 ** 40)), "step": int(rng.integers(0, 1000)),
+         "index_base": int(rng.integers(0, 2 ** 20)) * 8 + int(rng.integers(0, 8)),
+         "scale": float(rng.choice([1e-3, 0.02, 1.0, 300.0])), "ef": False, "obs": 0, "outer_2d": False}
+    if kind == "f32":
+        mode = str(rng.choice(["none", "tensorwise", "1d"]))
+        c["op"] = str(rng.choice(["qdq", "quantize"]))
+        c["ef"] = bool(rng.integers(2))
+        c["y_f32"] = bool(rng.integers(2))
+        if mode == "1d":
+            c.update(two_level="outer", obs=int(rng.choice([16, 32, 64, 128])))
+        else:
+            c["two_level"] = mode
+        c["rows"] = 16 * int(rng.integers(1, 20))
+        c["cols"] = max(16, c["obs"]) * int(rng.integers(1, max(2, 320 // max(16, c["obs"]))))
+    elif kind == "given":
+        o2d = bool(rng.integers(2))
+        c["op"] = str(rng.choice(["quantize", "ct"]))
+        obs = 64 if o2d else int(rng.choice([16, 32, 64]))
+        c.update(two_level="outer", obs=obs, outer_2d=o2d)
+        c["rows"] = (64 if o2d or c["op"] == "ct" else 16) * int(rng.integers(1, 5))
+        c["cols"] = obs * int(rng.integers(1, max(2, 320 // obs)))
+    elif kind == "inner2d":
+        mode = str(rng.choice(["none", "tensorwise", "2d"]))
+        c["op"] = str(rng.choice(["quantize", "ct"]))
+        c["ef"] = bool(rng.integers(2))
+        if mode == "2d":
+            c.update(two_level="outer", obs=64, outer_2d=True)
+            c["rows"], c["cols"] = 64 * int(rng.integers(1, 5)), 64 * int(rng.integers(1, 5))
+        else:
+            c["two_level"] = mode
+            c["rows"], c["cols"] = 16 * int(rng.integers(1, 17)), 16 * int(rng.integers(1, 21))
+    else:
+        c["op"] = str(rng.choice(["qdq", "quantize"]))
+        c["y_f32"] = bool(rng.integers(2))
+        c["x_f32"] = bool(rng.integers(2))
+        c["rows"], c["cols"] = int(rng.integers(1, 80)), 32 * int(rng.integers(1, 12))
+    return c
+
+
+@pytest.mark.parametrize("case", range(N_MORE), ids=lambda i: "more-%d" % i)
+def test_random_option_matches_oracle(case):
+    c = draw_more(case)
+    rng = np.random.default_rng(zlib.crc32(repr(c).encode()))
+    R, C = c["rows"], c["cols"]
+    a = rng.standard_normal((R, C)).astype(np.float32) * np.float32(c["scale"])
+    a *= np.exp(rng.standard_normal((R, 1))).astype(np.float32)
+    what = repr(c)
+    if c["kind"] == "mx":
+        x = a if c["x_f32"] else W.to_bf16(a)
+        ydt = "fp32" if c["y_f32"] else "bf16"
+        codes, scales, y = ref.mx_qdq(x, y_dtype=ydt)
+        g = fq.make_cfg(format="mxfp4")
+        xd = torch.from_numpy(x).cuda() if c["x_f32"] else _dev(x)
+        if c["op"] == "qdq":
+            out = fq.fp4_qdq(xd, g, with_codes=True, y_dtype=torch.float32 if c["y_f32"] else torch.bfloat16)
+            _same(_host(out["y"], np.float32 if c["y_f32"] else np.uint16), y, what + " y")
+        else:
+            out = fq.fp4_quantize(xd, g)
+        _same(_host(out["codes"], np.uint8), codes, what + " codes")
+        _same(_host(out["scales"], np.uint8), scales, what + " scales")
+        return
+    g, o = _cfgs(c)
+    if c["kind"] == "f32":
+        x = a
+        xd = torch.from_numpy(x).cuda()
+    else:
+        x = W.to_bf16(a)
+        xd = _dev(x)
+    z0 = (rng.standard_normal((R, C)) * 0.01 * c["scale"]).astype(np.float32) if c["ef"] else None
+    zo = None if z0 is None else z0.copy()
+    zd = None if z0 is None else torch.from_numpy(z0.copy()).cuda()
+    if c["kind"] == "inner2d":
+        g.inner_2d = 1
+        o["inner_2d"] = True
+    if c["kind"] == "given":
+        natural = ref.nv_quantize(x, cols=c["op"] == "ct", want_y=False, **o)
+        row_o = natural["row_outer"] * np.float32(rng.uniform(0.5, 2.0))
+        col_o = natural.get("col_outer")
+        col_o = None if col_o is None else col_o * np.float32(rng.uniform(0.5, 2.0))
+        g.outer_mode = 1
+        want = ref.nv_quantize(x, cols=c["op"] == "ct", want_y=False, given_outer=(row_o, col_o), **o)
+        ro = torch.from_numpy(np.ascontiguousarray(row_o, np.float32)).cuda()
+        co = None if col_o is None else torch.from_numpy(np.ascontiguousarray(col_o, np.float32)).cuda()
+        if c["op"] == "ct":
+            out = fq.fp4_cast_transpose(xd, g, row_outer=ro, col_outer=co)
+            for k in ("row_codes", "row_scales", "col_codes", "col_scales"):
+                _same(_host(out[k], np.uint8), want[k], what + " " + k)
+        else:
+            out = fq.fp4_quantize(xd, g, outer=ro)
+            _same(_host(out["codes"], np.uint8), want["row_codes"], what + " codes")
+            _same(_host(out["scales"], np.uint8), want["row_scales"], what + " scales")
+        return
+    if c["op"] == "ct":
+        want = ref.nv_quantize(x, residual=zo, cols=True, want_y=False, **o)
+        out = fq.fp4_cast_transpose(xd, g, residual=zd)
+        for k in ("row_codes", "row_scales", "col_codes", "col_scales"):
+            _same(_host(out[k], np.uint8), want[k], what + " " + k)
+    elif c["op"] == "qdq":
+        ydt = "fp32" if c.get("y_f32") else "bf16"
+        want = ref.nv_quantize(x, residual=zo, y_dtype=ydt, **o)
+        out = fq.fp4_qdq(xd, g, residual=zd, with_codes=True,
+                         y_dtype=torch.float32 if ydt == "fp32" else torch.bfloat16)
+        _same(_host(out["y"], np.float32 if ydt == "fp32" else np.uint16), want["row_y"], what + " y")
+        _same(_host(out["codes"], np.uint8), want["row_codes"], what + " codes")
+        _same(_host(out["scales"], np.uint8), want["row_scales"], what + " scales")
+    else:
+        want = ref.nv_quantize(x, residual=zo, want_y=False, **o)
+        out = fq.fp4_quantize(xd, g, residual=zd)
+        _same(_host(out["codes"], np.uint8), want["row_codes"], what + " codes")
+        _same(_host(out["scales"], np.uint8), want["row_scales"], what + " scales")
+    if "row_outer" in want and out.get("outer" if c["op"] != "ct" else "row_outer") is not None:
+        _same(_host(out["outer" if c["op"] != "ct" else "row_outer"], np.float32), want["row_outer"], what + " outer")
     if c["ef"]:
         _same(_host(zd, np.float32), zo, what + " residual")
