@@ -100,8 +100,8 @@ __device__ __forceinline__ float tile16_max(float m)
 
 // Codes of 16 normalised values with a given inner scale (CLAMP: no outer
 // scale bounds the quotients, see codes16_sr).
-template <int BIAS, bool SR, bool CLAMP>
-__device__ __forceinline__ uint2 encode16(const float (&vn)[16], const uint32_t (&u)[8], const float2* ktab,
+template <int BIAS, bool SR, bool CLAMP, int NU>
+__device__ __forceinline__ uint2 encode16(const float (&vn)[16], const uint32_t (&u)[NU], const float2* ktab,
                                           const BlockScale<BIAS>& sc)
 {
     if (SR) return codes16_sr<CLAMP>(vn, u, ktab[sc.code]);
@@ -109,9 +109,10 @@ __device__ __forceinline__ uint2 encode16(const float (&vn)[16], const uint32_t 
 }
 
 // One block's scale and codes; with I2D the scale comes from the 16 x 16 tile
-// (tile16_max) instead of the lane's own 16 values.
-template <int BIAS, bool SR, bool I2D, bool CLAMP>
-__device__ __forceinline__ uint2 quant16(const float (&vn)[16], const uint32_t (&u)[8], const double* tab,
+// (tile16_max) instead of the lane's own 16 values.  u: SR variates, two per
+// word (NU = 8) or one per word (NU = 16).
+template <int BIAS, bool SR, bool I2D, bool CLAMP, int NU>
+__device__ __forceinline__ uint2 quant16(const float (&vn)[16], const uint32_t (&u)[NU], const double* tab,
                                          const float2* ktab, BlockScale<BIAS>& sc)
 {
     const float b = max_abs16(vn);
@@ -580,7 +581,7 @@ void k_tile(TileArgs a)
             // ---------------- column phase
             const float* lf = reinterpret_cast<const float*>(lds_v);
             float cv[16];
-            uint32_t cu[8];
+            uint32_t cu[16];   // one variate per word
             const uint16_t* lu = reinterpret_cast<const uint16_t*>(lds_u);
 #pragma unroll
             for (int k = 0; k < 16; ++k) {
@@ -591,10 +592,7 @@ void k_tile(TileArgs a)
             // column cc of rows 16 rs .. 16 rs + 15, all in 16-row band rs
             const int lu_col = 8 * swz_u_chunk(16 * rs, cc >> 3) + (cc & 7);
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                cu[j] = SR ? (uint32_t)lu[(16 * rs + 2 * j) * kTile + lu_col] |
-                                 ((uint32_t)lu[(16 * rs + 2 * j + 1) * kTile + lu_col] << 16)
-                           : 0u;
+            for (int k = 0; k < 16; ++k) cu[k] = SR ? (uint32_t)lu[(16 * rs + k) * kTile + lu_col] : 0u;
             if (OUTER == kOuter1D) {
                 const bool actc = (cc < cur.cols_valid) && (16 * rs < cur.rows_valid);
                 float s_col;

@@ -195,18 +195,52 @@ __device__ __forceinline__ uint2 codes16_rne(const float (&vn)[16], float2 k)
 // |v_n| >= 2^123, and such values saturate (code 7) under every inner scale,
 // so OR-ing stays exact.
 
-// The code of c / 2^23 (first slot, seed as above) in bits 8 SEL .. 8 SEL + 2,
-// every other bit zero.  Only those magnitude bits of the result are used: the
-// compiler does not tie the builtin's first operand to the destination, so
-// the other bytes of the result are not defined.
+// The code of c / 2^23 (first slot, seed as above) into byte SEL of acc, the
+// other bytes kept: the instruction writes only the selected byte, its
+// destination being also its input.  The builtin for it does not tie that
+// input to the destination (the byte-select form would leave the other bytes
+// undefined), so the instruction is written out with the accumulator as a
+// read-write operand; the compiler pads what follows it for the partial-write
+// forwarding hazard as for any inline asm.  The second slot holds +0, whose
+// code is 0, so byte SEL becomes the element's code in its low nibble; the
+// only stray bit is the sign of a -0 (ceil of a negative T), which one mask
+// per word removes.
 template <int SEL>
-__device__ __forceinline__ uint32_t sr_code_at(float c, uint32_t seed)
+__device__ __forceinline__ void sr_code_into(uint32_t& acc, float c, uint32_t seed)
 {
     typedef float f32x2_t __attribute__((ext_vector_type(2)));
     f32x2_t v;
     v.x = c;
     v.y = 0.0f;
-    return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, v, seed, 0x1p23f, SEL) & (0x7u << (8 * SEL));
+    if constexpr (SEL == 0)
+        asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3" : "+v"(acc) : "v"(v), "v"(seed), "s"(0x1p23f));
+    else if constexpr (SEL == 1)
+        asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3 op_sel:[0,0,1,0]" : "+v"(acc) : "v"(v), "v"(seed),
+            "s"(0x1p23f));
+    else if constexpr (SEL == 2)
+        asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3 op_sel:[0,0,0,1]" : "+v"(acc) : "v"(v), "v"(seed),
+            "s"(0x1p23f));
+    else
+        asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3 op_sel:[0,0,1,1]" : "+v"(acc) : "v"(v), "v"(seed),
+            "s"(0x1p23f));
+}
+
+// The seed (~u16 << 16) | 0xFFFF of the variate in the low half of w (the high
+// half ignored) in one instruction: v_mad_i32_i24 takes w's low 24 bits as a
+// signed number, and times -2^16 its bits 16..23 only add multiples of 2^32, so
+// the result is -2^16 u16 - 1 = ~(u16 << 16) modulo 2^32.  (Written out: the
+// compiler turns the plain expression into a shift and a not.)
+__device__ __forceinline__ uint32_t sr_seed_lo(uint32_t w)
+{
+    uint32_t s;
+    asm("v_mad_i32_i24 %0, %1, %2, -1" : "=v"(s) : "v"(w), "s"(-65536));
+    return s;
+}
+
+// The seed of the variate in the high half of w: ~w | 0xFFFF.
+__device__ __forceinline__ uint32_t sr_seed_hi(uint32_t w)
+{
+    return ~w | 0xFFFFu;
 }
 
 // ceil(|v| / d * 2^23 - 2^-127) from (Kh, Kl) * 2^23 of the block's scale.
@@ -219,8 +253,10 @@ __device__ __forceinline__ float sr_fixed23(float v, float kh23, float kl23)
     return __builtin_ceilf(a);
 }
 
-template <bool CLAMP>
-__device__ __forceinline__ uint32_t codes8_sr(const float* vn, const uint32_t* u, float kh23, float kl23)
+// Eight SR codes; seed(k) gives element k's seed.  Even elements go to the
+// bytes of one word, odd ones to another, merged by a shift.
+template <bool CLAMP, class Seed>
+__device__ __forceinline__ uint32_t codes8_sr(const float* vn, Seed seed, float kh23, float kl23)
 {
     constexpr float kSignOnly = 0x1p125f;
     uint32_t sg = 0;
@@ -228,31 +264,41 @@ __device__ __forceinline__ uint32_t codes8_sr(const float* vn, const uint32_t* u
     sg = fp4x2_rne_scaled<1>(sg, vn[2], vn[3], kSignOnly);
     sg = fp4x2_rne_scaled<2>(sg, vn[4], vn[5], kSignOnly);
     sg = fp4x2_rne_scaled<3>(sg, vn[6], vn[7], kSignOnly);
-    // element 2j takes the low 16 bits of u[j], element 2j + 1 the high 16 bits
-    uint32_t ev, od, nw;
-    nw = ~u[0];
-    ev = sr_code_at<0>(sr_fixed23<CLAMP>(vn[0], kh23, kl23), (nw << 16) | 0xFFFFu);
-    od = sr_code_at<0>(sr_fixed23<CLAMP>(vn[1], kh23, kl23), nw | 0xFFFFu);
-    nw = ~u[1];
-    ev |= sr_code_at<1>(sr_fixed23<CLAMP>(vn[2], kh23, kl23), (nw << 16) | 0xFFFFu);
-    od |= sr_code_at<1>(sr_fixed23<CLAMP>(vn[3], kh23, kl23), nw | 0xFFFFu);
-    nw = ~u[2];
-    ev |= sr_code_at<2>(sr_fixed23<CLAMP>(vn[4], kh23, kl23), (nw << 16) | 0xFFFFu);
-    od |= sr_code_at<2>(sr_fixed23<CLAMP>(vn[5], kh23, kl23), nw | 0xFFFFu);
-    nw = ~u[3];
-    ev |= sr_code_at<3>(sr_fixed23<CLAMP>(vn[6], kh23, kl23), (nw << 16) | 0xFFFFu);
-    od |= sr_code_at<3>(sr_fixed23<CLAMP>(vn[7], kh23, kl23), nw | 0xFFFFu);
-    return sg | ev | (od << 4);
+    uint32_t ev = 0, od = 0;
+    sr_code_into<0>(ev, sr_fixed23<CLAMP>(vn[0], kh23, kl23), seed(0));
+    sr_code_into<0>(od, sr_fixed23<CLAMP>(vn[1], kh23, kl23), seed(1));
+    sr_code_into<1>(ev, sr_fixed23<CLAMP>(vn[2], kh23, kl23), seed(2));
+    sr_code_into<1>(od, sr_fixed23<CLAMP>(vn[3], kh23, kl23), seed(3));
+    sr_code_into<2>(ev, sr_fixed23<CLAMP>(vn[4], kh23, kl23), seed(4));
+    sr_code_into<2>(od, sr_fixed23<CLAMP>(vn[5], kh23, kl23), seed(5));
+    sr_code_into<3>(ev, sr_fixed23<CLAMP>(vn[6], kh23, kl23), seed(6));
+    sr_code_into<3>(od, sr_fixed23<CLAMP>(vn[7], kh23, kl23), seed(7));
+    return sg | (ev & 0x07070707u) | ((od & 0x07070707u) << 4);
 }
 
 // SR codes of 16 normalised values with the block's scale, given as its RNE
 // table entry k = (Kh, Kl); CLAMP when no outer scale bounds the quotients.
+// Variates packed two per word: element k's is bits 16 (k & 1) .. + 15 of u[k >> 1].
 template <bool CLAMP>
 __device__ __forceinline__ uint2 codes16_sr(const float (&vn)[16], const uint32_t (&u)[8], float2 k)
 {
     const float kh23 = k.x * 0x1p23f, kl23 = k.y * 0x1p23f;
-    const uint32_t lo = codes8_sr<CLAMP>(vn, u, kh23, kl23);
-    const uint32_t hi = codes8_sr<CLAMP>(vn + 8, u + 4, kh23, kl23);
+    auto lo_seed = [&](int e) { return (e & 1) ? sr_seed_hi(u[e >> 1]) : sr_seed_lo(u[e >> 1]); };
+    auto hi_seed = [&](int e) { return (e & 1) ? sr_seed_hi(u[4 + (e >> 1)]) : sr_seed_lo(u[4 + (e >> 1)]); };
+    const uint32_t lo = codes8_sr<CLAMP>(vn, lo_seed, kh23, kl23);
+    const uint32_t hi = codes8_sr<CLAMP>(vn + 8, hi_seed, kh23, kl23);
+    return make_uint2(lo, hi);
+}
+
+// The same with one variate per word (element k's in the low half of u[k]).
+template <bool CLAMP>
+__device__ __forceinline__ uint2 codes16_sr(const float (&vn)[16], const uint32_t (&u)[16], float2 k)
+{
+    const float kh23 = k.x * 0x1p23f, kl23 = k.y * 0x1p23f;
+    auto lo_seed = [&](int e) { return sr_seed_lo(u[e]); };
+    auto hi_seed = [&](int e) { return sr_seed_lo(u[8 + e]); };
+    const uint32_t lo = codes8_sr<CLAMP>(vn, lo_seed, kh23, kl23);
+    const uint32_t hi = codes8_sr<CLAMP>(vn + 8, hi_seed, kh23, kl23);
     return make_uint2(lo, hi);
 }
 
