@@ -84,7 +84,10 @@ __device__ __forceinline__ float div_inv64(float a, double inv)
 // flagging subnormal results is enough to catch every such case.
 __device__ __forceinline__ bool is_subnormal(float q)
 {
-    return __builtin_amdgcn_class(q, 0x090);   // -denormal | +denormal
+    // The binary32 form of the class test: the unsuffixed builtin takes a
+    // binary64 operand, and a widened binary32 is never a binary64 denormal,
+    // so that form folds to false.
+    return __builtin_amdgcn_classf(q, 0x090);   // -denormal | +denormal
 }
 
 // ---------------------------------------------------------------- inner scale grids

@@ -311,11 +311,6 @@ constexpr int tile_waves_per_simd()
     return tight ? 3 : 4;
 }
 
-// Smallest binary32 outer scale for which v / s_o can be subnormal for some
-// nonzero bf16 v: |v| >= 2^-133, so below 2^-7 every nonzero quotient is a
-// normal binary32 and the reciprocal-product division needs no re-check.
-constexpr float kNoSubnormalScale = 0x1p-7f;
-
 // Largest staged tail: scale bytes (2 x 256) and 1D outer scales of 16-element
 // groups (2 x 1024).
 constexpr int kTailMax = kStageRowOuter - kStageTail + 2 * 64 * 4 * 4;
@@ -494,10 +489,7 @@ void k_tile(TileArgs a)
 #pragma unroll
             for (int k = 0; k < 16; ++k) vn[k] = v[k];
         } else {
-            // without a residual the source is bf16: a small outer scale rules
-            // out subnormal quotients for the whole tile
-            const bool recheck = EF || OUTER == kOuter1D || GIVEN || !(s_row <= kNoSubnormalScale);
-            normalize16(v, s_row, inv_row, vn, recheck);
+            normalize16<SR>(v, s_row, inv_row, vn);
         }
         {
             BlockScale<BIAS> sc;
@@ -611,7 +603,7 @@ void k_tile(TileArgs a)
                     co.outer = s_col;
                 }
                 float cn[16];
-                normalize16(cv, s_col, outer_inv(s_col), cn, true);
+                normalize16<SR>(cv, s_col, outer_inv(s_col), cn);
 #pragma unroll
                 for (int k = 0; k < 16; ++k) cv[k] = cn[k];
             }

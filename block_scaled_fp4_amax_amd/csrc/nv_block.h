@@ -325,16 +325,35 @@ __device__ __forceinline__ void decode16(uint2 packed, float d, float (&p)[16])
 }
 
 // Normalise by an outer scale: v_n = RN32(v / s_o), v_n = +-0 when s_o == 0.
-// inv = RN64(1 / s_o) (0 when s_o == 0).  The reciprocal product is exact for
-// normal-range quotients; with `recheck` subnormal results are recomputed by
-// IEEE division (callers pass false only where no quotient can be subnormal).
-__device__ __forceinline__ void normalize16(const float (&v)[16], float s_o, double inv, float (&vn)[16],
-                                            bool recheck)
+// inv = RN64(1 / s_o) (0 when s_o == 0).
+// - The reciprocal product RN32(v inv) is exact for normal-range quotients:
+//   there v / s_o is at least 2^-49 of itself away from every binary32
+//   rounding midpoint.
+// - Below the normal range a quotient can be an exact midpoint of the
+//   subnormal grid, which the product may round past (for example
+//   s_o = 49 * 2^18 and v = 147 * 2^-132: 2^-149 against 2^-148). Such
+//   quotients are recomputed by binary32 division.
+// - Only stochastic rounding needs this (RECHECK). A subnormal v_n is below
+//   2^-117 of every nonzero inner scale, so its RNE code is 0 whatever its
+//   value. A block whose largest v_n is subnormal encodes a zero scale either
+//   way, and the dequantised value and residual follow from code, scale and
+//   s_o alone. Under stochastic rounding, whether t = RN32(v_n / d) is nonzero
+//   decides if a variate of 0 rounds up.
+// - A lane can have a subnormal quotient only if min |v| 2^126 < s_o. The
+//   scaling is exact, or overflows for |v| >= 4 where no quotient is subnormal.
+//   Only when that holds in some lane of the wave (a wave-uniform branch) are
+//   the results tested one by one.
+template <bool RECHECK>
+__device__ __forceinline__ void normalize16(const float (&v)[16], float s_o, double inv, float (&vn)[16])
 {
-    bool slow = false;
 #pragma unroll
     for (int k = 0; k < 16; ++k) vn[k] = div_inv64(v[k], inv);
-    if (recheck) {
+    if (!RECHECK) return;
+    float m = __builtin_fabsf(v[0]);
+#pragma unroll
+    for (int k = 1; k < 16; ++k) m = fminf(m, __builtin_fabsf(v[k]));
+    bool slow = false;
+    if (__builtin_amdgcn_ballot_w64(m * 0x1p126f < s_o) != 0) {
 #pragma unroll
         for (int k = 0; k < 16; ++k) slow |= is_subnormal(vn[k]);
     }
