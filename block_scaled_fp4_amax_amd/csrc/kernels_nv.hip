@@ -294,7 +294,7 @@ __global__ __launch_bounds__(kThreads) void k_nv_rows(RowArgs a, uint32_t nblock
 #pragma unroll
         for (int k = 0; k < 16; ++k) vn[k] = v[k];
     } else {
-        normalize16<SR>(v, s_o, outer_inv(s_o), vn);
+        normalize16<SR, !EF && !XF32>(v, s_o, outer_inv(s_o), vn);
     }
     const BlockScale<BIAS> sc = block_scale<BIAS>(max_abs16(vn), rtab);
     const uint2 packed = SR ? codes16_sr<OUTER == kOuterNone>(vn, u, ktab[sc.code]) : codes16_rne(vn, ktab[sc.code]);

@@ -489,7 +489,7 @@ void k_tile(TileArgs a)
 #pragma unroll
             for (int k = 0; k < 16; ++k) vn[k] = v[k];
         } else {
-            normalize16<SR>(v, s_row, inv_row, vn);
+            normalize16<SR, !EF>(v, s_row, inv_row, vn);
         }
         {
             BlockScale<BIAS> sc;
@@ -603,7 +603,7 @@ void k_tile(TileArgs a)
                     co.outer = s_col;
                 }
                 float cn[16];
-                normalize16<SR>(cv, s_col, outer_inv(s_col), cn);
+                normalize16<SR, !EF>(cv, s_col, outer_inv(s_col), cn);
 #pragma unroll
                 for (int k = 0; k < 16; ++k) cv[k] = cn[k];
             }

@@ -342,13 +342,18 @@ __device__ __forceinline__ void decode16(uint2 packed, float d, float (&p)[16])
 // - A lane can have a subnormal quotient only if min |v| 2^126 < s_o. The
 //   scaling is exact, or overflows for |v| >= 4 where no quotient is subnormal.
 //   Only when that holds in some lane of the wave (a wave-uniform branch) are
-//   the results tested one by one.
-template <bool RECHECK>
+//   the results tested one by one. For bf16 values (BF16: no residual was
+//   added) |v| >= 2^-133 rules it out while s_o <= 2^-7, so the minimum is
+//   taken only in waves where some lane's scale is larger.
+constexpr float kNoSubnormalScale = 0x1p-7f;
+
+template <bool RECHECK, bool BF16>
 __device__ __forceinline__ void normalize16(const float (&v)[16], float s_o, double inv, float (&vn)[16])
 {
 #pragma unroll
     for (int k = 0; k < 16; ++k) vn[k] = div_inv64(v[k], inv);
     if (!RECHECK) return;
+    if (BF16 && __builtin_amdgcn_ballot_w64(!(s_o <= kNoSubnormalScale)) == 0) return;
     float m = __builtin_fabsf(v[0]);
 #pragma unroll
     for (int k = 1; k < 16; ++k) m = fminf(m, __builtin_fabsf(v[k]));
