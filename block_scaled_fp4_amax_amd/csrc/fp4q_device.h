@@ -164,8 +164,12 @@ __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1
 // The eight 16-bit variates of elements 8*blk .. 8*blk+7: counter
 // (lo32 blk, hi32 blk, lo32 step, hi32 step), key (lo32 seed, hi32 seed);
 // element 8*blk + l takes 16-bit half (l & 1) of output word (l >> 1).
+// Element indices are taken modulo 2^64, so an element's counter is its wrapped
+// index >> 3, below 2^61.  Callers form blk from a base and offsets without
+// wrapping; it is congruent to the counter modulo 2^61 and reduced here.
 __device__ __forceinline__ u32x4 sr_words(uint64_t seed, uint64_t step, uint64_t blk)
 {
+    blk &= (uint64_t(1) << 61) - 1;
     u32x4 c = {(uint32_t)blk, (uint32_t)(blk >> 32), (uint32_t)step, (uint32_t)(step >> 32)};
     return philox4x32_10(c, (uint32_t)seed, (uint32_t)(seed >> 32));
 }
