@@ -4,8 +4,8 @@ Each case draws a format, a two-level mode (none, tensorwise, 1D outer groups
 of 16 / 32 / 64 / 128, the 2D 64 x 64 outer tile), RNE or stochastic rounding
 with a random seed, step and index base, an optional error-feedback residual,
 an entry point (fp4_qdq, fp4_quantize, fp4_cast_transpose staged or direct,
-fp4_cast_transpose_grouped) and a shape with ragged tiles where the mode allows
-them.  A second family draws the remaining options: FP32 sources and FP32
+fp4_cast_transpose_grouped), a shape with ragged tiles where the mode allows
+them, and a source row pitch (a column-sliced view).  A second family draws the remaining options: FP32 sources and FP32
 outputs, outer scales supplied by the caller, 16 x 16 inner tiles and MXFP4.
 Every output buffer is compared byte for byte with the oracle.  The draws are
 fixed by the case number, so a failure names a reproducible case."""
@@ -82,7 +82,19 @@ def draw(case):
         c["rows"] = row_mult * int(rng.integers(1, max(2, 320 // row_mult)))
     c["staged"] = bool(rng.integers(2))
     c["scale"] = float(rng.choice([1e-3, 0.02, 1.0, 300.0]))
+    c["pad"] = int(rng.choice([0, 0, 8, 24, 64]))   # source row pitch cols + pad (a column-sliced view)
     return c
+
+
+def _view(x, pad):
+    """x on the device, as the first columns of a wider row-major tensor when
+    pad > 0 (row pitch cols + pad)."""
+    if pad == 0:
+        return _dev(x)
+    R, C = x.shape
+    full = np.zeros((R, C + pad), np.uint16)
+    full[:, :C] = x
+    return _dev(full)[:, :C]
 
 
 def _cfgs(c):
@@ -113,17 +125,17 @@ def test_random_configuration_matches_oracle(case):
     if c["op"] in ("qdq", "quantize"):
         want = ref.nv_quantize(x, residual=zo, **o)
         if c["op"] == "qdq":
-            out = fq.fp4_qdq(_dev(x), g, residual=zd, with_codes=True)
+            out = fq.fp4_qdq(_view(x, c["pad"]), g, residual=zd, with_codes=True)
             _same(_host(out["y"], np.uint16), want["row_y"], what + " y")
         else:
-            out = fq.fp4_quantize(_dev(x), g, residual=zd)
+            out = fq.fp4_quantize(_view(x, c["pad"]), g, residual=zd)
         _same(_host(out["codes"], np.uint8), want["row_codes"], what + " codes")
         _same(_host(out["scales"], np.uint8), want["row_scales"], what + " scales")
         if "row_outer" in want:
             _same(_host(out["outer"], np.float32), want["row_outer"], what + " outer")
     elif c["op"] == "ct":
         want = ref.nv_quantize(x, residual=zo, cols=True, want_y=False, **o)
-        out = fq.fp4_cast_transpose(_dev(x), g, residual=zd, staged=c["staged"])
+        out = fq.fp4_cast_transpose(_view(x, c["pad"]), g, residual=zd, staged=c["staged"])
         for k in ("row_codes", "row_scales", "col_codes", "col_scales"):
             _same(_host(out[k], np.uint8), want[k], what + " " + k)
         for k in ("row_outer", "col_outer"):
@@ -131,7 +143,7 @@ def test_random_configuration_matches_oracle(case):
                 _same(_host(out[k], np.float32), want[k], what + " " + k)
     else:
         want = ref.nv_quantize_grouped(x, c["rows"], residual=zo, **o)
-        out = fq.fp4_cast_transpose_grouped(_dev(x), c["rows"], g, residual=zd, staged=c["staged"])
+        out = fq.fp4_cast_transpose_grouped(_view(x, c["pad"]), c["rows"], g, residual=zd, staged=c["staged"])
         for k in ("row_codes", "row_scales", "col_codes", "col_scales"):
             _same(_host(out[k], np.uint8).reshape(want[k].shape), want[k], what + " " + k)
         for k in ("row_outer", "col_outer"):
