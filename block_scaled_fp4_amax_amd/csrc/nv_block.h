@@ -334,8 +334,8 @@ __device__ __forceinline__ void decode16(uint2 packed, float d, float (&p)[16])
 //   s_o = 49 * 2^18 and v = 147 * 2^-132: 2^-149 against 2^-148). Such
 //   quotients are recomputed by binary32 division.
 // - Only stochastic rounding needs this (RECHECK). A subnormal v_n is below
-//   2^-117 of every nonzero inner scale, so its RNE code is 0 whatever its
-//   value. A block whose largest v_n is subnormal encodes a zero scale either
+//   2^-109 times every nonzero inner scale (the smallest is 2^-17, UE5M3), so
+//   its RNE code is 0 whatever its value. A block whose largest v_n is subnormal encodes a zero scale either
 //   way, and the dequantised value and residual follow from code, scale and
 //   s_o alone. Under stochastic rounding, whether t = RN32(v_n / d) is nonzero
 //   decides if a variate of 0 rounds up.
