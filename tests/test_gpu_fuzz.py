@@ -5,8 +5,10 @@ of 16 / 32 / 64 / 128, the 2D 64 x 64 outer tile), RNE or stochastic rounding
 with a random seed, step and index base, an optional error-feedback residual,
 an entry point (fp4_qdq, fp4_quantize, fp4_cast_transpose staged or direct,
 fp4_cast_transpose_grouped), a shape with ragged tiles where the mode allows
-them, and a source row pitch (a column-sliced view).  A second family draws the remaining options: FP32 sources and FP32
-outputs, outer scales supplied by the caller, 16 x 16 inner tiles and MXFP4.
+them, and a source row pitch (a column-sliced view).  A second family draws
+the remaining options: FP32 sources and FP32 outputs, outer scales supplied by
+the caller, 16 x 16 inner tiles and MXFP4.  A third takes configurations of
+the first kind and injects special values into the source and the residual.
 Every output buffer is compared byte for byte with the oracle.  The draws are
 fixed by the case number, so a failure names a reproducible case."""
 import zlib
@@ -278,5 +280,94 @@ def test_random_option_matches_oracle(case):
         _same(_host(out["scales"], np.uint8), want["row_scales"], what + " scales")
     if "row_outer" in want and out.get("outer" if c["op"] != "ct" else "row_outer") is not None:
         _same(_host(out["outer" if c["op"] != "ct" else "row_outer"], np.float32), want["row_outer"], what + " outer")
+    if c["ef"]:
+        _same(_host(zd, np.float32), zo, what + " residual")
+
+
+# ------------------------------------------------------------------ special values
+N_EDGE = 120
+_SPECIAL_BF16 = np.array([0x0000, 0x8000, 0x7F80, 0xFF80, 0x7FC0, 0xFFC1, 0x7F81, 0x0001, 0x8001, 0x007F,
+                          0x807F, 0x0080, 0x7F7F, 0xFF7F, 0x7F7E], np.uint16)
+
+
+def _inject(x, rng, density):
+    """bf16 bits with specials: zeros, infinities, NaNs, subnormals, the
+    largest finite values, E2M1 decision points and grid values times random
+    powers of two (and one ulp either side), and constant or zero 16-blocks."""
+    x = x.copy()
+    R, C = x.shape
+    n = max(1, int(density * R * C))
+    pos = rng.integers(0, R * C, size=n)
+    kind = rng.integers(0, 3, size=n)
+    flat = x.ravel()
+    sp = _SPECIAL_BF16[rng.integers(0, _SPECIAL_BF16.size, size=n)]
+    grid = W.MID_VALUES[rng.integers(0, W.MID_VALUES.size, size=n)] * np.exp2(rng.integers(-30, 31, size=n)).astype(np.float32)
+    gb = W.to_bf16(grid * np.where(rng.random(n) < 0.5, -1, 1).astype(np.float32))
+    gb = (gb.astype(np.int32) + rng.integers(-1, 2, size=n)).astype(np.uint16)
+    flat[pos] = np.where(kind == 0, sp, gb)
+    for _ in range(max(1, R * C // 2048)):           # whole 16-blocks: one constant, or zero
+        r, b = int(rng.integers(0, R)), int(rng.integers(0, C // 16))
+        flat[r * C + 16 * b: r * C + 16 * b + 16] = 0 if rng.random() < 0.5 else flat[r * C + 16 * b]
+    return x
+
+
+def _inject_residual(z, rng, density):
+    """Finite residual specials: signed zeros, binary32 subnormals, values near
+    the largest finite binary32 (so that x + r overflows)."""
+    z = z.copy()
+    n = max(1, int(density * z.size))
+    pos = rng.integers(0, z.size, size=n)
+    vals = np.array([0.0, -0.0, 1e-45, -1e-45, 1e-40, 3e38, -3e38, 3.4e38], np.float32)
+    z.ravel()[pos] = vals[rng.integers(0, vals.size, size=n)]
+    return z
+
+
+@pytest.mark.parametrize("case", range(N_EDGE), ids=lambda i: "edge-%d" % i)
+def test_random_configuration_with_special_values(case):
+    c = draw(9000 + case)
+    rng = np.random.default_rng(zlib.crc32(("edge" + repr(c)).encode()))
+    R = sum(c["rows"]) if c["op"] == "grouped" else c["rows"]
+    C = c["cols"]
+    a = rng.standard_normal((R, C)).astype(np.float32) * np.float32(c["scale"])
+    a *= np.exp(rng.standard_normal((R, 1))).astype(np.float32)
+    density = float(rng.choice([0.002, 0.02, 0.1]))
+    x = _inject(W.to_bf16(a), rng, density)
+    z0 = None
+    if c["ef"]:
+        z0 = _inject_residual((rng.standard_normal((R, C)) * 0.01 * c["scale"]).astype(np.float32), rng, density)
+    g, o = _cfgs(c)
+    zo = None if z0 is None else z0.copy()
+    zd = None if z0 is None else torch.from_numpy(z0.copy()).cuda()
+    what = repr(c) + " density %g" % density
+    if c["op"] in ("qdq", "quantize"):
+        want = ref.nv_quantize(x, residual=zo, **o)
+        if c["op"] == "qdq":
+            out = fq.fp4_qdq(_view(x, c["pad"]), g, residual=zd, with_codes=True)
+            _same(_host(out["y"], np.uint16), want["row_y"], what + " y")
+        else:
+            out = fq.fp4_quantize(_view(x, c["pad"]), g, residual=zd)
+        _same(_host(out["codes"], np.uint8), want["row_codes"], what + " codes")
+        _same(_host(out["scales"], np.uint8), want["row_scales"], what + " scales")
+        if "row_outer" in want:
+            _same(_host(out["outer"], np.float32), want["row_outer"], what + " outer")
+    elif c["op"] == "ct":
+        want = ref.nv_quantize(x, residual=zo, cols=True, want_y=False, **o)
+        out = fq.fp4_cast_transpose(_view(x, c["pad"]), g, residual=zd, staged=c["staged"])
+        for k in ("row_codes", "row_scales", "col_codes", "col_scales"):
+            _same(_host(out[k], np.uint8), want[k], what + " " + k)
+        for k in ("row_outer", "col_outer"):
+            if k in want:
+                _same(_host(out[k], np.float32), want[k], what + " " + k)
+    else:
+        want = ref.nv_quantize_grouped(x, c["rows"], residual=zo, **o)
+        out = fq.fp4_cast_transpose_grouped(_view(x, c["pad"]), c["rows"], g, residual=zd, staged=c["staged"])
+        for k in ("row_codes", "row_scales", "col_codes", "col_scales"):
+            _same(_host(out[k], np.uint8).reshape(want[k].shape), want[k], what + " " + k)
+        for k in ("row_outer", "col_outer"):
+            w = np.asarray(want.get(k, np.zeros(0, np.float32)), np.float32).ravel()
+            if out.get(k) is None:
+                assert w.size == 0, what + " " + k
+            else:
+                _same(_host(out[k], np.float32).ravel(), w, what + " " + k)
     if c["ef"]:
         _same(_host(zd, np.float32), zo, what + " residual")
