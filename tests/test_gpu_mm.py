@@ -207,3 +207,31 @@ def test_direct_lds_kernel_equals_register_staged(M, N, K, dtype):
     c, s = ref.mx_mm(a[0][rows], a[1][rows], *b, len(rows), N, K)
     got = direct[torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
     within_bound(got, c, s, K, "direct-to-LDS sampled rows", bf16=dtype == torch.bfloat16)
+
+
+N_MM_FUZZ = 48
+
+
+@pytest.mark.parametrize("case", range(N_MM_FUZZ), ids=lambda i: "mm-fuzz-%d" % i)
+def test_random_shapes(case):
+    """Seeded random M, N (1 .. 599), K (64 .. 2560), scale layout and C type:
+    exact (bf16 C: the RNE rounding of the exact sum) where every partial sum
+    is a binary32 number, within the accumulation bound otherwise."""
+    rng = np.random.default_rng(7000 + case)
+    M, N = int(rng.integers(1, 600)), int(rng.integers(1, 600))
+    K = 64 * int(rng.integers(1, 41))
+    layout = str(rng.choice(["row", "tiled"]))
+    exact = bool(rng.integers(2)) and K <= 1024
+    dtype = torch.float32 if rng.integers(2) else torch.bfloat16
+    lo, hi = (126, 129) if exact else (100, 150)
+    a, b = operand(rng, M, K, lo, hi), operand(rng, N, K, lo, hi)
+    c, s = ref.mx_mm(*a, *b, M, N, K)
+    got = gpu_mm(a, b, dtype=dtype, layout=layout)
+    what = "M %d N %d K %d %s %s" % (M, N, K, layout, dtype)
+    if exact and dtype == torch.float32:
+        np.testing.assert_array_equal(got, c, err_msg=what)
+    elif exact:
+        want = ref.bf16_to_f32(ref.f32_to_bf16(c.astype(np.float32))).astype(np.float64)
+        np.testing.assert_array_equal(got, want, err_msg=what)
+    else:
+        within_bound(got, c, s, K, what, bf16=dtype == torch.bfloat16)
