@@ -30,6 +30,15 @@ namespace fp4q {
 namespace {
 
 constexpr int kThreads = 256;
+// Lanes of a workgroup of the rowwise kernel.  The one-launch tensorwise form
+// takes 512: at 256 x 256 each workgroup's amax pass over the whole tensor is
+// then one round of sixteen loads per lane, and half as many workgroups make
+// that pass (4.5 us a call against 5.0 with 256 lanes and 6.7 with 1024).
+template <bool SMALL>
+constexpr int rows_threads()
+{
+    return SMALL ? 512 : kThreads;
+}
 
 
 __device__ __forceinline__ void load16_f32(const float* p, float (&z)[16])
@@ -135,19 +144,20 @@ __device__ __forceinline__ uint32_t amax_blocks(const void* x, int x_vec, const 
 // cols elements, row pitch ld), the workgroup's lanes taking 16-byte chunks in
 // turn, sixteen loads in flight per lane; a NaN / inf anywhere gives >= 0x7F80,
 // and the caller then takes the sanitised maximum the slow way.
+template <int NT>
 __device__ __forceinline__ uint32_t amax_bf16_chunks(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld)
 {
     const uint32_t cpr = (uint32_t)(cols / 8);                 // 16-byte chunks per row
     const uint32_t n = (uint32_t)(rows * cpr);
     const bool dense = ld == cols;                             // chunk c at x + 8 c (uniform)
     uint32_t m = 0;
-    for (uint32_t c0 = threadIdx.x; c0 < n; c0 += 16 * kThreads) {
+    for (uint32_t c0 = threadIdx.x; c0 < n; c0 += 16 * NT) {
         uint4 w[16];
         // ordinary (cached) loads: every workgroup of the launch reads the
         // same small tensor, so all but the first reads per XCD hit its L2
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
-            uint32_t c = c0 + (uint32_t)k * kThreads;
+            uint32_t c = c0 + (uint32_t)k * NT;
             c = c < n ? c : 0u;
             int64_t off;
             if (dense) {
@@ -173,15 +183,17 @@ __device__ __forceinline__ uint32_t amax_bf16_chunks(const uint16_t* x, int64_t 
 // needs no second launch.  With a residual it cannot: other workgroups rewrite
 // the residual in place while the amax is being taken.
 template <int BIAS, int OUTER, bool SR, bool EF, bool XF32, bool SMALL>
-__global__ __launch_bounds__(kThreads) void k_nv_rows(RowArgs a, uint32_t nblocks, uint32_t bpr)
+__global__ __launch_bounds__(rows_threads<SMALL>()) void k_nv_rows(RowArgs a, uint32_t nblocks, uint32_t bpr)
 {
+    constexpr int NT = rows_threads<SMALL>();
+    constexpr int NW = NT / 64;
     static_assert(!(SMALL && EF), "the one-launch tensorwise form reads the residual that it rewrites");
     __shared__ double rtab[16];
     __shared__ float2 ktab[kRneTableSize];
-    __shared__ uint32_t wmax[kThreads / 64];
+    __shared__ uint32_t wmax[NW];
     fill_recip_table(rtab, (int)threadIdx.x);
     fill_rne_table<BIAS>(ktab, (int)threadIdx.x);
-    const uint32_t b = blockIdx.x * kThreads + threadIdx.x;   // inner block id
+    const uint32_t b = blockIdx.x * NT + threadIdx.x;         // inner block id
     // the small form's bf16 source: the lane's own block is requested before
     // the amax pass, so its load overlaps that pass (lanes past the end load
     // block 0 and return below)
@@ -200,26 +212,33 @@ __global__ __launch_bounds__(kThreads) void k_nv_rows(RowArgs a, uint32_t nblock
         if (!XF32 && a.x_vec) {
             // bf16 without a residual: packed maxima of the raw bits; the
             // sanitised pass only if a NaN / inf turned up (a uniform branch)
-            m = wave_max_u32(amax_bf16_chunks(static_cast<const uint16_t*>(a.x), a.rows, a.cols, a.ld));
+            m = wave_max_u32(amax_bf16_chunks<NT>(static_cast<const uint16_t*>(a.x), a.rows, a.cols, a.ld));
             if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
             __syncthreads();
-            const uint32_t fast = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3])) << 16;
+            uint32_t fast = wmax[0];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) fast = max(fast, wmax[w]);
+            fast <<= 16;
             __syncthreads();
             if (fast < 0x7F800000u) {
                 m = fast;
             } else {
                 m = wave_max_u32(amax_blocks<XF32>(a.x, a.x_vec, nullptr, a.cols, a.ld, nblocks, bpr, threadIdx.x,
-                                                   kThreads));
+                                                   NT));
                 if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
                 __syncthreads();
-                m = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+                m = wmax[0];
+#pragma unroll
+                for (int w = 1; w < NW; ++w) m = max(m, wmax[w]);
             }
         } else {
-            m = amax_blocks<XF32>(a.x, a.x_vec, nullptr, a.cols, a.ld, nblocks, bpr, threadIdx.x, kThreads);
+            m = amax_blocks<XF32>(a.x, a.x_vec, nullptr, a.cols, a.ld, nblocks, bpr, threadIdx.x, NT);
             m = wave_max_u32(m);
             if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
             __syncthreads();
-            m = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+            m = wmax[0];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) m = max(m, wmax[w]);
         }
         s_small = __uint_as_float(m) / ScaleFmt<BIAS>::outer_den();
         if (a.outer && blockIdx.x == 0 && threadIdx.x == 0) a.outer[0] = s_small;
@@ -408,6 +427,8 @@ hipError_t launch_rows(int bias, int outer_kind, bool sr, bool x_f32, const RowA
     const uint32_t bpr = (uint32_t)(a.cols / 16);
     const uint32_t nblocks = (uint32_t)(a.rows * bpr);
     const uint32_t grid = (nblocks + kThreads - 1) / kThreads;
+    constexpr int kSmallThreads = rows_threads<true>();
+    const uint32_t grid_small = (nblocks + kSmallThreads - 1) / kSmallThreads;
     const bool ef = a.residual != nullptr;
     // tensorwise with no scale given: the one-launch small-tensor form, which
     // the host selects only without a residual (with one, the amax passes run
@@ -418,8 +439,8 @@ hipError_t launch_rows(int bias, int outer_kind, bool sr, bool x_f32, const RowA
     do {                                                                                                        \
         if constexpr (O == kOuterTensor && !E) {                                                                \
             if (small) {                                                                                        \
-                if (x_f32) hipLaunchKernelGGL((k_nv_rows<B, O, S, E, true, true>), dim3(grid), dim3(kThreads), 0, s, a, nblocks, bpr); \
-                else hipLaunchKernelGGL((k_nv_rows<B, O, S, E, false, true>), dim3(grid), dim3(kThreads), 0, s, a, nblocks, bpr); \
+                if (x_f32) hipLaunchKernelGGL((k_nv_rows<B, O, S, E, true, true>), dim3(grid_small), dim3(kSmallThreads), 0, s, a, nblocks, bpr); \
+                else hipLaunchKernelGGL((k_nv_rows<B, O, S, E, false, true>), dim3(grid_small), dim3(kSmallThreads), 0, s, a, nblocks, bpr); \
                 break;                                                                                          \
             }                                                                                                   \
         }                                                                                                       \
