@@ -347,7 +347,11 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemm(GemmArgs g)
 // planes (low and high four bytes of a row's eight).  The loads are issued from
 // inline assembly with explicit waits: the compiler's own wait insertion cannot
 // tell the two buffers apart and would wait for the next K-tile's loads before
-// every read of the current one.
+// every read of the current one.  Only waves 0..3 (one per SIMD) load.  A
+// burst of load instructions issues slowly (the K-tile's 68 KiB enter the CU at
+// the rate its memory path accepts them), and a wave that is issuing loads
+// issues no matrix instructions: with the loads on one wave of each SIMD, the
+// SIMD's other wave keeps the matrix pipe fed meanwhile.
 struct SmemLds {
     uint4 code[2][2][kChunks];                 // [buffer][A, B][chunk]         128 KiB
     uint32_t scale[2][2][2][kBM];              // [buffer][A, B][low, high][row]  8 KiB
@@ -388,21 +392,22 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p)
         (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p);
 }
 
-// The ten loads of K-tile kt into buffer buf issued by wave w: code blocks
-// 4 w .. 4 w + 3 of A and of B, and the scale words of 64 rows (waves 0..3: A
-// rows 64 w .., waves 4..7: B rows 64 (w - 4) ..).  Codes beyond the rows or K
-// load as zeros; the tiled scales are zero-padded.
+// The twenty loads of K-tile kt into buffer buf issued by wave w < 4: code
+// blocks 8 w .. 8 w + 7 of A and of B, and the scale words of rows 64 w ..
+// 64 w + 63 of A and of B.  Waves 4..7 load nothing.  Codes beyond the rows or
+// K load as zeros; the tiled scales are zero-padded.
 __device__ __forceinline__ void lds_tile(const GemmArgs& g, SmemLds& sm, const rsrc_t& ra, const rsrc_t& rb,
                                          const rsrc_t& ras, const rsrc_t& rbs, int kt, int rows_a, int rows_b,
                                          int buf, int wave, int lane)
 {
+    if (wave >= 4) return;                     // uniform
     const int kb_end = g.K / 2;
 #pragma unroll
     for (int o = 0; o < 2; ++o) {
         const int rows = o ? rows_b : rows_a;
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-            const int b = 4 * wave + h;
+        for (int h = 0; h < 8; ++h) {
+            const int b = 8 * wave + h;
             const int row = 8 * b + (lane >> 3);
             const int c = (lane & 7) ^ ((row >> 1) & 7);
             const int kb = kt * kRowB + 16 * c;
@@ -410,13 +415,16 @@ __device__ __forceinline__ void lds_tile(const GemmArgs& g, SmemLds& sm, const r
             lds_load16(o ? rb : ra, off, lds_addr(&sm.code[buf][o][b * 64]));
         }
     }
-    const int o = wave >> 2, r0 = 64 * (wave & 3);
+    const int r0 = 64 * wave;
     const uint32_t off = (uint32_t)((kt * kBM + r0 + lane) * 8);
-    lds_load4(o ? rbs : ras, off, lds_addr(&sm.scale[buf][o][0][r0]));
-    lds_load4(o ? rbs : ras, off + 4, lds_addr(&sm.scale[buf][o][1][r0]));
+#pragma unroll
+    for (int o = 0; o < 2; ++o) {
+        lds_load4(o ? rbs : ras, off, lds_addr(&sm.scale[buf][o][0][r0]));
+        lds_load4(o ? rbs : ras, off + 4, lds_addr(&sm.scale[buf][o][1][r0]));
+    }
 }
 
-constexpr int kLdsLoadsPerTile = 10;           // per wave
+constexpr int kLdsLoadsPerTile = 20;           // per loading wave
 
 template <bool CF32>
 __global__ __launch_bounds__(kThreads) void k_mx_gemm_lds(GemmArgs g)
@@ -451,7 +459,8 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemm_lds(GemmArgs g)
     for (int kt = 0; kt < nk; ++kt) {
         const int cur = kt & 1;
         // this wave's part of K-tile kt has landed (K-tile 1 may still be in
-        // flight at kt = 0); the barrier makes every wave's part visible
+        // flight at kt = 0; waves that load nothing wait for nothing); the
+        // barrier makes every wave's part visible
         if (kt == 0) wait_vm<kLdsLoadsPerTile>();
         else wait_vm<0>();
         __syncthreads();
@@ -543,12 +552,12 @@ hipError_t launch_mx_gemm(const GemmArgs& g, hipStream_t s)
     const int T = g.tiles_m * g.tiles_n;
     static_assert(sizeof(Smem) == sizeof(SmemLds), "both kernels take 136 KiB of the CU's 160 KiB");
     const size_t lds = sizeof(Smem);
-    // The direct-to-LDS kernel keeps one K-tile of loads in flight, the
-    // register-staged one up to two: measured on random operands, the former
-    // is ahead once K >= 8192 and there are at least four 256 x 256 tiles per
-    // CU (8192^3: +9%, 16384^2 x 8192: +15%), behind for shorter K or fewer
-    // tiles (8192^2 x 4096: -11%, 4096^2 x 8192: -6%).
-    const bool direct = g.scale_layout == kScaleTiled && g.K >= 8192 && T >= 1024;
+    // GEMM-ready scales take the direct-to-LDS kernel from three K-tiles on:
+    // measured on uniformly random operands it was ahead of the register-
+    // staged one by 4-14% on 17 of 18 shapes (K from 768 to 16384, M and N
+    // from 1024 to 16384), and even at 8192^2 x 2880, whose K tail the
+    // register-staged kernel skips.  Its wait for K-tile 0 needs two K-tiles.
+    const bool direct = g.scale_layout == kScaleTiled && g.K >= 3 * kBK;
     const int variant = direct ? 6 + (g.c_f32 ? 1 : 0)
                                : (g.scale_layout == kScaleTiled ? 4 : g.scale_layout == kScaleRow8 ? 2 : 0) +
                                      (g.c_f32 ? 1 : 0);

@@ -185,14 +185,18 @@ def test_graph_replays_equal_eager(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K,dtype", [(8192, 8192, 8192, torch.bfloat16), (8192, 8192, 8192, torch.float32),
-                                         (8100, 8200, 8256, torch.float32), (8192, 8192, 16384, torch.bfloat16)])
+                                         (8100, 8200, 8256, torch.float32), (8192, 8192, 16384, torch.bfloat16),
+                                         (300, 290, 1024, torch.float32), (333, 517, 2880, torch.bfloat16),
+                                         (1, 515, 960, torch.float32), (700, 90, 768, torch.float32),
+                                         (257, 1000, 4096, torch.bfloat16), (2048, 1, 1600, torch.float32)])
 def test_direct_lds_kernel_equals_register_staged(M, N, K, dtype):
-    """With GEMM-ready scales, K >= 8192 and at least 1024 tiles of 256 x 256
-    the library takes the direct-to-LDS kernel; with rowwise scales the
-    register-staged one.  Both issue the same instructions in the same K order,
-    so C must agree bit for bit over the whole matrix, ragged edges (8100 x
-    8200, a K tail of 64) included; sampled rows of the direct kernel's C are
-    checked against the oracle as well."""
+    """With GEMM-ready scales and K of at least three 256-value K-tiles the
+    library takes the direct-to-LDS kernel (only four of its eight waves load);
+    with rowwise scales the register-staged one.  Both issue the same
+    instructions in the same K order, so C must agree bit for bit over the
+    whole matrix, ragged edges (partial tiles, single rows and columns, K tails)
+    included; sampled rows of the direct kernel's C are checked against the
+    oracle as well."""
     rng = np.random.default_rng(M + N + K)
     a, b = operand(rng, M, K, 115, 135), operand(rng, N, K, 115, 135)
     A_row, B_row = dev_operand(a, "row"), dev_operand(b, "row")
@@ -203,7 +207,7 @@ def test_direct_lds_kernel_equals_register_staged(M, N, K, dtype):
     bits = torch.int16 if dtype == torch.bfloat16 else torch.int32
     same = staged.view(bits) == direct.view(bits)
     assert bool(same.all()), "%d of %d elements differ" % (int((~same).sum()), same.numel())
-    rows = np.array([0, 1, 255, 256, M // 2, M - 2, M - 1])
+    rows = np.unique(np.clip([0, 1, 255, 256, M // 2, M - 2, M - 1], 0, M - 1))
     c, s = ref.mx_mm(a[0][rows], a[1][rows], *b, len(rows), N, K)
     got = direct[torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
     within_bound(got, c, s, K, "direct-to-LDS sampled rows", bf16=dtype == torch.bfloat16)
