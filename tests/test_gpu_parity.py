@@ -502,6 +502,32 @@ def test_grouped_more_groups_than_one_launch_holds(tl, obs, o2d):
     same(host(zd, np.float32), zo, "residual")
 
 
+@pytest.mark.parametrize("o2d,staged", [(True, True), (True, False), (False, True), (False, False)])
+def test_grouped_last_launch_holds_one_group(o2d, staged):
+    """65 groups: the call's second launch holds the last group alone, at a
+    nonzero first row, which the kernel form without the group bookkeeping
+    (one group at row 0) must not take.  SR + error feedback, every buffer
+    against the oracle."""
+    rng = np.random.default_rng(31 + 2 * o2d + staged)
+    rows = [int(v) for v in rng.choice([64, 128, 192], size=65)]
+    C = 192
+    x = rand_bf16(rng, (sum(rows), C), 0.02)
+    z0 = (rng.standard_normal(x.shape) * 0.01).astype(np.float32)
+    g = fq.make_cfg(format="nvfp4", two_level="outer_block", outer_block_size=64, outer_2d=o2d,
+                    rounding="stochastic", seed=41, step=2, index_base=5)
+    zd = torch.from_numpy(z0.copy()).cuda()
+    out = fq.fp4_cast_transpose_grouped(dev(x), rows, g, residual=zd, staged=staged)
+    zo = z0.copy()
+    want = ref.nv_quantize_grouped(x, rows, two_level="outer", obs=64, outer_2d=o2d, stochastic=True, seed=41, step=2,
+                                   index_base=5, residual=zo)
+    for k in ("row_codes", "row_scales", "col_codes", "col_scales"):
+        same(host(out[k], np.uint8).reshape(want[k].shape), want[k], "65 groups %s" % k)
+    same(host(out["row_outer"], np.float32).ravel(), want["row_outer"], "row outer")
+    if not o2d:
+        same(host(out["col_outer"], np.float32).ravel(), want["col_outer"], "col outer")
+    same(host(zd, np.float32), zo, "residual")
+
+
 def test_cast_transpose_1d_obs128_sr_16384x4096():
     """1D outer groups of 128 (1 x 128 along rows, 128 x 1 down columns; ALTO
     page, Technical design) at full size: AMD-FP4, SR, the 16384-token
