@@ -275,6 +275,8 @@ __global__ __launch_bounds__(kThreads) void k_gather(GatherArgs a)
     const int nrb = a.tile0[a.ngroups] / a.tiles_c;    // 64-row bands in the launch
     const int opr = a.obs ? 64 / a.obs : 0;           // 1D outer groups per tile row
     const int64_t blk = a.stage_block;
+    const int64_t ntiles = a.tile0[a.ngroups];
+    const int64_t tailB = blk - kStageTail;
     const int units = a.kind_units[6];
     for (int u = blockIdx.x; u < units; u += gridDim.x) {
         int kind = 0;
@@ -299,14 +301,16 @@ __global__ __launch_bounds__(kThreads) void k_gather(GatherArgs a)
             const int ti = band - a.tile0[g] / a.tiles_c;
             const int Rg = a.row0[g + 1] - a.row0[g];
             const int64_t grow = a.row0[g] + 64 * ti;
-            const uint8_t* sb = a.stage + (int64_t)(a.tile0[g] + ti * a.tiles_c) * blk;   // block of tile (ti, 0)
+            const int64_t f = a.tile0[g] + ti * a.tiles_c;                       // tile (ti, 0)
+            const uint8_t* sb = a.stage + 2 * ntiles * 2048 + f * tailB - kStageTail;
             b.lines = min(64, Rg - 64 * ti);
             b.T = a.tiles_c;
-            b.tstride = blk;
+            b.tstride = tailB;
             if (kind == 0) {
                 b.P = (int32_t)(C / 2);
                 b.U = 32;
-                b.in = sb;
+                b.in = a.stage + f * 2048;
+                b.tstride = 2048;
                 b.dst = a.row_codes + grow * b.P;
             } else if (kind == 1) {
                 b.P = (int32_t)(C / 16);
@@ -324,15 +328,16 @@ __global__ __launch_bounds__(kThreads) void k_gather(GatherArgs a)
             const int g = band / a.tiles_c;
             const int tj = band - g * a.tiles_c;
             const int64_t Rg = a.row0[g + 1] - a.row0[g];
-            const uint8_t* sb = a.stage + (int64_t)(a.tile0[g] + tj) * blk;   // block of tile (0, tj)
+            const uint8_t* sb = a.stage + 2 * ntiles * 2048 + (int64_t)(a.tile0[g] + tj) * tailB - kStageTail;
             const int64_t c0 = 64 * (int64_t)tj;
             b.lines = (int)min((int64_t)64, C - c0);
             b.T = (int32_t)((Rg + 63) / 64);
-            b.tstride = (int64_t)a.tiles_c * blk;
+            b.tstride = (int64_t)a.tiles_c * tailB;
             if (kind == 3) {
                 b.P = (int32_t)(Rg / 2);
                 b.U = 32;
-                b.in = sb + kStageColCodes;
+                b.in = a.stage + (ntiles + a.tile0[g] + (int64_t)tj * b.T) * 2048;
+                b.tstride = 2048;
                 b.dst = a.col_codes + a.row0[g] * (C / 2) + c0 * b.P;
             } else if (kind == 4) {
                 b.P = (int32_t)(Rg / 16);

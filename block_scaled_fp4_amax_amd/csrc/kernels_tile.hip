@@ -411,7 +411,7 @@ void k_tile(TileArgs a)
     auto emit_tail = [&](int par) {
         const int n16 = tail_bytes / 16;
         const uint4 v = tail[par * (kTailCap / 16) + min(tid, n16 - 1)];
-        buf_store16(make_rsrc(prev_blk), (prev_ok && tid < n16) ? (uint32_t)(kStageTail + 16 * tid) : kOff, v);
+        buf_store16(make_rsrc(prev_blk), (prev_ok && tid < n16) ? (uint32_t)(16 * tid) : kOff, v);
     };
 
     // One tile: row phase, LDS transpose, column phase.  Writes the dequantised
@@ -741,11 +741,12 @@ void k_tile(TileArgs a)
             DirOut ro, co;
             tile_body(cur, in, ro, co);
             const bool ok = cur.rows_valid > 0 && cur.cols_valid > 0;
-            const uint8_t* blk = a.stage + (int64_t)st.t * a.stage_block;
-            const rsrc_t rb = make_rsrc(blk);
-            buf_store8(rb, ok ? (uint32_t)(r * 32 + sg * 8) : kOff, ro.codes);
-            buf_store8(rb, ok ? (uint32_t)(kStageColCodes + cc * 32 + rs * 8) : kOff, co.codes);
-            prev_blk = blk;
+            const int64_t ntiles = a.total_tiles;
+            const int tr = (cur.Rg + 63) >> 6;
+            const int64_t cidx = (int64_t)a.tile0[GROUPED ? cur.g : 0] + (int64_t)cur.tj * tr + cur.ti;
+            buf_store8(make_rsrc(a.stage + (int64_t)st.t * 2048), ok ? (uint32_t)(r * 32 + sg * 8) : kOff, ro.codes);
+            buf_store8(make_rsrc(a.stage + (ntiles + cidx) * 2048), ok ? (uint32_t)(cc * 32 + rs * 8) : kOff, co.codes);
+            prev_blk = a.stage + 2 * ntiles * 2048 + (int64_t)st.t * (a.stage_block - kStageTail);
             prev_ok = ok;
             if (!has_next) break;
             st = nst;

@@ -65,26 +65,33 @@ struct TileArgs {
     // Staged output (cast-transpose calls with an error-feedback residual, see
     // stage_applies): when `stage` is set, the walk unit is one 64 x 64 tile
     // (tiles_c = ceil(cols / 64), tile0 in tiles) and every code, scale byte and
-    // 1D outer scale goes to block `unit index` of `stage` (stage_block bytes,
+    // 1D outer scale goes to the staging area (stage_block bytes per tile,
     // layout below) as whole 128-byte lines; the host then launches the
-    // gather (launch_gather) that moves the blocks into the row-major outputs.
+    // gather (launch_gather) that moves them into the row-major outputs.
     uint8_t* stage;          // 128-byte aligned, or null for direct stores
     int32_t stage_block;     // bytes per tile block
 };
 
 enum OuterKind { kOuterNone = 0, kOuterTensor = 1, kOuter1D = 2, kOuter2D = 3 };
 
-// Staged tile block (bytes, offsets from the block start; every part a
-// multiple of 128 bytes):
-//   [0, 2048)       rowwise codes   [64 rows][32 bytes]
-//   [2048, 4096)    columnwise codes [64 columns][32 bytes]
-//   [4096, 4352)    rowwise scale bytes [64 rows][4]
-//   [4352, 4608)    columnwise scale bytes [64 columns][4]
-//   1D outer groups of obs (16, 32, 64) elements:
-//   [4608, +ob)     rowwise outer scales [64 rows][64 / obs] FP32
-//   [4608 + ob, +ob) columnwise outer scales [64 columns][64 / obs] FP32
-// with ob = 64 * (64 / obs) * 4.
-constexpr int32_t kStageColCodes = 2048;
+// Staging area of a launch of T tiles, T * stage_block bytes in three regions,
+// every part a multiple of 128 bytes:
+//   [0, 2048 T)          rowwise codes, tile t's [64 rows][32 bytes] at 2048 t
+//                        (t in the launch's row-major tile order);
+//   [2048 T, 4096 T)     columnwise codes, tile (g, ti, tj)'s [64 columns][32
+//                        bytes] at 2048 (T + tile0[g] + tj * tiles_r(g) + ti),
+//                        i.e. each group's tiles column by column;
+//   [4096 T, ...)        per tile t, at (stage_block - 4096) t, its tail:
+//     [0, 256)           rowwise scale bytes [64 rows][4]
+//     [256, 512)         columnwise scale bytes [64 columns][4]
+//     1D outer groups of obs (16, 32, 64) elements:
+//     [512, +ob)         rowwise outer scales [64 rows][64 / obs] FP32
+//     [512 + ob, +ob)    columnwise outer scales [64 columns][64 / obs] FP32
+//   with ob = 64 * (64 / obs) * 4.
+// So the gather reads each row band's and each column band's codes as one
+// contiguous run (grouped 32 x 2880^2 step: 678 -> 672 us against per-tile
+// blocks holding all four parts).  kStageTail and kStageRowOuter are the tail
+// parts' offsets plus 4096, as if the tail followed the two code blocks.
 constexpr int32_t kStageTail = 4096;      // scales and outer scales, staged in LDS
 constexpr int32_t kStageRowOuter = 4608;
 
