@@ -274,9 +274,14 @@ __global__ __launch_bounds__(kThreads) void k_gather(GatherArgs a)
     const int64_t C = a.cols;
     const int nrb = a.tile0[a.ngroups] / a.tiles_c;    // 64-row bands in the launch
     const int opr = a.obs ? 64 / a.obs : 0;           // 1D outer groups per tile row
+    // staging regions (launch.h): row codes, column codes, then one tail of
+    // tailB bytes per tile; `sb` below is where a tile's tail would start if
+    // it followed 4096 bytes of codes, so the tail parts sit at sb +
+    // kStageTail (scale bytes) and sb + kStageRowOuter (1D outer scales)
     const int64_t blk = a.stage_block;
     const int64_t ntiles = a.tile0[a.ngroups];
     const int64_t tailB = blk - kStageTail;
+    const uint8_t* const tails = a.stage + 2 * ntiles * kStageCodes;
     const int units = a.kind_units[6];
     for (int u = blockIdx.x; u < units; u += gridDim.x) {
         int kind = 0;
@@ -302,15 +307,15 @@ __global__ __launch_bounds__(kThreads) void k_gather(GatherArgs a)
             const int Rg = a.row0[g + 1] - a.row0[g];
             const int64_t grow = a.row0[g] + 64 * ti;
             const int64_t f = a.tile0[g] + ti * a.tiles_c;                       // tile (ti, 0)
-            const uint8_t* sb = a.stage + 2 * ntiles * 2048 + f * tailB - kStageTail;
+            const uint8_t* sb = tails + f * tailB - kStageTail;
             b.lines = min(64, Rg - 64 * ti);
             b.T = a.tiles_c;
             b.tstride = tailB;
             if (kind == 0) {
                 b.P = (int32_t)(C / 2);
                 b.U = 32;
-                b.in = a.stage + f * 2048;
-                b.tstride = 2048;
+                b.in = a.stage + f * kStageCodes;                                  // band's run of row codes
+                b.tstride = kStageCodes;
                 b.dst = a.row_codes + grow * b.P;
             } else if (kind == 1) {
                 b.P = (int32_t)(C / 16);
@@ -328,7 +333,7 @@ __global__ __launch_bounds__(kThreads) void k_gather(GatherArgs a)
             const int g = band / a.tiles_c;
             const int tj = band - g * a.tiles_c;
             const int64_t Rg = a.row0[g + 1] - a.row0[g];
-            const uint8_t* sb = a.stage + 2 * ntiles * 2048 + (int64_t)(a.tile0[g] + tj) * tailB - kStageTail;
+            const uint8_t* sb = tails + (int64_t)(a.tile0[g] + tj) * tailB - kStageTail;   // tile (0, tj)
             const int64_t c0 = 64 * (int64_t)tj;
             b.lines = (int)min((int64_t)64, C - c0);
             b.T = (int32_t)((Rg + 63) / 64);
@@ -336,8 +341,8 @@ __global__ __launch_bounds__(kThreads) void k_gather(GatherArgs a)
             if (kind == 3) {
                 b.P = (int32_t)(Rg / 2);
                 b.U = 32;
-                b.in = a.stage + (ntiles + a.tile0[g] + (int64_t)tj * b.T) * 2048;
-                b.tstride = 2048;
+                b.in = a.stage + (ntiles + a.tile0[g] + (int64_t)tj * b.T) * kStageCodes;   // band's run
+                b.tstride = kStageCodes;
                 b.dst = a.col_codes + a.row0[g] * (C / 2) + c0 * b.P;
             } else if (kind == 4) {
                 b.P = (int32_t)(Rg / 16);

@@ -741,12 +741,16 @@ void k_tile(TileArgs a)
             DirOut ro, co;
             tile_body(cur, in, ro, co);
             const bool ok = cur.rows_valid > 0 && cur.cols_valid > 0;
+            // staging regions (launch.h): row codes by tile index, column
+            // codes by the tile's column-major index in its group, tails
             const int64_t ntiles = a.total_tiles;
-            const int tr = (cur.Rg + 63) >> 6;
+            const int tr = (cur.Rg + 63) >> 6;                   // tile rows of the group
             const int64_t cidx = (int64_t)a.tile0[GROUPED ? cur.g : 0] + (int64_t)cur.tj * tr + cur.ti;
-            buf_store8(make_rsrc(a.stage + (int64_t)st.t * 2048), ok ? (uint32_t)(r * 32 + sg * 8) : kOff, ro.codes);
-            buf_store8(make_rsrc(a.stage + (ntiles + cidx) * 2048), ok ? (uint32_t)(cc * 32 + rs * 8) : kOff, co.codes);
-            prev_blk = a.stage + 2 * ntiles * 2048 + (int64_t)st.t * (a.stage_block - kStageTail);
+            buf_store8(make_rsrc(a.stage + (int64_t)st.t * kStageCodes), ok ? (uint32_t)(r * 32 + sg * 8) : kOff,
+                       ro.codes);
+            buf_store8(make_rsrc(a.stage + (ntiles + cidx) * kStageCodes), ok ? (uint32_t)(cc * 32 + rs * 8) : kOff,
+                       co.codes);
+            prev_blk = a.stage + 2 * ntiles * kStageCodes + (int64_t)st.t * (a.stage_block - kStageTail);
             prev_ok = ok;
             if (!has_next) break;
             st = nst;

@@ -92,6 +92,7 @@ enum OuterKind { kOuterNone = 0, kOuterTensor = 1, kOuter1D = 2, kOuter2D = 3 };
 // contiguous run (grouped 32 x 2880^2 step: 678 -> 672 us against per-tile
 // blocks holding all four parts).  kStageTail and kStageRowOuter are the tail
 // parts' offsets plus 4096, as if the tail followed the two code blocks.
+constexpr int32_t kStageCodes = 2048;     // one tile's codes of one direction
 constexpr int32_t kStageTail = 4096;      // scales and outer scales, staged in LDS
 constexpr int32_t kStageRowOuter = 4608;
 
