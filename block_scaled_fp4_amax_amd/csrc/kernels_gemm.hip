@@ -335,7 +335,7 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemm(GemmArgs g)
 }
 
 // Direct-to-LDS variant for the GEMM-ready scale layout.  gfx950's buffer loads
-// with the LDS flag write a wave's 64 results (16 or 4 bytes each) to 64
+// with the LDS flag write a wave's 64 results (16 bytes each here) to 64
 // consecutive LDS slots at a wave-uniform base, bypassing registers, so a
 // K-tile moves into LDS without register staging or LDS write instructions.
 // Two buffers: K-tile kt + 1 is requested right after the barrier that opens
@@ -343,18 +343,20 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemm(GemmArgs g)
 // overwrites); the first two K-tiles are requested before the loop.  Slot l of
 // code block b (1 KiB, rows 8 b .. 8 b + 7) receives row 8 b + l / 8, stored
 // chunk l % 8, i.e. K-chunk (l % 8) ^ ((row / 2) & 7) of the row: the same
-// swizzled layout the register-staged kernel writes.  Scale words go to two
-// planes (low and high four bytes of a row's eight).  The loads are issued from
-// inline assembly with explicit waits: the compiler's own wait insertion cannot
-// tell the two buffers apart and would wait for the next K-tile's loads before
-// every read of the current one.  Only waves 0..3 (one per SIMD) load.  A
+// swizzled layout the register-staged kernel writes.  Scale rows (eight bytes
+// each) arrive two per lane: issuing a load costs about the same whatever its
+// width, and four 4-byte scale loads per loading wave took 2% longer (8192^3:
+// 285 against 279 us).  The loads are issued from inline assembly with
+// explicit waits: the compiler's own wait insertion cannot tell the two
+// buffers apart and would wait for the next K-tile's loads before every read
+// of the current one.  Only waves 0..3 (one per SIMD) load.  A
 // burst of load instructions issues slowly (the K-tile's 68 KiB enter the CU at
 // the rate its memory path accepts them), and a wave that is issuing loads
 // issues no matrix instructions: with the loads on one wave of each SIMD, the
 // SIMD's other wave keeps the matrix pipe fed meanwhile.
 struct SmemLds {
     uint4 code[2][2][kChunks];                 // [buffer][A, B][chunk]         128 KiB
-    uint32_t scale[2][2][2][kBM];              // [buffer][A, B][low, high][row]  8 KiB
+    uint2 scale[2][2][kBM];                    // [buffer][A, B][row]  8 KiB
 };
 
 // The loads set m0 (the LDS base) themselves; no other instruction of these
@@ -369,13 +371,6 @@ __device__ __forceinline__ void lds_load16(rsrc_t r, uint32_t voff, uint32_t lds
                  : "memory", "m0");
 }
 
-__device__ __forceinline__ void lds_load4(rsrc_t r, uint32_t voff, uint32_t lds_base)
-{
-    asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dword %0, %2, 0 offen lds"
-                 :
-                 : "v"(voff), "s"(lds_base), "s"(r)
-                 : "memory", "m0");
-}
 #pragma clang diagnostic pop
 
 // wait until at most N of this wave's vector-memory loads are outstanding
@@ -392,9 +387,9 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p)
         (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p);
 }
 
-// The twenty loads of K-tile kt into buffer buf issued by wave w < 4: code
-// blocks 8 w .. 8 w + 7 of A and of B, and the scale words of rows 64 w ..
-// 64 w + 63 of A and of B.  Waves 4..7 load nothing.  Codes beyond the rows or
+// The seventeen loads of K-tile kt into buffer buf issued by wave w < 4: code
+// blocks 8 w .. 8 w + 7 of A and of B, and one 1 KiB block of scale rows.
+// Waves 4..7 load nothing.  Codes beyond the rows or
 // K load as zeros; the tiled scales are zero-padded.
 __device__ __forceinline__ void lds_tile(const GemmArgs& g, SmemLds& sm, const rsrc_t& ra, const rsrc_t& rb,
                                          const rsrc_t& ras, const rsrc_t& rbs, int kt, int rows_a, int rows_b,
@@ -415,16 +410,13 @@ __device__ __forceinline__ void lds_tile(const GemmArgs& g, SmemLds& sm, const r
             lds_load16(o ? rb : ra, off, lds_addr(&sm.code[buf][o][b * 64]));
         }
     }
-    const int r0 = 64 * wave;
-    const uint32_t off = (uint32_t)((kt * kBM + r0 + lane) * 8);
-#pragma unroll
-    for (int o = 0; o < 2; ++o) {
-        lds_load4(o ? rbs : ras, off, lds_addr(&sm.scale[buf][o][0][r0]));
-        lds_load4(o ? rbs : ras, off + 4, lds_addr(&sm.scale[buf][o][1][r0]));
-    }
+    // scale rows: wave w takes rows 128 (w & 1) .. + 127 of operand w >> 1,
+    // two 8-byte rows per lane
+    const int o = wave >> 1, r0 = 128 * (wave & 1);
+    lds_load16(o ? rbs : ras, (uint32_t)((kt * kBM + r0) * 8 + 16 * lane), lds_addr(&sm.scale[buf][o][r0]));
 }
 
-constexpr int kLdsLoadsPerTile = 20;           // per loading wave
+constexpr int kLdsLoadsPerTile = 17;           // per loading wave
 
 template <bool CF32>
 __global__ __launch_bounds__(kThreads) void k_mx_gemm_lds(GemmArgs g)
@@ -469,12 +461,12 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemm_lds(GemmArgs g)
 #pragma unroll
         for (int i = 0; i < kTM; ++i) {
             const int r = wm * 32 * kTM + i * 32 + lr;
-            sa[i] = make_uint2(sm.scale[cur][0][0][r], sm.scale[cur][0][1][r]);
+            sa[i] = sm.scale[cur][0][r];
         }
 #pragma unroll
         for (int j = 0; j < kTN; ++j) {
             const int r = wn * 32 * kTN + j * 32 + lr;
-            sb[j] = make_uint2(sm.scale[cur][1][0][r], sm.scale[cur][1][1][r]);
+            sb[j] = sm.scale[cur][1][r];
         }
         v8i_t av[2][kTM], bv[2][kTN];
         auto read_ops = [&](int ks, int p) __attribute__((always_inline)) {
